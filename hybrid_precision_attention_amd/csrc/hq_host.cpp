@@ -1,0 +1,195 @@
+// Host side of libhq: the extern "C" entry points declared in include/hq.h.
+//
+// Every check runs here, before anything is launched, so that a bad call
+// returns an error without touching device memory (and can be exercised on a
+// machine without a GPU).  Launch configuration and workspace sizing also
+// live here; the kernels themselves are in the *.hip files.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "hq.h"
+#include "hq_launch.h"
+
+namespace hq {
+
+namespace {
+
+constexpr int kMaxGroup = 16;      // query heads per KV head handled by one MFMA tile
+constexpr int kDecodeTargetWG = 512;   // workgroups a decode launch aims for
+constexpr int kDecodeWaves = 4;        // waves per decode workgroup
+constexpr int kBlk = 32;               // tokens per decode block
+constexpr int kPartFloats = 132;       // m, l, 2 pad, o[128]
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dims(const hq_dims* d) {
+  if (!d) return HQ_ERR_ARG;
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return HQ_ERR_ARG;
+  if (d->W < 0 || d->cap_q < 0 || d->cap_vl < 0 || d->cap_stg < 0) return HQ_ERR_ARG;
+  if (!(d->rho >= 0.0 && d->rho <= 1.0)) return HQ_ERR_ARG;
+  if (d->d != 128) return HQ_ERR_UNSUPPORTED;
+  if (d->Hq / d->Hkv > kMaxGroup) return HQ_ERR_UNSUPPORTED;
+  // keep every flat index comfortably inside int64 and every per-unit row
+  // count inside int32
+  const int64_t units = static_cast<int64_t>(d->B) * d->Hkv;
+  if (units > (1 << 24)) return HQ_ERR_ARG;
+  return HQ_OK;
+}
+
+int check_cache(const hq_dims& d, const hq_cache* c) {
+  if (!c) return HQ_ERR_ARG;
+  const void* must[] = {c->kq, c->vq, c->kq_meta, c->vq_meta, c->q_pos, c->kvl, c->vvl,
+                        c->vl_pos, c->kstg, c->vstg, c->n_q, c->n_vl, c->n_stg};
+  for (const void* p : must)
+    if (!p) return HQ_ERR_ARG;
+  if (d.W > 0 && (!c->kwin || !c->vwin)) return HQ_ERR_ARG;
+  for (const void* p : must)
+    if (!aligned16(p)) return HQ_ERR_ALIGN;
+  if (d.W > 0 && (!aligned16(c->kwin) || !aligned16(c->vwin))) return HQ_ERR_ALIGN;
+  return HQ_OK;
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int32_t n_vertical(double rho, int32_t n_nw) {
+  if (n_nw <= 0) return 0;
+  return static_cast<int32_t>(floor(rho * static_cast<double>(n_nw) + 1e-6));
+}
+
+DecodePlan plan_decode(const hq_dims& d, int32_t L) {
+  const int64_t units = static_cast<int64_t>(d.B) * d.Hkv;
+  const int32_t n_nw = std::max<int32_t>(0, L - d.W);
+  const int32_t n_vl = std::min(n_vertical(d.rho, n_nw), d.cap_vl);
+  const int64_t n_q = std::max<int32_t>(0, n_nw - n_vl);
+  const int32_t n_win = std::min(d.W, L);
+  const int64_t n_f = static_cast<int64_t>(n_vl) + n_win + d.cap_stg;
+  const double bq = 160.0 * static_cast<double>(n_q);
+  const double bf = 512.0 * static_cast<double>(n_f);
+  const int64_t cap = std::max<int64_t>(1, cdiv(kDecodeTargetWG, units));
+  const double fq = (bq + bf) > 0 ? bq / (bq + bf) : 0.5;
+  int64_t nq = std::llround(static_cast<double>(cap) * fq);
+  int64_t nf = std::llround(static_cast<double>(cap) * (1.0 - fq));
+  nq = std::max<int64_t>(1, std::min<int64_t>(nq, std::max<int64_t>(1, cdiv(cdiv(n_q, kBlk), 4 * kDecodeWaves))));
+  nf = std::max<int64_t>(1, std::min<int64_t>(nf, std::max<int64_t>(1, cdiv(cdiv(n_f, kBlk), kDecodeWaves))));
+  DecodePlan p;
+  p.nsplit_q = static_cast<int>(nq);
+  p.nsplit_f = static_cast<int>(nf);
+  p.n_win = n_win;
+  return p;
+}
+
+size_t decode_counter_bytes(const hq_dims& d) {
+  const size_t units = static_cast<size_t>(d.B) * d.Hkv;
+  return (units * 4 + 255) / 256 * 256;
+}
+
+size_t decode_ws_bytes(const hq_dims& d, int32_t /*L_max*/) {
+  // plan_decode never exceeds cap + 2 splits per unit, whatever L is
+  const size_t units = static_cast<size_t>(d.B) * d.Hkv;
+  const size_t cap = std::max<size_t>(1, (kDecodeTargetWG + units - 1) / units);
+  const size_t G = static_cast<size_t>(d.Hq / d.Hkv);
+  return decode_counter_bytes(d) + units * (cap + 2) * G * kPartFloats * sizeof(float);
+}
+
+}  // namespace hq
+
+using namespace hq;
+
+extern "C" {
+
+int hq_abi_version(void) { return 1; }
+
+const char* hq_status_string(int status) {
+  switch (status) {
+    case HQ_OK: return "ok";
+    case HQ_ERR_ARG: return "invalid argument (null pointer, shape or range)";
+    case HQ_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 128, Hq/Hkv <= 16)";
+    case HQ_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case HQ_ERR_CAPACITY: return "cache region capacity too small";
+    case HQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case HQ_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t hq_workspace_bytes(const hq_dims* dims, int op, int32_t L_max) {
+  if (check_dims(dims) != HQ_OK || L_max < 0) return 0;
+  if (op == HQ_OP_DECODE) return decode_ws_bytes(*dims, L_max);
+  if (op == HQ_OP_SELECT) return L_max >= 1 ? select_ws_bytes(*dims, L_max) : 0;
+  return 0;
+}
+
+int hq_quant_pack(const hq_dims* dims, const uint16_t* k, const uint16_t* v, int32_t L,
+                  const uint8_t* vl_flag, const hq_cache* cache, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L < 0) return HQ_ERR_ARG;
+  if (L > 0 && (!k || !v || !vl_flag)) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (L > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(vl_flag))) return HQ_ERR_ALIGN;
+  if (dims->cap_q < std::max(0, L - dims->W)) return HQ_ERR_CAPACITY;
+  if (launch_quant_pack(*dims, k, v, L, vl_flag, *cache, stream) != hipSuccess) return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_append_merge(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                    const uint16_t* k_new, const uint16_t* v_new,
+                    const uint8_t* evict_is_vl_or_null, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t < 0 || !k_new || !v_new) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(k_new) || !aligned16(v_new)) return HQ_ERR_ALIGN;
+  if (evict_is_vl_or_null && !aligned16(evict_is_vl_or_null)) return HQ_ERR_ALIGN;
+  if (dims->cap_stg < 1) return HQ_ERR_CAPACITY;
+  if (dims->cap_q < std::max(0, t - dims->W)) return HQ_ERR_CAPACITY;
+  if (launch_append_merge(*dims, *cache, t, k_new, v_new, evict_is_vl_or_null, stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L, const uint16_t* q,
+                   uint16_t* out, float* lse_or_null, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L < 0 || !q || !out) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(q) || !aligned16(out)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  if (!ws || ws_bytes < decode_ws_bytes(*dims, L)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  const DecodePlan plan = plan_decode(*dims, L);
+  if (launch_decode(*dims, *cache, L, plan, q, out, lse_or_null, ws, stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_select_vertical(const hq_dims* dims, const uint16_t* qbuf, int32_t nb, const uint16_t* k,
+                       int32_t L, const float* lse_or_null, float* score_inout,
+                       int32_t* vl_idx, uint8_t* vl_flag, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L < 1 || nb < 1 || nb > 64 || nb > L) return HQ_ERR_ARG;
+  if (!qbuf || !k || !score_inout || !vl_flag) return HQ_ERR_ARG;
+  const int32_t n_vl = n_vertical(dims->rho, std::max(0, L - dims->W));
+  if (n_vl > 0 && !vl_idx) return HQ_ERR_ARG;
+  if (!aligned16(qbuf) || !aligned16(k) || !aligned16(score_inout) || !aligned16(vl_flag))
+    return HQ_ERR_ALIGN;
+  if (vl_idx && !aligned16(vl_idx)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  if (!ws || ws_bytes < select_ws_bytes(*dims, L)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  if (launch_select(*dims, qbuf, nb, k, L, lse_or_null, score_inout, vl_idx, vl_flag, ws,
+                    stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+}  // extern "C"

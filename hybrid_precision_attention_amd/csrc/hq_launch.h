@@ -1,0 +1,47 @@
+// Internal interface between the host entry points (hq_host.cpp) and the
+// kernel launchers (*.hip).  Arguments are validated before these are called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hq.h"
+
+namespace hq {
+
+// Decode split plan: how many workgroups scan the K4V4 region and the FP16
+// region (vertical lines + window + staging) of each unit.
+struct DecodePlan {
+  int nsplit_q;
+  int nsplit_f;
+  int n_win;          // valid window slots: min(W, L)
+};
+
+DecodePlan plan_decode(const hq_dims& d, int32_t L);
+size_t decode_ws_bytes(const hq_dims& d, int32_t L_max);
+size_t decode_counter_bytes(const hq_dims& d);
+
+size_t select_ws_bytes(const hq_dims& d, int32_t L_max);
+
+hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t* v,
+                             int32_t L, const uint8_t* vl_flag, const hq_cache& c,
+                             hipStream_t s);
+
+hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
+                               const uint16_t* k_new, const uint16_t* v_new,
+                               const uint8_t* evict_is_vl, hipStream_t s);
+
+hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L,
+                         const DecodePlan& plan, const uint16_t* q, uint16_t* out,
+                         float* lse, void* ws, hipStream_t s);
+
+hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb,
+                         const uint16_t* k, int32_t L, const float* lse_in,
+                         float* score, int32_t* vl_idx, uint8_t* vl_flag, void* ws,
+                         hipStream_t s);
+
+// floor(rho * n_nw + 1e-6): size of the vertical-line set of n_nw candidates.
+int32_t n_vertical(double rho, int32_t n_nw);
+
+}  // namespace hq

@@ -1,0 +1,228 @@
+// hq_quant_pack and hq_append_merge kernels for gfx950.
+//
+// Building the hybrid cache of a prefix (agihunt digest "HyQuant: Hybrid-
+// Precision Quantization for LLM Attention", method and decode paragraphs;
+// HyQuant README, Overview item 3): vertical-line tokens and the recent
+// window stay FP16, every other non-window token is quantised to K4V4 and
+// stored in ascending position.  New decode tokens are staged and then merged
+// into the hybrid layout, the token leaving the window being quantised.
+#include <hip/hip_runtime.h>
+
+#include "hq_device.h"
+#include "hq_launch.h"
+
+namespace hq {
+
+namespace {
+
+constexpr int kChunk = 256;     // prefix positions per pack workgroup
+constexpr int kPackThreads = 256;
+
+struct PackArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint8_t* flag;
+  hq_cache c;
+  int32_t L, W, cap_q, cap_vl;
+};
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One workgroup per (chunk of 256 positions, unit).  Each workgroup counts the
+// flagged non-window positions before its chunk, ranks its own positions, and
+// then quantises (K4V4) or copies (vertical line, window) its tokens with
+// eight threads per token: {K, V} x four groups of 32 elements.
+__global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
+  __shared__ int s_wave[4];
+  __shared__ int s_kind[kChunk];
+  __shared__ int s_slot[kChunk];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t u = blockIdx.y;
+  const int L = a.L, W = a.W;
+  const int n_nw = max(0, L - W);
+  const int p0 = blockIdx.x * kChunk;
+  const int p1 = min(L, p0 + kChunk);
+  const uint8_t* flag = a.flag + u * L;
+
+  // flagged non-window positions before this chunk
+  int cnt = 0;
+  const int lim = min(p0, n_nw);
+  for (int i = tid; i < lim; i += kPackThreads) cnt += flag[i] != 0;
+  cnt = wave_sum(cnt);
+  if (lane == 0) s_wave[wave] = cnt;
+  __syncthreads();
+  const int before = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+  __syncthreads();
+
+  // rank of each flagged position inside the chunk
+  const int p = p0 + tid;
+  const int f = (p < p1 && p < n_nw && flag[p] != 0) ? 1 : 0;
+  const uint64_t bal = __ballot(f);
+  const int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wave[wave] = __popcll(bal);
+  __syncthreads();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += s_wave[w];
+  const int chunk_total = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+  const int flagged_before = before + wave_off + in_wave;   // raw, before p
+  const int vl_before = min(flagged_before, a.cap_vl);      // stored VL tokens before p
+
+  int kind = 0, slot = 0;                                   // 0 none, 1 K4, 2 VL, 3 window
+  if (p < p1) {
+    if (p >= n_nw) {
+      kind = 3;
+      slot = p % W;
+    } else if (f && flagged_before < a.cap_vl) {
+      kind = 2;
+      slot = flagged_before;
+      a.c.vl_pos[u * a.cap_vl + slot] = p;
+    } else {
+      kind = 1;
+      slot = p - vl_before;
+      a.c.q_pos[u * a.cap_q + slot] = p;
+    }
+  }
+  s_kind[tid] = kind;
+  s_slot[tid] = slot;
+  if (p1 == L && tid == 0) {          // the last chunk of the unit sets the counters
+    const int n_vl = min(before + chunk_total, a.cap_vl);
+    a.c.n_vl[u] = n_vl;
+    a.c.n_q[u] = n_nw - n_vl;
+    a.c.n_stg[u] = 0;
+  }
+  __syncthreads();
+
+  const int sub = tid & 7;            // {K,V} x group
+  const int kv = sub >> 2, g = sub & 3;
+  for (int t0 = 0; t0 < kChunk; t0 += kPackThreads / 8) {
+    const int tl = t0 + (tid >> 3);
+    const int pp = p0 + tl;
+    if (pp >= p1) break;
+    const int knd = s_kind[tl], sl = s_slot[tl];
+    const uint16_t* src = (kv ? a.v : a.k) + (u * L + pp) * kD + g * kGroup;
+    uint32_t x[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w4 = ld16(src + 8 * i);
+      x[4 * i + 0] = w4.x; x[4 * i + 1] = w4.y; x[4 * i + 2] = w4.z; x[4 * i + 3] = w4.w;
+    }
+    if (knd == 1) {
+      uint32_t codes[4], meta;
+      quant_group32(x, codes, &meta);
+      uint8_t* dst = (kv ? a.c.vq : a.c.kq) + (u * a.cap_q + sl) * kRowBytes + g * 16;
+      st16(dst, make_uint4(codes[0], codes[1], codes[2], codes[3]));
+      uint32_t* md = reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta);
+      md[(u * a.cap_q + sl) * kMetaWords + g] = meta;
+    } else {
+      uint16_t* dst;
+      if (knd == 2) dst = (kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + sl) * kD + g * kGroup;
+      else dst = (kv ? a.c.vwin : a.c.kwin) + (u * W + sl) * kD + g * kGroup;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st16(dst + 8 * i, make_uint4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]));
+    }
+  }
+}
+
+struct MergeArgs {
+  hq_cache c;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const uint8_t* evict_is_vl;
+  int32_t t, W, cap_q, cap_vl, cap_stg;
+};
+
+// One wave per unit.  Lanes 0-15 carry the K row, lanes 16-31 the V row, 16
+// bytes each.  The token leaving the window is either copied to the
+// vertical-line region or quantised by eight lanes (K/V x four groups) after
+// a pass through LDS.
+__global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
+  __shared__ uint32_t s_row[2][kD / 2];
+  const int lane = threadIdx.x;
+  const int64_t u = blockIdx.x;
+  const bool mover = lane < 32;
+  const int kv = (lane >> 4) & 1, part = lane & 15;
+  const int W = a.W, t = a.t;
+  const int nstg = a.c.n_stg[u];
+  const int nq = a.c.n_q[u];
+  const int nvl = a.c.n_vl[u];
+  uint16_t* stg = (kv ? a.c.vstg : a.c.kstg) + u * a.cap_stg * kD + 8 * part;
+
+  if (nstg > 0) {
+    const uint4 staged = mover ? ld16(stg) : make_uint4(0, 0, 0, 0);
+    int ev = -1;
+    uint4 evv = staged;
+    uint16_t* win = nullptr;
+    if (W > 0) {
+      const int slot = (t - 1) % W;
+      win = (kv ? a.c.vwin : a.c.kwin) + (u * W + slot) * kD + 8 * part;
+      ev = t - 1 - W;
+      if (ev >= 0 && mover) evv = ld16(win);
+    } else {
+      ev = t - 1;
+    }
+    if (ev >= 0) {
+      const bool to_vl = a.evict_is_vl && a.evict_is_vl[u] != 0 && nvl < a.cap_vl;
+      if (to_vl) {
+        if (mover) st16((kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + nvl) * kD + 8 * part, evv);
+        if (lane == 0) {
+          a.c.vl_pos[u * a.cap_vl + nvl] = ev;
+          a.c.n_vl[u] = nvl + 1;
+        }
+      } else if (nq < a.cap_q) {
+        if (mover) {
+          s_row[kv][4 * part + 0] = evv.x;
+          s_row[kv][4 * part + 1] = evv.y;
+          s_row[kv][4 * part + 2] = evv.z;
+          s_row[kv][4 * part + 3] = evv.w;
+        }
+        __syncthreads();
+        if (lane < 8) {
+          const int qkv = lane >> 2, g = lane & 3;
+          uint32_t x[16], codes[4], meta;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = s_row[qkv][16 * g + i];
+          quant_group32(x, codes, &meta);
+          st16((qkv ? a.c.vq : a.c.kq) + (u * a.cap_q + nq) * kRowBytes + g * 16,
+               make_uint4(codes[0], codes[1], codes[2], codes[3]));
+          reinterpret_cast<uint32_t*>(qkv ? a.c.vq_meta : a.c.kq_meta)
+              [(u * a.cap_q + nq) * kMetaWords + g] = meta;
+        }
+        if (lane == 0) {
+          a.c.q_pos[u * a.cap_q + nq] = ev;
+          a.c.n_q[u] = nq + 1;
+        }
+      }
+    }
+    if (W > 0 && mover) st16(win, staged);
+  }
+  const uint16_t* src = (kv ? a.v_new : a.k_new) + u * kD + 8 * part;
+  if (mover) st16(stg, ld16(src));
+  if (lane == 0) a.c.n_stg[u] = 1;
+}
+
+}  // namespace
+
+hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t* v, int32_t L,
+                             const uint8_t* vl_flag, const hq_cache& c, hipStream_t s) {
+  PackArgs a{k, v, vl_flag, c, L, d.W, d.cap_q, d.cap_vl};
+  const int chunks = L > 0 ? (L + kChunk - 1) / kChunk : 1;
+  dim3 grid(chunks, d.B * d.Hkv);
+  hipLaunchKernelGGL(quant_pack_kernel, grid, dim3(kPackThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
+                               const uint16_t* k_new, const uint16_t* v_new,
+                               const uint8_t* evict_is_vl, hipStream_t s) {
+  MergeArgs a{c, k_new, v_new, evict_is_vl, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+  hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hq

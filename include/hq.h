@@ -1,0 +1,199 @@
+/*
+ * hq.h -- C ABI of the hybrid K4V4/FP16 decode-attention library (libhq.so).
+ *
+ * The method (HyQuant: hybrid-precision quantization for LLM attention) keeps
+ * a small set of "vertical-line" key positions and the most recent window of
+ * W tokens in FP16, stores every other cached token as packed 4-bit keys and
+ * values (K4V4), and fuses the dequantisation into the decode attention scan
+ * so no full-precision cache is ever materialised.  Sources, by page title:
+ *   - agihunt.info digest "HyQuant: Hybrid-Precision Quantization for LLM
+ *     Attention", method paragraph: the three-way key partition (vertical
+ *     lines / recent window / quantised rest), the column-attention-mass
+ *     score, top-rho over the non-window prefix (default 5 %), at most 64
+ *     buffered FP16 queries, a lightweight reduction every 64 tokens;
+ *     decode paragraph: dequantisation fused into the attention scan, the
+ *     vertical-line set chosen on prefill-tail queries and kept fixed during
+ *     decode, new tokens staged first and then merged into the hybrid layout.
+ *   - HyQuant README, "Overview" items 1 and 3 (running column-mass score;
+ *     K4V4 + FP16 cache, online softmax over quantised blocks), "Overhead"
+ *     and "Mode reference" (window_size, top_ratio).
+ *
+ * 4-bit layout (the pages say only "K4V4"; this library fixes it): per token
+ * and per group of 32 consecutive head_dim elements, asymmetric uint4 codes
+ * with an fp16 {scale, min}: scale = fp16_rne((max - min) / 15), code =
+ * clamp(round_half_even((x - min) / scale), 0, 15) (all 0 when scale == 0),
+ * x_hat = code * scale + min.  Byte j of a packed row holds element 2j in the
+ * low nibble and element 2j+1 in the high nibble.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
+ *     16-byte aligned (HQ_ERR_ALIGN otherwise).  fp16 data is passed as the
+ *     raw uint16_t bit patterns.  The library allocates nothing and keeps no
+ *     state between calls.
+ *   - Calls are asynchronous on `stream`.  All argument checks run on the host
+ *     before anything is launched; on an error nothing is launched and no
+ *     output is touched.  A launch failure returns HQ_ERR_HIP.
+ *   - head_dim d must be 128 (HQ_ERR_UNSUPPORTED otherwise); Hq % Hkv == 0;
+ *     query head h uses KV head h / (Hq / Hkv).  A "unit" is one
+ *     (sequence b, KV head) pair; units are independent.
+ *   - The softmax scale is 1/sqrt(d); logsumexp outputs are natural-log.
+ *   - Calls that write the same cache or workspace must not run concurrently
+ *     on different streams.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HQ_OK               0
+#define HQ_ERR_ARG         -1   /* null pointer, bad shape or out-of-range scalar */
+#define HQ_ERR_UNSUPPORTED -2   /* head_dim other than 128 */
+#define HQ_ERR_ALIGN       -3   /* a tensor pointer not 16-byte aligned */
+#define HQ_ERR_CAPACITY    -4   /* a cache region too small for the request */
+#define HQ_ERR_WORKSPACE   -5   /* workspace missing or smaller than required */
+#define HQ_ERR_HIP         -6   /* a HIP launch or runtime call failed */
+
+/* Problem shape: batch, query/KV heads, head_dim, window W, vertical-line
+ * ratio rho in [0, 1], and the capacities (tokens per unit) of the K4V4,
+ * vertical-line and staging regions of a cache. */
+typedef struct {
+  int32_t B, Hq, Hkv, d;
+  int32_t W;
+  double rho;
+  int32_t cap_q, cap_vl, cap_stg;
+} hq_dims;
+
+/* One layer's hybrid cache.  u = b * Hkv + kv_head indexes the units.
+ *   kq, vq        [B][Hkv][cap_q][d/2]     packed 4-bit K and V codes
+ *   kq_meta,      [B][Hkv][cap_q][d/32][2] fp16 {scale, min} per group
+ *   vq_meta
+ *   q_pos         [B][Hkv][cap_q]          source position of each K4V4 slot;
+ *                                          slots are in ascending position
+ *   kvl, vvl      [B][Hkv][cap_vl][d]      fp16 vertical-line tokens
+ *   vl_pos        [B][Hkv][cap_vl]         their positions
+ *   kwin, vwin    [B][Hkv][W][d]           fp16 window ring, slot = pos mod W
+ *   kstg, vstg    [B][Hkv][cap_stg][d]     fp16 staging (the newest token)
+ *   n_q, n_vl,    [B][Hkv]                 device counters: tokens held in the
+ *   n_stg                                  K4V4, vertical-line and staging
+ *                                          regions of each unit
+ * kwin/vwin may be NULL when W == 0. */
+typedef struct {
+  uint8_t *kq, *vq;
+  uint16_t *kq_meta, *vq_meta;
+  int32_t *q_pos;
+  uint16_t *kvl, *vvl;
+  int32_t *vl_pos;
+  uint16_t *kwin, *vwin;
+  uint16_t *kstg, *vstg;
+  int32_t *n_q, *n_vl, *n_stg;
+} hq_cache;
+
+/* Operation ids for hq_workspace_bytes. */
+#define HQ_OP_SELECT 1
+#define HQ_OP_DECODE 2
+
+/*
+ * hq_select_vertical -- column-mass score and top-rho vertical-line set
+ * (agihunt digest, method paragraph; README Overview item 1).
+ *
+ * For every unit, each buffered query j (position p_j = L - nb + j) of each
+ * query head of the unit's group has a causal softmax row over keys 0..p_j.
+ * The row's probabilities at the non-window columns i < L - W are summed over
+ * heads and queries and ADDED to score_inout[b][kvh][i] (a running score;
+ * zero it before the first refresh).  Columns i >= L - W are left unchanged.
+ * Then the n_vl = floor(rho * (L - W) + 1e-6) columns of [0, L - W) with the
+ * largest accumulated score are selected, ties going to the lower position.
+ *
+ *   qbuf        [B][Hq][nb][d] fp16, 1 <= nb <= min(64, L)
+ *   k           [B][Hkv][L][d] fp16 dense keys of the prefix
+ *   lse_or_null [B][Hq][nb] fp32 natural-log LSE of each buffered row, or
+ *               NULL to compute it here (a first pass over the keys)
+ *   score_inout [B][Hkv][L] fp32
+ *   vl_idx      [B][Hkv][n_vl] int32 out: selected positions, ascending
+ *   vl_flag     [B][Hkv][L] uint8 out: 1 at selected positions, else 0
+ *   ws          device workspace of at least
+ *               hq_workspace_bytes(dims, HQ_OP_SELECT, L) bytes
+ * Only dims->B, Hq, Hkv, d, W, rho are read.  Requires L >= 1.
+ */
+int hq_select_vertical(const hq_dims* dims, const uint16_t* qbuf, int32_t nb,
+                       const uint16_t* k, int32_t L, const float* lse_or_null,
+                       float* score_inout, int32_t* vl_idx, uint8_t* vl_flag,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hq_quant_pack -- build the hybrid cache of a prefix 0..L-1 (agihunt
+ * digest, decode paragraph; README Overview item 3).
+ *
+ * Window positions [max(0, L-W), L) are copied to ring slot (pos mod W).
+ * Non-window positions flagged in vl_flag [B][Hkv][L] are copied in
+ * ascending position to the vertical-line region (the first cap_vl of them;
+ * any beyond cap_vl are treated as unflagged).  Every other non-window
+ * position is quantised and stored in ascending position in the K4V4 region.
+ * Counters are set; nothing is staged (n_stg = 0).
+ * Requires cap_q >= max(0, L - W) (HQ_ERR_CAPACITY) and L >= 0.
+ */
+int hq_quant_pack(const hq_dims* dims, const uint16_t* k, const uint16_t* v,
+                  int32_t L, const uint8_t* vl_flag, const hq_cache* cache,
+                  hipStream_t stream);
+
+/*
+ * hq_append_merge -- stage the token at position t and merge the one staged
+ * before it (agihunt digest, decode paragraph).
+ *
+ * If a token is staged (position t-1): with W > 0 it moves to ring slot
+ * (t-1) mod W, and the token that slot held (position t-1-W, when >= 0)
+ * leaves the window; with W == 0 the staged token itself leaves.  A leaving
+ * token goes to the vertical-line region when evict_is_vl[u] is nonzero and
+ * the region has room, else it is quantised and appended to the K4V4 region.
+ * Then k_new/v_new [B][Hkv][d] fp16 are staged (n_stg = 1).
+ * evict_is_vl_or_null: [B][Hkv] uint8, or NULL for all zero (the fixed
+ * vertical-line set of the pages).  Requires cap_stg >= 1 and
+ * cap_q >= max(0, t - W) (HQ_ERR_CAPACITY), t >= 0.
+ */
+int hq_append_merge(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                    const uint16_t* k_new, const uint16_t* v_new,
+                    const uint8_t* evict_is_vl_or_null, hipStream_t stream);
+
+/*
+ * hq_decode_attn -- one decode query per head over the hybrid cache
+ * (agihunt digest, decode paragraph; README Overview item 3).
+ *
+ * Query q [B][Hq][d] fp16 at position L attends to the unit's K4V4 slots
+ * (dequantised in registers), its vertical-line tokens, the window ring
+ * positions [max(0, L-W), L) and the staged tokens, in one online softmax
+ * split over the sequence and merged by log-sum-exp.  Writes
+ * out [B][Hq][d] fp16 and, if lse_or_null is not NULL, the natural-log
+ * logsumexp [B][Hq] fp32.  A head with no keys at all gets out = 0 and
+ * lse = -inf.
+ *
+ * ws: at least hq_workspace_bytes(dims, HQ_OP_DECODE, L) bytes.  Its first
+ * 4*B*Hkv bytes are arrival counters that must be zero before the first call
+ * that uses this workspace (allocate it zero-filled); every completed call
+ * leaves them zero again.
+ * Requires L >= 0.
+ */
+int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L,
+                   const uint16_t* q, uint16_t* out, float* lse_or_null,
+                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes an operation needs for any prefix length up to L_max;
+ * 0 for an invalid request. */
+size_t hq_workspace_bytes(const hq_dims* dims, int op, int32_t L_max);
+
+/* Static description of a status code. */
+const char* hq_status_string(int status);
+
+/* Library ABI version (incremented on any change of this header). */
+int hq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */

@@ -149,15 +149,16 @@ def quantize_groups(X: np.ndarray):
     32 consecutive head_dim elements.
 
     min m and max M of the group; scale s = fp16(round-to-nearest-even of
-    (M - m) / 15); code = clamp(round-half-even((x - m) / s), 0, 15), all 0
-    when s == 0.  Every step is exact in fp64 before its single rounding.
+    (M - m) / 15); a zero minimum or a zero scale is stored as +0; code =
+    clamp(round-half-even((x - m) / s), 0, 15), all 0 when s == 0.  Every
+    step is exact in fp64 before its single rounding.
     Returns codes uint8 [n][d], scale fp16 [n][d/32], min fp16 [n][d/32].
     """
     n, d = X.shape
     x = X.astype(np.float64).reshape(n, d // GROUP, GROUP)
-    m = x.min(axis=2)
+    m = x.min(axis=2) + 0.0        # a zero minimum is stored as +0
     M = x.max(axis=2)
-    s16 = ((M - m) / QMAX).astype(np.float16)
+    s16 = (((M - m) + 0.0) / QMAX).astype(np.float16)   # a zero range gives scale +0
     s = s16.astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((x - m[:, :, None]) / s[:, :, None])

@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/hq.h declares, and rejects bad calls on the host before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hybrid_precision_attention_amd as H
+from hybrid_precision_attention_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "hq.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hq_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
+            "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(H.lib, n), n
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert H.hq_status_string(s) != "unknown status"
+    assert H.hq_status_string(7) == "unknown status"
+    assert H.lib.hq_abi_version() == 1
+
+
+def _fake_cache(W=128, base=1 << 20):
+    """Non-null, 16-byte aligned fake device pointers: calls that fail
+    validation never dereference them."""
+    c = B.hq_cache()
+    for i, (n, _) in enumerate(B.hq_cache._fields_):
+        setattr(c, n, base + 4096 * i)
+    if W == 0:
+        c.kwin = None
+        c.vwin = None
+    return c
+
+
+P = 1 << 24       # fake aligned pointer
+
+
+def _dims(**kw):
+    d = dict(B=1, Hq=32, Hkv=8, W=128, rho=0.05, cap_q=32640, cap_vl=1632, cap_stg=1)
+    d.update(kw)
+    return B.make_dims(**d)
+
+
+def _pack(d, L=32768, cache=None, k=P, v=P, flag=P):
+    c = cache or _fake_cache(d.W)
+    return H.lib.hq_quant_pack(ctypes.byref(d), k, v, L, flag, ctypes.byref(c), None)
+
+
+def test_dims_validation():
+    assert _pack(_dims(Hq=30, Hkv=8)) == -1            # Hq % Hkv
+    assert _pack(_dims(B=0)) == -1
+    assert _pack(_dims(W=-1)) == -1
+    assert _pack(_dims(rho=1.5)) == -1
+    assert _pack(_dims(rho=float("nan"))) == -1
+    assert _pack(_dims(d=64)) == -2                    # unsupported head_dim
+    assert _pack(_dims(Hq=64, Hkv=2)) == -2            # G = 32 > 16
+    assert H.lib.hq_quant_pack(None, P, P, 10, P, ctypes.byref(_fake_cache()), None) == -1
+
+
+def test_pack_validation():
+    d = _dims()
+    assert _pack(d, L=-1) == -1
+    assert _pack(d, k=None) == -1
+    assert _pack(d, k=P + 4) == -3                      # misaligned
+    assert _pack(_dims(cap_q=100)) == -4                # capacity
+    c = _fake_cache()
+    c.kq = None
+    assert _pack(d, cache=c) == -1
+    c = _fake_cache()
+    c.kq_meta = (1 << 20) + 8
+    assert _pack(d, cache=c) == -3
+    assert _pack(_dims(W=128), cache=_fake_cache(W=0)) == -1   # W > 0 needs a ring
+
+
+def test_merge_validation():
+    d = _dims()
+    c = _fake_cache()
+    f = H.lib.hq_append_merge
+    assert f(ctypes.byref(d), ctypes.byref(c), -1, P, P, None, None) == -1
+    assert f(ctypes.byref(d), ctypes.byref(c), 100, None, P, None, None) == -1
+    assert f(ctypes.byref(d), ctypes.byref(c), 100, P + 2, P, None, None) == -3
+    assert f(ctypes.byref(d), ctypes.byref(c), 100, P, P, P + 1, None) == -3
+    assert f(ctypes.byref(_dims(cap_stg=0)), ctypes.byref(c), 100, P, P, None, None) == -4
+    assert f(ctypes.byref(_dims(cap_q=10)), ctypes.byref(c), 1000, P, P, None, None) == -4
+
+
+def test_decode_validation():
+    d = _dims()
+    c = _fake_cache()
+    need = H.hq_workspace_bytes(d, H.HQ_OP_DECODE, 32768)
+    assert need > 0
+    f = H.lib.hq_decode_attn
+    assert f(ctypes.byref(d), ctypes.byref(c), -1, P, P, None, P, need, None) == -1
+    assert f(ctypes.byref(d), ctypes.byref(c), 10, None, P, None, P, need, None) == -1
+    assert f(ctypes.byref(d), ctypes.byref(c), 10, P, P + 8, None, P, need, None) == -3
+    assert f(ctypes.byref(d), ctypes.byref(c), 10, P, P, None, None, need, None) == -5
+    assert f(ctypes.byref(d), ctypes.byref(c), 10, P, P, None, P, need - 1, None) == -5
+    assert f(ctypes.byref(d), ctypes.byref(c), 10, P, P, P + 4, P, need, None) == -3
+
+
+def test_select_validation():
+    d = _dims()
+    need = H.hq_workspace_bytes(d, H.HQ_OP_SELECT, 32768)
+    assert need > 0
+    f = H.lib.hq_select_vertical
+    args = lambda nb=64, L=32768, ws=P, wsb=need, idx=P: (
+        ctypes.byref(d), P, nb, P, L, None, P, idx, P, ws, wsb, None)
+    assert f(*args(nb=0)) == -1
+    assert f(*args(nb=65)) == -1
+    assert f(*args(nb=64, L=32)) == -1                  # nb > L
+    assert f(*args(L=0, nb=1)) == -1
+    assert f(*args(idx=None)) == -1                     # n_vl > 0 needs vl_idx
+    assert f(*args(ws=None)) == -5
+    assert f(*args(wsb=need - 1)) == -5
+
+
+def test_workspace_bytes():
+    d = _dims()
+    assert H.hq_workspace_bytes(d, 99, 100) == 0
+    assert H.hq_workspace_bytes(d, H.HQ_OP_DECODE, -1) == 0
+    assert H.hq_workspace_bytes(_dims(d=64), H.HQ_OP_DECODE, 100) == 0
+    small = H.hq_workspace_bytes(d, H.HQ_OP_SELECT, 1024)
+    big = H.hq_workspace_bytes(d, H.HQ_OP_SELECT, 32768)
+    assert 0 < small <= big

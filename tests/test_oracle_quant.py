@@ -110,6 +110,22 @@ def test_invariants_random():
     assert np.all(np.abs(x - (c * s + m)) <= s / 2 + 1e-300)
 
 
+def test_signed_zero_is_stored_as_plus_zero():
+    """A group of -0 values (or one whose minimum is -0): zero range, so the
+    scale is 0 and every code 0; the stored scale and min are +0 (bits 0)."""
+    X = np.zeros((2, 128), np.float16)
+    X[0] = np.float16(-0.0)
+    X[1, :32] = np.float16(-0.0)
+    X[1, 32:] = np.abs(np.random.default_rng(1).standard_normal(96)).astype(np.float16)
+    X[1, 32] = np.float16(-0.0)
+    codes, s, m = O.quantize_groups(X)
+    assert np.all(codes[0] == 0) and np.all(codes[1, :32] == 0)
+    assert s.view(np.uint16)[0].tolist() == [0, 0, 0, 0]
+    assert m.view(np.uint16)[0].tolist() == [0, 0, 0, 0]
+    assert s.view(np.uint16)[1, 0] == 0 and m.view(np.uint16)[1, 0] == 0
+    assert m.view(np.uint16)[1, 1] == 0 and s.view(np.uint16)[1, 1] != 0
+
+
 def test_nibble_order_golden():
     with open(os.path.join(GOLD, "nibble_order.json")) as f:
         g = json.load(f)
