@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid K4V4/FP16 decode-attention path on one MI355X.
+
+A timed *step* is one streaming decode step of the whole hot path:
+hq_append_merge (stage the new token, merge the previous one, quantise the
+token leaving the window) and hq_decode_attn (split-K fused scan + in-kernel
+log-sum-exp merge); every 64th step also runs the vertical-line refresh
+hq_select_vertical over 64 buffered queries (the pages' refresh cadence), so
+its cost is amortised into the step.  hq_quant_pack, which builds the cache
+once after the prefill, is timed on its own and reported beside the step.
+
+The cache footprint of one small-batch layer fits in the 256 MB Infinity
+Cache, so the step rotates over R independent cache replicas (R * footprint
+>= 1 GiB) to measure HBM rather than cache bandwidth.
+
+Prints one JSON line.  ``value`` is the effective HBM bandwidth of the step:
+algorithmic bytes (what the method must move: 160 B per K4V4 token and 512 B
+per FP16 token per KV head, q in, out, merge and amortised refresh traffic)
+divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "hybrid K4V4 decode-attn µs/step + HBM GB/s (% of peak) at L=32K, B=1..32"
+PEAK_GBS = 8000.0
+REFRESH = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=128)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="llama31_8b")
+    p.add_argument("--B", type=int, default=None, help="batch override (e.g. the qwen3_8b sweep)")
+    p.add_argument("--rho", type=float, default=None)
+    p.add_argument("--L", type=int, default=None)
+    p.add_argument("--replicas", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--decode-only", action="store_true",
+                   help="time only hq_decode_attn launches (profiling runs)")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="run a plain device copy of this many bytes (counter calibration) and exit")
+    return p.parse_args()
+
+
+def src_hash():
+    import hashlib
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "hybrid_precision_attention_amd", "csrc", "decode_attn.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(wl_name, B):
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when they were taken on another kernel source or workload."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != src_hash():
+        return None
+    if kv.get("workload") != wl_name or int(kv.get("B", -1)) != B:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path shards by "
+              "(sequence, KV head) with no exchange, so N GPUs are N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "launches": 3}))
+        return
+
+    import hybrid_precision_attention_amd as H
+    from hq_inputs import workload, batch
+
+    over = {}
+    if args.B is not None:
+        over["B"] = args.B
+    if args.rho is not None:
+        over["rho"] = args.rho
+    if args.L is not None:
+        over["L"] = args.L
+    wl = workload(args.workload, **over)
+    B, Hq, Hkv, d, L, W = wl.B, wl.Hq, wl.Hkv, wl.d, wl.L, wl.W
+    G = Hq // Hkv
+    U = B * Hkv
+    dev = torch.device("cuda")
+    torch.manual_seed(0)
+
+    # ---- inputs (seeded, synthetic) and the one-time cache build ----------
+    t0 = time.time()
+    x = batch(wl, steps=1)
+    K = torch.from_numpy(x["K"]).to(dev)
+    V = torch.from_numpy(x["V"]).to(dev)
+    qbuf = torch.from_numpy(x["qbuf"]).to(dev)
+    del x
+    gen_s = time.time() - t0
+    n_nw = max(0, L - W)
+    n_vl = H.n_vertical(wl.rho, n_nw)
+    total_steps = args.warmup + args.steps
+    dims_sel = H.make_dims(B, Hq, Hkv, W, wl.rho)
+    ws_sel = H.workspace(dims_sel, H.HQ_OP_SELECT, L)
+    score = torch.zeros((B, Hkv, L), dtype=torch.float32, device=dev)
+    vl_idx = torch.zeros((B, Hkv, max(1, n_vl)), dtype=torch.int32, device=dev)
+    vl_flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device=dev)
+    H.hq_select_vertical(dims_sel, qbuf, K, L, score, vl_idx, vl_flag, ws_sel)
+
+    per_unit_fp16 = 512 * (n_vl + min(W, L) + 1)
+    footprint = U * (160 * (n_nw - n_vl) + per_unit_fp16)
+    R = args.replicas or max(1, math.ceil((1 << 30) / max(footprint, 1)))
+    L_max = L + total_steps + 64 + 8
+    base = H.HybridCache.allocate(B, Hq, Hkv, W, wl.rho, L_max)
+    H.hq_quant_pack(base.dims, K, V, L, vl_flag, base)
+    torch.cuda.synchronize()
+    caches = [base] + [base.clone() for _ in range(R - 1)]
+    dims = base.dims
+    ws = [H.workspace(dims, H.HQ_OP_DECODE, L_max) for _ in range(R)]
+    pos = [L] * R
+    pool = 64
+    gk = torch.Generator(device=dev).manual_seed(1)
+    k_new = torch.randn((pool, B, Hkv, d), generator=gk, device=dev).half()
+    v_new = torch.randn((pool, B, Hkv, d), generator=gk, device=dev).half()
+    q_new = torch.randn((pool, B, Hq, d), generator=gk, device=dev).half()
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    # dense keys for the refresh, rotated too (64 MiB per layer at L = 32K)
+    k_bytes = K.numel() * 2
+    R_sel = max(1, min(8, math.ceil((512 << 20) / k_bytes)))
+    K_rep = [K] + [K.clone() for _ in range(R_sel - 1)]
+    del V
+
+    def step(i, ev=None):
+        r = i % R
+        t = pos[r]
+        j = i % pool
+        H.hq_append_merge(dims, caches[r], t, k_new[j], v_new[j])
+        if ev is not None:
+            ev[0].record()
+        H.hq_decode_attn(dims, caches[r], t, q_new[j], out, ws[r], lse=lse)
+        if ev is not None:
+            ev[1].record()
+        pos[r] = t + 1
+        if i % REFRESH == REFRESH - 1:
+            H.hq_select_vertical(dims_sel, qbuf, K_rep[(i // REFRESH) % R_sel], L, score,
+                                 vl_idx, vl_flag, ws_sel)
+
+    if args.decode_only:
+        for i in range(total_steps):
+            r = i % R
+            H.hq_decode_attn(dims, caches[r], pos[r], q_new[i % pool], out, ws[r], lse=lse)
+        torch.cuda.synchronize()
+        print(json.dumps({"decode_only_launches": total_steps, "replicas": R}))
+        return
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / args.steps
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    # ---- per-row timings (each on its own, same rotation) -----------------
+    def time_loop(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    sel_ms = time_loop(lambda i: H.hq_select_vertical(dims_sel, qbuf, K_rep[i % R_sel], L, score,
+                                                      vl_idx, vl_flag, ws_sel), 8)
+    spare = H.HybridCache.allocate(B, Hq, Hkv, W, wl.rho, L_max)
+    pack_ms = time_loop(lambda i: H.hq_quant_pack(spare.dims, K_rep[i % R_sel], K_rep[(i + 1) % R_sel],
+                                                  L, vl_flag, spare), 4)
+
+    def merge_only(i):
+        r = i % R
+        H.hq_append_merge(dims, caches[r], pos[r], k_new[i % pool], v_new[i % pool])
+        pos[r] += 1
+    merge_ms = time_loop(merge_only, 64)
+
+    # ---- algorithmic bytes ------------------------------------------------
+    n_q_mid = (n_nw - n_vl) + (args.warmup + args.steps // 2) // R
+    dec_bytes = U * (160 * n_q_mid + 512 * (n_vl + min(W, L) + 1)) + B * Hq * d * 2 * 2
+    merge_bytes = U * (512 * 5 + 160)      # read staged/evictee/new, write ring/stage, K4 slot
+    sel_bytes = 2 * U * L * d * 2 + B * Hq * wl.nb * d * 2 * 2 + U * n_nw * 4 * 2 + U * L
+    step_bytes = dec_bytes + merge_bytes + sel_bytes / REFRESH
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl.name, B)
+
+    # ---- CPU baseline: the oracle on a bounded sample ---------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, base, H, torch)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}-shaped layer", "B": B, "Hq": Hq, "Hkv": Hkv, "d": d,
+                   "L": L, "W": W, "rho": wl.rho, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel (hq_decode_attn)",
+                     "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "step_us": round(ms_step * 1e3, 2),
+        "rows_us": {"decode": round(dec_avg_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
+                    "select": round(sel_ms * 1e3, 2), "pack": round(pack_ms * 1e3, 2)},
+        "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step, 4),
+                         "amortized": round(sel_ms / (sel_ms + REFRESH * (ms_step - sel_ms / REFRESH)), 4)},
+        "replicas": R, "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(rec))
+
+
+def cpu_baseline(wl, cache, H, torch):
+    """Time the fp64 oracle's decode step on whole units of the same cache
+    until about 10 s of CPU work, and report it in the metric's unit."""
+    from oracle import hq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    B, Hkv, G, L, W, d = wl.B, wl.Hkv, wl.G, wl.L, wl.W, wl.d
+    rng = np.random.default_rng(0)
+    units = [(b, g) for b in range(B) for g in range(Hkv)]
+    done, nbytes, t_cpu = 0, 0, 0.0
+    for (b, g) in units:
+        t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()}
+        nq, nvl = int(t["n_q"]), int(t["n_vl"])
+        c = O.empty_unit_cache(d, W)
+        c["kq"], c["vq"] = t["kq"][:nq], t["vq"][:nq]
+        c["kq_meta"], c["vq_meta"], c["q_pos"] = t["kq_meta"][:nq], t["vq_meta"][:nq], t["q_pos"][:nq]
+        c["kvl"], c["vvl"], c["vl_pos"] = t["kvl"][:nvl], t["vvl"][:nvl], t["vl_pos"][:nvl]
+        if W:
+            c["kwin"], c["vwin"] = t["kwin"], t["vwin"]
+        q = rng.standard_normal((G, d)).astype(np.float16)
+        kn = rng.standard_normal(d).astype(np.float16)
+        t0 = time.perf_counter()
+        O.append_merge_unit(c, L, kn, kn)
+        O.decode_fused(c, q, L)
+        t_cpu += time.perf_counter() - t0
+        done += 1
+        nbytes += 160 * c["kq"].shape[0] + 512 * (c["kvl"].shape[0] + min(W, L) + 1) + G * d * 4
+        if t_cpu > 10.0:
+            break
+    return {"value": round(nbytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 oracle merge + fused decode of {done} of {len(units)} (sequence, KV head) "
+                      f"units of the same cache, {t_cpu:.1f} s CPU; GB/s of the same algorithmic bytes"}
+
+
+if __name__ == "__main__":
+    main()

@@ -10,10 +10,12 @@
 // Work decomposition.  Grid = (splits, units).  The first nsplit_q
 // workgroups of a unit scan contiguous ranges of its K4V4 slots, the rest scan
 // ranges of the FP16 sequence (vertical lines, then window slots, then
-// staging).  Each workgroup has four waves that take 32-token blocks in turn;
-// the waves' (max, sum, output) triples are merged in LDS into one partial
-// record, and the last workgroup of the unit to arrive (an atomic counter in
-// the workspace) merges the unit's records by log-sum-exp and writes out/lse.
+// staging); the host sizes both kinds to carry about the same bytes.  Each
+// workgroup has eight waves that take 32-token blocks in turn.  The waves'
+// (max, sum, output) states are merged pairwise through LDS in the lanes'
+// own register layout, giving one partial record per workgroup; the last
+// workgroup of the unit to arrive (an atomic counter in the workspace) merges
+// the unit's records by log-sum-exp and writes out/lse.
 //
 // Per 32-token block a wave runs, for the G query heads of the unit (padded
 // to 16):  S = K Q^T with two 16-token tiles x four k-steps of
@@ -24,14 +26,18 @@
 //    group j of token t with one 128-bit load; k-step kk uses its dword kk.
 //    The nibble unpack yields element order {0,4,1,5,2,6,3,7}, and Q (the B
 //    operand) is permuted the same way once per wave.
-//  * V^T (A operand, M = dims, K = tokens): lane (r, j) loads dword r (dims
-//    8r..8r+7) of the eight tokens it owns and MFMA i uses nibble i, so the
-//    wave's loads still cover whole 64-byte code rows.
+//  * V^T (A operand, M = dims, K = tokens): lane (r, j) needs dword r (dims
+//    8r..8r+7) of the eight tokens it owns, and MFMA i uses nibble i.  The
+//    block's V codes and all its {scale, min} words arrive with 128/64-bit
+//    loads and are transposed through a per-wave LDS staging area: six vector
+//    memory instructions per block instead of twenty.
 //  * P^T (B operand) is the softmax of the lane's own S values: the tokens a
 //    lane holds after QK are exactly the tokens its PV k-slice contracts.
 //  * O^T (D): lane (head n, j) ends with dims 32j..32j+31 of head n.
-// Nibbles become fp16 by OR-ing them under the exponent of 1024 (0x6400),
-// subtracting 1024 (exact) and one fused multiply-add with {scale, min}.
+// Nibbles become fp16 by OR-ing them under the exponent of 1024 (0x6400):
+// the low nibble of a byte gives 1024 + c, the high nibble (masked in place)
+// 1024 + 16c; subtracting 1024 is exact, and one fused multiply-add with
+// {scale, min} (or {scale/16, min}) finishes the dequantisation.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -42,11 +48,14 @@ namespace hq {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
+constexpr int kMaxSplit = 256;      // partial records per unit
 constexpr uint32_t kMagic = 0x64006400u;
+constexpr uint32_t kLo = 0x000F000Fu;
+constexpr uint32_t kHi = 0x00F000F0u;
 
 struct DecodeArgs {
   hq_cache c;
@@ -65,37 +74,30 @@ __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
-// four packed fp16 pairs -> half8
 __device__ __forceinline__ half8_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return as_half8(make_uint4(a, b, c, d));
 }
 
-// (1024 + code) pair -> code * scale + min, rounded once to fp16
+// biased fp16 pair (1024 + k) -> k * s + m, rounded once
 __device__ __forceinline__ uint32_t dq_pair(uint32_t biased, half2_t s, half2_t m) {
   const half2_t c = as_half2(biased) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
   return as_u32(__builtin_elementwise_fma(c, s, m));
 }
 
+__device__ __forceinline__ half2_t sixteenth(half2_t s) {
+  return s * (half2_t){(_Float16)0.0625f, (_Float16)0.0625f};
+}
+
 // Eight nibbles of one K group -> A-operand half8 in element order
-// {0,4,1,5,2,6,3,7}; meta = scale | min << 16.
-__device__ __forceinline__ half8_t dq_k8(uint32_t w, uint32_t meta) {
-  const half2_t s = as_half2((meta & 0xFFFFu) * 0x10001u);
-  const half2_t m = as_half2((meta >> 16) * 0x10001u);
-  const uint32_t p0 = (w & 0x000F000Fu) | kMagic;
-  const uint32_t p1 = ((w >> 4) & 0x000F000Fu) | kMagic;
-  const uint32_t p2 = ((w >> 8) & 0x000F000Fu) | kMagic;
-  const uint32_t p3 = ((w >> 12) & 0x000F000Fu) | kMagic;
-  return pack4(dq_pair(p0, s, m), dq_pair(p1, s, m), dq_pair(p2, s, m), dq_pair(p3, s, m));
+// {0,4,1,5,2,6,3,7}; s/s16/m are the group's scale, scale/16 and min.
+__device__ __forceinline__ half8_t dq_k8(uint32_t w, half2_t s, half2_t s16, half2_t m) {
+  const uint32_t w8 = w >> 8;
+  return pack4(dq_pair((w & kLo) | kMagic, s, m), dq_pair((w & kHi) | kMagic, s16, m),
+               dq_pair((w8 & kLo) | kMagic, s, m), dq_pair((w8 & kHi) | kMagic, s16, m));
 }
 
 __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float wave_max_over_j(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
 }
 
 // Online-softmax state of one wave: lane (head n, j).
@@ -107,98 +109,142 @@ struct SoftState {
 
 // Fold one 32-token block of raw scores s[8] (tokens 4j+r and 16+4j+r, -inf
 // when masked) into the state; returns the B operand P^T for the PV MFMAs.
+// The accumulator is rescaled only when some head's running max grew.
 __device__ __forceinline__ half8_t softmax_block(SoftState& st, const float s[8], float c2) {
-  float bm = s[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) bm = fmaxf(bm, s[e]);
-  bm = wave_max_over_j(bm);
+  float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                   fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
   const float m_new = fmaxf(st.m, bm);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = exp2f((st.m - m_use) * c2);
+  if (__any(m_new > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f((st.m - m_use) * c2);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
+  }
+  st.m = m_new;
   const float nmc = -m_use * c2;
   float p[8];
-  float ps = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(fmaf(s[e], c2, nmc));
-    ps += p[e];
-  }
-  st.l = fmaf(st.l, alpha, ps);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
-  st.m = m_new;
+  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, nmc));
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   half8_t pb;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pb[e] = static_cast<_Float16>(p[e]);
   return pb;
 }
 
-// Raw loads of one K4V4 block for one lane.
+// Raw loads of one K4V4 block for one lane: six wide loads per 32 tokens
+// (the memory pipeline, not HBM, limits a kernel that issues many narrow ones).
 struct K4Raw {
-  uint4 ka, kb;                     // code bytes of group j of tokens tb+t and tb+16+t
-  uint32_t kma, kmb;                // their {scale, min}
-  uint32_t vc[8];                   // dword r of the V code rows of the lane's 8 tokens
-  uint32_t vm[8];                   // {scale, min} of group r/4 of those tokens
+  uint4 ka, kb;                     // K codes, group j of tokens tb+n and tb+16+n
+  uint4 va, vb;                     // V codes, 16 bytes of the 2 KB block (row-major)
+  uint2 kmw, vmw;                   // two {scale, min} words of K and of V
 };
+
+// Per-wave LDS staging of the V codes and all metadata of one block, read
+// back transposed: V rows padded to 80 bytes so the eight 4-byte reads of a
+// lane column land in distinct banks.
+struct K4Stage {
+  uint32_t v[32][20];
+  uint32_t km[128];                 // word 4t + g: {scale, min} of token t, group g
+  uint32_t vm[128];
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ int k4_token(int tb, int j, int e) {
   return tb + (e < 4 ? 4 * j + e : 16 + 4 * j + (e - 4));
 }
 
+// Rows past the unit's last token are clamped to it, so every address stays
+// inside the unit and masked tokens still dequantise to finite values.
 __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint32_t* kmeta,
                                         const uint8_t* vq, const uint32_t* vmeta, int tb,
-                                        int nq, int n, int j) {
+                                        int nq, int lane, int n, int j) {
   const int ta = min(tb + n, nq - 1);
   const int tbb = min(tb + 16 + n, nq - 1);
   r.ka = ld16(kq + static_cast<int64_t>(ta) * kRowBytes + 16 * j);
   r.kb = ld16(kq + static_cast<int64_t>(tbb) * kRowBytes + 16 * j);
-  r.kma = kmeta[static_cast<int64_t>(ta) * kMetaWords + j];
-  r.kmb = kmeta[static_cast<int64_t>(tbb) * kMetaWords + j];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = min(k4_token(tb, j, e), nq - 1);
-    r.vc[e] = *reinterpret_cast<const uint32_t*>(vq + static_cast<int64_t>(t) * kRowBytes + 4 * n);
-    r.vm[e] = vmeta[static_cast<int64_t>(t) * kMetaWords + (n >> 2)];
-  }
+  const int tv0 = min(tb + (lane >> 2), nq - 1);
+  const int tv1 = min(tb + 16 + (lane >> 2), nq - 1);
+  r.va = ld16(vq + static_cast<int64_t>(tv0) * kRowBytes + 16 * (lane & 3));
+  r.vb = ld16(vq + static_cast<int64_t>(tv1) * kRowBytes + 16 * (lane & 3));
+  const int tm = min(tb + (lane >> 1), nq - 1);
+  r.kmw = *reinterpret_cast<const uint2*>(kmeta + static_cast<int64_t>(tm) * kMetaWords + 2 * (lane & 1));
+  r.vmw = *reinterpret_cast<const uint2*>(vmeta + static_cast<int64_t>(tm) * kMetaWords + 2 * (lane & 1));
 }
 
-__device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, const half8_t qb[4],
-                                           int tb, int nq, int j, float c2) {
-  float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t ka[4] = {r.ka.x, r.ka.y, r.ka.z, r.ka.w};
-  const uint32_t kb[4] = {r.kb.x, r.kb.y, r.kb.z, r.kb.w};
+__device__ __forceinline__ void qk_tile(float4_t& acc, uint4 codes, uint32_t meta,
+                                        const half8_t qb[4]) {
+  const half2_t s = as_half2((meta & 0xFFFFu) * 0x10001u);
+  const half2_t m = as_half2((meta >> 16) * 0x10001u);
+  const half2_t s16 = sixteenth(s);
+  acc = mfma(dq_k8(codes.x, s, s16, m), qb[0], acc);
+  acc = mfma(dq_k8(codes.y, s, s16, m), qb[1], acc);
+  acc = mfma(dq_k8(codes.z, s, s16, m), qb[2], acc);
+  acc = mfma(dq_k8(codes.w, s, s16, m), qb[3], acc);
+}
+
+__device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stage& sg,
+                                           const half8_t qb[4], int tb, int nq, int lane, int n,
+                                           int j, float c2) {
+  // stage, then read back the transposed operands
+  wave_sync();
+  *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
+  *reinterpret_cast<uint4*>(&sg.v[16 + (lane >> 2)][4 * (lane & 3)]) = r.vb;
+  *reinterpret_cast<uint2*>(&sg.km[2 * lane]) = r.kmw;
+  *reinterpret_cast<uint2*>(&sg.vm[2 * lane]) = r.vmw;
+  wave_sync();
+  const uint32_t kma = sg.km[4 * n + j];
+  const uint32_t kmb = sg.km[64 + 4 * n + j];
+  uint32_t vc[8], vm[8];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    sa = mfma(dq_k8(ka[kk], r.kma), qb[kk], sa);
-    sb = mfma(dq_k8(kb[kk], r.kmb), qb[kk], sb);
+  for (int e = 0; e < 8; ++e) {
+    const int t = k4_token(0, j, e);
+    vc[e] = sg.v[t][n];
+    vm[e] = sg.vm[4 * t + (n >> 2)];
   }
-  float s[8];
+
+  float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+  qk_tile(sa, r.ka, kma, qb);
+  qk_tile(sb, r.kb, kmb, qb);
+  float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  if (tb + kBlk > nq) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    s[e] = (tb + 4 * j + e < nq) ? sa[e] : -INFINITY;
-    s[4 + e] = (tb + 16 + 4 * j + e < nq) ? sb[e] : -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      if (tb + 4 * j + e >= nq) s[e] = -INFINITY;
+      if (tb + 16 + 4 * j + e >= nq) s[4 + e] = -INFINITY;
+    }
   }
   const half8_t pb = softmax_block(st, s, c2);
 
   // V^T operands: token pairs (2p, 2p+1) interleaved so one and_or gives a
-  // (1024 + code) fp16 pair for both tokens
-  uint32_t xlo[4], xhi[4];
-  half2_t sp[4], mp[4];
+  // biased fp16 pair for both tokens
+  uint32_t xl[4], xh[4];
+  half2_t sp[4], sp16[4], mp[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    xlo[p] = __builtin_amdgcn_perm(r.vc[2 * p + 1], r.vc[2 * p], 0x05040100u);
-    xhi[p] = __builtin_amdgcn_perm(r.vc[2 * p + 1], r.vc[2 * p], 0x07060302u);
-    sp[p] = as_half2(__builtin_amdgcn_perm(r.vm[2 * p + 1], r.vm[2 * p], 0x05040100u));
-    mp[p] = as_half2(__builtin_amdgcn_perm(r.vm[2 * p + 1], r.vm[2 * p], 0x07060302u));
+    xl[p] = __builtin_amdgcn_perm(vc[2 * p + 1], vc[2 * p], 0x05040100u);
+    xh[p] = __builtin_amdgcn_perm(vc[2 * p + 1], vc[2 * p], 0x07060302u);
+    sp[p] = as_half2(__builtin_amdgcn_perm(vm[2 * p + 1], vm[2 * p], 0x05040100u));
+    mp[p] = as_half2(__builtin_amdgcn_perm(vm[2 * p + 1], vm[2 * p], 0x07060302u));
+    sp16[p] = sixteenth(sp[p]);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int sh = 4 * (i & 3);
     uint32_t v[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t x = (i < 4) ? xlo[p] : xhi[p];
-      v[p] = dq_pair(((x >> sh) & 0x000F000Fu) | kMagic, sp[p], mp[p]);
+      uint32_t x = (i < 4) ? xl[p] : xh[p];
+      if (i & 2) x >>= 8;
+      v[p] = (i & 1) ? dq_pair((x & kHi) | kMagic, sp16[p], mp[p])
+                     : dq_pair((x & kLo) | kMagic, sp[p], mp[p]);
     }
     st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pb, st.o[i]);
   }
@@ -213,38 +259,46 @@ __device__ __forceinline__ const uint16_t* f16_row(const uint16_t* vl, const uin
   return stg + static_cast<int64_t>(v - nvl - nwin) * kD;
 }
 
-__device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4],
-                                            const uint16_t* kvl, const uint16_t* kwin,
-                                            const uint16_t* kstg, const uint16_t* vvl,
-                                            const uint16_t* vwin, const uint16_t* vstg, int tb,
-                                            int nvl, int nwin, int nf, int n, int j, float c2) {
-  const int ta = min(tb + n, nf - 1);
-  const int tbb = min(tb + 16 + n, nf - 1);
-  const uint16_t* ra = f16_row(kvl, kwin, kstg, ta, nvl, nwin) + 32 * j;
-  const uint16_t* rb = f16_row(kvl, kwin, kstg, tbb, nvl, nwin) + 32 * j;
-  uint4 ka[4], kb[4];
+struct F16Rows {
+  const uint16_t *kvl, *kwin, *kstg, *vvl, *vwin, *vstg;
+  int nvl, nwin, nf;
+};
+
+// K rows of one FP16 block: lane (t, j) loads dims 32j..32j+31 of tokens
+// tb+t and tb+16+t (natural element order).
+__device__ __forceinline__ void load_f16_k(uint4 kr[8], const F16Rows& f, int tb, int n, int j) {
+  const int ta = min(tb + n, f.nf - 1);
+  const int tbb = min(tb + 16 + n, f.nf - 1);
+  const uint16_t* ra = f16_row(f.kvl, f.kwin, f.kstg, ta, f.nvl, f.nwin) + 32 * j;
+  const uint16_t* rb = f16_row(f.kvl, f.kwin, f.kstg, tbb, f.nvl, f.nwin) + 32 * j;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    ka[kk] = ld16(ra + 8 * kk);
-    kb[kk] = ld16(rb + 8 * kk);
+    kr[kk] = ld16(ra + 8 * kk);
+    kr[4 + kk] = ld16(rb + 8 * kk);
   }
+}
+
+__device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], const F16Rows& f,
+                                            const uint4 kr[8], int tb, int n, int j, float c2) {
   uint4 vr[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int t = min(k4_token(tb, j, e), nf - 1);
-    vr[e] = ld16(f16_row(vvl, vwin, vstg, t, nvl, nwin) + 8 * n);
+    const int t = min(k4_token(tb, j, e), f.nf - 1);
+    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * n);
   }
   float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    sa = mfma(as_half8(ka[kk]), qn[kk], sa);
-    sb = mfma(as_half8(kb[kk]), qn[kk], sb);
+    sa = mfma(as_half8(kr[kk]), qn[kk], sa);
+    sb = mfma(as_half8(kr[4 + kk]), qn[kk], sb);
   }
-  float s[8];
+  float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+  if (tb + kBlk > f.nf) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    s[e] = (tb + 4 * j + e < nf) ? sa[e] : -INFINITY;
-    s[4 + e] = (tb + 16 + 4 * j + e < nf) ? sb[e] : -INFINITY;
+    for (int e = 0; e < 4; ++e) {
+      if (tb + 4 * j + e >= f.nf) s[e] = -INFINITY;
+      if (tb + 16 + 4 * j + e >= f.nf) s[4 + e] = -INFINITY;
+    }
   }
   const half8_t pb = softmax_block(st, s, c2);
 #pragma unroll
@@ -261,14 +315,60 @@ __device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4],
   }
 }
 
+// LDS image of one wave's state, element-major so lanes hit distinct banks.
+struct WaveImage {
+  float v[34][64];                  // m, l, o[32]
+};
+
+__device__ __forceinline__ void put_state(WaveImage& w, const SoftState& st, int lane) {
+  w.v[0][lane] = st.m;
+  w.v[1][lane] = st.l;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w.v[2 + 4 * i + r][lane] = st.o[i][r];
+}
+
+// merge another wave's state (same lane layout) into this one
+__device__ __forceinline__ void merge_state(SoftState& st, const WaveImage& w, int lane, float c2) {
+  const float mo = w.v[0][lane];
+  const float mm = fmaxf(st.m, mo);
+  if (mm == -INFINITY) return;
+  const float fa = __builtin_amdgcn_exp2f((st.m - mm) * c2);
+  const float fb = __builtin_amdgcn_exp2f((mo - mm) * c2);
+  st.m = mm;
+  st.l = st.l * fa + w.v[1][lane] * fb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st.o[i][r] = st.o[i][r] * fa + w.v[2 + 4 * i + r][lane] * fb;
+}
+
+// Partial records cross XCDs.  They are written and read with device-scope
+// relaxed atomics (write-through / coherent-read of the XCD-local L2), and the
+// writer waits for its stores before counting its arrival, so no fence has to
+// write back or invalidate a whole L2.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][kD + 4];
+  // the per-wave staging areas of the scan and the images of the merges share
+  // LDS (a barrier separates the two uses)
+  __shared__ union {
+    K4Stage stage[kWaves];                         // 28 KB
+    WaveImage img[kWaves / 2];                     // 34.8 KB
+  } s_lds;
+  WaveImage* s_img = s_lds.img;
+  __shared__ float s_mm[16], s_lt[16];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = lane & 15, j = lane >> 4;
   const int64_t u = blockIdx.y;
   const int split = blockIdx.x;
@@ -312,13 +412,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
     int blk = b0 + wave;
     if (blk < b1) {
+      // one block of prefetch; the load is unconditional (the last one re-reads
+      // an in-range block) so that the wait before the compute only covers the
+      // previous iteration's loads
+      K4Stage& sg = s_lds.stage[wave];
       K4Raw cur;
-      load_k4(cur, kq, kmeta, vq, vmeta, blk * kBlk, nq, n, j);
+      load_k4(cur, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
       for (; blk < b1; blk += kWaves) {
         K4Raw nxt;
-        const int nb = blk + kWaves;
-        if (nb < b1) load_k4(nxt, kq, kmeta, vq, vmeta, nb * kBlk, nq, n, j);
-        compute_k4(st, cur, qb, blk * kBlk, nq, j, c2);
+        load_k4(nxt, kq, kmeta, vq, vmeta, min(blk + kWaves, b1 - 1) * kBlk, nq, lane, n, j);
+        compute_k4(st, cur, sg, qb, blk * kBlk, nq, lane, n, j, c2);
         cur = nxt;
       }
     }
@@ -334,84 +437,110 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     half8_t qn[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
-    const uint16_t* kvl = a.c.kvl + u * a.cap_vl * kD;
-    const uint16_t* vvl = a.c.vvl + u * a.cap_vl * kD;
-    const uint16_t* kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
-    const uint16_t* vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-    const uint16_t* kstg = a.c.kstg + u * a.cap_stg * kD;
-    const uint16_t* vstg = a.c.vstg + u * a.cap_stg * kD;
-    for (int blk = b0 + wave; blk < b1; blk += kWaves)
-      process_f16(st, qn, kvl, kwin, kstg, vvl, vwin, vstg, blk * kBlk, nvl, nwin, nf, n, j, c2);
-  }
-
-  // wave -> LDS
-  float lt = st.l;
-  lt += __shfl_xor(lt, 16);
-  lt += __shfl_xor(lt, 32);
-  if (j == 0) {
-    s_m[wave][n] = st.m;
-    s_l[wave][n] = lt;
-  }
+    F16Rows f;
+    f.kvl = a.c.kvl + u * a.cap_vl * kD;
+    f.vvl = a.c.vvl + u * a.cap_vl * kD;
+    f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+    f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+    f.kstg = a.c.kstg + u * a.cap_stg * kD;
+    f.vstg = a.c.vstg + u * a.cap_stg * kD;
+    f.nvl = nvl;
+    f.nwin = nwin;
+    f.nf = nf;
+    int blk = b0 + wave;
+    if (blk < b1) {
+      uint4 kcur[8];
+      load_f16_k(kcur, f, blk * kBlk, n, j);
+      for (; blk < b1; blk += kWaves) {
+        uint4 knxt[8];
+        load_f16_k(knxt, f, min(blk + kWaves, b1 - 1) * kBlk, n, j);
+        process_f16(st, qn, f, kcur, blk * kBlk, n, j, c2);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_o[wave][n][32 * j + 8 * r + i] = st.o[i][r];
-  __syncthreads();
-
-  // workgroup partial record
-  float* rec0 = a.part + (u * nsplit + split) * static_cast<int64_t>(G) * kPart;
-  for (int idx = tid; idx < G * kD; idx += kThreads) {
-    const int g = idx >> 7, dim = idx & (kD - 1);
-    float mm = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mm = fmaxf(mm, s_m[w][g]);
-    float o = 0.0f, ls = 0.0f;
-    if (mm != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2f((s_m[w][g] - mm) * c2);
-        o = fmaf(f, s_o[w][g][dim], o);
-        ls = fmaf(f, s_l[w][g], ls);
+        for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
       }
     }
-    float* rec = rec0 + g * kPart;
-    rec[4 + dim] = o;
-    if (dim == 0) {
-      rec[0] = mm;
-      rec[1] = ls;
-    }
   }
 
-  // arrival counter: the last workgroup of the unit merges all records
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(a.counters + u, 1);
-    s_last = (old == nsplit - 1);
+  __syncthreads();                                 // staging areas are free from here
+  // pairwise merge of the eight waves: 8 -> 4 -> 2 -> 1
+#pragma unroll
+  for (int half = kWaves / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) put_state(s_img[wave - half], st, lane);
+    __syncthreads();
+    if (wave < half) merge_state(st, s_img[wave], lane, c2);
+    __syncthreads();
+  }
+
+  // wave 0 writes the workgroup's partial record (heads 0..G-1), waits for
+  // the stores, and counts the workgroup's arrival
+  float* recs = a.part + u * nsplit * static_cast<int64_t>(G) * kPart;
+  if (wave == 0) {
+    float lt = st.l;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (n < G) {
+      float* rec = recs + (static_cast<int64_t>(split) * G + n) * kPart;
+      if (j == 0) {
+        st_agent(rec, st.m);
+        st_agent(rec + 1, lt);
+      }
+      float* o = rec + 4 + 32 * j;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_agent(o + 8 * r + i, st.o[i][r]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (lane == 0) {
+      const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      s_last = (old == nsplit - 1);
+    }
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
-  const float* recu = a.part + u * nsplit * static_cast<int64_t>(G) * kPart;
+  // the last workgroup: (m, l) of every record -> LDS, then per-head max,
+  // weights and denominators, then the weighted sum of the outputs
+  float* s_pm = &s_img[0].v[0][0];
+  float* s_pl = s_pm + kMaxSplit * 16;
+  for (int idx = tid; idx < nsplit * G; idx += kThreads) {
+    const float* rec = recs + static_cast<int64_t>(idx) * kPart;
+    s_pm[idx] = ld_agent(rec);
+    s_pl[idx] = ld_agent(rec + 1);
+  }
+  __syncthreads();
+  for (int g = wave; g < G; g += kWaves) {
+    float mx = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, s_pm[s * G + g]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float lt = 0.0f;
+    for (int s = lane; s < nsplit; s += 64) {
+      const float f = (mx == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s_pm[s * G + g] - mx) * c2);
+      s_pm[s * G + g] = f;
+      lt += f * s_pl[s * G + g];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lt += __shfl_xor(lt, o);
+    if (lane == 0) {
+      s_mm[g] = mx;
+      s_lt[g] = lt;
+    }
+  }
+  __syncthreads();
   for (int idx = tid; idx < G * kD; idx += kThreads) {
     const int g = idx >> 7, dim = idx & (kD - 1);
-    float mm = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mm = fmaxf(mm, recu[(static_cast<int64_t>(s) * G + g) * kPart]);
-    float o = 0.0f, ls = 0.0f;
-    if (mm != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* rec = recu + (static_cast<int64_t>(s) * G + g) * kPart;
-        const float f = exp2f((rec[0] - mm) * c2);
-        o = fmaf(f, rec[4 + dim], o);
-        ls = fmaf(f, rec[1], ls);
-      }
-    }
-    const float res = ls > 0.0f ? o / ls : 0.0f;
-    a.out[(b * a.Hq + h0 + g) * kD + dim] =
-        __builtin_bit_cast(uint16_t, static_cast<_Float16>(res));
+    const float* src = recs + static_cast<int64_t>(g) * kPart + 4 + dim;
+    float o = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < nsplit; ++s)
+      o = fmaf(s_pm[s * G + g], ld_agent(src + static_cast<int64_t>(s) * G * kPart), o);
+    const float lt = s_lt[g];
+    const float res = lt > 0.0f ? o / lt : 0.0f;
+    a.out[(b * a.Hq + h0 + g) * kD + dim] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(res));
     if (dim == 0 && a.lse)
-      a.lse[b * a.Hq + h0 + g] = ls > 0.0f ? (mm * c2 + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+      a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (s_mm[g] * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
   }
   if (tid == 0) a.counters[u] = 0;
 }

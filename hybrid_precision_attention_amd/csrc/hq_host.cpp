@@ -18,10 +18,13 @@ namespace hq {
 namespace {
 
 constexpr int kMaxGroup = 16;      // query heads per KV head handled by one MFMA tile
-constexpr int kDecodeTargetWG = 512;   // workgroups a decode launch aims for
-constexpr int kDecodeWaves = 4;        // waves per decode workgroup
-constexpr int kBlk = 32;               // tokens per decode block
-constexpr int kPartFloats = 132;       // m, l, 2 pad, o[128]
+constexpr int kCUs = 256;          // MI355X compute units
+constexpr int kDecodeWaves = 8;    // waves per decode workgroup
+constexpr int kBlk = 32;           // tokens per decode block
+constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most
+constexpr int kMaxSplit = 256;     // decode workgroups per unit, at most (LDS of the final merge)
+constexpr int kPartFloats = 132;   // m, l, 2 pad, o[128]
+constexpr double kWgBytes = 192.0 * 1024;  // bytes one decode workgroup streams at small batch
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -61,6 +64,13 @@ int32_t n_vertical(double rho, int32_t n_nw) {
   return static_cast<int32_t>(floor(rho * static_cast<double>(n_nw) + 1e-6));
 }
 
+// Splits per unit for the decode: workgroups carry about equal bytes (160 per
+// K4V4 token, 512 per FP16 token).  Small problems get one workgroup per CU;
+// large ones up to eight per CU so that uneven finishing times average out.
+static int64_t max_splits(int64_t units) {
+  return std::min<int64_t>(kMaxSplit, cdiv(kMaxWG, units) + 3);
+}
+
 DecodePlan plan_decode(const hq_dims& d, int32_t L) {
   const int64_t units = static_cast<int64_t>(d.B) * d.Hkv;
   const int32_t n_nw = std::max<int32_t>(0, L - d.W);
@@ -70,12 +80,19 @@ DecodePlan plan_decode(const hq_dims& d, int32_t L) {
   const int64_t n_f = static_cast<int64_t>(n_vl) + n_win + d.cap_stg;
   const double bq = 160.0 * static_cast<double>(n_q);
   const double bf = 512.0 * static_cast<double>(n_f);
-  const int64_t cap = std::max<int64_t>(1, cdiv(kDecodeTargetWG, units));
-  const double fq = (bq + bf) > 0 ? bq / (bq + bf) : 0.5;
-  int64_t nq = std::llround(static_cast<double>(cap) * fq);
-  int64_t nf = std::llround(static_cast<double>(cap) * (1.0 - fq));
-  nq = std::max<int64_t>(1, std::min<int64_t>(nq, std::max<int64_t>(1, cdiv(cdiv(n_q, kBlk), 4 * kDecodeWaves))));
-  nf = std::max<int64_t>(1, std::min<int64_t>(nf, std::max<int64_t>(1, cdiv(cdiv(n_f, kBlk), kDecodeWaves))));
+  const double total = static_cast<double>(units) * (bq + bf);
+  const double per_cu = std::min(8.0, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
+  const double wg_bytes = std::max(total / (kCUs * per_cu), 1.0);
+  const int64_t blk_q = cdiv(n_q, kBlk), blk_f = cdiv(n_f, kBlk);
+  int64_t nq = std::max<int64_t>(1, std::llround(bq / wg_bytes));
+  int64_t nf = std::max<int64_t>(1, std::llround(bf / wg_bytes));
+  nq = std::min<int64_t>(nq, std::max<int64_t>(1, cdiv(blk_q, kDecodeWaves)));
+  nf = std::min<int64_t>(nf, std::max<int64_t>(1, cdiv(blk_f, kDecodeWaves)));
+  const int64_t cap = max_splits(units);
+  if (nq + nf > cap) {               // keep the proportion, respect the bound
+    nf = std::max<int64_t>(1, (nf * cap) / (nq + nf));
+    nq = std::max<int64_t>(1, cap - nf);
+  }
   DecodePlan p;
   p.nsplit_q = static_cast<int>(nq);
   p.nsplit_f = static_cast<int>(nf);
@@ -89,11 +106,12 @@ size_t decode_counter_bytes(const hq_dims& d) {
 }
 
 size_t decode_ws_bytes(const hq_dims& d, int32_t /*L_max*/) {
-  // plan_decode never exceeds cap + 2 splits per unit, whatever L is
-  const size_t units = static_cast<size_t>(d.B) * d.Hkv;
-  const size_t cap = std::max<size_t>(1, (kDecodeTargetWG + units - 1) / units);
+  // plan_decode never exceeds max_splits(units) splits per unit, whatever L is
+  const int64_t units = static_cast<int64_t>(d.B) * d.Hkv;
   const size_t G = static_cast<size_t>(d.Hq / d.Hkv);
-  return decode_counter_bytes(d) + units * (cap + 2) * G * kPartFloats * sizeof(float);
+  return decode_counter_bytes(d) +
+         static_cast<size_t>(units) * static_cast<size_t>(max_splits(units)) * G * kPartFloats *
+             sizeof(float);
 }
 
 }  // namespace hq
