@@ -162,14 +162,20 @@ def main():
     K_rep = [K] + [K.clone() for _ in range(R_sel - 1)]
     del V
 
+    dec = [H.bind_decode(dims, caches[r], q_new[0], out, ws[r], lse=lse) for r in range(R)]
+    mrg = [H.bind_merge(dims, caches[r]) for r in range(R)]
+    kp = [k_new[j].data_ptr() for j in range(pool)]
+    vp = [v_new[j].data_ptr() for j in range(pool)]
+    qp = [q_new[j].data_ptr() for j in range(pool)]
+
     def step(i, ev=None):
         r = i % R
         t = pos[r]
         j = i % pool
-        H.hq_append_merge(dims, caches[r], t, k_new[j], v_new[j])
+        mrg[r](t, kp[j], vp[j])
         if ev is not None:
             ev[0].record()
-        H.hq_decode_attn(dims, caches[r], t, q_new[j], out, ws[r], lse=lse)
+        dec[r](t, qp[j])
         if ev is not None:
             ev[1].record()
         pos[r] = t + 1
@@ -180,7 +186,7 @@ def main():
     if args.decode_only:
         for i in range(total_steps):
             r = i % R
-            H.hq_decode_attn(dims, caches[r], pos[r], q_new[i % pool], out, ws[r], lse=lse)
+            dec[r](pos[r], qp[i % pool])
         torch.cuda.synchronize()
         print(json.dumps({"decode_only_launches": total_steps, "replicas": R}))
         return
@@ -222,7 +228,7 @@ def main():
 
     def merge_only(i):
         r = i % R
-        H.hq_append_merge(dims, caches[r], pos[r], k_new[i % pool], v_new[i % pool])
+        mrg[r](pos[r], kp[i % pool], vp[i % pool])
         pos[r] += 1
     merge_ms = time_loop(merge_only, 64)
 

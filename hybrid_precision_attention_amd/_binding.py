@@ -136,8 +136,13 @@ class HybridCache:
         return HybridCache(dims, t)
 
     def struct(self) -> hq_cache:
-        return hq_cache(*[(self.t[n].data_ptr() if self.t[n] is not None else None)
-                          for n, _ in hq_cache._fields_])
+        """The ``hq_cache`` of these buffers (built once: tensors never move)."""
+        cs = getattr(self, "_struct", None)
+        if cs is None:
+            cs = hq_cache(*[(self.t[n].data_ptr() if self.t[n] is not None else None)
+                            for n, _ in hq_cache._fields_])
+            self._struct = cs
+        return cs
 
     def clone(self) -> "HybridCache":
         return HybridCache(hq_dims.from_buffer_copy(self.dims),
@@ -189,3 +194,41 @@ def hq_decode_attn(dims, cache: HybridCache, L, q, out, ws, lse=None, stream=Non
                             _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
                             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_attn")
+
+
+# --------------------------------------------------------------------------
+# Pre-bound calls: the pointer arguments are marshalled once, so a decode
+# loop pays one ctypes call per launch and nothing else.
+# --------------------------------------------------------------------------
+def bind_decode(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):
+    """Returns f(L, q_ptr=None): hq_decode_attn on fixed buffers; q_ptr
+    optionally points at another query tensor of the same shape."""
+    cs = cache.struct()
+    d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
+    qp = _ptr(q, torch.float16, "q")
+    op, lp = _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse")
+    wp, wb, sp = _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)
+    fn = lib.hq_decode_attn
+
+    def call(L, q_ptr=None):
+        st = fn(d_ref, c_ref, L, q_ptr or qp, op, lp, wp, wb, sp)
+        if st:
+            raise HQError(st, "hq_decode_attn")
+    call.keep = (dims, cs, q, out, ws, lse)
+    return call
+
+
+def bind_merge(dims, cache: HybridCache, evict_is_vl=None, stream=None):
+    """Returns f(t, k_ptr, v_ptr): hq_append_merge of the token at t whose
+    [B][Hkv][d] fp16 rows start at the given device addresses."""
+    cs = cache.struct()
+    d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
+    ep, sp = _ptr(evict_is_vl, torch.uint8, "evict_is_vl"), _stream(stream)
+    fn = lib.hq_append_merge
+
+    def call(t, k_ptr, v_ptr):
+        st = fn(d_ref, c_ref, t, k_ptr, v_ptr, ep, sp)
+        if st:
+            raise HQError(st, "hq_append_merge")
+    call.keep = (dims, cs, evict_is_vl)
+    return call

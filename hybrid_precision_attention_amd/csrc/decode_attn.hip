@@ -52,10 +52,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
-constexpr int kMaxSplit = 256;      // partial records per unit
-constexpr uint32_t kMagic = 0x64006400u;
-constexpr uint32_t kLo = 0x000F000Fu;
-constexpr uint32_t kHi = 0x00F000F0u;
+constexpr int kMaxSplit = 128;      // partial records per unit
 
 struct DecodeArgs {
   hq_cache c;
@@ -78,6 +75,20 @@ __device__ __forceinline__ half8_t pack4(uint32_t a, uint32_t b, uint32_t c, uin
   return as_half8(make_uint4(a, b, c, d));
 }
 
+// Unpack constants held in VGPRs: gfx950 VOP3 encodings take no literal, so
+// with the masks in registers (x & mask) | magic is one v_and_or_b32.
+struct Masks {
+  uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ Masks make_masks() {
+  Masks k;
+  asm volatile("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
+  asm volatile("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(k.magic));
+  return k;
+}
+
 // biased fp16 pair (1024 + k) -> k * s + m, rounded once
 __device__ __forceinline__ uint32_t dq_pair(uint32_t biased, half2_t s, half2_t m) {
   const half2_t c = as_half2(biased) - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
@@ -90,10 +101,11 @@ __device__ __forceinline__ half2_t sixteenth(half2_t s) {
 
 // Eight nibbles of one K group -> A-operand half8 in element order
 // {0,4,1,5,2,6,3,7}; s/s16/m are the group's scale, scale/16 and min.
-__device__ __forceinline__ half8_t dq_k8(uint32_t w, half2_t s, half2_t s16, half2_t m) {
+__device__ __forceinline__ half8_t dq_k8(uint32_t w, half2_t s, half2_t s16, half2_t m,
+                                        const Masks& k) {
   const uint32_t w8 = w >> 8;
-  return pack4(dq_pair((w & kLo) | kMagic, s, m), dq_pair((w & kHi) | kMagic, s16, m),
-               dq_pair((w8 & kLo) | kMagic, s, m), dq_pair((w8 & kHi) | kMagic, s16, m));
+  return pack4(dq_pair((w & k.lo) | k.magic, s, m), dq_pair((w & k.hi) | k.magic, s16, m),
+               dq_pair((w8 & k.lo) | k.magic, s, m), dq_pair((w8 & k.hi) | k.magic, s16, m));
 }
 
 __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
@@ -113,8 +125,12 @@ struct SoftState {
 __device__ __forceinline__ half8_t softmax_block(SoftState& st, const float s[8], float c2) {
   float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                    fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  {  // max over the four j-lanes of the head (lanes l^16, l^32)
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+  }
   const float m_new = fmaxf(st.m, bm);
   const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
   if (__any(m_new > st.m)) {
@@ -181,19 +197,19 @@ __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint3
 }
 
 __device__ __forceinline__ void qk_tile(float4_t& acc, uint4 codes, uint32_t meta,
-                                        const half8_t qb[4]) {
-  const half2_t s = as_half2((meta & 0xFFFFu) * 0x10001u);
-  const half2_t m = as_half2((meta >> 16) * 0x10001u);
+                                        const half8_t qb[4], const Masks& k) {
+  const half2_t s = as_half2(__builtin_amdgcn_perm(meta, meta, 0x01000100u));
+  const half2_t m = as_half2(__builtin_amdgcn_perm(meta, meta, 0x03020302u));
   const half2_t s16 = sixteenth(s);
-  acc = mfma(dq_k8(codes.x, s, s16, m), qb[0], acc);
-  acc = mfma(dq_k8(codes.y, s, s16, m), qb[1], acc);
-  acc = mfma(dq_k8(codes.z, s, s16, m), qb[2], acc);
-  acc = mfma(dq_k8(codes.w, s, s16, m), qb[3], acc);
+  acc = mfma(dq_k8(codes.x, s, s16, m, k), qb[0], acc);
+  acc = mfma(dq_k8(codes.y, s, s16, m, k), qb[1], acc);
+  acc = mfma(dq_k8(codes.z, s, s16, m, k), qb[2], acc);
+  acc = mfma(dq_k8(codes.w, s, s16, m, k), qb[3], acc);
 }
 
 __device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stage& sg,
-                                           const half8_t qb[4], int tb, int nq, int lane, int n,
-                                           int j, float c2) {
+                                           const half8_t qb[4], const Masks& k, int tb, int nq,
+                                           int lane, int n, int j, float c2) {
   // stage, then read back the transposed operands
   wave_sync();
   *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
@@ -212,8 +228,8 @@ __device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stag
   }
 
   float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-  qk_tile(sa, r.ka, kma, qb);
-  qk_tile(sb, r.kb, kmb, qb);
+  qk_tile(sa, r.ka, kma, qb, k);
+  qk_tile(sb, r.kb, kmb, qb, k);
   float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
   if (tb + kBlk > nq) {
 #pragma unroll
@@ -243,8 +259,8 @@ __device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stag
     for (int p = 0; p < 4; ++p) {
       uint32_t x = (i < 4) ? xl[p] : xh[p];
       if (i & 2) x >>= 8;
-      v[p] = (i & 1) ? dq_pair((x & kHi) | kMagic, sp16[p], mp[p])
-                     : dq_pair((x & kLo) | kMagic, sp[p], mp[p]);
+      v[p] = (i & 1) ? dq_pair((x & k.hi) | k.magic, sp16[p], mp[p])
+                     : dq_pair((x & k.lo) | k.magic, sp[p], mp[p]);
     }
     st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pb, st.o[i]);
   }
@@ -356,11 +372,12 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 }
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  // the per-wave staging areas of the scan and the images of the merges share
-  // LDS (a barrier separates the two uses)
+  // the per-wave staging areas of the scan, the images of the wave merge and
+  // the record weights of the final merge share LDS (barriers separate them)
   __shared__ union {
     K4Stage stage[kWaves];                         // 28 KB
     WaveImage img[kWaves / 2];                     // 34.8 KB
+    float fin[2 * kMaxSplit * 16];                 // 16 KB
   } s_lds;
   WaveImage* s_img = s_lds.img;
   __shared__ float s_mm[16], s_lt[16];
@@ -416,12 +433,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       // an in-range block) so that the wait before the compute only covers the
       // previous iteration's loads
       K4Stage& sg = s_lds.stage[wave];
+      const Masks km = make_masks();
       K4Raw cur;
       load_k4(cur, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
       for (; blk < b1; blk += kWaves) {
         K4Raw nxt;
         load_k4(nxt, kq, kmeta, vq, vmeta, min(blk + kWaves, b1 - 1) * kBlk, nq, lane, n, j);
-        compute_k4(st, cur, sg, qb, blk * kBlk, nq, lane, n, j, c2);
+        compute_k4(st, cur, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
         cur = nxt;
       }
     }
@@ -462,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
 
   __syncthreads();                                 // staging areas are free from here
-  // pairwise merge of the eight waves: 8 -> 4 -> 2 -> 1
+  // pairwise merge of the waves: 8 -> 4 -> 2 -> 1
 #pragma unroll
   for (int half = kWaves / 2; half >= 1; half >>= 1) {
     if (wave >= half && wave < 2 * half) put_state(s_img[wave - half], st, lane);
@@ -502,8 +520,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   // the last workgroup: (m, l) of every record -> LDS, then per-head max,
   // weights and denominators, then the weighted sum of the outputs
-  float* s_pm = &s_img[0].v[0][0];
-  float* s_pl = s_pm + kMaxSplit * 16;
+  float* s_pm = s_lds.fin;
+  float* s_pl = s_lds.fin + kMaxSplit * 16;
   for (int idx = tid; idx < nsplit * G; idx += kThreads) {
     const float* rec = recs + static_cast<int64_t>(idx) * kPart;
     s_pm[idx] = ld_agent(rec);

@@ -22,7 +22,7 @@ constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kDecodeWaves = 8;    // waves per decode workgroup
 constexpr int kBlk = 32;           // tokens per decode block
 constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most
-constexpr int kMaxSplit = 256;     // decode workgroups per unit, at most (LDS of the final merge)
+constexpr int kMaxSplit = 128;     // decode workgroups per unit, at most (LDS of the final merge)
 constexpr int kPartFloats = 132;   // m, l, 2 pad, o[128]
 constexpr double kWgBytes = 192.0 * 1024;  // bytes one decode workgroup streams at small batch
 
