@@ -370,6 +370,11 @@ __device__ __forceinline__ void st_agent(float* p, float v) {
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte store with the same device-scope write-through policy, so a lane's
+// contiguous part of a record leaves in whole lines
+__device__ __forceinline__ void st4_agent(float* p, float4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+}
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // the per-wave staging areas of the scan, the images of the wave merge and
@@ -502,11 +507,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         st_agent(rec, st.m);
         st_agent(rec + 1, lt);
       }
-      float* o = rec + 4 + 32 * j;
+      float* o = rec + 4 + 32 * j;                 // dims 32j + 8r + i
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st_agent(o + 8 * r + i, st.o[i][r]);
+      for (int r = 0; r < 4; ++r) {
+        st4_agent(o + 8 * r, (float4_t){st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]});
+        st4_agent(o + 8 * r + 4, (float4_t){st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]});
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0) {
