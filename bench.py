@@ -64,6 +64,17 @@ def src_hash():
     return h.hexdigest()[:16]
 
 
+def graph_upload(g, torch):
+    """Upload an instantiated graph before its timed replay (hipGraphUpload)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipGraphUpload.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    st = hip.hipGraphUpload(ctypes.c_void_p(g.raw_cuda_graph_exec()),
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"hipGraphUpload failed ({st})")
+
+
 def load_traffic(wl_name, B):
     """HBM bytes per decode launch from the committed rocprofv3 counter runs,
     or None when they were taken on another kernel source or workload."""
@@ -162,28 +173,30 @@ def main():
     K_rep = [K] + [K.clone() for _ in range(R_sel - 1)]
     del V
 
-    dec = [H.bind_decode(dims, caches[r], q_new[0], out, ws[r], lse=lse) for r in range(R)]
-    mrg = [H.bind_merge(dims, caches[r]) for r in range(R)]
     kp = [k_new[j].data_ptr() for j in range(pool)]
     vp = [v_new[j].data_ptr() for j in range(pool)]
     qp = [q_new[j].data_ptr() for j in range(pool)]
 
-    def step(i, ev=None):
-        r = i % R
-        t = pos[r]
-        j = i % pool
-        mrg[r](t, kp[j], vp[j])
-        if ev is not None:
-            ev[0].record()
-        dec[r](t, qp[j])
-        if ev is not None:
-            ev[1].record()
-        pos[r] = t + 1
-        if i % REFRESH == REFRESH - 1:
-            H.hq_select_vertical(dims_sel, qbuf, K_rep[(i // REFRESH) % R_sel], L, score,
-                                 vl_idx, vl_flag, ws_sel)
+    def make_step(stream):
+        """Step function launching on ``stream`` (pointer arguments marshalled once)."""
+        dec = [H.bind_decode(dims, caches[r], q_new[0], out, ws[r], lse=lse, stream=stream)
+               for r in range(R)]
+        mrg = [H.bind_merge(dims, caches[r], stream=stream) for r in range(R)]
+
+        def step(i):
+            r = i % R
+            t = pos[r]
+            j = i % pool
+            mrg[r](t, kp[j], vp[j])
+            dec[r](t, qp[j])
+            pos[r] = t + 1
+            if i % REFRESH == REFRESH - 1:
+                H.hq_select_vertical(dims_sel, qbuf, K_rep[(i // REFRESH) % R_sel], L, score,
+                                     vl_idx, vl_flag, ws_sel, stream=stream)
+        return step, dec
 
     if args.decode_only:
+        _, dec = make_step(torch.cuda.current_stream())
         for i in range(total_steps):
             r = i % R
             dec[r](pos[r], qp[i % pool])
@@ -191,23 +204,56 @@ def main():
         print(json.dumps({"decode_only_launches": total_steps, "replicas": R}))
         return
 
+    eager_step, _ = make_step(torch.cuda.current_stream())
     for i in range(args.warmup):
-        step(i)
+        eager_step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+
+    # The K timed steps are captured once into a HIP graph (through torch) and
+    # replayed once, so the host's per-launch cost stays out of the step time.
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(torch.cuda.current_stream())
+        graph_upload(g, torch)
+        return g
+
+    def timed_steps(stream):
+        st, _ = make_step(stream)
+        for k in range(args.steps):
+            st(args.warmup + k)
+    g_steps = capture(timed_steps)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t_host = time.perf_counter()
     start.record()
-    for k in range(args.steps):
-        step(args.warmup + k, evs[k])
+    g_steps.replay()
     stop.record()
     torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
     total_ms = start.elapsed_time(stop)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
     ms_step = total_ms / args.steps
-    dec_avg_ms = float(np.mean(dec_ms))
+
+    # Average decode launch duration: the same decode launches back to back
+    # (rotating replicas, current positions), replayed from a graph between
+    # HIP events on the launching stream.
+    n_dec = args.steps
+
+    def dec_body(stream):
+        _, dec = make_step(stream)
+        for i in range(n_dec):
+            r = i % R
+            dec[r](pos[r], qp[i % pool])
+    g_dec = capture(dec_body)
+    g_dec.replay()                                  # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_dec.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_avg_ms = e0.elapsed_time(e1) / n_dec
 
     # ---- per-row timings (each on its own, same rotation) -----------------
     def time_loop(fn, n):
@@ -225,6 +271,8 @@ def main():
     spare = H.HybridCache.allocate(B, Hq, Hkv, W, wl.rho, L_max)
     pack_ms = time_loop(lambda i: H.hq_quant_pack(spare.dims, K_rep[i % R_sel], K_rep[(i + 1) % R_sel],
                                                   L, vl_flag, spare), 4)
+
+    mrg = [H.bind_merge(dims, caches[r]) for r in range(R)]
 
     def merge_only(i):
         r = i % R
@@ -259,7 +307,8 @@ def main():
                      "traffic": traffic, "kernel": "decode_kernel (hq_decode_attn)",
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
-        "step_us": round(ms_step * 1e3, 2),
+        "step_us": round(ms_step * 1e3, 2), "timed_host_s": round(t_host, 4),
+        "timing": "K steps captured as one HIP graph, replayed once between HIP events",
         "rows_us": {"decode": round(dec_avg_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
                     "select": round(sel_ms * 1e3, 2), "pack": round(pack_ms * 1e3, 2)},
         "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step, 4),

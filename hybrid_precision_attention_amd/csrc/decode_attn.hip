@@ -331,61 +331,45 @@ __device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], 
   }
 }
 
-// LDS image of one wave's state, element-major so lanes hit distinct banks.
-struct WaveImage {
-  float v[34][64];                  // m, l, o[32]
+// LDS image of the waves' states for up to eight heads at a time:
+// o[w][g][dim], plus each wave's running max and denominator per head.
+constexpr int kImgHeads = 8;
+struct WgImage {
+  float o[kWaves][kImgHeads][kD];
+  float m[kWaves][kImgHeads];
+  float l[kWaves][kImgHeads];
 };
 
-__device__ __forceinline__ void put_state(WaveImage& w, const SoftState& st, int lane) {
-  w.v[0][lane] = st.m;
-  w.v[1][lane] = st.l;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w.v[2 + 4 * i + r][lane] = st.o[i][r];
-}
-
-// merge another wave's state (same lane layout) into this one
-__device__ __forceinline__ void merge_state(SoftState& st, const WaveImage& w, int lane, float c2) {
-  const float mo = w.v[0][lane];
-  const float mm = fmaxf(st.m, mo);
-  if (mm == -INFINITY) return;
-  const float fa = __builtin_amdgcn_exp2f((st.m - mm) * c2);
-  const float fb = __builtin_amdgcn_exp2f((mo - mm) * c2);
-  st.m = mm;
-  st.l = st.l * fa + w.v[1][lane] * fb;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) st.o[i][r] = st.o[i][r] * fa + w.v[2 + 4 * i + r][lane] * fb;
-}
+// Per-thread partial of the final merge: (max, denominator, four dims).
+struct FinPart {
+  float m, l, pad0, pad1;
+  float4_t o;
+};
 
 // Partial records cross XCDs.  They are written and read with device-scope
 // relaxed atomics (write-through / coherent-read of the XCD-local L2), and the
 // writer waits for its stores before counting its arrival, so no fence has to
 // write back or invalidate a whole L2.
-__device__ __forceinline__ void st_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// 8-byte device-scope load of two adjacent record floats
+__device__ __forceinline__ float2 ld2_agent(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(float2, v);
 }
-__device__ __forceinline__ float ld_agent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// 16-byte store with the same device-scope write-through policy, so a lane's
-// contiguous part of a record leaves in whole lines
+// 16-byte store with the device-scope write-through policy (sc1), so a
+// record leaves in whole lines
 __device__ __forceinline__ void st4_agent(float* p, float4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-  // the per-wave staging areas of the scan, the images of the wave merge and
-  // the record weights of the final merge share LDS (barriers separate them)
+  // the per-wave staging areas of the scan, the image of the waves' states
+  // and the partials of the final merge share LDS (barriers separate them)
   __shared__ union {
     K4Stage stage[kWaves];                         // 28 KB
-    WaveImage img[kWaves / 2];                     // 34.8 KB
-    float fin[2 * kMaxSplit * 16];                 // 16 KB
+    WgImage img;                                   // 33 KB
+    FinPart fin[kThreads];                         // 16 KB
   } s_lds;
-  WaveImage* s_img = s_lds.img;
-  __shared__ float s_mm[16], s_lt[16];
   __shared__ int s_last;
 
   const int tid = threadIdx.x;
@@ -484,87 +468,136 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  __syncthreads();                                 // staging areas are free from here
-  // pairwise merge of the waves: 8 -> 4 -> 2 -> 1
-#pragma unroll
-  for (int half = kWaves / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) put_state(s_img[wave - half], st, lane);
-    __syncthreads();
-    if (wave < half) merge_state(st, s_img[wave], lane, c2);
-    __syncthreads();
-  }
-
-  // wave 0 writes the workgroup's partial record (heads 0..G-1), waits for
-  // the stores, and counts the workgroup's arrival
+  // Merge the eight waves' states and publish the workgroup's record.  The
+  // waves write their states to LDS once; thread (head g, dims 4c..4c+3)
+  // merges them and stores its part of the record with 16-byte device-scope
+  // stores, at most eight heads per round.
   float* recs = a.part + u * nsplit * static_cast<int64_t>(G) * kPart;
-  if (wave == 0) {
-    float lt = st.l;
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    if (n < G) {
-      float* rec = recs + (static_cast<int64_t>(split) * G + n) * kPart;
-      if (j == 0) {
-        st_agent(rec, st.m);
-        st_agent(rec + 1, lt);
-      }
-      float* o = rec + 4 + 32 * j;                 // dims 32j + 8r + i
+  float lsum = st.l;                               // the head's denominator: sum over j
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  WgImage& img = s_lds.img;
+  for (int g0 = 0; g0 < G; g0 += kImgHeads) {
+    __syncthreads();                               // staging areas / previous round free
+    const int gl = n - g0;
+    if (gl >= 0 && gl < kImgHeads && n < G) {
+      float* o = &img.o[wave][gl][32 * j];         // dims 32j + 8r + i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        st4_agent(o + 8 * r, (float4_t){st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]});
-        st4_agent(o + 8 * r + 4, (float4_t){st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]});
+        *reinterpret_cast<float4_t*>(o + 8 * r) = (float4_t){st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]};
+        *reinterpret_cast<float4_t*>(o + 8 * r + 4) = (float4_t){st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]};
+      }
+      if (j == 0) {
+        img.m[wave][gl] = st.m;
+        img.l[wave][gl] = lsum;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (lane == 0) {
-      const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (old == nsplit - 1);
+    __syncthreads();
+    const int gn = min(kImgHeads, G - g0);
+    if (tid < gn * (kD / 4)) {
+      const int gl2 = tid >> 5, c = tid & 31;
+      float mw[kWaves];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = img.m[w][gl2];
+        mx = fmaxf(mx, mw[w]);
+      }
+      float lt = 0.0f;
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = __builtin_amdgcn_exp2f((mw[w] - mx) * c2);
+          lt = fmaf(f, img.l[w][gl2], lt);
+          acc += f * *reinterpret_cast<const float4_t*>(&img.o[w][gl2][4 * c]);
+        }
+      }
+      float* rec = recs + (static_cast<int64_t>(split) * G + g0 + gl2) * kPart;
+      if (c == 0) st4_agent(rec, (float4_t){mx, lt, 0.0f, 0.0f});
+      st4_agent(rec + 4 + 4 * c, acc);
     }
+  }
+  // every store of the record is complete before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == nsplit - 1);
   }
   __syncthreads();
   if (!s_last) return;
 
-  // the last workgroup: (m, l) of every record -> LDS, then per-head max,
-  // weights and denominators, then the weighted sum of the outputs
-  float* s_pm = s_lds.fin;
-  float* s_pl = s_lds.fin + kMaxSplit * 16;
-  for (int idx = tid; idx < nsplit * G; idx += kThreads) {
-    const float* rec = recs + static_cast<int64_t>(idx) * kPart;
-    s_pm[idx] = ld_agent(rec);
-    s_pl[idx] = ld_agent(rec + 1);
-  }
-  __syncthreads();
-  for (int g = wave; g < G; g += kWaves) {
-    float mx = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) mx = fmaxf(mx, s_pm[s * G + g]);
+  // The last workgroup merges the unit's records.  Thread (sub, head g, dims
+  // 4c..4c+3) folds records sub, sub + S, ... with all of a chunk's loads in
+  // flight at once; the S partials of an output are then combined in LDS.
+  const int items = G * (kD / 4);
+  const int S = max(1, kThreads / items);
+  for (int it0 = 0; it0 < items; it0 += kThreads) {
+    const int item = it0 + tid % items;
+    const int sub = tid / items;
+    const bool active = sub < S && item < items;
+    FinPart part = {-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+    if (active) {
+      const int g = item >> 5, c = item & 31;
+      const float* base = recs + static_cast<int64_t>(g) * kPart;
+      constexpr int kChunk = 8;
+      for (int s0 = sub; s0 < nsplit; s0 += kChunk * S) {
+        float2 ml[kChunk], o01[kChunk], o23[kChunk];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float lt = 0.0f;
-    for (int s = lane; s < nsplit; s += 64) {
-      const float f = (mx == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f((s_pm[s * G + g] - mx) * c2);
-      s_pm[s * G + g] = f;
-      lt += f * s_pl[s * G + g];
-    }
+        for (int k = 0; k < kChunk; ++k) {
+          const int sidx = min(s0 + k * S, nsplit - 1);   // clamped; weight 0 below
+          const float* rec = base + static_cast<int64_t>(sidx) * G * kPart;
+          ml[k] = ld2_agent(rec);
+          o01[k] = ld2_agent(rec + 4 + 4 * c);
+          o23[k] = ld2_agent(rec + 6 + 4 * c);
+        }
+        float mx = part.m;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lt += __shfl_xor(lt, o);
-    if (lane == 0) {
-      s_mm[g] = mx;
-      s_lt[g] = lt;
+        for (int k = 0; k < kChunk; ++k)
+          if (s0 + k * S < nsplit) mx = fmaxf(mx, ml[k].x);
+        if (mx == -INFINITY) continue;
+        const float fa = __builtin_amdgcn_exp2f((part.m - mx) * c2);
+        part.l *= fa;
+        part.o *= fa;
+#pragma unroll
+        for (int k = 0; k < kChunk; ++k) {
+          const float f = (s0 + k * S < nsplit) ? __builtin_amdgcn_exp2f((ml[k].x - mx) * c2) : 0.0f;
+          part.l = fmaf(f, ml[k].y, part.l);
+          part.o += f * (float4_t){o01[k].x, o01[k].y, o23[k].x, o23[k].y};
+        }
+        part.m = mx;
+      }
     }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += kThreads) {
-    const int g = idx >> 7, dim = idx & (kD - 1);
-    const float* src = recs + static_cast<int64_t>(g) * kPart + 4 + dim;
-    float o = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < nsplit; ++s)
-      o = fmaf(s_pm[s * G + g], ld_agent(src + static_cast<int64_t>(s) * G * kPart), o);
-    const float lt = s_lt[g];
-    const float res = lt > 0.0f ? o / lt : 0.0f;
-    a.out[(b * a.Hq + h0 + g) * kD + dim] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(res));
-    if (dim == 0 && a.lse)
-      a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (s_mm[g] * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    if (it0 > 0) __syncthreads();                  // previous round's partials read
+    s_lds.fin[tid] = part;
+    __syncthreads();
+    if (active && sub == 0) {
+      float mx = -INFINITY;
+      for (int q = 0; q < S; ++q) mx = fmaxf(mx, s_lds.fin[tid + q * items].m);
+      float lt = 0.0f;
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if (mx != -INFINITY) {
+        for (int q = 0; q < S; ++q) {
+          const FinPart& pq = s_lds.fin[tid + q * items];
+          const float f = __builtin_amdgcn_exp2f((pq.m - mx) * c2);
+          lt = fmaf(f, pq.l, lt);
+          acc += f * pq.o;
+        }
+      }
+      const int g = item >> 5, c = item & 31;
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      uint16_t* dst = a.out + (b * a.Hq + h0 + g) * kD + 4 * c;
+      uint2 pk;
+      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[0] * inv)) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[1] * inv)) << 16);
+      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[2] * inv)) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[3] * inv)) << 16);
+      *reinterpret_cast<uint2*>(dst) = pk;
+      if (c == 0 && a.lse)
+        a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    }
   }
   if (tid == 0) a.counters[u] = 0;
 }

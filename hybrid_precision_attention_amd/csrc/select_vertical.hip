@@ -7,21 +7,27 @@
 // paragraph; HyQuant README, Overview item 1).
 //
 // Rows of a unit are its R = G * nb buffered queries (row r = g * nb + jq, at
-// position L - nb + jq).  Three kernels stream the unit's keys:
-//   1. row_stats: per 256-key tile, the (max, sum of exp) of every row over
-//      the tile's causal keys;  2. row_lse: merge the tiles -> natural-log
-//      LSE per row (skipped when the caller passes it);  3. col_mass: per
-//      256-key tile of the non-window prefix, sum over rows of
-//      exp(tau q.k - lse) and add it to the running score.
-// Both streaming passes compute S = K Q^T with v_mfma_f32_16x16x32_f16
-// (A = 16 keys, B = 16 rows), each wave owning 64 keys for all row blocks.
-// The sums use a fixed order (no float atomics) so reruns are bit-identical.
-// 4. topk: one workgroup per unit finds the n_vl-th largest score by an
-//    MSB-first radix select over order-preserving integer keys (per-wave LDS
-//    histograms), then flags positions in ascending order (ties at the
-//    threshold to the lower positions) and compacts them into vl_idx.
+// position L - nb + jq).  Two streaming kernels read the unit's keys:
+//   1. row_stats: per streaming workgroup, the (max, sum of exp) of every row
+//      over the workgroup's causal keys (skipped when the caller passes the
+//      rows' LSE);
+//   2. col_mass: merges those into each row's LSE, then for every key of the
+//      non-window prefix sums exp(tau q.k - lse) over the rows and adds it to
+//      the running score.
+// Both compute S = K Q^T with v_mfma_f32_16x16x32_f16 (A = 16 keys, B = 16
+// rows).  A workgroup stages up to 256 rows of queries in LDS; each of its
+// eight waves holds 64 keys in registers with the next 64 in flight, and the
+// next row block's MFMAs are interleaved with the current block's
+// exponentials.  More than 256 rows (G > 4) form row groups on the grid.
+// Every sum has a fixed order (no float atomics): reruns are bit-identical.
+//   3. topk: one workgroup per unit finds the n_vl-th largest score by a
+//      radix select over order-preserving integer keys, then flags positions
+//      in ascending order (ties at the threshold to the lower positions) and
+//      compacts them into vl_idx.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 
 #include "hq_device.h"
 #include "hq_launch.h"
@@ -30,26 +36,38 @@ namespace hq {
 
 namespace {
 
-constexpr int kTile = 256;          // keys per streaming workgroup
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxRows = 16 * 64;   // G <= 16, nb <= 64
+constexpr int kSWaves = 8;            // waves per streaming workgroup
+constexpr int kSThreads = 64 * kSWaves;
+constexpr int kChunk = 64;            // keys a wave holds in registers at a time
+constexpr int kRG = 256;              // rows per row group (queries staged in LDS)
+constexpr int kRB = kRG / 16;         // 16-row blocks per row group
 constexpr int kTopThreads = 1024;
 
 struct SelArgs {
   const uint16_t* qbuf;
   const uint16_t* k;
   const float* lse;                 // natural log, [B][Hq][nb]
-  float* lse_out;                   // where row_lse writes
-  float2* stats;                    // [U][ntiles][R] (max raw score, sum exp2)
+  float2* stats;                    // [U][nwg1][R] (max raw score, sum exp2)
+  float* colpart;                   // [nrg][U][n_nw] column mass per row group (nrg > 1)
   float* score;
   int32_t* vl_idx;
   uint8_t* vl_flag;
-  int32_t Hq, Hkv, G, nb, L, W, R, ntiles, n_nw, n_vl;
+  int32_t Hq, Hkv, G, nb, L, W, R, n_nw, n_vl;
+  int32_t C;                        // chunks per wave
+  int32_t wg_keys;                  // keys per streaming workgroup = 64 * 8 * C
+  int32_t nwg1, nrg, U;
+  int32_t lse_from_stats;           // 1: rows' LSE merged from stats by col_mass
   float c2;                         // log2(e) / sqrt(d)
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+
+// float -> unsigned key with the same order (-0 folded onto +0)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t bits = __builtin_bit_cast(uint32_t, f);
+  if (bits == 0x80000000u) bits = 0;
+  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
 
 // max / sum with lanes l^16 and l^32 (the four j-lanes of a row), through the
 // VALU lane-swap instructions rather than the LDS crossbar
@@ -71,7 +89,8 @@ __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
 }
 
 // K operand of the wave's 64 keys: lane (key t, j) holds dims 32j..32j+31 of
-// key k0 + 16x + t for x = 0..3, natural order (k-step kk = dims 32j+8kk..).
+// key k0 + 16x + t for x = 0..3 (k-step kk = dims 32j+8kk..).  Keys past the
+// last one are clamped to it, so the loads are unconditional.
 __device__ __forceinline__ void load_keys(uint4 kr[4][4], const uint16_t* kunit, int k0, int L,
                                           int n, int j) {
 #pragma unroll
@@ -83,61 +102,62 @@ __device__ __forceinline__ void load_keys(uint4 kr[4][4], const uint16_t* kunit,
   }
 }
 
-// B operand of one 16-row block: lane (row n, j) = row rb*16+n, dims 32j...
-// Rows past the last one are clamped to it (their scores are masked), so the
-// loads are unconditional and a prefetch stays in flight across the compute.
-__device__ __forceinline__ void load_rows(half8_t qb[4], const SelArgs& a, int64_t b, int h0,
-                                          int rb, int n, int j) {
-  const int r = min(rb * 16 + n, a.R - 1);
-  const int g = r / a.nb, jq = r - g * a.nb;
-  const uint16_t* p = a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 32 * j;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qb[kk] = as_half8(ld16(p + 8 * kk));
-}
+// Rows [256 rg, 256 rg + 256) of the unit's buffered queries in LDS, in the
+// B-operand order of the MFMA: q[rb][kk][16 j + n] = dims 32j + 8kk .. +7 of
+// row 16 rb + n.  Rows past the last one repeat it (their results are
+// discarded).  Every lane of a wave then reads 16 consecutive bytes.
+using QStage = uint4[kRB][4][64];
 
-__device__ __forceinline__ void scores(float4_t s[4], const uint4 kr[4][4], const half8_t qb[4]) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    s[x] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s[x] = mfma(as_half8(kr[x][kk]), qb[kk], s[x]);
+__device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t b, int h0, int rg) {
+  for (int idx = threadIdx.x; idx < kRG * 16; idx += kSThreads) {
+    const int rr = idx >> 4, ch = idx & 15;
+    const int r = min(rg * kRG + rr, a.R - 1);
+    const int g = r / a.nb, jq = r - g * a.nb;
+    sq[rr >> 4][ch & 3][16 * (ch >> 2) + (rr & 15)] =
+        ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
   }
 }
 
-// Pass 1: per (tile, unit), (max, sum exp2) of each row over the tile's keys.
-__global__ __launch_bounds__(kThreads) void row_stats_kernel(SelArgs a) {
-  __shared__ float2 s_st[kWaves][kMaxRows];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, j = lane >> 4;
-  const int64_t u = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int64_t b = u / a.Hkv;
-  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
-  const int k0 = tile * kTile + 64 * wave;
-  // every key of this wave precedes every buffered query: no causal mask
-  const bool interior = k0 + 64 <= a.L - a.nb;
-  const uint16_t* kunit = a.k + u * a.L * kD;
-  uint4 kr[4][4];
-  load_keys(kr, kunit, k0, a.L, n, j);
-  const int nrb = (a.R + 15) / 16;
+__device__ __forceinline__ void scores(float4_t s[4], const uint4 kr[4][4], const QStage& sq,
+                                       int rb, int lane) {
   half8_t qb[4];
-  load_rows(qb, a, b, h0, 0, n, j);
-  for (int rb = 0; rb < nrb; ++rb) {
-    half8_t qn[4];                                   // next row block, loaded early
-    load_rows(qn, a, b, h0, min(rb + 1, nrb - 1), n, j);
-    __builtin_amdgcn_sched_barrier(0);               // keep the prefetch ahead of the compute
-    float4_t s[4];
-    scores(s, kr, qb);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
-    const int r = rb * 16 + n;
+  for (int kk = 0; kk < 4; ++kk) qb[kk] = as_half8(sq[rb][kk][lane]);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) s[x] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  // four independent accumulation chains, interleaved
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int x = 0; x < 4; ++x) s[x] = mfma(as_half8(kr[x][kk]), qb[kk], s[x]);
+}
+
+// Streaming workgroup (x, unit, row group): keys [x * wg_keys, ...), wave w
+// taking 64-key chunks w, w + 8, ... with the next chunk's keys in flight
+// while the current one is computed; the row group's queries sit in LDS.
+// Inside a chunk the scores of row block rb + 1 are issued to the matrix
+// cores before the exponentials of row block rb, so the two overlap.
+
+// Pass 1 over one chunk: every lane keeps its own running (max, sum) per row
+// block for the keys it holds (no cross-lane work inside the loop).
+template <bool kMasked>
+__device__ __forceinline__ void chunk_row_stats(float2 (*st)[64], const uint4 kr[4][4],
+                                                const QStage& sq, const SelArgs& a, int rg, int k0,
+                                                int lane, int n, int j) {
+  float4_t sc[4];
+  scores(sc, kr, sq, 0, lane);
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    float4_t sn[4];
+    if (rb + 1 < kRB) scores(sn, kr, sq, rb + 1, lane);
     float v[16];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * x + e] = s[x][e];
-    if (!interior) {
+      for (int e = 0; e < 4; ++e) v[4 * x + e] = sc[x][e];
+    if (kMasked) {
       // keys past the prefix or after the row's own position do not count
+      const int r = min(rg * kRG + rb * 16 + n, a.R - 1);
       const int prow = a.L - a.nb + (r - (r / a.nb) * a.nb);
 #pragma unroll
       for (int x = 0; x < 4; ++x)
@@ -147,271 +167,466 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(SelArgs a) {
           if (!(key < a.L && key <= prow)) v[4 * x + e] = -INFINITY;
         }
     }
-    float mx = v[0];
+    const float2 old = st[rb][lane];
+    float mx = old.x;
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, v[e]);
-    mx = max_j(mx);
-    float sum = 0.0f;
-    if (mx != -INFINITY) {
-      const float nmc = -mx * a.c2;
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(v[e], v[e + 1]));
+    const float mu = (kMasked && mx == -INFINITY) ? 0.0f : mx;
+    const float nmc = -mu * a.c2;
+    float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(fmaf(v[e], a.c2, nmc));
+    for (int e = 0; e < 16; e += 2) {
+      s0 += __builtin_amdgcn_exp2f(fmaf(v[e], a.c2, nmc));
+      s1 += __builtin_amdgcn_exp2f(fmaf(v[e + 1], a.c2, nmc));
     }
-    sum = sum_j(sum);
-    if (j == 0 && r < a.R) s_st[wave][r] = make_float2(mx, sum);
+    st[rb][lane] = make_float2(mx, fmaf(old.y, __builtin_amdgcn_exp2f(fmaf(old.x, a.c2, nmc)), s0 + s1));
+    if (!kMasked && rb + 1 < kRB) {
+      // the next row block's 16 MFMAs interleaved with this block's VALU
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+    if (rb + 1 < kRB) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sc[x] = sn[x];
+    }
+  }
+}
+
+// Pass 1: per (workgroup, row), (max raw score, sum exp2) over its keys.
+__global__ __launch_bounds__(kSThreads) void row_stats_kernel(SelArgs a) {
+  __shared__ QStage s_q;                                    // 64 KB
+  // each lane's running (max, sum) of row 16 rb + n over the keys it held
+  __shared__ float2 s_run[kSWaves][kRB][64];                // 64 KB
+  __shared__ float2 s_st[kSWaves][kRG];                     // 16 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int64_t u = blockIdx.y;
+  const int rg = blockIdx.z;
+  const int64_t b = u / a.Hkv;
+  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
+  const int wg0 = blockIdx.x * a.wg_keys;
+  const uint16_t* kunit = a.k + u * a.L * kD;
+  uint4 kr[4][4];
+  load_keys(kr, kunit, wg0 + kChunk * wave, a.L, n, j);
+  stage_rows(s_q, a, b, h0, rg);
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) s_run[wave][rb][lane] = make_float2(-INFINITY, 0.0f);
+  __syncthreads();
+
+  for (int i = 0; i < a.C; ++i) {
+    const int k0 = wg0 + kChunk * (wave + kSWaves * i);
+    if (k0 >= a.L) break;
+    uint4 kn[4][4];
+    load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
+    __builtin_amdgcn_sched_barrier(0);                      // keep the prefetch ahead
+    // every key of the chunk precedes every buffered query: no causal mask
+    if (k0 + kChunk <= a.L - a.nb)
+      chunk_row_stats<false>(s_run[wave], kr, s_q, a, rg, k0, lane, n, j);
+    else
+      chunk_row_stats<true>(s_run[wave], kr, s_q, a, rg, k0, lane, n, j);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kr[x][kk] = kn[x][kk];
+  }
+  // merge the four j-lanes of each row, then the waves
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float2 v = s_run[wave][rb][lane];
+    const float m = max_j(v.x);
+    const float mu = (m == -INFINITY) ? 0.0f : m;
+    const float sum = sum_j(v.y * __builtin_amdgcn_exp2f((v.x - mu) * a.c2));
+    if (j == 0) s_st[wave][rb * 16 + n] = make_float2(m, sum);
   }
   __syncthreads();
-  float2* out = a.stats + (u * a.ntiles + tile) * a.R;
-  for (int r = tid; r < a.R; r += kThreads) {
+  float2* out = a.stats + (u * a.nwg1 + blockIdx.x) * a.R + rg * kRG;
+  const int nr = min(kRG, a.R - rg * kRG);
+  for (int r = tid; r < nr; r += kSThreads) {
     float mx = s_st[0][r].x;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_st[w][r].x);
+    for (int w = 1; w < kSWaves; ++w) mx = fmaxf(mx, s_st[w][r].x);
     float sum = 0.0f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
+      for (int w = 0; w < kSWaves; ++w)
         sum = fmaf(s_st[w][r].y, __builtin_amdgcn_exp2f((s_st[w][r].x - mx) * a.c2), sum);
     }
     out[r] = make_float2(mx, sum);
   }
 }
 
-// Merge the tiles' row statistics into the natural-log LSE of every row: one
-// wave per row, lanes over tiles, a butterfly merge of (max, sum) pairs.
-__global__ __launch_bounds__(kThreads) void row_lse_kernel(SelArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t u = blockIdx.y;
-  if (r >= a.R) return;
-  const int64_t b = u / a.Hkv;
-  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
-  const float2* st = a.stats + u * a.ntiles * a.R + r;
-  float mx = -INFINITY, sum = 0.0f;
-  for (int t = lane; t < a.ntiles; t += 64) {
-    const float2 v = st[static_cast<int64_t>(t) * a.R];
-    const float m2 = fmaxf(mx, v.x);
-    if (m2 != -INFINITY)
-      sum = sum * exp2f((mx - m2) * a.c2) + v.y * exp2f((v.x - m2) * a.c2);
-    mx = m2;
-  }
+// Pass 2 over one chunk: acc[4x + e] += sum over the lane's rows of
+// exp2(c2 s - lse log2 e) for key k0 + 16x + 4j + e.
+template <bool kMasked>
+__device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][4], const QStage& sq,
+                                               const float* s_nl, const SelArgs& a, int rg, int k0,
+                                               int lane, int n, int j) {
+  float4_t sc[4];
+  scores(sc, kr, sq, 0, lane);
+  float nl_c = s_nl[n];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float om = __shfl_xor(mx, o), os = __shfl_xor(sum, o);
-    const float m2 = fmaxf(mx, om);
-    if (m2 != -INFINITY) sum = sum * exp2f((mx - m2) * a.c2) + os * exp2f((om - m2) * a.c2);
-    mx = m2;
-  }
-  if (lane == 0) {
-    const int g = r / a.nb, jq = r - g * a.nb;
-    a.lse_out[(b * a.Hq + h0 + g) * a.nb + jq] = (mx * a.c2 + log2f(sum)) * 0.69314718055994531f;
-  }
-}
-
-// Pass 2: column mass of a 256-key tile of the non-window prefix.
-__global__ __launch_bounds__(kThreads) void col_mass_kernel(SelArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, j = lane >> 4;
-  const int64_t u = blockIdx.y;
-  const int64_t b = u / a.Hkv;
-  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
-  const int k0 = blockIdx.x * kTile + 64 * wave;
-  if (k0 >= a.n_nw) return;
-  // all 64 keys are non-window and precede every buffered query
-  const bool interior = k0 + 64 <= min(a.n_nw, a.L - a.nb);
-  const uint16_t* kunit = a.k + u * a.L * kD;
-  uint4 kr[4][4];
-  load_keys(kr, kunit, k0, a.L, n, j);
-  float acc[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-  const float log2e = 1.4426950408889634f;
-  const int nrb = (a.R + 15) / 16;
-  auto row_lse = [&](int rb) {
-    const int rc = min(rb * 16 + n, a.R - 1);
-    const int g = rc / a.nb, jq = rc - g * a.nb;
-    return a.lse[(b * a.Hq + h0 + g) * a.nb + jq];
-  };
-  half8_t qb[4];
-  load_rows(qb, a, b, h0, 0, n, j);
-  float lse_cur = row_lse(0);
-  for (int rb = 0; rb < nrb; ++rb) {
-    half8_t qn[4];                                   // next row block, loaded early
-    const int rn = min(rb + 1, nrb - 1);
-    load_rows(qn, a, b, h0, rn, n, j);
-    const float lse_nxt = row_lse(rn);
-    __builtin_amdgcn_sched_barrier(0);               // keep the prefetch ahead of the compute
-    const int r = rb * 16 + n;
-    const float nl2 = (r < a.R) ? -lse_cur * log2e : -INFINITY;   // padded rows add 0
-    float4_t s[4];
-    scores(s, kr, qb);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qb[kk] = qn[kk];
-    lse_cur = lse_nxt;
-    if (interior) {
+  for (int rb = 0; rb < kRB; ++rb) {
+    float4_t sn[4];
+    float nl_n = 0.0f;
+    if (rb + 1 < kRB) {
+      scores(sn, kr, sq, rb + 1, lane);
+      nl_n = s_nl[(rb + 1) * 16 + n];
+    }
+    if (!kMasked) {
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[4 * x + e] += __builtin_amdgcn_exp2f(fmaf(s[x][e], a.c2, nl2));
+          acc[4 * x + e] += __builtin_amdgcn_exp2f(fmaf(sc[x][e], a.c2, nl_c));
+      if (rb + 1 < kRB) {
+        // the next row block's 16 MFMAs interleaved with this block's 48 VALU
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
     } else {
-      const int rc = min(r, a.R - 1);
-      const int prow = a.L - a.nb + (rc - (rc / a.nb) * a.nb);
+      const int r = min(rg * kRG + rb * 16 + n, a.R - 1);
+      const int prow = a.L - a.nb + (r - (r / a.nb) * a.nb);
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = k0 + 16 * x + 4 * j + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[x][e], a.c2, nl2));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[x][e], a.c2, nl_c));
           acc[4 * x + e] += (key < a.n_nw && key <= prow) ? p : 0.0f;
         }
     }
-  }
-  // sum over the 16 row lanes of each key (butterfly: every lane gets the total)
+    if (rb + 1 < kRB) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float v = acc[e];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    acc[e] = v;
-  }
-  if (n < 4) {
-    float* sc = a.score + u * a.L;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      if (x != n) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = k0 + 16 * x + 4 * j + e;
-        if (key < a.n_nw) sc[key] += acc[4 * x + e];
-      }
+      for (int x = 0; x < 4; ++x) sc[x] = sn[x];
+      nl_c = nl_n;
     }
   }
 }
 
-// float -> unsigned key with the same order (-0 folded onto +0)
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t bits = __builtin_bit_cast(uint32_t, f);
-  if (bits == 0x80000000u) bits = 0;
-  return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+// Pass 2: column mass of the non-window keys: per key, the sum over the row
+// group's rows of exp(tau q.k - lse), added to the running score (one row
+// group) or written as the group's part (several; top-k folds them in).
+__global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
+  __shared__ QStage s_q;                                    // 64 KB
+  __shared__ float s_nl[kRG];                               // -lse * log2(e), -inf for padding
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int64_t u = blockIdx.y;
+  const int rg = blockIdx.z;
+  const int64_t b = u / a.Hkv;
+  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
+  const int wg0 = blockIdx.x * a.wg_keys;
+  const uint16_t* kunit = a.k + u * a.L * kD;
+  const int lim = a.n_nw;
+  uint4 kr[4][4];
+  load_keys(kr, kunit, wg0 + kChunk * wave, a.L, n, j);
+  stage_rows(s_q, a, b, h0, rg);
+  for (int rr = tid; rr < kRG; rr += kSThreads) {
+    const int r = rg * kRG + rr;
+    float nl = -INFINITY;                                   // padding rows add nothing
+    if (r < a.R) {
+      if (a.lse_from_stats) {
+        // merge the row's (max, sum exp2) over the pass-1 workgroups: the
+        // max first, then one exponential per workgroup (no serial chain)
+        const float2* st = a.stats + u * a.nwg1 * a.R + r;
+        float mx = -INFINITY;
+        for (int t = 0; t < a.nwg1; ++t) mx = fmaxf(mx, st[static_cast<int64_t>(t) * a.R].x);
+        float s0 = 0.0f, s1 = 0.0f;
+        int t = 0;
+        for (; t + 1 < a.nwg1; t += 2) {
+          const float2 v0 = st[static_cast<int64_t>(t) * a.R], v1 = st[static_cast<int64_t>(t + 1) * a.R];
+          s0 = fmaf(v0.y, __builtin_amdgcn_exp2f((v0.x - mx) * a.c2), s0);
+          s1 = fmaf(v1.y, __builtin_amdgcn_exp2f((v1.x - mx) * a.c2), s1);
+        }
+        if (t < a.nwg1) {
+          const float2 v0 = st[static_cast<int64_t>(t) * a.R];
+          s0 = fmaf(v0.y, __builtin_amdgcn_exp2f((v0.x - mx) * a.c2), s0);
+        }
+        nl = -(mx * a.c2 + log2f(s0 + s1));                 // -lse * log2(e)
+      } else {
+        const int g = r / a.nb, jq = r - g * a.nb;
+        nl = -a.lse[(b * a.Hq + h0 + g) * a.nb + jq] * 1.4426950408889634f;
+      }
+    }
+    s_nl[rr] = nl;
+  }
+  __syncthreads();
+  float* sc = a.score + u * a.L;
+  float* part = a.colpart + (static_cast<int64_t>(rg) * a.U + u) * a.n_nw;
+  // lane (n, j) owns key k0 + 16 (n >> 2) + 4 j + (n & 3) of each chunk: the
+  // key whose total it ends with after the reduce-scatter below
+  const int own = 16 * (n >> 2) + 4 * j + (n & 3);
+  for (int i = 0; i < a.C; ++i) {
+    const int k0 = wg0 + kChunk * (wave + kSWaves * i);
+    if (k0 >= lim) break;
+    // the running score of the owned key, loaded before the prefetch so that
+    // waiting for it does not wait for the next chunk's keys
+    const int key = k0 + own;
+    const float prev = (a.nrg == 1) ? sc[min(key, lim - 1)] : 0.0f;
+    uint4 kn[4][4];
+    load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
+    __builtin_amdgcn_sched_barrier(0);                      // keep the prefetch ahead
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    // all 64 keys are non-window and precede every buffered query
+    if (k0 + kChunk <= min(lim, a.L - a.nb))
+      chunk_col_mass<false>(acc, kr, s_q, s_nl, a, rg, k0, lane, n, j);
+    else
+      chunk_col_mass<true>(acc, kr, s_q, s_nl, a, rg, k0, lane, n, j);
+    // reduce-scatter over the 16 row lanes: after the step with bit b the
+    // lane keeps the half of the values whose index bit b equals its own and
+    // adds the partner's copy of that half; lane n ends with the total of
+    // value n = 4x + e
+    float t8[8], t4[4], t2[2];
+    {
+      const bool hi = (n & 8) != 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float keep = hi ? acc[q + 8] : acc[q], send = hi ? acc[q] : acc[q + 8];
+        t8[q] = keep + __shfl_xor(send, 8);
+      }
+    }
+    {
+      const bool hi = (n & 4) != 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float keep = hi ? t8[q + 4] : t8[q], send = hi ? t8[q] : t8[q + 4];
+        t4[q] = keep + __shfl_xor(send, 4);
+      }
+    }
+    {
+      const bool hi = (n & 2) != 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float keep = hi ? t4[q + 2] : t4[q], send = hi ? t4[q] : t4[q + 2];
+        t2[q] = keep + __shfl_xor(send, 2);
+      }
+    }
+    float tot;
+    {
+      const bool hi = (n & 1) != 0;
+      const float keep = hi ? t2[1] : t2[0], send = hi ? t2[0] : t2[1];
+      tot = keep + __shfl_xor(send, 1);
+    }
+    if (key < lim) {
+      if (a.nrg == 1) sc[key] = prev + tot;
+      else part[key] = tot;
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kr[x][kk] = kn[x][kk];
+  }
 }
 
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kKeysPerThread = 32;              // register-resident keys per thread
+constexpr int kSeg = kKeysPerThread * kTopThreads;
+constexpr int kSampleStride = 8;                // rows k = 0, 8, 16, 24 form the sample
 
-// Block-wide exclusive prefix sum of one count per thread; the total goes to
-// *total.  Two barriers.
-__device__ __forceinline__ int block_scan(int v, int* s_w, int* total) {
+struct TopShared {
+  int hist[kTopWaves][256];
+  int red[2][kTopWaves];
+  uint32_t sel[4];
+  int cnt[kKeysPerThread * kTopWaves];
+  int tot;
+};
+
+// Sum of two ints over the workgroup (every thread gets both totals).
+__device__ __forceinline__ void block_sum2(int& x, int& y, TopShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    x += __shfl_xor(x, o);
+    y += __shfl_xor(y, o);
+  }
+  if (lane == 0) {
+    sh.red[0][wave] = x;
+    sh.red[1][wave] = y;
+  }
+  __syncthreads();
+  x = 0;
+  y = 0;
+#pragma unroll
+  for (int w = 0; w < kTopWaves; ++w) {
+    x += sh.red[0][w];
+    y += sh.red[1][w];
+  }
+  __syncthreads();
+}
+
+// One histogram pass: keys in [lo, hi] counted into 256 bins of 2^shift keys
+// (per-wave LDS histograms; the lanes that share the first in-range lane's
+// bin add with one atomic, since same-address LDS atomics serialise), then
+// merged into hist[0].  Keys past the first segment are re-read.
+__device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], const float* sc, int n,
+                                          uint32_t lo, uint32_t hi, int shift, bool sample,
+                                          TopShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kTopWaves * 256; i += kTopThreads) (&sh.hist[0][0])[i] = 0;
+  __syncthreads();
+  auto add = [&](uint32_t key, bool valid) {
+    const bool in = valid && key >= lo && key <= hi;
+    const uint32_t bin = (key - lo) >> shift;
+    const uint64_t act = __ballot(in);
+    if (act) {
+      const int leader = __builtin_ctzll(act);
+      const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+      const uint64_t same = __ballot(in && bin == lbin);
+      if (lane == leader) atomicAdd(&sh.hist[wave][lbin], __popcll(same));
+      else if (in && bin != lbin) atomicAdd(&sh.hist[wave][bin], 1);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < kKeysPerThread; ++k) {
+    if (sample && (k % kSampleStride) != 0) continue;
+    add(keys[k], tid + k * kTopThreads < n);
+  }
+  if (!sample) {
+    for (int i = kSeg + tid; i < n; i += kTopThreads) add(order_key(sc[i]), true);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kTopWaves; ++w) c += sh.hist[w][tid];
+    sh.hist[0][tid] = c;
+  }
+  __syncthreads();
+}
+
+// Wave 0: the bin holding the kk-th largest counted key (bins scanned from
+// the top): sel = {bin, rank inside the bin, count of the bin}.
+__device__ __forceinline__ void find_bin(int kk, TopShared& sh) {
+  const int lane = threadIdx.x & 63;
+  int c[4], tot = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    c[e] = sh.hist[0][255 - 4 * lane - e];        // lane l owns bins 255-4l .. 252-4l
+    tot += c[e];
+  }
+  int incl = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) s_w[wave] = incl;
-  __syncthreads();
-  int off = 0, tot = 0;
+  const int before = incl - tot;                  // keys in higher bins
+  if (before < kk && incl >= kk) {
+    int cum = before;
 #pragma unroll
-  for (int w = 0; w < kTopWaves; ++w) {
-    const int c = s_w[w];
-    off += (w < wave) ? c : 0;
-    tot += c;
+    for (int e = 0; e < 4; ++e) {
+      if (cum + c[e] >= kk) {
+        sh.sel[0] = static_cast<uint32_t>(255 - 4 * lane - e);
+        sh.sel[1] = static_cast<uint32_t>(kk - cum);
+        sh.sel[2] = static_cast<uint32_t>(c[e]);
+        break;
+      }
+      cum += c[e];
+    }
   }
-  __syncthreads();
-  *total = tot;
-  return off + incl - v;
 }
 
-// One workgroup per unit.  Radix select of the n_vl-th largest key over the
-// unit's non-window scores (MSB first, 8-bit digits; each wave has its own
-// LDS histogram so atomics only contend inside a wave), then a pass in which
-// each thread owns 32 consecutive positions: flags, and ascending indices,
-// with ties at the threshold taken from the lowest positions.
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+  return max(0, 32 - static_cast<int>(__clz(hi - lo)) - 8);
+}
+
+// One workgroup per unit: the n_vl-th largest score of the non-window prefix
+// by a radix select over order-preserving integer keys, then flags and
+// ascending indices, ties at the threshold taken from the lowest positions.
+// Thread t holds the keys of positions t + 1024 k (k < 32) in registers.
+// Before the radix passes, a 1/8 sample brackets the cut-off; one exact count
+// checks the bracket (else the full range is used), so the passes then see
+// a few hundred keys instead of all of them.
 __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
-  __shared__ int s_hist[kTopWaves][256];
-  __shared__ int s_w[kTopWaves];
-  __shared__ uint32_t s_sel[2];
+  __shared__ TopShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t u = blockIdx.x;
-  const float* sc = a.score + u * a.L;
+  float* sc = a.score + u * a.L;
   uint8_t* flag = a.vl_flag + u * a.L;
   int32_t* idx = a.vl_idx + u * a.n_vl;
   const int n = a.n_nw, k_want = a.n_vl;
 
-  // The k_want-th largest key lies in [lo, hi]; each pass splits the range
-  // into 256 bins of 2^shift keys, so the bins follow the keys' actual
-  // spread (scores share their leading bits, fixed 8-bit digits would put
-  // nearly all of them in one bin and serialise the LDS atomics).
-  uint32_t thresh = 0;
-  int take_eq = 0;
-  uint32_t keys_first[kKeysPerThread];   // keys of the first 32 rows of 1024
-#pragma unroll
-  for (int k = 0; k < kKeysPerThread; ++k) keys_first[k] = 0;
+  // several row groups: fold their column-mass parts into the running score
+  // (each position stays with the thread that reads it below)
+  if (a.nrg > 1) {
+    for (int i = tid; i < n; i += kTopThreads) {
+      float v = sc[i];
+      for (int g = 0; g < a.nrg; ++g) v += a.colpart[(static_cast<int64_t>(g) * a.U + u) * a.n_nw + i];
+      sc[i] = v;
+    }
+  }
+
+  uint32_t keys[kKeysPerThread];
+  uint32_t thresh = 0;                 // keys > thresh are taken
+  int take_eq = 0;                     // and this many keys == thresh, lowest positions first
   if (k_want > 0) {
-    uint32_t* keys = keys_first;
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
+    // unconditional loads (clamped index) so that all 32 are in flight at once
 #pragma unroll
-    for (int k = 0; k < kKeysPerThread; ++k) {
-      const int i = tid + k * kTopThreads;
-      keys[k] = i < n ? order_key(sc[i]) : 0u;
-      if (i < n) {
-        kmin = min(kmin, keys[k]);
-        kmax = max(kmax, keys[k]);
-      }
-    }
-    for (int i = kKeysPerThread * kTopThreads + tid; i < n; i += kTopThreads) {
-      const uint32_t key = order_key(sc[i]);
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-    }
-    if (lane == 0) {
-      s_hist[0][wave] = static_cast<int>(kmin);
-      s_hist[1][wave] = static_cast<int>(kmax);
-    }
-    __syncthreads();
-    uint32_t lo = 0xFFFFFFFFu, hi = 0;
-    for (int w = 0; w < kTopWaves; ++w) {
-      lo = min(lo, static_cast<uint32_t>(s_hist[0][w]));
-      hi = max(hi, static_cast<uint32_t>(s_hist[1][w]));
-    }
-    __syncthreads();
-    int kk = k_want;                      // rank of the target inside [lo, hi]
-    while (lo < hi) {
-      const uint32_t span = hi - lo;
-      const int shift = max(0, 32 - __clz(span) - 8);
-      for (int i = tid; i < kTopWaves * 256; i += kTopThreads) (&s_hist[0][0])[i] = 0;
-      __syncthreads();
+    for (int k = 0; k < kKeysPerThread; ++k) keys[k] = order_key(sc[min(tid + k * kTopThreads, n - 1)]);
+    uint32_t lo = 0, hi = 0;
+    int kk = k_want;                   // rank of the target inside [lo, hi]
+    {
+      // the key range [min, max]
+      uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
 #pragma unroll
       for (int k = 0; k < kKeysPerThread; ++k) {
-        const int i = tid + k * kTopThreads;
-        if (i < n && keys[k] >= lo && keys[k] <= hi)
-          atomicAdd(&s_hist[wave][(keys[k] - lo) >> shift], 1);
+        if (tid + k * kTopThreads < n) {
+          kmin = min(kmin, keys[k]);
+          kmax = max(kmax, keys[k]);
+        }
       }
-      for (int i = kKeysPerThread * kTopThreads + tid; i < n; i += kTopThreads) {
+      for (int i = kSeg + tid; i < n; i += kTopThreads) {
         const uint32_t key = order_key(sc[i]);
-        if (key >= lo && key <= hi) atomicAdd(&s_hist[wave][(key - lo) >> shift], 1);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
       }
-      __syncthreads();
-      if (tid < 256) {
-        int c = 0;
 #pragma unroll
-        for (int w = 0; w < kTopWaves; ++w) c += s_hist[w][tid];
-        s_hist[0][tid] = c;
+      for (int o = 32; o >= 1; o >>= 1) {
+        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+      }
+      if (lane == 0) {
+        sh.red[0][wave] = static_cast<int>(kmin);
+        sh.red[1][wave] = static_cast<int>(kmax);
       }
       __syncthreads();
+      lo = 0xFFFFFFFFu;
+      hi = 0;
+      for (int w = 0; w < kTopWaves; ++w) {
+        lo = min(lo, static_cast<uint32_t>(sh.red[0][w]));
+        hi = max(hi, static_cast<uint32_t>(sh.red[1][w]));
+      }
+      __syncthreads();
+    }
+
+    // bracket from the sample (positions k = 0 mod 8 of the first segment)
+    if (n <= kSeg && n >= 8192 && lo < hi) {
+      const int shift = range_shift(lo, hi);
+      hist_pass(keys, sc, n, lo, hi, shift, true, sh);
+      // sampled positions: t + 1024 k with k % 8 == 0 and below n
+      int ns = 0;
+#pragma unroll
+      for (int k = 0; k < kKeysPerThread; k += kSampleStride) ns += (k * kTopThreads < n) ? min(kTopThreads, n - k * kTopThreads) : 0;
+      const float ts = static_cast<float>(k_want) * ns / n;
+      const float dl = 4.0f * sqrtf(ts) + 16.0f;
+      const int r_top = static_cast<int>(fmaxf(0.0f, ts - dl));            // sample keys surely above
+      const int r_bot = static_cast<int>(fminf(static_cast<float>(ns), ts + dl));
       if (wave == 0) {
-        // lane l owns bins 255-4l .. 252-4l (highest bins in lane 0)
+        // bins (from the top) where the cumulative sample count passes r_top and reaches r_bot
         int c[4], tot = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c[e] = s_hist[0][255 - 4 * lane - e];
+          c[e] = sh.hist[0][255 - 4 * lane - e];
           tot += c[e];
         }
         int incl = tot;
@@ -420,59 +635,94 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
           const int y = __shfl_up(incl, o);
           if (lane >= o) incl += y;
         }
-        const int before = incl - tot;           // keys in higher bins
-        if (before < kk && incl >= kk) {
-          int cum = before;
+        int cum = incl - tot;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (cum + c[e] >= kk) {
-              s_sel[0] = static_cast<uint32_t>(255 - 4 * lane - e);
-              s_sel[1] = static_cast<uint32_t>(kk - cum);
-              break;
-            }
-            cum += c[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int b = 255 - 4 * lane - e;
+          if (cum <= r_top && cum + c[e] > r_top) sh.sel[0] = static_cast<uint32_t>(b);
+          if (cum < r_bot && cum + c[e] >= r_bot) sh.sel[1] = static_cast<uint32_t>(b);
+          cum += c[e];
         }
       }
       __syncthreads();
-      const uint32_t bin = s_sel[0];
-      kk = static_cast<int>(s_sel[1]);
+      const uint32_t b_top = sh.sel[0], b_bot = sh.sel[1];
+      __syncthreads();
+      const uint32_t blo = (r_bot >= ns) ? lo : lo + (b_bot << shift);
+      const uint32_t bhi = (r_top <= 0) ? hi : min(hi, lo + (b_top << shift) + ((1u << shift) - 1u));
+      int c_above = 0, c_in = 0;
+#pragma unroll
+      for (int k = 0; k < kKeysPerThread; ++k) {
+        if (tid + k * kTopThreads < n) {
+          c_above += keys[k] > bhi;
+          c_in += (keys[k] >= blo && keys[k] <= bhi);
+        }
+      }
+      block_sum2(c_above, c_in, sh);
+      if (c_above < k_want && k_want <= c_above + c_in) {
+        lo = blo;
+        hi = bhi;
+        kk = k_want - c_above;
+      }
+    }
+
+    bool whole_bin = false;
+    while (lo < hi) {
+      const int shift = range_shift(lo, hi);
+      hist_pass(keys, sc, n, lo, hi, shift, false, sh);
+      if (wave == 0) find_bin(kk, sh);
+      __syncthreads();
+      const uint32_t bin = sh.sel[0];
+      kk = static_cast<int>(sh.sel[1]);
+      const int cbin = static_cast<int>(sh.sel[2]);
       __syncthreads();
       const uint32_t nlo = lo + (bin << shift);
       const uint32_t nhi = min(hi, nlo + ((1u << shift) - 1u));
+      if (kk == cbin && nlo > 0) {
+        // every key of the bin is taken: the cut is just below it
+        whole_bin = true;
+        lo = nlo - 1;
+        break;
+      }
       lo = nlo;
       hi = nhi;
     }
     thresh = lo;
-    take_eq = kk;
+    take_eq = whole_bin ? 0 : kk;
   }
 
-  // Flags and indices.  Positions are handled in segments of 32 rows of
-  // 1024 (position seg + 1024 k + tid), so loads and flag stores coalesce.
+  // Flags and indices, segment by segment (position seg + tid + 1024 k).
   // Keys equal to the threshold are taken lowest position first; when all of
   // them are taken (no tie at the cut-off, the usual case) no ranking is
   // needed.  Indices are compacted with per-(row, wave) ballot counts and one
   // scan over them.
-  __shared__ int s_cnt[kKeysPerThread * kTopWaves];
-  __shared__ int s_tot;
   int base = 0;          // taken positions before the segment
   int eq_seen = 0;       // threshold-equal positions before the segment
-  for (int seg = 0; seg < a.L; seg += kKeysPerThread * kTopThreads) {
+  for (int seg = 0; seg < a.L; seg += kSeg) {
     uint32_t gt = 0, eq = 0;            // bit k: row k of this thread
     if (k_want > 0) {
+      if (seg == 0) {
 #pragma unroll
-      for (int k = 0; k < kKeysPerThread; ++k) {
-        const int i = seg + tid + k * kTopThreads;
-        if (i < n) {
-          const uint32_t key = seg == 0 ? keys_first[k] : order_key(sc[i]);
-          gt |= static_cast<uint32_t>(key > thresh) << k;
-          eq |= static_cast<uint32_t>(key == thresh) << k;
+        for (int k = 0; k < kKeysPerThread; ++k) {
+          if (tid + k * kTopThreads < n) {
+            gt |= static_cast<uint32_t>(keys[k] > thresh) << k;
+            eq |= static_cast<uint32_t>(keys[k] == thresh) << k;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kKeysPerThread; ++k) {
+          const int i = seg + tid + k * kTopThreads;
+          const uint32_t key = order_key(sc[min(i, max(n - 1, 0))]);
+          if (i < n) {
+            gt |= static_cast<uint32_t>(key > thresh) << k;
+            eq |= static_cast<uint32_t>(key == thresh) << k;
+          }
         }
       }
     }
     // how many threshold-equal keys the segment holds, in total
-    int eq_tot;
-    (void)block_scan(__popc(eq), s_w, &eq_tot);
+    int eq_tot = __popc(eq), dummy = 0;
+    block_sum2(eq_tot, dummy, sh);
     uint32_t take = gt;
     if (eq_seen + eq_tot <= take_eq) {
       take |= eq;                        // every equal key of the segment is taken
@@ -481,12 +731,12 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       int seen = eq_seen;
       for (int k = 0; k < kKeysPerThread; ++k) {
         const uint64_t bal = __ballot((eq >> k) & 1u);
-        if (lane == 0) s_w[wave] = __popcll(bal);
+        if (lane == 0) sh.red[0][wave] = __popcll(bal);
         __syncthreads();
         int off = 0, tot = 0;
         for (int w = 0; w < kTopWaves; ++w) {
-          off += (w < wave) ? s_w[w] : 0;
-          tot += s_w[w];
+          off += (w < wave) ? sh.red[0][w] : 0;
+          tot += sh.red[0][w];
         }
         __syncthreads();
         const int rank = seen + off + __popcll(bal & ((1ull << lane) - 1ull));
@@ -499,7 +749,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
 #pragma unroll
     for (int k = 0; k < kKeysPerThread; ++k) {
       const uint64_t bal = __ballot((take >> k) & 1u);
-      if (lane == 0) s_cnt[k * kTopWaves + wave] = __popcll(bal);
+      if (lane == 0) sh.cnt[k * kTopWaves + wave] = __popcll(bal);
     }
     __syncthreads();
     if (wave == 0) {
@@ -507,7 +757,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       int c[8], run = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        c[e] = s_cnt[8 * lane + e];
+        c[e] = sh.cnt[8 * lane + e];
         run += c[e];
       }
       int incl = run;
@@ -520,10 +770,10 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = c[e];
-        s_cnt[8 * lane + e] = acc;
+        sh.cnt[8 * lane + e] = acc;
         acc += v;
       }
-      if (lane == 63) s_tot = incl;
+      if (lane == 63) sh.tot = incl;
     }
     __syncthreads();
 #pragma unroll
@@ -532,22 +782,26 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       const bool t = (take >> k) & 1u;
       if (i < a.L) flag[i] = static_cast<uint8_t>(t);
       const uint64_t bal = __ballot(t);
-      if (t) idx[base + s_cnt[k * kTopWaves + wave] + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+      if (t) idx[base + sh.cnt[k * kTopWaves + wave] + __popcll(bal & ((1ull << lane) - 1ull))] = i;
     }
-    base += s_tot;
+    base += sh.tot;
     __syncthreads();
   }
 }
 
 }  // namespace
 
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
 size_t select_ws_bytes(const hq_dims& d, int32_t L_max) {
   const size_t units = static_cast<size_t>(d.B) * d.Hkv;
   const size_t R = static_cast<size_t>(d.Hq / d.Hkv) * 64;
-  const size_t ntiles = (static_cast<size_t>(L_max) + kTile - 1) / kTile;
-  const size_t stats = units * ntiles * R * sizeof(float2);
-  const size_t lse = static_cast<size_t>(d.B) * d.Hq * 64 * sizeof(float);
-  return (stats + 255) / 256 * 256 + lse;
+  const size_t nrg = (R + kRG - 1) / kRG;
+  // at least two chunks per wave: a streaming workgroup covers >= 1024 keys
+  const size_t nwg = (static_cast<size_t>(L_max) + 2 * kChunk * kSWaves - 1) / (2 * kChunk * kSWaves);
+  const size_t stats = units * nwg * R * sizeof(float2);
+  const size_t part = nrg > 1 ? nrg * units * static_cast<size_t>(L_max) * sizeof(float) : 0;
+  return round256(stats) + round256(part);
 }
 
 hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, const uint16_t* k,
@@ -563,28 +817,39 @@ hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, con
   a.L = L;
   a.W = d.W;
   a.R = a.G * nb;
-  a.ntiles = (L + kTile - 1) / kTile;
   a.n_nw = L > d.W ? L - d.W : 0;
   a.n_vl = n_vertical(d.rho, a.n_nw);
   a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
   const size_t units = static_cast<size_t>(d.B) * d.Hkv;
-  const size_t stats_bytes = units * a.ntiles * a.R * sizeof(float2);
-  a.stats = reinterpret_cast<float2*>(ws);
-  a.lse_out = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (stats_bytes + 255) / 256 * 256);
+  a.U = static_cast<int32_t>(units);
+  a.nrg = (a.R + kRG - 1) / kRG;
+  // chunks per wave: 2 (one in flight while one is computed) up to 16, so
+  // that large batches run a few workgroups per CU over time
+  const int64_t chunks = static_cast<int64_t>(units) * ((L + kChunk - 1) / kChunk) * a.nrg;
+  a.C = static_cast<int32_t>(std::min<int64_t>(16, std::max<int64_t>(2, (chunks + 8191) / 8192)));
+  a.wg_keys = kChunk * kSWaves * a.C;
+  a.nwg1 = (L + a.wg_keys - 1) / a.wg_keys;
+  const size_t stats_bytes = units * a.nwg1 * a.R * sizeof(float2);
+  const size_t part_bytes = a.nrg > 1 ? static_cast<size_t>(a.nrg) * units * a.n_nw * sizeof(float) : 0;
+  char* w = reinterpret_cast<char*>(ws);
+  a.stats = reinterpret_cast<float2*>(w);
+  a.colpart = reinterpret_cast<float*>(w + round256(stats_bytes));
   a.score = score;
   a.vl_idx = vl_idx;
   a.vl_flag = vl_flag;
   const unsigned U = static_cast<unsigned>(units);
+  const unsigned nrg = static_cast<unsigned>(a.nrg);
   if (lse_in) {
     a.lse = lse_in;
+    a.lse_from_stats = 0;
   } else {
-    hipLaunchKernelGGL(row_stats_kernel, dim3(a.ntiles, U), dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(row_lse_kernel, dim3((a.R + kWaves - 1) / kWaves, U), dim3(kThreads), 0, s, a);
-    a.lse = a.lse_out;
+    hipLaunchKernelGGL(row_stats_kernel, dim3(a.nwg1, U, nrg), dim3(kSThreads), 0, s, a);
+    a.lse = nullptr;
+    a.lse_from_stats = 1;
   }
   if (a.n_nw > 0) {
-    const unsigned t2 = static_cast<unsigned>((a.n_nw + kTile - 1) / kTile);
-    hipLaunchKernelGGL(col_mass_kernel, dim3(t2, U), dim3(kThreads), 0, s, a);
+    const unsigned nwg2 = static_cast<unsigned>((a.n_nw + a.wg_keys - 1) / a.wg_keys);
+    hipLaunchKernelGGL(col_mass_kernel, dim3(nwg2, U, nrg), dim3(kSThreads), 0, s, a);
   }
   hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();

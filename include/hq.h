@@ -118,7 +118,8 @@ typedef struct {
  *   vl_idx      [B][Hkv][n_vl] int32 out: selected positions, ascending
  *   vl_flag     [B][Hkv][L] uint8 out: 1 at selected positions, else 0
  *   ws          device workspace of at least
- *               hq_workspace_bytes(dims, HQ_OP_SELECT, L) bytes
+ *               hq_workspace_bytes(dims, HQ_OP_SELECT, L) bytes (scratch:
+ *               no initial contents are required)
  * Only dims->B, Hq, Hkv, d, W, rho are read.  Requires L >= 1.
  */
 int hq_select_vertical(const hq_dims* dims, const uint16_t* qbuf, int32_t nb,

@@ -129,3 +129,74 @@ def test_select_deterministic():
     b = gpu_select(x, wl)
     assert np.array_equal(a[0].cpu().numpy().view(np.uint32), b[0].cpu().numpy().view(np.uint32))
     assert np.array_equal(a[2], b[2])
+
+
+def _own_topk_exact(wl, score_g, idx_g, flag_g, n_vl):
+    """Flags and indices are exactly the top-n_vl of the GPU's own scores."""
+    n_nw = max(0, wl.L - wl.W)
+    sg = score_g.cpu().numpy()
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            mine = exact_topk(sg[b, g, :n_nw], n_vl)
+            assert np.array_equal(np.nonzero(flag_g[b, g])[0], mine), f"b{b} g{g} flags"
+            assert np.array_equal(idx_g[b, g], mine), f"b{b} g{g} indices"
+
+
+def test_select_unrepresentative_sample():
+    # running scores that are 0 exactly at the positions the top-k samples
+    # (t + 1024 k, k = 0 mod 8) and large elsewhere: the sample's bracket
+    # misses the cut-off and the full-range radix select must take over
+    wl = workload("llama31_8b")
+    x = batch(wl, steps=1)
+    rng = np.random.default_rng(5)
+    base = rng.uniform(1.0, 2.0, size=(wl.B, wl.Hkv, wl.L)).astype(np.float32)
+    pos = np.arange(wl.L)
+    sampled = ((pos // 1024) % 8) == 0
+    base[:, :, sampled] = 0.0
+    s_in = torch.from_numpy(base).to("cuda")
+    score_g, idx_g, flag_g, n_vl = gpu_select(x, wl, score_in=s_in)
+    _own_topk_exact(wl, score_g, idx_g, flag_g, n_vl)
+
+
+def test_select_all_tied_scores():
+    # a running score so large that every column mass rounds away: all
+    # scores are equal, so the lowest n_vl positions are the set
+    wl = workload("llama31_8b")
+    x = batch(wl, steps=1)
+    s_in = torch.full((wl.B, wl.Hkv, wl.L), 1.0e9, dtype=torch.float32, device="cuda")
+    score_g, idx_g, flag_g, n_vl = gpu_select(x, wl, score_in=s_in)
+    assert torch.all(score_g[:, :, :wl.L - wl.W] == 1.0e9)
+    _own_topk_exact(wl, score_g, idx_g, flag_g, n_vl)
+    assert np.array_equal(idx_g[0, 0], np.arange(n_vl))
+
+
+def test_select_workspace_reuse():
+    # one workspace across calls (a rho = 0 call in between): the score
+    # histogram the kernels pass along must be left zeroed by every call
+    wl = workload("llama31_8b", L=12000)
+    x = batch(wl, steps=1)
+    B, Hkv, Hq, L = wl.B, wl.Hkv, wl.Hq, wl.L
+    n_vl = O.n_vertical(wl.rho, L - wl.W)
+    ws = H.workspace(H.make_dims(B, Hq, Hkv, wl.W, wl.rho), H.HQ_OP_SELECT, L)
+    q, k = dev(x["qbuf"]), dev(x["K"])
+
+    def run(rho):
+        dims = H.make_dims(B, Hq, Hkv, wl.W, rho)
+        score = torch.zeros((B, Hkv, L), dtype=torch.float32, device="cuda")
+        idx = torch.full((B, Hkv, max(1, n_vl)), -1, dtype=torch.int32, device="cuda")
+        flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device="cuda")
+        H.hq_select_vertical(dims, q, k, L, score, idx, flag, ws)
+        torch.cuda.synchronize()
+        return score.cpu().numpy(), idx.cpu().numpy(), flag.cpu().numpy()
+
+    s1, i1, f1 = run(wl.rho)
+    _, _, f0 = run(0.0)
+    assert not f0.any()
+    s2, i2, f2 = run(wl.rho)
+    s3, i3, f3 = run(wl.rho)
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(f1, f2) and np.array_equal(f1, f3)
+    assert np.array_equal(i1[:, :, :n_vl], i2[:, :, :n_vl]) and np.array_equal(i1, i3)
+    for b in range(B):
+        for g in range(Hkv):
+            assert np.array_equal(i1[b, g, :n_vl], exact_topk(s1[b, g, :L - wl.W], n_vl))
