@@ -7,13 +7,12 @@
 // decode paragraph; HyQuant README, Overview item 3: online softmax over
 // quantised blocks).
 //
-// Work decomposition.  Grid = (splits, units).  The first nsplit_q
-// workgroups of a unit scan contiguous ranges of its K4V4 slots, the rest scan
-// ranges of the FP16 sequence (vertical lines, then window slots, then
-// staging); the host sizes both kinds to carry about the same bytes.  Each
-// workgroup has eight waves that take 32-token blocks in turn.  The waves'
-// (max, sum, output) states are merged pairwise through LDS in the lanes'
-// own register layout, giving one partial record per workgroup; the last
+// Work decomposition.  Grid = (splits, units).  A unit's work list is its
+// K4V4 slots in 32-token blocks followed by its FP16 sequence (vertical lines,
+// window slots, staging) in 32-token blocks; the unit's nsplit * 8 waves take
+// the items round-robin, so every wave gets the same number of blocks to
+// within one whatever the mix.  Each workgroup merges its eight waves'
+// (max, sum, output) states through LDS into one partial record; the last
 // workgroup of the unit to arrive (an atomic counter in the workspace) merges
 // the unit's records by log-sum-exp and writes out/lse.
 //
@@ -63,7 +62,7 @@ struct DecodeArgs {
   int32_t* counters;
   int32_t Hq, Hkv, G, W, cap_q, cap_vl, cap_stg;
   int32_t n_win;
-  int32_t nsplit_q, nsplit_f;
+  int32_t nsplit;                   // workgroups per unit
   float c2;                         // log2(e) / sqrt(d)
 };
 
@@ -183,17 +182,20 @@ __device__ __forceinline__ int k4_token(int tb, int j, int e) {
 __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint32_t* kmeta,
                                         const uint8_t* vq, const uint32_t* vmeta, int tb,
                                         int nq, int lane, int n, int j) {
-  const int ta = min(tb + n, nq - 1);
-  const int tbb = min(tb + 16 + n, nq - 1);
-  r.ka = ld16(kq + static_cast<int64_t>(ta) * kRowBytes + 16 * j);
-  r.kb = ld16(kq + static_cast<int64_t>(tbb) * kRowBytes + 16 * j);
-  const int tv0 = min(tb + (lane >> 2), nq - 1);
-  const int tv1 = min(tb + 16 + (lane >> 2), nq - 1);
-  r.va = ld16(vq + static_cast<int64_t>(tv0) * kRowBytes + 16 * (lane & 3));
-  r.vb = ld16(vq + static_cast<int64_t>(tv1) * kRowBytes + 16 * (lane & 3));
-  const int tm = min(tb + (lane >> 1), nq - 1);
-  r.kmw = *reinterpret_cast<const uint2*>(kmeta + static_cast<int64_t>(tm) * kMetaWords + 2 * (lane & 1));
-  r.vmw = *reinterpret_cast<const uint2*>(vmeta + static_cast<int64_t>(tm) * kMetaWords + 2 * (lane & 1));
+  // 32-bit byte offsets from the unit's (wave-uniform) base pointers, so the
+  // loads take the scalar-base + vector-offset form with no 64-bit math
+  const int last = nq - 1;
+  const uint32_t oka = static_cast<uint32_t>(min(tb + n, last)) * kRowBytes + 16 * j;
+  const uint32_t okb = static_cast<uint32_t>(min(tb + 16 + n, last)) * kRowBytes + 16 * j;
+  const uint32_t ova = static_cast<uint32_t>(min(tb + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
+  const uint32_t ovb = static_cast<uint32_t>(min(tb + 16 + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
+  const uint32_t om = static_cast<uint32_t>(min(tb + (lane >> 1), last)) * (kMetaWords * 4) + 8 * (lane & 1);
+  r.ka = ld16(kq + oka);
+  r.kb = ld16(kq + okb);
+  r.va = ld16(vq + ova);
+  r.vb = ld16(vq + ovb);
+  r.kmw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kmeta) + om);
+  r.vmw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vmeta) + om);
 }
 
 __device__ __forceinline__ void qk_tile(float4_t& acc, uint4 codes, uint32_t meta,
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int n = lane & 15, j = lane >> 4;
   const int64_t u = blockIdx.y;
   const int split = blockIdx.x;
-  const int nsplit = a.nsplit_q + a.nsplit_f;
+  const int nsplit = a.nsplit;
   const int G = a.G;
   const int64_t b = u / a.Hkv;
   const int h0 = static_cast<int>(u % a.Hkv) * G;
@@ -401,11 +403,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  if (split < a.nsplit_q) {
-    const int nq = min(a.c.n_q[u], a.cap_q);
-    const int nblk = (nq + kBlk - 1) / kBlk;
-    const int b0 = static_cast<int>(static_cast<int64_t>(nblk) * split / a.nsplit_q);
-    const int b1 = static_cast<int>(static_cast<int64_t>(nblk) * (split + 1) / a.nsplit_q);
+  // The unit's work list: its K4V4 blocks, then its FP16 blocks (vertical
+  // lines, window, staging), 32 tokens each.  Wave w of workgroup `split`
+  // (global wave gw of the unit's nsplit * 8) takes items gw, gw + nwaves, ...
+  const int nwaves = nsplit * kWaves;
+  const int gw = split * kWaves + wave;
+  const int nq = min(a.c.n_q[u], a.cap_q);
+  const int nblk_q = (nq + kBlk - 1) / kBlk;
+  if (gw < nblk_q) {
     half8_t qb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -416,51 +421,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
     const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
     const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
-    int blk = b0 + wave;
-    if (blk < b1) {
-      // one block of prefetch; the load is unconditional (the last one re-reads
-      // an in-range block) so that the wait before the compute only covers the
-      // previous iteration's loads
-      K4Stage& sg = s_lds.stage[wave];
-      const Masks km = make_masks();
-      K4Raw cur;
-      load_k4(cur, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
-      for (; blk < b1; blk += kWaves) {
-        K4Raw nxt;
-        load_k4(nxt, kq, kmeta, vq, vmeta, min(blk + kWaves, b1 - 1) * kBlk, nq, lane, n, j);
-        compute_k4(st, cur, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
-        cur = nxt;
-      }
+    // one block of prefetch in two alternating buffers (no register copies);
+    // the loads are unconditional (past the end they re-read the last block)
+    // so that the wait before a compute only covers its own loads
+    K4Stage& sg = s_lds.stage[wave];
+    const Masks km = make_masks();
+    const int last = nblk_q - 1;
+    K4Raw ra, rb;
+    int blk = gw;
+    load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+    for (; blk < nblk_q; blk += 2 * nwaves) {
+      load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+      compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
+      if (blk + nwaves >= nblk_q) break;
+      load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+      compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
     }
-  } else {
-    const int sf = split - a.nsplit_q;
+  }
+  {
     const int nvl = min(a.c.n_vl[u], a.cap_vl);
     const int nst = min(a.c.n_stg[u], a.cap_stg);
     const int nwin = a.n_win;
     const int nf = nvl + nwin + nst;
-    const int nblk = (nf + kBlk - 1) / kBlk;
-    const int b0 = static_cast<int>(static_cast<int64_t>(nblk) * sf / a.nsplit_f);
-    const int b1 = static_cast<int>(static_cast<int64_t>(nblk) * (sf + 1) / a.nsplit_f);
-    half8_t qn[4];
+    const int nblk_f = (nf + kBlk - 1) / kBlk;
+    // this wave's first item past the K4 blocks
+    const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
+    if (first < nblk_f) {
+      half8_t qn[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
-    F16Rows f;
-    f.kvl = a.c.kvl + u * a.cap_vl * kD;
-    f.vvl = a.c.vvl + u * a.cap_vl * kD;
-    f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
-    f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-    f.kstg = a.c.kstg + u * a.cap_stg * kD;
-    f.vstg = a.c.vstg + u * a.cap_stg * kD;
-    f.nvl = nvl;
-    f.nwin = nwin;
-    f.nf = nf;
-    int blk = b0 + wave;
-    if (blk < b1) {
+      for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
+      F16Rows f;
+      f.kvl = a.c.kvl + u * a.cap_vl * kD;
+      f.vvl = a.c.vvl + u * a.cap_vl * kD;
+      f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+      f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+      f.kstg = a.c.kstg + u * a.cap_stg * kD;
+      f.vstg = a.c.vstg + u * a.cap_stg * kD;
+      f.nvl = nvl;
+      f.nwin = nwin;
+      f.nf = nf;
+      int blk = first;
       uint4 kcur[8];
       load_f16_k(kcur, f, blk * kBlk, n, j);
-      for (; blk < b1; blk += kWaves) {
+      for (; blk < nblk_f; blk += nwaves) {
         uint4 knxt[8];
-        load_f16_k(knxt, f, min(blk + kWaves, b1 - 1) * kBlk, n, j);
+        load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
         process_f16(st, qn, f, kcur, blk * kBlk, n, j, c2);
 #pragma unroll
         for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
@@ -621,11 +626,10 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.cap_vl = d.cap_vl;
   a.cap_stg = d.cap_stg;
   a.n_win = plan.n_win;
-  a.nsplit_q = plan.nsplit_q;
-  a.nsplit_f = plan.nsplit_f;
+  a.nsplit = plan.nsplit;
   a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
   (void)L;
-  dim3 grid(plan.nsplit_q + plan.nsplit_f, d.B * d.Hkv);
+  dim3 grid(plan.nsplit, d.B * d.Hkv);
   hipLaunchKernelGGL(decode_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

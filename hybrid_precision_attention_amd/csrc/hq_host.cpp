@@ -72,30 +72,26 @@ static int64_t max_splits(int64_t units) {
 }
 
 DecodePlan plan_decode(const hq_dims& d, int32_t L) {
+  // Workgroups per unit: the whole launch carries about kWgBytes per
+  // workgroup with one to eight workgroups per CU, and no workgroup has
+  // fewer than one 32-token block per wave.  (The host estimates n_q and
+  // n_vl from L and rho; the kernel reads the true counts.)
   const int64_t units = static_cast<int64_t>(d.B) * d.Hkv;
   const int32_t n_nw = std::max<int32_t>(0, L - d.W);
   const int32_t n_vl = std::min(n_vertical(d.rho, n_nw), d.cap_vl);
   const int64_t n_q = std::max<int32_t>(0, n_nw - n_vl);
   const int32_t n_win = std::min(d.W, L);
   const int64_t n_f = static_cast<int64_t>(n_vl) + n_win + d.cap_stg;
-  const double bq = 160.0 * static_cast<double>(n_q);
-  const double bf = 512.0 * static_cast<double>(n_f);
-  const double total = static_cast<double>(units) * (bq + bf);
+  const double per_unit = 160.0 * static_cast<double>(n_q) + 512.0 * static_cast<double>(n_f);
+  const double total = static_cast<double>(units) * per_unit;
   const double per_cu = std::min(8.0, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
   const double wg_bytes = std::max(total / (kCUs * per_cu), 1.0);
-  const int64_t blk_q = cdiv(n_q, kBlk), blk_f = cdiv(n_f, kBlk);
-  int64_t nq = std::max<int64_t>(1, std::llround(bq / wg_bytes));
-  int64_t nf = std::max<int64_t>(1, std::llround(bf / wg_bytes));
-  nq = std::min<int64_t>(nq, std::max<int64_t>(1, cdiv(blk_q, kDecodeWaves)));
-  nf = std::min<int64_t>(nf, std::max<int64_t>(1, cdiv(blk_f, kDecodeWaves)));
-  const int64_t cap = max_splits(units);
-  if (nq + nf > cap) {               // keep the proportion, respect the bound
-    nf = std::max<int64_t>(1, (nf * cap) / (nq + nf));
-    nq = std::max<int64_t>(1, cap - nf);
-  }
+  const int64_t items = cdiv(n_q, kBlk) + cdiv(n_f, kBlk);
+  int64_t ns = std::max<int64_t>(1, std::llround(per_unit / wg_bytes));
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, cdiv(items, kDecodeWaves)));
+  ns = std::min<int64_t>(ns, max_splits(units));
   DecodePlan p;
-  p.nsplit_q = static_cast<int>(nq);
-  p.nsplit_f = static_cast<int>(nf);
+  p.nsplit = static_cast<int>(ns);
   p.n_win = n_win;
   return p;
 }

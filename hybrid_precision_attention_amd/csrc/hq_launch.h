@@ -13,8 +13,7 @@ namespace hq {
 // Decode split plan: how many workgroups scan the K4V4 region and the FP16
 // region (vertical lines + window + staging) of each unit.
 struct DecodePlan {
-  int nsplit_q;
-  int nsplit_f;
+  int nsplit;         // workgroups per unit
   int n_win;          // valid window slots: min(W, L)
 };
 
