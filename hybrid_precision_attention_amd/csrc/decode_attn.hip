@@ -333,6 +333,228 @@ __device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-column path, for G <= 4 query heads per KV head.
+//
+// The 16 MFMA columns are (head h, group g) pairs, column c = 4h + g.  In the
+// QK product the B operand of column c is zero outside group g's 32 dims, so
+// every K4V4 code can enter the MFMA as its biased fp16 value (1024 + c, or
+// 1024 + 16c for a high nibble, whose query entry is pre-scaled by 1/16) and
+// the group's scale and min are applied once per (token, column):
+//     q.k_g = s (D - R) + m qs,
+// R = 1024 * (sum of the column's operand entries), qs = sum of the group's
+// query entries.  A head's four columns are then added inside the lane quad.
+// For PV, column c carries P'[t] = s_v[t][g] P[h][t]; output rows of group g
+// (the lanes with j = g) collect sum_t (bias + code) P'.  One more MFMA
+// against a constant-1024 operand gives the bias (corr) and one against the
+// mins gives sum_t m_v[t][g] P[h][t] (mt):
+//     O = (o - corr) * (1, or 1/16 for a high nibble) + mt.
+// The codes thus need no per-element arithmetic beyond the exponent OR.
+// ---------------------------------------------------------------------------
+struct GState {
+  float m;                          // running max of raw scores of head h (same in the quad, all j)
+  float l;                          // this lane's share of the running denominator
+  float4_t o[8];                    // o[i][rr]: dims 32j + 8rr + i of head h, used where g == j
+  float4_t corr;                    // 1024 * sum_t P'[t] (every row alike)
+  float4_t mt;                      // sum_t m_v[t][j] P[h][t] (every row alike)
+};
+
+// sum over the lane quad (the four group columns of a head); every lane of
+// the quad ends with the same bits
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+__device__ __forceinline__ half8_t k_biased(uint32_t w, const Masks& k) {
+  const uint32_t w8 = w >> 8;
+  return pack4((w & k.lo) | k.magic, (w & k.hi) | k.magic, (w8 & k.lo) | k.magic, (w8 & k.hi) | k.magic);
+}
+
+// Online softmax of one block of raw scores s[8] into the grouped state;
+// p[8] gets the block's probabilities.
+__device__ __forceinline__ void softmax_g(GState& st, const float s[8], float c2, float p[8]) {
+  float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                   fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  {  // max over the four j-lanes of the column (lanes l^16, l^32)
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+  }
+  const float m_new = fmaxf(st.m, bm);
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  if (__any(m_new > st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f((st.m - m_use) * c2);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
+    st.corr *= alpha;
+    st.mt *= alpha;
+  }
+  st.m = m_new;
+  const float nmc = -m_use * c2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, nmc));
+  st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+}
+
+// One K4V4 block in the grouped layout, in two phases.  Lane (column c, j);
+// g = c & 3.
+//  A: stage V codes and metadata through the wave's LDS area (metadata by
+//     group: km[32 g + t], vm[32 g + t]), read back this lane's operands,
+//     run the QK MFMAs and apply the K scales and mins -> raw scores.
+//  B: online softmax, P' = s_v P, PV + bias + min-term MFMAs.
+struct K4Mid {
+  float s[8];                       // raw scores of the lane's tokens (head c >> 2)
+  uint32_t vc[8];                   // V code dword c of the lane's eight tokens
+  uint4 vma, vmb;                   // V {scale, min} of the tokens, group g
+  uint4 mha, mhb;                   // V {scale, min} of the tokens, group c >> 2
+};
+
+__device__ __forceinline__ void k4_phase_a(K4Mid& x, const K4Raw& r, K4Stage& sg,
+                                           const half8_t qg[4], float rc, float qsc,
+                                           const Masks& k, int tb, int nq, int lane, int c, int j) {
+  const int g = c & 3;
+  wave_sync();
+  *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
+  *reinterpret_cast<uint4*>(&sg.v[16 + (lane >> 2)][4 * (lane & 3)]) = r.vb;
+  {  // this lane loaded token lane/2, groups 2 (lane & 1) and 2 (lane & 1) + 1
+    const int tm = lane >> 1, g0 = 2 * (lane & 1);
+    sg.km[32 * g0 + tm] = r.kmw.x;
+    sg.km[32 * (g0 + 1) + tm] = r.kmw.y;
+    sg.vm[32 * g0 + tm] = r.vmw.x;
+    sg.vm[32 * (g0 + 1) + tm] = r.vmw.y;
+  }
+  wave_sync();
+  // {scale, min} of the lane's row tokens 4j + r (tile a) and 16 + 4j + r (tile b)
+  const uint4 kma = *reinterpret_cast<const uint4*>(&sg.km[32 * g + 4 * j]);
+  const uint4 kmb = *reinterpret_cast<const uint4*>(&sg.km[32 * g + 16 + 4 * j]);
+  x.vma = *reinterpret_cast<const uint4*>(&sg.vm[32 * g + 4 * j]);
+  x.vmb = *reinterpret_cast<const uint4*>(&sg.vm[32 * g + 16 + 4 * j]);
+  // mins of the same tokens in group c >> 2: the A operand (row c) of the min term
+  x.mha = *reinterpret_cast<const uint4*>(&sg.vm[32 * (c >> 2) + 4 * j]);
+  x.mhb = *reinterpret_cast<const uint4*>(&sg.vm[32 * (c >> 2) + 16 + 4 * j]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x.vc[e] = sg.v[k4_token(0, j, e)][c];
+
+  // accumulators start at -R, so they end at D - R
+  float4_t da = {-rc, -rc, -rc, -rc}, db = {-rc, -rc, -rc, -rc};
+  const uint32_t wa[4] = {r.ka.x, r.ka.y, r.ka.z, r.ka.w};
+  const uint32_t wb[4] = {r.kb.x, r.kb.y, r.kb.z, r.kb.w};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    da = mfma(k_biased(wa[kk], k), qg[kk], da);
+    db = mfma(k_biased(wb[kk], k), qg[kk], db);
+  }
+  const uint32_t ka4[4] = {kma.x, kma.y, kma.z, kma.w};
+  const uint32_t kb4[4] = {kmb.x, kmb.y, kmb.z, kmb.w};
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const half2_t ma = as_half2(ka4[rr]), mb = as_half2(kb4[rr]);
+    x.s[rr] = fmaf(static_cast<float>(ma[0]), da[rr], static_cast<float>(ma[1]) * qsc);
+    x.s[4 + rr] = fmaf(static_cast<float>(mb[0]), db[rr], static_cast<float>(mb[1]) * qsc);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x.s[e] = quad_sum(x.s[e]);
+  if (tb + kBlk > nq) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (tb + 4 * j + e >= nq) x.s[e] = -INFINITY;
+      if (tb + 16 + 4 * j + e >= nq) x.s[4 + e] = -INFINITY;
+    }
+  }
+}
+
+__device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Masks& k, float c2) {
+  float pr[8];
+  softmax_g(st, x.s, c2, pr);
+  // B operands: P' = s_v P for the codes, P for the min term
+  half8_t p16;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p16[e] = static_cast<_Float16>(pr[e]);
+  // the V scales of the eight tokens, paired like the operand halves
+  const half8_t sv = pack4(__builtin_amdgcn_perm(x.vma.y, x.vma.x, 0x05040100u),
+                           __builtin_amdgcn_perm(x.vma.w, x.vma.z, 0x05040100u),
+                           __builtin_amdgcn_perm(x.vmb.y, x.vmb.x, 0x05040100u),
+                           __builtin_amdgcn_perm(x.vmb.w, x.vmb.z, 0x05040100u));
+  const half8_t pp = p16 * sv;
+  const half8_t am = pack4(__builtin_amdgcn_perm(x.mha.y, x.mha.x, 0x07060302u),
+                           __builtin_amdgcn_perm(x.mha.w, x.mha.z, 0x07060302u),
+                           __builtin_amdgcn_perm(x.mhb.y, x.mhb.x, 0x07060302u),
+                           __builtin_amdgcn_perm(x.mhb.w, x.mhb.z, 0x07060302u));
+  // V^T operands: biased codes, token pairs interleaved as in the generic path
+  uint32_t xl[4], xh[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    xl[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x05040100u);
+    xh[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x07060302u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w = (i < 4) ? xl[q] : xh[q];
+      if (i & 2) w >>= 8;
+      v[q] = (w & ((i & 1) ? k.hi : k.lo)) | k.magic;
+    }
+    st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pp, st.o[i]);
+  }
+  st.corr = mfma(pack4(k.magic, k.magic, k.magic, k.magic), pp, st.corr);
+  st.mt = mfma(am, p16, st.mt);
+}
+
+// One FP16 block in the grouped layout: the same columns (no bias, no
+// scale), P for even and 16 P for odd output dims, so that the FP16 and
+// K4V4 contributions share one accumulator under O = (o - corr) (1 or 1/16) + mt.
+__device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], const F16Rows& f,
+                                              const uint4 kr[8], int tb, int c, int j, float c2) {
+  uint4 vr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = min(k4_token(tb, j, e), f.nf - 1);
+    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * c);
+  }
+  float4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    da = mfma(as_half8(kr[kk]), qf[kk], da);
+    db = mfma(as_half8(kr[4 + kk]), qf[kk], db);
+  }
+  float s[8] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = quad_sum(s[e]);
+  if (tb + kBlk > f.nf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (tb + 4 * j + e >= f.nf) s[e] = -INFINITY;
+      if (tb + 16 + 4 * j + e >= f.nf) s[4 + e] = -INFINITY;
+    }
+  }
+  float pr[8];
+  softmax_g(st, s, c2, pr);
+  half8_t p1, p16x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p1[e] = static_cast<_Float16>(pr[e]);
+    p16x[e] = p1[e] * static_cast<_Float16>(16.0f);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a0[4] = {vr[2 * q].x, vr[2 * q].y, vr[2 * q].z, vr[2 * q].w};
+      const uint32_t a1[4] = {vr[2 * q + 1].x, vr[2 * q + 1].y, vr[2 * q + 1].z, vr[2 * q + 1].w};
+      v[q] = __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], sel);
+    }
+    st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), (i & 1) ? p16x : p1, st.o[i]);
+  }
+}
+
 // LDS image of the waves' states for up to eight heads at a time:
 // o[w][g][dim], plus each wave's running max and denominator per head.
 constexpr int kImgHeads = 8;
@@ -364,6 +586,7 @@ __device__ __forceinline__ void st4_agent(float* p, float4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
+template <bool kG4>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // the per-wave staging areas of the scan, the image of the waves' states
   // and the partials of the final merge share LDS (barriers separate them)
@@ -386,91 +609,217 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int h0 = static_cast<int>(u % a.Hkv) * G;
   const float c2 = a.c2;
 
-  // this lane's slice of the query: head h0 + n, dims 32j..32j+31
-  uint4 qraw[4];
-  if (n < G) {
-    const uint16_t* qp = a.q + (b * a.Hq + h0 + n) * kD + 32 * j;
+  // Every lane ends its scan with one head's state: `valid` lanes hold
+  // dims 32j + 8r + i (r < 4, i < 8) of head `head` in ofin[i][r]; m_h is the
+  // head's running max and l_h the lane's share of its denominator.
+  int head;
+  bool valid;
+  float m_h, l_h;
+  float4_t ofin[8];
+  if constexpr (kG4) {
+    // lane (column c = n = 4h + g, j): the head and group of its column
+    const int h = n >> 2, g = n & 3;
+    const bool active = (g == j) && (h < G);
+    // FP16 B operand: dims 32j + 8kk .. of head h where g == j, else zero
+    half8_t qf[4], qg[4];
+    {
+      const uint16_t* qp = a.q + (b * a.Hq + h0 + min(h, G - 1)) * kD + 32 * j;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qraw[kk] = ld16(qp + 8 * kk);
-  } else {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qraw[kk] = make_uint4(0, 0, 0, 0);
-  }
-
-  SoftState st;
-  st.m = -INFINITY;
-  st.l = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // The unit's work list: its K4V4 blocks, then its FP16 blocks (vertical
-  // lines, window, staging), 32 tokens each.  Wave w of workgroup `split`
-  // (global wave gw of the unit's nsplit * 8) takes items gw, gw + nwaves, ...
-  const int nwaves = nsplit * kWaves;
-  const int gw = split * kWaves + wave;
-  const int nq = min(a.c.n_q[u], a.cap_q);
-  const int nblk_q = (nq + kBlk - 1) / kBlk;
-  if (gw < nblk_q) {
-    half8_t qb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const half8_t nat = as_half8(qraw[kk]);
-      qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
-    }
-    const uint8_t* kq = a.c.kq + u * a.cap_q * kRowBytes;
-    const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
-    const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
-    const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
-    // one block of prefetch in two alternating buffers (no register copies);
-    // the loads are unconditional (past the end they re-read the last block)
-    // so that the wait before a compute only covers its own loads
-    K4Stage& sg = s_lds.stage[wave];
-    const Masks km = make_masks();
-    const int last = nblk_q - 1;
-    K4Raw ra, rb;
-    int blk = gw;
-    load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
-    for (; blk < nblk_q; blk += 2 * nwaves) {
-      load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
-      compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
-      if (blk + nwaves >= nblk_q) break;
-      load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
-      compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
-    }
-  }
-  {
-    const int nvl = min(a.c.n_vl[u], a.cap_vl);
-    const int nst = min(a.c.n_stg[u], a.cap_stg);
-    const int nwin = a.n_win;
-    const int nf = nvl + nwin + nst;
-    const int nblk_f = (nf + kBlk - 1) / kBlk;
-    // this wave's first item past the K4 blocks
-    const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
-    if (first < nblk_f) {
-      half8_t qn[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
-      F16Rows f;
-      f.kvl = a.c.kvl + u * a.cap_vl * kD;
-      f.vvl = a.c.vvl + u * a.cap_vl * kD;
-      f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
-      f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-      f.kstg = a.c.kstg + u * a.cap_stg * kD;
-      f.vstg = a.c.vstg + u * a.cap_stg * kD;
-      f.nvl = nvl;
-      f.nwin = nwin;
-      f.nf = nf;
-      int blk = first;
-      uint4 kcur[8];
-      load_f16_k(kcur, f, blk * kBlk, n, j);
-      for (; blk < nblk_f; blk += nwaves) {
-        uint4 knxt[8];
-        load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
-        process_f16(st, qn, f, kcur, blk * kBlk, n, j, c2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+      for (int kk = 0; kk < 4; ++kk) {
+        qf[kk] = active ? as_half8(ld16(qp + 8 * kk)) : as_half8(make_uint4(0, 0, 0, 0));
+        // K4V4 B operand: the unpack order {0,4,1,5,2,6,3,7}, high-nibble
+        // entries (odd dims) scaled by 1/16
+        const half8_t sh = __builtin_shufflevector(qf[kk], qf[kk], 0, 4, 1, 5, 2, 6, 3, 7);
+        const _Float16 k16 = static_cast<_Float16>(0.0625f);
+        qg[kk] = (half8_t){sh[0], sh[1], sh[2] * k16, sh[3] * k16, sh[4], sh[5], sh[6] * k16, sh[7] * k16};
       }
     }
+    // R = 1024 * (sum of column c's operand entries) and qs = sum of group g
+    // of head h (every j needs them, so each lane reads the group itself)
+    float rc = 0.0f, qsc = 0.0f;
+    if (h < G) {
+      const uint16_t* qp = a.q + (b * a.Hq + h0 + h) * kD + 32 * g;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8_t v = as_half8(ld16(qp + 8 * kk));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(v[e]);
+          qsc += x;
+          rc += (e & 1) ? static_cast<float>(v[e] * static_cast<_Float16>(0.0625f)) : x;
+        }
+      }
+      rc *= 1024.0f;
+    }
+
+    GState st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    st.corr = (float4_t){0.f, 0.f, 0.f, 0.f};
+    st.mt = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    const int nwaves = nsplit * kWaves;
+    const int gw = split * kWaves + wave;
+    const int nq = min(a.c.n_q[u], a.cap_q);
+    const int nblk_q = (nq + kBlk - 1) / kBlk;
+    if (gw < nblk_q) {
+      const uint8_t* kq = a.c.kq + u * a.cap_q * kRowBytes;
+      const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
+      const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
+      const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+      K4Stage& sg = s_lds.stage[wave];
+      const Masks km = make_masks();
+      const int last = nblk_q - 1;
+      K4Raw ra, rb;
+      K4Mid x;
+      int blk = gw;
+      load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+      for (; blk < nblk_q; blk += 2 * nwaves) {
+        load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+        k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
+        k4_phase_b(st, x, km, c2);
+        if (blk + nwaves >= nblk_q) break;
+        load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+        k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + nwaves) * kBlk, nq, lane, n, j);
+        k4_phase_b(st, x, km, c2);
+      }
+    }
+    {
+      const int nvl = min(a.c.n_vl[u], a.cap_vl);
+      const int nst = min(a.c.n_stg[u], a.cap_stg);
+      const int nwin = a.n_win;
+      const int nf = nvl + nwin + nst;
+      const int nblk_f = (nf + kBlk - 1) / kBlk;
+      const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
+      if (first < nblk_f) {
+        F16Rows f;
+        f.kvl = a.c.kvl + u * a.cap_vl * kD;
+        f.vvl = a.c.vvl + u * a.cap_vl * kD;
+        f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+        f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+        f.kstg = a.c.kstg + u * a.cap_stg * kD;
+        f.vstg = a.c.vstg + u * a.cap_stg * kD;
+        f.nvl = nvl;
+        f.nwin = nwin;
+        f.nf = nf;
+        int blk = first;
+        uint4 kcur[8];
+        load_f16_k(kcur, f, blk * kBlk, n, j);
+        for (; blk < nblk_f; blk += nwaves) {
+          uint4 knxt[8];
+          load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
+          process_f16_g(st, qf, f, kcur, blk * kBlk, n, j, c2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+        }
+      }
+    }
+    // the head's state, unbiased: O = (o - corr) (1 or 1/16) + mt
+    head = h;
+    valid = active;
+    m_h = st.m;
+    l_h = st.l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = (i & 1) ? 0.0625f : 1.0f;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ofin[i][rr] = fmaf(st.o[i][rr] - st.corr[rr], f, st.mt[rr]);
+    }
+  } else {
+    // this lane's slice of the query: head h0 + n, dims 32j..32j+31
+    uint4 qraw[4];
+    if (n < G) {
+      const uint16_t* qp = a.q + (b * a.Hq + h0 + n) * kD + 32 * j;
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qraw[kk] = ld16(qp + 8 * kk);
+    } else {
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qraw[kk] = make_uint4(0, 0, 0, 0);
+    }
+
+    SoftState st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+  #pragma unroll
+    for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // The unit's work list: its K4V4 blocks, then its FP16 blocks (vertical
+    // lines, window, staging), 32 tokens each.  Wave w of workgroup `split`
+    // (global wave gw of the unit's nsplit * 8) takes items gw, gw + nwaves, ...
+    const int nwaves = nsplit * kWaves;
+    const int gw = split * kWaves + wave;
+    const int nq = min(a.c.n_q[u], a.cap_q);
+    const int nblk_q = (nq + kBlk - 1) / kBlk;
+    if (gw < nblk_q) {
+      half8_t qb[4];
+  #pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8_t nat = as_half8(qraw[kk]);
+        qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
+      }
+      const uint8_t* kq = a.c.kq + u * a.cap_q * kRowBytes;
+      const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
+      const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
+      const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+      // one block of prefetch in two alternating buffers (no register copies);
+      // the loads are unconditional (past the end they re-read the last block)
+      // so that the wait before a compute only covers its own loads
+      K4Stage& sg = s_lds.stage[wave];
+      const Masks km = make_masks();
+      const int last = nblk_q - 1;
+      K4Raw ra, rb;
+      int blk = gw;
+      load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+      for (; blk < nblk_q; blk += 2 * nwaves) {
+        load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+        compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
+        if (blk + nwaves >= nblk_q) break;
+        load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+        compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
+      }
+    }
+    {
+      const int nvl = min(a.c.n_vl[u], a.cap_vl);
+      const int nst = min(a.c.n_stg[u], a.cap_stg);
+      const int nwin = a.n_win;
+      const int nf = nvl + nwin + nst;
+      const int nblk_f = (nf + kBlk - 1) / kBlk;
+      // this wave's first item past the K4 blocks
+      const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
+      if (first < nblk_f) {
+        half8_t qn[4];
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
+        F16Rows f;
+        f.kvl = a.c.kvl + u * a.cap_vl * kD;
+        f.vvl = a.c.vvl + u * a.cap_vl * kD;
+        f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+        f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+        f.kstg = a.c.kstg + u * a.cap_stg * kD;
+        f.vstg = a.c.vstg + u * a.cap_stg * kD;
+        f.nvl = nvl;
+        f.nwin = nwin;
+        f.nf = nf;
+        int blk = first;
+        uint4 kcur[8];
+        load_f16_k(kcur, f, blk * kBlk, n, j);
+        for (; blk < nblk_f; blk += nwaves) {
+          uint4 knxt[8];
+          load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
+          process_f16(st, qn, f, kcur, blk * kBlk, n, j, c2);
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+        }
+      }
+    }
+    head = n;
+    valid = n < G;
+    m_h = st.m;
+    l_h = st.l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ofin[i] = st.o[i];
   }
 
   // Merge the eight waves' states and publish the workgroup's record.  The
@@ -478,22 +827,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // merges them and stores its part of the record with 16-byte device-scope
   // stores, at most eight heads per round.
   float* recs = a.part + u * nsplit * static_cast<int64_t>(G) * kPart;
-  float lsum = st.l;                               // the head's denominator: sum over j
+  float lsum = l_h;                                // the head's denominator: sum over j
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
   WgImage& img = s_lds.img;
   for (int g0 = 0; g0 < G; g0 += kImgHeads) {
     __syncthreads();                               // staging areas / previous round free
-    const int gl = n - g0;
-    if (gl >= 0 && gl < kImgHeads && n < G) {
+    const int gl = head - g0;
+    if (gl >= 0 && gl < kImgHeads && valid) {
       float* o = &img.o[wave][gl][32 * j];         // dims 32j + 8r + i
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<float4_t*>(o + 8 * r) = (float4_t){st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]};
-        *reinterpret_cast<float4_t*>(o + 8 * r + 4) = (float4_t){st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]};
+        *reinterpret_cast<float4_t*>(o + 8 * r) = (float4_t){ofin[0][r], ofin[1][r], ofin[2][r], ofin[3][r]};
+        *reinterpret_cast<float4_t*>(o + 8 * r + 4) = (float4_t){ofin[4][r], ofin[5][r], ofin[6][r], ofin[7][r]};
       }
       if (j == 0) {
-        img.m[wave][gl] = st.m;
+        img.m[wave][gl] = m_h;
         img.l[wave][gl] = lsum;
       }
     }
@@ -630,7 +979,10 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
   (void)L;
   dim3 grid(plan.nsplit, d.B * d.Hkv);
-  hipLaunchKernelGGL(decode_kernel, grid, dim3(kThreads), 0, s, a);
+  if (a.G <= 4)
+    hipLaunchKernelGGL(decode_kernel<true>, grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<false>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
