@@ -1,0 +1,38 @@
+// Plain streaming read: the measured HBM ceiling the benchmark reports next to
+// the nominal peak.  Grid-stride over 16-byte words, eight loads in flight per
+// thread, every loaded word folded into a checksum.
+#include <hip/hip_runtime.h>
+
+#include "hq_probe.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src, size_t n,
+                                                          uint32_t* sink, uint32_t never) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * 256;
+  size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == never) sink[0] = acc;
+}
+
+}  // namespace
+
+extern "C" int hq_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
+                                    int grid, hipStream_t stream) {
+  if (!src || !sink || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) || grid < 1)
+    return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, stream,
+                     static_cast<const uint4*>(src), bytes / 16, sink, never);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
