@@ -148,26 +148,28 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
   const bool mover = lane < 32;
   const int kv = (lane >> 4) & 1, part = lane & 15;
   const int W = a.W, t = a.t;
+  // Every address is known from the arguments, so all loads are issued
+  // before any is used: the counters, the staged row, the ring slot the
+  // staged token goes to (its old token is the evictee) and the new token.
+  uint16_t* stg = (kv ? a.c.vstg : a.c.kstg) + u * a.cap_stg * kD + 8 * part;
+  uint16_t* win = W > 0 ? (kv ? a.c.vwin : a.c.kwin) + (u * W + (t - 1 + W) % W) * kD + 8 * part
+                        : nullptr;
+  const uint16_t* src = (kv ? a.v_new : a.k_new) + u * kD + 8 * part;
   const int nstg = a.c.n_stg[u];
   const int nq = a.c.n_q[u];
   const int nvl = a.c.n_vl[u];
-  uint16_t* stg = (kv ? a.c.vstg : a.c.kstg) + u * a.cap_stg * kD + 8 * part;
+  const bool flag_vl = a.evict_is_vl && a.evict_is_vl[u] != 0;
+  const uint4 staged = mover ? ld16(stg) : make_uint4(0, 0, 0, 0);
+  const uint4 old = (mover && win) ? ld16(win) : make_uint4(0, 0, 0, 0);
+  const uint4 fresh = mover ? ld16(src) : make_uint4(0, 0, 0, 0);
 
   if (nstg > 0) {
-    const uint4 staged = mover ? ld16(stg) : make_uint4(0, 0, 0, 0);
-    int ev = -1;
-    uint4 evv = staged;
-    uint16_t* win = nullptr;
-    if (W > 0) {
-      const int slot = (t - 1) % W;
-      win = (kv ? a.c.vwin : a.c.kwin) + (u * W + slot) * kD + 8 * part;
-      ev = t - 1 - W;
-      if (ev >= 0 && mover) evv = ld16(win);
-    } else {
-      ev = t - 1;
-    }
+    // the staged token (position t - 1) enters the ring; the token it
+    // replaces (t - 1 - W) leaves the window; with no window it leaves itself
+    const int ev = W > 0 ? t - 1 - W : t - 1;
+    const uint4 evv = W > 0 ? old : staged;
     if (ev >= 0) {
-      const bool to_vl = a.evict_is_vl && a.evict_is_vl[u] != 0 && nvl < a.cap_vl;
+      const bool to_vl = flag_vl && nvl < a.cap_vl;
       if (to_vl) {
         if (mover) st16((kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + nvl) * kD + 8 * part, evv);
         if (lane == 0) {
@@ -201,8 +203,7 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
     }
     if (W > 0 && mover) st16(win, staged);
   }
-  const uint16_t* src = (kv ? a.v_new : a.k_new) + u * kD + 8 * part;
-  if (mover) st16(stg, ld16(src));
+  if (mover) st16(stg, fresh);
   if (lane == 0) a.c.n_stg[u] = 1;
 }
 
