@@ -401,6 +401,71 @@ def decode(caches, q, L, fused=True):
 
 
 # --------------------------------------------------------------------------
+# Decode-time running refresh [D method paragraph: running column-mass score
+# from at most 64 buffered queries, refreshed every 64 tokens; R Overview
+# item 1].  Readings: the buffered queries are the last nb decode queries;
+# each row's normaliser is the LSE its decode step produced (one pass over
+# the keys); the keys are the hybrid cache as stored at refresh time, a
+# K4V4 key taken as the fp16 rounding of code * scale + min (the compute
+# type of the attention scan); every cached position accumulates (window and
+# staged tokens too, since their mass decides promotion when they leave the
+# window); the cut-off is the n_vl-th largest running score over the
+# non-window prefix; a token leaving the window becomes a vertical line when
+# its running score reaches the cut-off.
+# --------------------------------------------------------------------------
+def hybrid_keys_fp16(cache: Dict, t: int):
+    """Positions and keys [n][d] (fp64) of every key cached at decode
+    position t: K4V4 slots as fp16(code * scale + min), then the FP16
+    vertical lines, window and staged token."""
+    regs = hybrid_regions(cache, t)
+    k4 = regs[0]
+    pos = [k4[1]] + [r[1] for r in regs[1:]]
+    keys = [k4[2].astype(np.float16).astype(np.float64)] + [r[2] for r in regs[1:]]
+    return np.concatenate(pos), np.concatenate(keys)
+
+
+def refresh_hybrid_unit(cache: Dict, t: int, qgrp: np.ndarray, lse: np.ndarray,
+                        rho: float, score: np.ndarray):
+    """One refresh at decode position t (the staged token).  qgrp [G][nb][d]
+    are the last nb decode queries (positions t - nb + 1 .. t), lse [G][nb]
+    the natural-log LSE of each at its own decode step.  For every cached key
+    at position i, exp(tau q.k_i - lse) of every row with i <= its position
+    is added to score[i] (in place).  Returns (cut, vl positions): the n_vl-th
+    largest running score over [0, t - W) (+inf when n_vl = 0) and the top-rho
+    set there (ascending, ties to the lower position)."""
+    G, nb, d = qgrp.shape
+    W = cache["W"]
+    tau = softmax_scale(d)
+    pos, keys = hybrid_keys_fp16(cache, t)
+    rows_pos = t - nb + 1 + np.arange(nb)
+    for h in range(G):
+        z = tau * (qgrp[h].astype(np.float64) @ keys.T)            # [nb][n]
+        a = np.exp(z - lse[h][:, None]) * (pos[None, :] <= rows_pos[:, None])
+        score[pos] += a.sum(axis=0)
+    n_nw = max(0, t - W)
+    n_vl = n_vertical(rho, n_nw)
+    if n_vl == 0:
+        return math.inf, np.zeros(0, np.int64)
+    sel = top_rho(score[:n_nw], n_vl)
+    return float(score[sel].min()), sel
+
+
+def append_merge_scored_unit(cache: Dict, t: int, k_new: np.ndarray, v_new: np.ndarray,
+                             score: np.ndarray, cut: float) -> bool:
+    """append_merge_unit where the token leaving the window (position
+    t - 1 - W, or t - 1 with no window) becomes a vertical line exactly when
+    score[pos] >= cut.  Returns that decision (False when nothing leaves)."""
+    W = cache["W"]
+    ev = -1
+    if cache["stg_pos"].size:
+        p = int(cache["stg_pos"][0])
+        ev = p - W if W > 0 else p
+    promote = ev >= 0 and bool(score[ev] >= cut)
+    append_merge_unit(cache, t, k_new, v_new, promote)
+    return promote
+
+
+# --------------------------------------------------------------------------
 # Byte accounting [R Overhead; D limitations paragraph]
 # --------------------------------------------------------------------------
 def k4v4_bytes_per_token(d: int = 128) -> int:

@@ -1,0 +1,158 @@
+"""Pins of the oracle's decode-time running refresh and scored merge (CPU).
+
+* With every non-window token in FP16 (rho = 1) the refresh's increment is
+  the plain causal column mass of dense keys (the pinned attention rows).
+* With each row's normaliser computed from the same keys, every buffered row
+  adds exactly 1 over the cached positions (mass conservation), whatever the
+  quantised part holds.
+* A K4V4 key enters as the fp16 rounding of code * scale + min, checked
+  against a hand dequantisation of one token.
+* The cut-off is the n_vl-th largest running score of the non-window prefix
+  (brute-force sort), +inf when n_vl = 0; the set is the exact top-n_vl.
+* The scored merge promotes exactly when score >= cut, and is otherwise the
+  plain merge.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import hq_oracle as O
+
+
+def _prefix(L, d=128, seed=0):
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((L + 8, d)).astype(np.float16)
+    V = rng.standard_normal((L + 8, d)).astype(np.float16)
+    return K, V, rng
+
+
+def _exact_lse(keys, pos, qrows, rows_pos, d):
+    """Natural-log LSE of each row over the keys at positions <= its own."""
+    tau = 1.0 / math.sqrt(d)
+    out = np.zeros(len(qrows))
+    for r, (q, p) in enumerate(zip(qrows, rows_pos)):
+        z = tau * (keys[pos <= p] @ q.astype(np.float64))
+        m = z.max()
+        out[r] = m + math.log(np.exp(z - m).sum())
+    return out
+
+
+def test_refresh_all_fp16_equals_dense_column_mass():
+    L, W, G, nb, d = 200, 16, 2, 12, 128
+    K, V, rng = _prefix(L)
+    flag = np.ones(L, np.uint8)                     # rho = 1: no K4V4 token
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, flag)
+    t = L
+    O.append_merge_unit(c, t, K[t], V[t])           # the cache holds 0..t
+    q = rng.standard_normal((G, nb, d)).astype(np.float16)
+    rows_pos = t - nb + 1 + np.arange(nb)
+    lse = np.zeros((G, nb))
+    for h in range(G):
+        _, lse[h] = O.attention_rows(K[:t + 1], q[h], rows_pos, d)
+    score = np.zeros(t + 8)
+    O.refresh_hybrid_unit(c, t, q, lse, 1.0, score)
+    want = np.zeros(t + 8)
+    for h in range(G):
+        a, _ = O.attention_rows(K[:t + 1], q[h], rows_pos, d)
+        want[:t + 1] += a.sum(axis=0)
+    assert np.allclose(score, want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("W,rho", [(16, 0.05), (0, 0.1), (64, 0.0)])
+def test_refresh_mass_conservation(W, rho):
+    L, G, nb, d = 300, 4, 16, 128
+    K, V, rng = _prefix(L, seed=3)
+    n_nw = max(0, L - W)
+    flag = np.zeros(L, np.uint8)
+    flag[rng.choice(n_nw, size=n_nw // 20, replace=False)] = 1
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, flag)
+    for t in range(L, L + 3):
+        O.append_merge_unit(c, t, K[t], V[t])
+    t = L + 2
+    q = rng.standard_normal((G, nb, d)).astype(np.float16)
+    pos, keys = O.hybrid_keys_fp16(c, t)
+    assert sorted(pos.tolist()) == list(range(t + 1))
+    rows_pos = t - nb + 1 + np.arange(nb)
+    lse = np.stack([_exact_lse(keys, pos, q[h], rows_pos, d) for h in range(G)])
+    score = np.zeros(t + 1)
+    O.refresh_hybrid_unit(c, t, q, lse, rho, score)
+    assert abs(score.sum() - G * nb) < 1e-9
+    # running: a second identical refresh doubles every entry
+    s2 = score.copy()
+    O.refresh_hybrid_unit(c, t, q, lse, rho, s2)
+    assert np.allclose(s2, 2 * score, rtol=1e-14)
+
+
+def test_k4_key_is_fp16_of_code_scale_min():
+    L, W, d = 80, 8, 128
+    K, V, _ = _prefix(L, seed=5)
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
+    O.append_merge_unit(c, L, K[L], V[L])
+    pos, keys = O.hybrid_keys_fp16(c, L)
+    slot = 7
+    codes = np.zeros(d, np.int64)
+    row = c["kq"][slot]
+    for b in range(d // 2):                      # low nibble first
+        codes[2 * b] = row[b] & 0xF
+        codes[2 * b + 1] = row[b] >> 4
+    want = np.zeros(d)
+    for g in range(d // 32):
+        s, m = (float(x) for x in c["kq_meta"][slot, g])
+        for e in range(32):
+            want[32 * g + e] = float(np.float16(codes[32 * g + e] * s + m))
+    i = int(np.nonzero(pos == c["q_pos"][slot])[0][0])
+    assert np.array_equal(keys[i], want)
+
+
+def test_cut_off_and_set():
+    L, W, G, nb, d, rho = 400, 32, 2, 8, 128, 0.05
+    K, V, rng = _prefix(L, seed=7)
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
+    O.append_merge_unit(c, L, K[L], V[L])
+    q = rng.standard_normal((G, nb, d)).astype(np.float16)
+    lse = np.full((G, nb), 3.0)
+    score = rng.uniform(0, 1, L + 1)
+    score[10] = score[11] = score[12] = 5.0       # a tie at the top
+    cut, sel = O.refresh_hybrid_unit(c, L, q, lse, rho, score)
+    n_nw = L - W
+    n_vl = O.n_vertical(rho, n_nw)
+    srt = sorted(((-score[i], i) for i in range(n_nw)))
+    assert cut == -srt[n_vl - 1][0]
+    assert sel.tolist() == sorted(i for _, i in srt[:n_vl])
+    cut0, sel0 = O.refresh_hybrid_unit(c, L, q, lse, 0.0, score.copy())
+    assert cut0 == math.inf and sel0.size == 0
+
+
+def test_scored_merge_promotes_exactly_at_the_cut():
+    L, W, d = 120, 16, 128
+    K, V, _ = _prefix(L, seed=9)
+    for promote_score, want in [(0.75, True), (0.5, True), (0.49, False)]:
+        c = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
+        ref = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
+        score = np.zeros(L + 8)
+        assert O.append_merge_scored_unit(c, L, K[L], V[L], score, 0.5) is False   # only stages
+        O.append_merge_unit(ref, L, K[L], V[L])
+        score[L - W] = promote_score                 # the token leaving next
+        got = O.append_merge_scored_unit(c, L + 1, K[L + 1], V[L + 1], score, 0.5)
+        O.append_merge_unit(ref, L + 1, K[L + 1], V[L + 1], evict_is_vl=want)
+        assert got is want
+        for key in ("kq", "vq", "kq_meta", "vq_meta", "q_pos", "kvl", "vvl", "vl_pos"):
+            assert np.array_equal(c[key].view(np.uint8), ref[key].view(np.uint8)), key
+
+
+def test_refresh_causal_rows_skip_later_keys():
+    """A buffered row never sees keys after its own position: with the staged
+    token's key made huge, only the last row (the staged token itself) puts
+    mass on it."""
+    L, W, G, nb, d = 100, 8, 1, 4, 128
+    K, V, rng = _prefix(L, seed=11)
+    K[L] = np.float16(8.0)
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
+    O.append_merge_unit(c, L, K[L], V[L])
+    q = np.ones((G, nb, d), np.float16)
+    lse = np.zeros((G, nb))
+    score = np.zeros(L + 1)
+    O.refresh_hybrid_unit(c, L, q, lse, 0.05, score)
+    tau = 1 / math.sqrt(d)
+    assert score[L] == pytest.approx(math.exp(tau * 8.0 * d), rel=1e-12)
