@@ -49,12 +49,17 @@ lib.hq_append_merge.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache
                                 _p, _p, _p, _p]
 lib.hq_decode_attn.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32,
                                _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.hq_refresh_hybrid.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32,
+                                  _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p]
+lib.hq_append_merge_scored.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache),
+                                       ctypes.c_int32, _p, _p, _p, ctypes.c_int32, _p, _p]
 lib.hq_workspace_bytes.argtypes = [ctypes.POINTER(hq_dims), ctypes.c_int, ctypes.c_int32]
 lib.hq_workspace_bytes.restype = ctypes.c_size_t
 lib.hq_status_string.argtypes = [ctypes.c_int]
 lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
-for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn"):
+for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
+           "hq_refresh_hybrid", "hq_append_merge_scored"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -194,6 +199,29 @@ def hq_decode_attn(dims, cache: HybridCache, L, q, out, ws, lse=None, stream=Non
                             _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
                             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_attn")
+
+
+def hq_refresh_hybrid(dims, cache: HybridCache, t, qbuf, lse, score, vl_idx, vl_flag, cut,
+                      stream=None):
+    """score [B][Hkv][score_ld] (score_ld = its last dimension)."""
+    cs = cache.struct()
+    st = lib.hq_refresh_hybrid(ctypes.byref(dims), ctypes.byref(cs), t,
+                               _ptr(qbuf, torch.float16, "qbuf"), qbuf.shape[2],
+                               _ptr(lse, torch.float32, "lse"), _ptr(score, torch.float32, "score"),
+                               score.shape[-1], _ptr(vl_idx, torch.int32, "vl_idx"),
+                               _ptr(vl_flag, torch.uint8, "vl_flag"),
+                               _ptr(cut, torch.float32, "cut"), _stream(stream))
+    _check(st, "hq_refresh_hybrid")
+
+
+def hq_append_merge_scored(dims, cache: HybridCache, t, k_new, v_new, score, cut, stream=None):
+    cs = cache.struct()
+    st = lib.hq_append_merge_scored(ctypes.byref(dims), ctypes.byref(cs), t,
+                                    _ptr(k_new, torch.float16, "k_new"),
+                                    _ptr(v_new, torch.float16, "v_new"),
+                                    _ptr(score, torch.float32, "score"), score.shape[-1],
+                                    _ptr(cut, torch.float32, "cut"), _stream(stream))
+    _check(st, "hq_append_merge_scored")
 
 
 # --------------------------------------------------------------------------

@@ -116,7 +116,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 1; }
+int hq_abi_version(void) { return 2; }
 
 const char* hq_status_string(int status) {
   switch (status) {
@@ -202,6 +202,44 @@ int hq_select_vertical(const hq_dims* dims, const uint16_t* qbuf, int32_t nb, co
   if (!aligned16(ws)) return HQ_ERR_ALIGN;
   if (launch_select(*dims, qbuf, nb, k, L, lse_or_null, score_inout, vl_idx, vl_flag, ws,
                     stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_refresh_hybrid(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                      const uint16_t* qbuf, int32_t nb, const float* lse, float* score_inout,
+                      int32_t score_ld, int32_t* vl_idx, uint8_t* vl_flag, float* cut_out,
+                      hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t < 0 || nb < 1 || nb > 64 || nb > t + 1 || score_ld < t + 1) return HQ_ERR_ARG;
+  if (!qbuf || !lse || !score_inout || !vl_flag || !cut_out) return HQ_ERR_ARG;
+  const int32_t n_vl = n_vertical(dims->rho, std::max(0, t - dims->W));
+  if (n_vl > 0 && !vl_idx) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(qbuf) || !aligned16(lse) || !aligned16(score_inout) || !aligned16(vl_flag) ||
+      !aligned16(cut_out))
+    return HQ_ERR_ALIGN;
+  if (vl_idx && !aligned16(vl_idx)) return HQ_ERR_ALIGN;
+  if (launch_refresh(*dims, *cache, t, qbuf, nb, lse, score_inout, score_ld, vl_idx, vl_flag,
+                     cut_out, stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_append_merge_scored(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                           const uint16_t* k_new, const uint16_t* v_new, const float* score,
+                           int32_t score_ld, const float* cut, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t < 0 || !k_new || !v_new || !score || !cut || score_ld < std::max(t, 1)) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(score) || !aligned16(cut))
+    return HQ_ERR_ALIGN;
+  if (dims->cap_stg < 1) return HQ_ERR_CAPACITY;
+  if (dims->cap_q < std::max(0, t - dims->W)) return HQ_ERR_CAPACITY;
+  if (launch_append_merge_scored(*dims, *cache, t, k_new, v_new, score, score_ld, cut, stream) !=
+      hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }

@@ -40,6 +40,15 @@ hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb,
                          float* score, int32_t* vl_idx, uint8_t* vl_flag, void* ws,
                          hipStream_t s);
 
+hipError_t launch_refresh(const hq_dims& d, const hq_cache& c, int32_t t, const uint16_t* qbuf,
+                          int32_t nb, const float* lse, float* score, int32_t score_ld,
+                          int32_t* vl_idx, uint8_t* vl_flag, float* cut, hipStream_t s);
+
+hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32_t t,
+                                      const uint16_t* k_new, const uint16_t* v_new,
+                                      const float* score, int32_t score_ld, const float* cut,
+                                      hipStream_t s);
+
 // floor(rho * n_nw + 1e-6): size of the vertical-line set of n_nw candidates.
 int32_t n_vertical(double rho, int32_t n_nw);
 

@@ -134,6 +134,11 @@ struct MergeArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   const uint8_t* evict_is_vl;
+  // scored promotion (when score is set): the leaving token becomes a
+  // vertical line when its running score reaches the unit's cut-off
+  const float* score;               // [U][score_ld]
+  const float* cut;                 // [U]
+  int32_t score_ld;
   int32_t t, W, cap_q, cap_vl, cap_stg;
 };
 
@@ -158,7 +163,9 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
   const int nstg = a.c.n_stg[u];
   const int nq = a.c.n_q[u];
   const int nvl = a.c.n_vl[u];
-  const bool flag_vl = a.evict_is_vl && a.evict_is_vl[u] != 0;
+  const int ev = W > 0 ? t - 1 - W : t - 1;   // position of the token that would leave
+  bool flag_vl = a.evict_is_vl && a.evict_is_vl[u] != 0;
+  if (a.score && ev >= 0) flag_vl = a.score[u * a.score_ld + ev] >= a.cut[u];
   const uint4 staged = mover ? ld16(stg) : make_uint4(0, 0, 0, 0);
   const uint4 old = (mover && win) ? ld16(win) : make_uint4(0, 0, 0, 0);
   const uint4 fresh = mover ? ld16(src) : make_uint4(0, 0, 0, 0);
@@ -166,7 +173,6 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
   if (nstg > 0) {
     // the staged token (position t - 1) enters the ring; the token it
     // replaces (t - 1 - W) leaves the window; with no window it leaves itself
-    const int ev = W > 0 ? t - 1 - W : t - 1;
     const uint4 evv = W > 0 ? old : staged;
     if (ev >= 0) {
       const bool to_vl = flag_vl && nvl < a.cap_vl;
@@ -221,7 +227,16 @@ hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t
 hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
                                const uint16_t* k_new, const uint16_t* v_new,
                                const uint8_t* evict_is_vl, hipStream_t s) {
-  MergeArgs a{c, k_new, v_new, evict_is_vl, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+  MergeArgs a{c, k_new, v_new, evict_is_vl, nullptr, nullptr, 0, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+  hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32_t t,
+                                      const uint16_t* k_new, const uint16_t* v_new,
+                                      const float* score, int32_t score_ld, const float* cut,
+                                      hipStream_t s) {
+  MergeArgs a{c, k_new, v_new, nullptr, score, cut, score_ld, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
   hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -58,6 +58,10 @@ struct SelArgs {
   int32_t nwg1, nrg, U;
   int32_t lse_from_stats;           // 1: rows' LSE merged from stats by col_mass
   float c2;                         // log2(e) / sqrt(d)
+  float* cut;                       // [U] top-k cut-off value out (nullable)
+  // decode-time refresh only: the hybrid cache at decode position t
+  hq_cache c;
+  int32_t t, cap_q, cap_vl, cap_stg;
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
@@ -67,6 +71,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t bits = __builtin_bit_cast(uint32_t, f);
   if (bits == 0x80000000u) bits = 0;
   return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
 // max / sum with lanes l^16 and l^32 (the four j-lanes of a row), through the
@@ -310,6 +317,41 @@ __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][
   }
 }
 
+// Sum over the 16 row lanes of a wave: lane (n, j) ends with the total of
+// acc[n], i.e. of list entry 16 (n >> 2) + 4 j + (n & 3) of the chunk.  At
+// the step with bit b the lane keeps the half of the values whose index bit
+// b equals its own and adds the partner's copy of that half.
+__device__ __forceinline__ float reduce_scatter16(const float acc[16], int n) {
+  float t8[8], t4[4], t2[2];
+  {
+    const bool hi = (n & 8) != 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float keep = hi ? acc[q + 8] : acc[q], send = hi ? acc[q] : acc[q + 8];
+      t8[q] = keep + __shfl_xor(send, 8);
+    }
+  }
+  {
+    const bool hi = (n & 4) != 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float keep = hi ? t8[q + 4] : t8[q], send = hi ? t8[q] : t8[q + 4];
+      t4[q] = keep + __shfl_xor(send, 4);
+    }
+  }
+  {
+    const bool hi = (n & 2) != 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float keep = hi ? t4[q + 2] : t4[q], send = hi ? t4[q] : t4[q + 2];
+      t2[q] = keep + __shfl_xor(send, 2);
+    }
+  }
+  const bool hi = (n & 1) != 0;
+  const float keep = hi ? t2[1] : t2[0], send = hi ? t2[0] : t2[1];
+  return keep + __shfl_xor(send, 1);
+}
+
 // Pass 2: column mass of the non-window keys: per key, the sum over the row
 // group's rows of exp(tau q.k - lse), added to the running score (one row
 // group) or written as the group's part (several; top-k folds them in).
@@ -382,41 +424,7 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
       chunk_col_mass<false>(acc, kr, s_q, s_nl, a, rg, k0, lane, n, j);
     else
       chunk_col_mass<true>(acc, kr, s_q, s_nl, a, rg, k0, lane, n, j);
-    // reduce-scatter over the 16 row lanes: after the step with bit b the
-    // lane keeps the half of the values whose index bit b equals its own and
-    // adds the partner's copy of that half; lane n ends with the total of
-    // value n = 4x + e
-    float t8[8], t4[4], t2[2];
-    {
-      const bool hi = (n & 8) != 0;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float keep = hi ? acc[q + 8] : acc[q], send = hi ? acc[q] : acc[q + 8];
-        t8[q] = keep + __shfl_xor(send, 8);
-      }
-    }
-    {
-      const bool hi = (n & 4) != 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float keep = hi ? t8[q + 4] : t8[q], send = hi ? t8[q] : t8[q + 4];
-        t4[q] = keep + __shfl_xor(send, 4);
-      }
-    }
-    {
-      const bool hi = (n & 2) != 0;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float keep = hi ? t4[q + 2] : t4[q], send = hi ? t4[q] : t4[q + 2];
-        t2[q] = keep + __shfl_xor(send, 2);
-      }
-    }
-    float tot;
-    {
-      const bool hi = (n & 1) != 0;
-      const float keep = hi ? t2[1] : t2[0], send = hi ? t2[0] : t2[1];
-      tot = keep + __shfl_xor(send, 1);
-    }
+    const float tot = reduce_scatter16(acc, n);
     if (key < lim) {
       if (a.nrg == 1) sc[key] = prev + tot;
       else part[key] = tot;
@@ -425,6 +433,253 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) kr[x][kk] = kn[x][kk];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-time refresh over the hybrid cache.  The unit's keys are its cache
+// as stored at decode position t, in list order: the K4V4 slots, the
+// vertical lines, the window positions t - nwin .. t - 1 (ring slot pos mod
+// W) and the staged token (position t).  A K4V4 key enters the scores as the
+// fp16 rounding of code * scale + min, the value the attention scan computes
+// with.  Row r = g * nb + jq is the buffered query at position
+// t - nb + 1 + jq; every cached key at a position up to the row's own gets
+// exp(tau q.k - lse) added to the running score at that position.
+// ---------------------------------------------------------------------------
+struct HybridList {
+  int nq, nvl, nwin, nst, n;
+};
+
+__device__ __forceinline__ HybridList hybrid_list(const SelArgs& a, int64_t u) {
+  HybridList h;
+  h.nq = min(max(a.c.n_q[u], 0), a.cap_q);
+  h.nvl = min(max(a.c.n_vl[u], 0), a.cap_vl);
+  h.nwin = min(a.W, a.t);
+  h.nst = min(max(a.c.n_stg[u], 0), min(a.cap_stg, 1));
+  h.n = h.nq + h.nvl + h.nwin + h.nst;
+  return h;
+}
+
+constexpr int kNoPos = 0x7FFFFFFF;   // list entries past the last key
+
+// K4V4 entries k0 + 16x + n (all of them below nq) for lane (n, j): the
+// group-j codes, {scale, min} and position of each.
+struct K4Raw {
+  uint4 codes[4];
+  uint32_t meta[4];
+  int pos[4];
+};
+
+__device__ __forceinline__ void load_k4raw(K4Raw& r, const SelArgs& a, int64_t u, int k0, int n, int j) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int64_t sl = u * a.cap_q + k0 + 16 * x + n;
+    r.codes[x] = ld16(a.c.kq + sl * kRowBytes + 16 * j);
+    r.meta[x] = reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j];
+    r.pos[x] = a.c.q_pos[sl];
+  }
+}
+
+// Eight 4-bit codes (element e in bits 4e .. 4e + 3) to eight fp16
+// code * scale + min, each rounded once: the code goes into the mantissa of
+// 1024 (giving exactly 1024 + code), 1024 is taken off (exact), then one
+// fused multiply-add.
+__device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t m2) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // byte i: element 2i
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // byte i: element 2i + 1
+  const half2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // low half: element 2i, high half: element 2i + 1
+    const uint32_t pair = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u + 0x00010001u * i) | 0x64006400u;
+    const half2_t c = __builtin_bit_cast(half2_t, pair) - k1024;
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, m2));
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ void dequant_group(uint4 out[4], uint4 codes, uint32_t meta) {
+  const half2_t sm = __builtin_bit_cast(half2_t, meta);
+  const half2_t s2 = {sm[0], sm[0]}, m2 = {sm[1], sm[1]};
+  out[0] = dequant8(codes.x, s2, m2);
+  out[1] = dequant8(codes.y, s2, m2);
+  out[2] = dequant8(codes.z, s2, m2);
+  out[3] = dequant8(codes.w, s2, m2);
+}
+
+// fp16 operands of any 64 list entries, lane (n, j) holding dims
+// 32j .. 32j + 31 of entry k0 + 16x + n in kr[x] (zeros past the list) and its
+// position in pos[x] (kNoPos past the list).  Used for the few chunks that
+// are not all K4V4, so the loads are simply issued in order.
+__device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelArgs& a,
+                                         const HybridList& h, int64_t u, int k0, int n, int j) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int ki = k0 + 16 * x + n;
+    if (ki < h.nq) {
+      const int64_t sl = u * a.cap_q + ki;
+      dequant_group(kr[x], ld16(a.c.kq + sl * kRowBytes + 16 * j),
+                    reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j]);
+      pos[x] = a.c.q_pos[sl];
+    } else {
+      int e = ki - h.nq;
+      const uint16_t* row = nullptr;
+      int p = kNoPos;
+      if (e < h.nvl) {
+        row = a.c.kvl + (u * a.cap_vl + e) * kD;
+        p = a.c.vl_pos[u * a.cap_vl + e];
+      } else if ((e -= h.nvl) < h.nwin) {
+        p = a.t - h.nwin + e;
+        row = a.c.kwin + (u * a.W + p % a.W) * kD;
+      } else if (e - h.nwin < h.nst) {
+        p = a.t;
+        row = a.c.kstg + u * a.cap_stg * kD;
+      }
+      pos[x] = p;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kr[x][kk] = row ? ld16(row + 32 * j + 8 * kk) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// acc[4x + e] += sum over the row group's rows of exp2(c2 s - lse log2 e)
+// for list entry k0 + 16x + 4j + e; masked: a row counts only when the
+// entry's position kp (kNoPos past the list) is at most its own.
+template <bool kMasked>
+__device__ __forceinline__ void chunk_refresh(float acc[16], const uint4 kr[4][4], const QStage& sq,
+                                              const float* s_nl, const int* s_prow, const int kp[16],
+                                              float c2, int lane, int n) {
+  float4_t sc[4];
+  scores(sc, kr, sq, 0, lane);
+  float nl_c = s_nl[n];
+  int pr_c = kMasked ? s_prow[n] : 0;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    float4_t sn[4];
+    float nl_n = 0.0f;
+    int pr_n = 0;
+    if (rb + 1 < kRB) {
+      scores(sn, kr, sq, rb + 1, lane);
+      nl_n = s_nl[(rb + 1) * 16 + n];
+      if (kMasked) pr_n = s_prow[(rb + 1) * 16 + n];
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[x][e], c2, nl_c));
+        if (kMasked) acc[4 * x + e] += (kp[4 * x + e] <= pr_c) ? p : 0.0f;
+        else acc[4 * x + e] += p;
+      }
+    if (!kMasked && rb + 1 < kRB) {
+      // the next row block's 16 MFMAs interleaved with this block's 48 VALU
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
+    if (rb + 1 < kRB) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) sc[x] = sn[x];
+      nl_c = nl_n;
+      pr_c = pr_n;
+    }
+  }
+}
+
+// Workgroup (x, unit): list entries [x * wg_keys, ...), wave w taking
+// 64-entry chunks w, w + 8, ...; while a chunk is computed, the next one's
+// K4V4 codes are in flight (the other chunks, a few per unit, load in place).
+// Row groups (G * nb > 256) run one after another inside the workgroup, each
+// adding its mass to the score entries it owns.
+__global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
+  __shared__ QStage s_q;                                    // 64 KB
+  __shared__ float s_nl[kRG];                               // -lse * log2(e), -inf for padding
+  __shared__ int s_prow[kRG];                               // row position, -1 for padding
+  __shared__ int s_kpos[kSWaves][kChunk];                   // positions of the wave's chunk
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, j = lane >> 4;
+  const int64_t u = blockIdx.y;
+  const int64_t b = u / a.Hkv;
+  const int h0 = static_cast<int>(u % a.Hkv) * a.G;
+  const int wg0 = blockIdx.x * a.wg_keys;
+  const HybridList h = hybrid_list(a, u);
+  if (wg0 >= h.n) return;                                   // the whole workgroup leaves
+  // K4V4 and vertical-line positions precede t - W, so every row (position
+  // t - nb + 1 or later) sees them when nb <= W + 1
+  const int n_unmasked = (a.nb <= a.W + 1) ? h.nq + h.nvl : 0;
+  float* sc_u = a.score + u * a.L;
+  const int own = 16 * (n >> 2) + 4 * j + (n & 3);
+  for (int rg = 0; rg < a.nrg; ++rg) {
+    if (rg > 0) {
+      // this workgroup's score updates of the last row group are visible to
+      // its reloads below
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+    K4Raw raw;
+    {
+      const int k0 = wg0 + kChunk * wave;
+      if (k0 + kChunk <= h.nq) load_k4raw(raw, a, u, k0, n, j);
+    }
+    stage_rows(s_q, a, b, h0, rg);
+    for (int rr = tid; rr < kRG; rr += kSThreads) {
+      const int r = rg * kRG + rr;
+      float nl = -INFINITY;
+      int pr = -1;
+      if (r < a.R) {
+        const int g = r / a.nb, jq = r - g * a.nb;
+        nl = -a.lse[(b * a.Hq + h0 + g) * a.nb + jq] * 1.4426950408889634f;
+        pr = a.t - a.nb + 1 + jq;
+      }
+      s_nl[rr] = nl;
+      s_prow[rr] = pr;
+    }
+    __syncthreads();
+    for (int i = 0; i < a.C; ++i) {
+      const int k0 = wg0 + kChunk * (wave + kSWaves * i);
+      if (k0 >= h.n) break;
+      uint4 kr[4][4];
+      int kpos[4];
+      if (k0 + kChunk <= h.nq) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          dequant_group(kr[x], raw.codes[x], raw.meta[x]);
+          kpos[x] = raw.pos[x];
+        }
+      } else {
+        load_any(kr, kpos, a, h, u, k0, n, j);
+      }
+      // positions through LDS: lane (n, j) needs those of entries 16x + 4j + e
+#pragma unroll
+      for (int x = 0; x < 4; ++x) s_kpos[wave][16 * x + n] = kpos[x];
+      const int op = s_kpos[wave][own];
+      const bool owned = op >= 0 && op < a.L;
+      // the running score of the owned position, loaded before the prefetch
+      const float prev = owned ? sc_u[op] : 0.0f;
+      const int k1 = k0 + kChunk * kSWaves;
+      if (k1 + kChunk <= h.nq && i + 1 < a.C) load_k4raw(raw, a, u, k1, n, j);
+      __builtin_amdgcn_sched_barrier(0);                    // keep the prefetch ahead
+      float acc[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      if (k0 + kChunk <= n_unmasked) {
+        chunk_refresh<false>(acc, kr, s_q, s_nl, s_prow, nullptr, a.c2, lane, n);
+      } else {
+        int kp[16];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kp[4 * x + e] = s_kpos[wave][16 * x + 4 * j + e];
+        chunk_refresh<true>(acc, kr, s_q, s_nl, s_prow, kp, a.c2, lane, n);
+      }
+      const float tot = reduce_scatter16(acc, n);
+      if (owned && k0 + own < h.n) sc_u[op] = prev + tot;
+    }
   }
 }
 
@@ -697,6 +952,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   // scan over them.
   int base = 0;          // taken positions before the segment
   int eq_seen = 0;       // threshold-equal positions before the segment
+  uint32_t tmin = 0xFFFFFFFFu;   // smallest taken key: the n_vl-th largest score
   for (int seg = 0; seg < a.L; seg += kSeg) {
     uint32_t gt = 0, eq = 0;            // bit k: row k of this thread
     if (k_want > 0) {
@@ -706,6 +962,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
           if (tid + k * kTopThreads < n) {
             gt |= static_cast<uint32_t>(keys[k] > thresh) << k;
             eq |= static_cast<uint32_t>(keys[k] == thresh) << k;
+            if (keys[k] > thresh) tmin = min(tmin, keys[k]);
           }
         }
       } else {
@@ -716,6 +973,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
           if (i < n) {
             gt |= static_cast<uint32_t>(key > thresh) << k;
             eq |= static_cast<uint32_t>(key == thresh) << k;
+            if (key > thresh) tmin = min(tmin, key);
           }
         }
       }
@@ -745,6 +1003,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       }
     }
     eq_seen += eq_tot;
+    if (take & eq) tmin = min(tmin, thresh);
     // per (row, wave) counts of taken positions, then their exclusive prefix
 #pragma unroll
     for (int k = 0; k < kKeysPerThread; ++k) {
@@ -787,6 +1046,19 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
     base += sh.tot;
     __syncthreads();
   }
+  if (a.cut) {
+    // the n_vl-th largest score: the smallest taken key (+inf when none)
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+      tmin = min(tmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmin), o)));
+    if (lane == 0) sh.red[0][wave] = static_cast<int>(tmin);
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = 0xFFFFFFFFu;
+      for (int w = 0; w < kTopWaves; ++w) m = min(m, static_cast<uint32_t>(sh.red[0][w]));
+      a.cut[u] = (k_want > 0) ? key_value(m) : INFINITY;
+    }
+  }
 }
 
 }  // namespace
@@ -807,7 +1079,7 @@ size_t select_ws_bytes(const hq_dims& d, int32_t L_max) {
 hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, const uint16_t* k,
                          int32_t L, const float* lse_in, float* score, int32_t* vl_idx,
                          uint8_t* vl_flag, void* ws, hipStream_t s) {
-  SelArgs a;
+  SelArgs a{};
   a.qbuf = qbuf;
   a.k = k;
   a.Hq = d.Hq;
@@ -851,6 +1123,47 @@ hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, con
     const unsigned nwg2 = static_cast<unsigned>((a.n_nw + a.wg_keys - 1) / a.wg_keys);
     hipLaunchKernelGGL(col_mass_kernel, dim3(nwg2, U, nrg), dim3(kSThreads), 0, s, a);
   }
+  hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_refresh(const hq_dims& d, const hq_cache& c, int32_t t, const uint16_t* qbuf,
+                          int32_t nb, const float* lse, float* score, int32_t score_ld,
+                          int32_t* vl_idx, uint8_t* vl_flag, float* cut, hipStream_t s) {
+  SelArgs a{};
+  a.qbuf = qbuf;
+  a.lse = lse;
+  a.score = score;
+  a.vl_idx = vl_idx;
+  a.vl_flag = vl_flag;
+  a.cut = cut;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.Hq / d.Hkv;
+  a.nb = nb;
+  a.L = score_ld;
+  a.W = d.W;
+  a.R = a.G * nb;
+  a.n_nw = t > d.W ? t - d.W : 0;
+  a.n_vl = n_vertical(d.rho, a.n_nw);
+  a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
+  a.c = c;
+  a.t = t;
+  a.cap_q = d.cap_q;
+  a.cap_vl = d.cap_vl;
+  a.cap_stg = d.cap_stg;
+  const size_t units = static_cast<size_t>(d.B) * d.Hkv;
+  a.U = static_cast<int32_t>(units);
+  a.nrg = (a.R + kRG - 1) / kRG;
+  // a cache holding positions 0..t has t + 1 keys per unit
+  const int64_t nk = static_cast<int64_t>(t) + 1;
+  const int64_t chunks = static_cast<int64_t>(units) * ((nk + kChunk - 1) / kChunk) * a.nrg;
+  a.C = static_cast<int32_t>(std::min<int64_t>(16, std::max<int64_t>(2, (chunks + 8191) / 8192)));
+  a.wg_keys = kChunk * kSWaves * a.C;
+  const unsigned nwg = static_cast<unsigned>((nk + a.wg_keys - 1) / a.wg_keys);
+  const unsigned U = static_cast<unsigned>(units);
+  hipLaunchKernelGGL(refresh_mass_kernel, dim3(nwg, U), dim3(kSThreads), 0, s, a);
+  a.nrg = 1;                       // the scores are complete: nothing to fold
   hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();
 }

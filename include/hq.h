@@ -183,6 +183,59 @@ int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L,
                    const uint16_t* q, uint16_t* out, float* lse_or_null,
                    void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * hq_refresh_hybrid -- decode-time refresh of the running vertical-line
+ * score over the hybrid cache, and the cut-off a leaving token must reach
+ * (agihunt digest, method paragraph: the column-mass score is a running
+ * estimate over at most 64 buffered FP16 queries, refreshed every 64 tokens;
+ * README Overview item 1).
+ *
+ * The cache is the one at decode position t, as hq_quant_pack and
+ * hq_append_merge leave it: the K4V4 and vertical-line regions hold the
+ * positions below t - W, the window ring positions max(0, t - W) .. t - 1,
+ * and the staging region the token at t (at most one staged token is read).
+ * A K4V4 key enters as the fp16 rounding of code * scale + min.  Buffered
+ * query j of each query head (position p_j = t - nb + 1 + j) adds, for every
+ * cached key at a position i <= p_j, exp(q.k_i / sqrt(d) - lse_j) to
+ * score_inout[b][kvh][i], summed over the unit's heads and queries; lse_j is
+ * the row's natural-log logsumexp from its own decode step.  Then the
+ * n_vl = floor(rho * (t - W) + 1e-6) positions of [0, t - W) with the largest
+ * running score are selected (ties to the lower position) into vl_idx and
+ * vl_flag, and cut_out receives the n_vl-th largest running score (+inf
+ * when n_vl = 0): hq_append_merge_scored promotes a leaving token whose score
+ * reaches it.
+ *
+ *   qbuf        [B][Hq][nb][d] fp16, the last nb decode queries, 1 <= nb <= 64,
+ *               nb <= t + 1
+ *   lse         [B][Hq][nb] fp32
+ *   score_inout [B][Hkv][score_ld] fp32, score_ld >= t + 1 (a running score;
+ *               zero it before the first refresh)
+ *   vl_idx      [B][Hkv][n_vl] int32 out, ascending (may be NULL when n_vl = 0)
+ *   vl_flag     [B][Hkv][score_ld] uint8 out: 1 at selected positions, else 0
+ *   cut_out     [B][Hkv] fp32 out
+ * Keys a cache holds beyond positions 0..t are not scored; positions outside
+ * [0, score_ld) are skipped.  Requires t >= 0.
+ */
+int hq_refresh_hybrid(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                      const uint16_t* qbuf, int32_t nb, const float* lse,
+                      float* score_inout, int32_t score_ld, int32_t* vl_idx,
+                      uint8_t* vl_flag, float* cut_out, hipStream_t stream);
+
+/*
+ * hq_append_merge_scored -- hq_append_merge where the token leaving the
+ * window becomes a vertical line exactly when its running score reaches the
+ * unit's cut-off: score[b][kvh][pos] >= cut[b][kvh] (agihunt digest, method
+ * and decode paragraphs; README Overview item 1).
+ *
+ *   score [B][Hkv][score_ld] fp32, score_ld >= max(t, 1)
+ *   cut   [B][Hkv] fp32 (from hq_refresh_hybrid)
+ * Everything else, including the capacity rules, is as in hq_append_merge.
+ */
+int hq_append_merge_scored(const hq_dims* dims, const hq_cache* cache, int32_t t,
+                           const uint16_t* k_new, const uint16_t* v_new,
+                           const float* score, int32_t score_ld, const float* cut,
+                           hipStream_t stream);
+
 /* Workspace bytes an operation needs for any prefix length up to L_max;
  * 0 for an invalid request. */
 size_t hq_workspace_bytes(const hq_dims* dims, int op, int32_t L_max);

@@ -22,6 +22,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
+            "hq_refresh_hybrid", "hq_append_merge_scored",
             "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
@@ -31,7 +32,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 1
+    assert H.lib.hq_abi_version() == 2
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -126,6 +127,41 @@ def test_select_validation():
     assert f(*args(idx=None)) == -1                     # n_vl > 0 needs vl_idx
     assert f(*args(ws=None)) == -5
     assert f(*args(wsb=need - 1)) == -5
+
+
+def test_refresh_validation():
+    d = _dims()
+    c = _fake_cache()
+    f = H.lib.hq_refresh_hybrid
+    args = lambda t=1000, nb=64, ld=1001, idx=P, cut=P, lse=P, q=P: (
+        ctypes.byref(d), ctypes.byref(c), t, q, nb, lse, P, ld, idx, P, cut, None)
+    assert f(*args(t=-1)) == -1
+    assert f(*args(nb=0)) == -1
+    assert f(*args(nb=65)) == -1
+    assert f(*args(t=10, nb=12, ld=11)) == -1           # nb > t + 1
+    assert f(*args(ld=1000)) == -1                       # score row shorter than t + 1
+    assert f(*args(idx=None)) == -1                      # n_vl > 0 needs vl_idx
+    assert f(*args(cut=None)) == -1
+    assert f(*args(lse=None)) == -1
+    assert f(*args(q=P + 8)) == -3
+    assert f(*args(cut=P + 4)) == -3
+    bad = _fake_cache()
+    bad.q_pos = None
+    assert f(ctypes.byref(d), ctypes.byref(bad), 1000, P, 64, P, P, 1001, P, P, P, None) == -1
+
+
+def test_scored_merge_validation():
+    d = _dims()
+    c = _fake_cache()
+    f = H.lib.hq_append_merge_scored
+    args = lambda t=100, ld=100, score=P, cut=P, k=P: (
+        ctypes.byref(d), ctypes.byref(c), t, k, P, score, ld, cut, None)
+    assert f(*args(t=-1)) == -1
+    assert f(*args(score=None)) == -1
+    assert f(*args(cut=None)) == -1
+    assert f(*args(ld=99)) == -1                         # the leaving position may be t - 1
+    assert f(*args(k=P + 2)) == -3
+    assert f(ctypes.byref(_dims(cap_stg=0)), ctypes.byref(c), 100, P, P, P, 100, P, None) == -4
 
 
 def test_workspace_bytes():
