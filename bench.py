@@ -282,6 +282,8 @@ def main():
         mrg[r](pos[r], kp[i % pool], vp[i % pool])
         pos[r] += 1
     merge_ms = time_loop(merge_only, 64)
+    torch.cuda.synchronize()
+    refresh = refresh_timing(H, torch, wl, dims, caches, pos, qbuf, capture)
 
     # ---- algorithmic bytes ------------------------------------------------
     n_q_mid = (n_nw - n_vl) + (args.warmup + args.steps // 2) // R
@@ -332,6 +334,7 @@ def main():
         "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step, 4),
                          "amortized": round(sel_ms / (sel_ms + REFRESH * (ms_step - sel_ms / REFRESH)), 4)},
         "select_util": sel_util,
+        "decode_time_refresh": refresh,
         "b_sweep": sweep,
         "read_ceiling": ceiling,
         "replicas": R, "input_gen_s": round(gen_s, 1),
@@ -339,6 +342,55 @@ def main():
     if ceiling:
         rec["roofline"]["frac_of_measured_ceiling"] = round(achieved / ceiling["read_gbs"], 4)
     print(json.dumps(rec))
+
+
+def refresh_timing(H, torch, wl, dims, caches, pos, qbuf, capture):
+    """hq_refresh_hybrid (the decode-time running refresh over the hybrid
+    cache, every 64 tokens) at the cache each replica holds now: average of
+    back-to-back calls over the replicas, replayed from a HIP graph."""
+    B, Hq, Hkv, d, W = wl.B, wl.Hq, wl.Hkv, wl.d, wl.W
+    U, G, nb = B * Hkv, Hq // Hkv, qbuf.shape[2]
+    R = len(caches)
+    ld = max(pos) + 1
+    lse = torch.full((B, Hq, nb), 8.0, dtype=torch.float32, device="cuda")
+    score = torch.zeros((B, Hkv, ld), dtype=torch.float32, device="cuda")
+    flag = torch.zeros((B, Hkv, ld), dtype=torch.uint8, device="cuda")
+    cut = torch.zeros((B, Hkv), dtype=torch.float32, device="cuda")
+    n_vl_max = H.n_vertical(wl.rho, max(0, ld - W))
+    idx = torch.zeros((B, Hkv, max(1, n_vl_max)), dtype=torch.int32, device="cuda")
+    ts = [p - 1 for p in pos]                      # each replica's staged position
+    n = 2 * R
+
+    def body(stream):
+        for i in range(n):
+            r = i % R
+            H.hq_refresh_hybrid(dims, caches[r], ts[r], qbuf, lse, score, idx, flag, cut, stream=stream)
+    g = capture(body)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    t = ts[0]
+    n_nw = max(0, t - W)
+    n_vl = H.n_vertical(wl.rho, n_nw)
+    n_q = n_nw - n_vl
+    n_f = n_vl + min(W, t) + 1
+    # keys only: K4V4 codes + {scale, min} + position (84 B), FP16 key (256 B,
+    # + 4 B position for a vertical line); the score read and written, the
+    # top-k pass over it (score read, flags written), queries and LSE in
+    byts = (U * (84 * n_q + 256 * n_f + 4 * n_vl + 8 * (t + 1) + 5 * n_nw)
+            + B * Hq * nb * (d * 2 + 4))
+    flops = 2 * U * (t + 1) * G * nb * d
+    return {"us": round(us, 2), "t": t, "nb": nb,
+            "hbm_gbs": round(byts / (us * 1e-6) / 1e9, 1),
+            "mfma_tflops": round(flops / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flops / (us * 1e-6) / 1e12 / PEAK_F16_TFLOPS, 4),
+            "bytes": byts, "flops": flops,
+            "per_step_us": round(us / REFRESH, 3)}
 
 
 def graph_decode_us(H, torch, dims, caches, wss, L, q, out, n):
@@ -439,8 +491,9 @@ def read_ceiling(torch, nbytes=1 << 30):
 
 
 def cpu_baseline(wl, cache, H, torch):
-    """Time the fp64 oracle's decode step on whole units of the same cache
-    until about 10 s of CPU work, and report it in the metric's unit."""
+    """Time the fp64 oracle on whole decode steps of the same cache (every
+    unit merges a new token, then decodes) until about 10 s of CPU work, and
+    report it in the metric's unit."""
     from oracle import hq_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -449,31 +502,36 @@ def cpu_baseline(wl, cache, H, torch):
         threads = 1
     B, Hkv, G, L, W, d = wl.B, wl.Hkv, wl.G, wl.L, wl.W, wl.d
     rng = np.random.default_rng(0)
-    units = [(b, g) for b in range(B) for g in range(Hkv)]
-    done, nbytes, t_cpu = 0, 0, 0.0
-    for (b, g) in units:
-        t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()}
-        nq, nvl = int(t["n_q"]), int(t["n_vl"])
-        c = O.empty_unit_cache(d, W)
-        c["kq"], c["vq"] = t["kq"][:nq], t["vq"][:nq]
-        c["kq_meta"], c["vq_meta"], c["q_pos"] = t["kq_meta"][:nq], t["vq_meta"][:nq], t["q_pos"][:nq]
-        c["kvl"], c["vvl"], c["vl_pos"] = t["kvl"][:nvl], t["vvl"][:nvl], t["vl_pos"][:nvl]
-        if W:
-            c["kwin"], c["vwin"] = t["kwin"], t["vwin"]
-        q = rng.standard_normal((G, d)).astype(np.float16)
-        kn = rng.standard_normal(d).astype(np.float16)
-        t0 = time.perf_counter()
-        O.append_merge_unit(c, L, kn, kn)
-        O.decode_fused(c, q, L)
-        t_cpu += time.perf_counter() - t0
-        done += 1
-        nbytes += 160 * c["kq"].shape[0] + 512 * (c["kvl"].shape[0] + min(W, L) + 1) + G * d * 4
-        if t_cpu > 10.0:
-            break
+    caches = []
+    for b in range(B):
+        for g in range(Hkv):
+            t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()}
+            nq, nvl = int(t["n_q"]), int(t["n_vl"])
+            c = O.empty_unit_cache(d, W)
+            c["kq"], c["vq"] = t["kq"][:nq], t["vq"][:nq]
+            c["kq_meta"], c["vq_meta"], c["q_pos"] = t["kq_meta"][:nq], t["vq_meta"][:nq], t["q_pos"][:nq]
+            c["kvl"], c["vvl"], c["vl_pos"] = t["kvl"][:nvl], t["vvl"][:nvl], t["vl_pos"][:nvl]
+            if W:
+                c["kwin"], c["vwin"] = t["kwin"], t["vwin"]
+            caches.append(c)
+    steps, nbytes, t_cpu = 0, 0, 0.0
+    while t_cpu < 10.0 and steps < 500:
+        pos = L + steps
+        for c in caches:
+            q = rng.standard_normal((G, d)).astype(np.float16)
+            kn = rng.standard_normal(d).astype(np.float16)
+            t0 = time.perf_counter()
+            O.append_merge_unit(c, pos, kn, kn)
+            O.decode_fused(c, q, pos)
+            t_cpu += time.perf_counter() - t0
+            n_win = min(W, pos)
+            nbytes += 160 * c["kq"].shape[0] + 512 * (c["kvl"].shape[0] + n_win + 1) + G * d * 4
+        steps += 1
     return {"value": round(nbytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 oracle merge + fused decode of {done} of {len(units)} (sequence, KV head) "
-                      f"units of the same cache, {t_cpu:.1f} s CPU; GB/s of the same algorithmic bytes"}
+            "sample": f"fp64 oracle merge + fused decode, {steps} whole decode steps of all "
+                      f"{len(caches)} (sequence, KV head) units of the same cache, {t_cpu:.1f} s CPU; "
+                      f"GB/s of the same algorithmic bytes"}
 
 
 if __name__ == "__main__":
