@@ -115,13 +115,24 @@ __device__ __forceinline__ void load_keys(uint4 kr[4][4], const uint16_t* kunit,
 // discarded).  Every lane of a wave then reads 16 consecutive bytes.
 using QStage = uint4[kRB][4][64];
 
+constexpr int kStageIters = kRG * 16 / kSThreads;   // 16-byte pieces per thread
+
 __device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t b, int h0, int rg) {
-  for (int idx = threadIdx.x; idx < kRG * 16; idx += kSThreads) {
+  // all of the thread's loads are issued before any is stored
+  uint4 v[kStageIters];
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) {
+    const int idx = threadIdx.x + i * kSThreads;
     const int rr = idx >> 4, ch = idx & 15;
     const int r = min(rg * kRG + rr, a.R - 1);
     const int g = r / a.nb, jq = r - g * a.nb;
-    sq[rr >> 4][ch & 3][16 * (ch >> 2) + (rr & 15)] =
-        ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
+    v[i] = ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
+  }
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) {
+    const int idx = threadIdx.x + i * kSThreads;
+    const int rr = idx >> 4, ch = idx & 15;
+    sq[rr >> 4][ch & 3][16 * (ch >> 2) + (rr & 15)] = v[i];
   }
 }
 
@@ -371,34 +382,49 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
   uint4 kr[4][4];
   load_keys(kr, kunit, wg0 + kChunk * wave, a.L, n, j);
   stage_rows(s_q, a, b, h0, rg);
-  for (int rr = tid; rr < kRG; rr += kSThreads) {
+  if (a.lse_from_stats) {
+    // merge each row's (max, sum exp2) over the pass-1 workgroups: thread
+    // pair (row, half) takes every other workgroup, eight loads in flight at
+    // a time, as running (max, sum) pairs; the halves then combine
+    static_assert(kSThreads == 2 * kRG, "two threads per row");
+    const int rr = tid >> 1, half = tid & 1;
     const int r = rg * kRG + rr;
-    float nl = -INFINITY;                                   // padding rows add nothing
-    if (r < a.R) {
-      if (a.lse_from_stats) {
-        // merge the row's (max, sum exp2) over the pass-1 workgroups: the
-        // max first, then one exponential per workgroup (no serial chain)
-        const float2* st = a.stats + u * a.nwg1 * a.R + r;
-        float mx = -INFINITY;
-        for (int t = 0; t < a.nwg1; ++t) mx = fmaxf(mx, st[static_cast<int64_t>(t) * a.R].x);
-        float s0 = 0.0f, s1 = 0.0f;
-        int t = 0;
-        for (; t + 1 < a.nwg1; t += 2) {
-          const float2 v0 = st[static_cast<int64_t>(t) * a.R], v1 = st[static_cast<int64_t>(t + 1) * a.R];
-          s0 = fmaf(v0.y, __builtin_amdgcn_exp2f((v0.x - mx) * a.c2), s0);
-          s1 = fmaf(v1.y, __builtin_amdgcn_exp2f((v1.x - mx) * a.c2), s1);
-        }
-        if (t < a.nwg1) {
-          const float2 v0 = st[static_cast<int64_t>(t) * a.R];
-          s0 = fmaf(v0.y, __builtin_amdgcn_exp2f((v0.x - mx) * a.c2), s0);
-        }
-        nl = -(mx * a.c2 + log2f(s0 + s1));                 // -lse * log2(e)
-      } else {
+    const float2* st = a.stats + u * a.nwg1 * a.R + min(r, a.R - 1);
+    float mx = -INFINITY, sum = 0.0f;
+    for (int t0 = half; t0 < a.nwg1; t0 += 16) {
+      float2 v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = st[static_cast<int64_t>(min(t0 + 2 * e, a.nwg1 - 1)) * a.R];
+      float cm = mx;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t0 + 2 * e < a.nwg1) cm = fmaxf(cm, v[e].x);
+      if (cm != -INFINITY) {
+        float s = sum * __builtin_amdgcn_exp2f((mx - cm) * a.c2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 2 * e < a.nwg1) s = fmaf(v[e].y, __builtin_amdgcn_exp2f((v[e].x - cm) * a.c2), s);
+        sum = s;
+        mx = cm;
+      }
+    }
+    const float mo = __shfl_xor(mx, 1), so = __shfl_xor(sum, 1);
+    const float m = fmaxf(mx, mo);
+    float tot = 0.0f;
+    if (m != -INFINITY)
+      tot = sum * __builtin_amdgcn_exp2f((mx - m) * a.c2) + so * __builtin_amdgcn_exp2f((mo - m) * a.c2);
+    if (half == 0) s_nl[rr] = (r < a.R) ? -(m * a.c2 + log2f(tot)) : -INFINITY;   // -lse * log2(e)
+  } else {
+    for (int rr = tid; rr < kRG; rr += kSThreads) {
+      const int r = rg * kRG + rr;
+      float nl = -INFINITY;                                 // padding rows add nothing
+      if (r < a.R) {
         const int g = r / a.nb, jq = r - g * a.nb;
         nl = -a.lse[(b * a.Hq + h0 + g) * a.nb + jq] * 1.4426950408889634f;
       }
+      s_nl[rr] = nl;
     }
-    s_nl[rr] = nl;
   }
   __syncthreads();
   float* sc = a.score + u * a.L;
@@ -688,12 +714,15 @@ constexpr int kKeysPerThread = 32;              // register-resident keys per th
 constexpr int kSeg = kKeysPerThread * kTopThreads;
 constexpr int kSampleStride = 8;                // rows k = 0, 8, 16, 24 form the sample
 
+constexpr int kListMax = 4096;                  // keys of a confirmed bracket kept in LDS
+
 struct TopShared {
   int hist[kTopWaves][256];
   int red[2][kTopWaves];
   uint32_t sel[4];
   int cnt[kKeysPerThread * kTopWaves];
   int tot;
+  uint32_t list[kListMax];
 };
 
 // Sum of two ints over the workgroup (every thread gets both totals).
@@ -748,6 +777,35 @@ __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], c
   }
   if (!sample) {
     for (int i = kSeg + tid; i < n; i += kTopThreads) add(order_key(sc[i]), true);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kTopWaves; ++w) c += sh.hist[w][tid];
+    sh.hist[0][tid] = c;
+  }
+  __syncthreads();
+}
+
+// hist_pass over the compacted keys of a bracket (cnt <= kListMax).
+__device__ __forceinline__ void hist_list(int cnt, uint32_t lo, uint32_t hi, int shift, TopShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kTopWaves * 256; i += kTopThreads) (&sh.hist[0][0])[i] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < cnt; i0 += kTopThreads) {
+    const int i = i0 + tid;
+    const uint32_t key = sh.list[max(min(i, cnt - 1), 0)];
+    const bool in = i < cnt && key >= lo && key <= hi;
+    const uint32_t bin = (key - lo) >> shift;
+    const uint64_t act = __ballot(in);
+    if (act) {
+      const int leader = __builtin_ctzll(act);
+      const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+      const uint64_t same = __ballot(in && bin == lbin);
+      if (lane == leader) atomicAdd(&sh.hist[wave][lbin], __popcll(same));
+      else if (in && bin != lbin) atomicAdd(&sh.hist[wave][bin], 1);
+    }
   }
   __syncthreads();
   if (tid < 256) {
@@ -830,6 +888,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
     for (int k = 0; k < kKeysPerThread; ++k) keys[k] = order_key(sc[min(tid + k * kTopThreads, n - 1)]);
     uint32_t lo = 0, hi = 0;
     int kk = k_want;                   // rank of the target inside [lo, hi]
+    int list_n = -1;                   // >= 0: the keys in [lo, hi] are in sh.list
     {
       // the key range [min, max]
       uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
@@ -904,26 +963,50 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       __syncthreads();
       const uint32_t blo = (r_bot >= ns) ? lo : lo + (b_bot << shift);
       const uint32_t bhi = (r_top <= 0) ? hi : min(hi, lo + (b_top << shift) + ((1u << shift) - 1u));
-      int c_above = 0, c_in = 0;
+      int c_above = 0;
+      uint32_t inmask = 0;                         // bit k: key k lies in the bracket
 #pragma unroll
       for (int k = 0; k < kKeysPerThread; ++k) {
         if (tid + k * kTopThreads < n) {
           c_above += keys[k] > bhi;
-          c_in += (keys[k] >= blo && keys[k] <= bhi);
+          inmask |= static_cast<uint32_t>(keys[k] >= blo && keys[k] <= bhi) << k;
         }
       }
+      const int c_mine = __popc(inmask);
+      int c_in = c_mine;
       block_sum2(c_above, c_in, sh);
       if (c_above < k_want && k_want <= c_above + c_in) {
         lo = blo;
         hi = bhi;
         kk = k_want - c_above;
+        if (c_in <= kListMax) {
+          // the bracket's keys into LDS, in thread order: the radix passes
+          // below then read c_in keys instead of all n
+          int incl = c_mine;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+          }
+          if (lane == 63) sh.red[0][wave] = incl;
+          __syncthreads();
+          int off = incl - c_mine;
+          for (int w = 0; w < wave; ++w) off += sh.red[0][w];
+#pragma unroll
+          for (int k = 0; k < kKeysPerThread; ++k) {
+            if ((inmask >> k) & 1u) sh.list[off++] = keys[k];
+          }
+          __syncthreads();
+          list_n = c_in;
+        }
       }
     }
 
     bool whole_bin = false;
     while (lo < hi) {
       const int shift = range_shift(lo, hi);
-      hist_pass(keys, sc, n, lo, hi, shift, false, sh);
+      if (list_n >= 0) hist_list(list_n, lo, hi, shift, sh);
+      else hist_pass(keys, sc, n, lo, hi, shift, false, sh);
       if (wave == 0) find_bin(kk, sh);
       __syncthreads();
       const uint32_t bin = sh.sel[0];
