@@ -91,6 +91,55 @@ __device__ __forceinline__ float sum_j(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Cross-lane moves inside the VALU (no LDS round trip).  DPP: lane ^ 1 and
+// lane ^ 2 (quad permutes), the mirror inside each half-row of 8 (lane ^ 7)
+// and inside each row of 16 (lane ^ 15); v_permlane16/32_swap exchange rows.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kCtrl, 0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dppf(float x) {
+  return __uint_as_float(dpp<kCtrl>(__float_as_uint(x)));
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kRowMirror = 0x140;
+
+// op over the 64 lanes of a wave; every lane gets the result
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_all(uint32_t x, Op op) {
+  x = op(x, dpp<kXor1>(x));
+  x = op(x, dpp<kXor2>(x));
+  x = op(x, dpp<kHalfMirror>(x));
+  x = op(x, dpp<kRowMirror>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
+__device__ __forceinline__ int wave_sum(int x) {
+  return static_cast<int>(wave_all(static_cast<uint32_t>(x), [](uint32_t p, uint32_t q) { return p + q; }));
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  return wave_all(x, [](uint32_t p, uint32_t q) { return min(p, q); });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  return wave_all(x, [](uint32_t p, uint32_t q) { return max(p, q); });
+}
+
+// inclusive prefix sum over the 64 lanes: row_shr 1, 2, 4, 8 (zero fill)
+// inside each row of 16, then the totals of the earlier rows
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  x += static_cast<int>(dpp<0x111>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp<0x112>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp<0x114>(static_cast<uint32_t>(x)));
+  x += static_cast<int>(dpp<0x118>(static_cast<uint32_t>(x)));
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -136,11 +185,12 @@ __device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t
   }
 }
 
-__device__ __forceinline__ void scores(float4_t s[4], const uint4 kr[4][4], const QStage& sq,
-                                       int rb, int lane) {
-  half8_t qb[4];
+__device__ __forceinline__ void load_q(half8_t qb[4], const QStage& sq, int rb, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qb[kk] = as_half8(sq[rb][kk][lane]);
+}
+
+__device__ __forceinline__ void mfma_scores(float4_t s[4], const uint4 kr[4][4], const half8_t qb[4]) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) s[x] = (float4_t){0.f, 0.f, 0.f, 0.f};
   // four independent accumulation chains, interleaved
@@ -149,6 +199,11 @@ __device__ __forceinline__ void scores(float4_t s[4], const uint4 kr[4][4], cons
 #pragma unroll
     for (int x = 0; x < 4; ++x) s[x] = mfma(as_half8(kr[x][kk]), qb[kk], s[x]);
 }
+
+// The row statistics keep their LDS operands ahead of use: the query operands
+// of row block rb + 2 and the running state of rb + 1 are read while row block
+// rb is computed.  (The column-mass loops keep theirs one block ahead: two
+// would not fit their registers.)
 
 // Streaming workgroup (x, unit, row group): keys [x * wg_keys, ...), wave w
 // taking 64-key chunks w, w + 8, ... with the next chunk's keys in flight
@@ -163,11 +218,20 @@ __device__ __forceinline__ void chunk_row_stats(float2 (*st)[64], const uint4 kr
                                                 const QStage& sq, const SelArgs& a, int rg, int k0,
                                                 int lane, int n, int j) {
   float4_t sc[4];
-  scores(sc, kr, sq, 0, lane);
+  half8_t q1[4], q2[4];
+  load_q(q1, sq, 0, lane);
+  mfma_scores(sc, kr, q1);
+  load_q(q1, sq, 1, lane);
+  float2 old = st[0][lane];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     float4_t sn[4];
-    if (rb + 1 < kRB) scores(sn, kr, sq, rb + 1, lane);
+    float2 old_n = old;
+    if (rb + 2 < kRB) load_q(q2, sq, rb + 2, lane);
+    if (rb + 1 < kRB) {
+      old_n = st[rb + 1][lane];
+      mfma_scores(sn, kr, q1);
+    }
     float v[16];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -185,10 +249,11 @@ __device__ __forceinline__ void chunk_row_stats(float2 (*st)[64], const uint4 kr
           if (!(key < a.L && key <= prow)) v[4 * x + e] = -INFINITY;
         }
     }
-    const float2 old = st[rb][lane];
-    float mx = old.x;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(v[e], v[e + 1]));
+    // a tree of three-input maxima (v_max3_f32) over the 16 values and the old max
+    const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+    const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+    const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]), m5 = fmaxf(fmaxf(v[15], old.x), m0);
+    const float mx = fmaxf(fmaxf(m1, m2), fmaxf(fmaxf(m3, m4), m5));
     const float mu = (kMasked && mx == -INFINITY) ? 0.0f : mx;
     const float nmc = -mu * a.c2;
     float s0 = 0.0f, s1 = 0.0f;
@@ -199,7 +264,9 @@ __device__ __forceinline__ void chunk_row_stats(float2 (*st)[64], const uint4 kr
     }
     st[rb][lane] = make_float2(mx, fmaf(old.y, __builtin_amdgcn_exp2f(fmaf(old.x, a.c2, nmc)), s0 + s1));
     if (!kMasked && rb + 1 < kRB) {
-      // the next row block's 16 MFMAs interleaved with this block's VALU
+      // the LDS reads first, then the next row block's 16 MFMAs interleaved
+      // with this block's VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -209,6 +276,9 @@ __device__ __forceinline__ void chunk_row_stats(float2 (*st)[64], const uint4 kr
     if (rb + 1 < kRB) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) sc[x] = sn[x];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) q1[kk] = q2[kk];
+      old = old_n;
     }
   }
 }
@@ -284,15 +354,18 @@ __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][
                                                const float* s_nl, const SelArgs& a, int rg, int k0,
                                                int lane, int n, int j) {
   float4_t sc[4];
-  scores(sc, kr, sq, 0, lane);
+  half8_t qb[4];
+  load_q(qb, sq, 0, lane);
+  mfma_scores(sc, kr, qb);
   float nl_c = s_nl[n];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     float4_t sn[4];
     float nl_n = 0.0f;
     if (rb + 1 < kRB) {
-      scores(sn, kr, sq, rb + 1, lane);
+      load_q(qb, sq, rb + 1, lane);
       nl_n = s_nl[(rb + 1) * 16 + n];
+      mfma_scores(sn, kr, qb);
     }
     if (!kMasked) {
 #pragma unroll
@@ -329,9 +402,11 @@ __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][
 }
 
 // Sum over the 16 row lanes of a wave: lane (n, j) ends with the total of
-// acc[n], i.e. of list entry 16 (n >> 2) + 4 j + (n & 3) of the chunk.  At
-// the step with bit b the lane keeps the half of the values whose index bit
-// b equals its own and adds the partner's copy of that half.
+// acc[n], i.e. of entry 16 (n >> 2) + 4 j + (n & 3) of the chunk.  At the
+// step for bit b the lane keeps the half of the values whose index bit b
+// equals its own and adds the partner's copy of that half; any partner that
+// differs in bit b and agrees in the higher bits will do, so the partners
+// are the DPP row mirror (bit 3), half-row mirror (bit 2) and quad swaps.
 __device__ __forceinline__ float reduce_scatter16(const float acc[16], int n) {
   float t8[8], t4[4], t2[2];
   {
@@ -339,7 +414,7 @@ __device__ __forceinline__ float reduce_scatter16(const float acc[16], int n) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float keep = hi ? acc[q + 8] : acc[q], send = hi ? acc[q] : acc[q + 8];
-      t8[q] = keep + __shfl_xor(send, 8);
+      t8[q] = keep + dppf<kRowMirror>(send);
     }
   }
   {
@@ -347,7 +422,7 @@ __device__ __forceinline__ float reduce_scatter16(const float acc[16], int n) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float keep = hi ? t8[q + 4] : t8[q], send = hi ? t8[q] : t8[q + 4];
-      t4[q] = keep + __shfl_xor(send, 4);
+      t4[q] = keep + dppf<kHalfMirror>(send);
     }
   }
   {
@@ -355,12 +430,12 @@ __device__ __forceinline__ float reduce_scatter16(const float acc[16], int n) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const float keep = hi ? t4[q + 2] : t4[q], send = hi ? t4[q] : t4[q + 2];
-      t2[q] = keep + __shfl_xor(send, 2);
+      t2[q] = keep + dppf<kXor2>(send);
     }
   }
   const bool hi = (n & 1) != 0;
   const float keep = hi ? t2[1] : t2[0], send = hi ? t2[0] : t2[1];
-  return keep + __shfl_xor(send, 1);
+  return keep + dppf<kXor1>(send);
 }
 
 // Pass 2: column mass of the non-window keys: per key, the sum over the row
@@ -409,7 +484,7 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
         mx = cm;
       }
     }
-    const float mo = __shfl_xor(mx, 1), so = __shfl_xor(sum, 1);
+    const float mo = dppf<kXor1>(mx), so = dppf<kXor1>(sum);
     const float m = fmaxf(mx, mo);
     float tot = 0.0f;
     if (m != -INFINITY)
@@ -577,7 +652,9 @@ __device__ __forceinline__ void chunk_refresh(float acc[16], const uint4 kr[4][4
                                               const float* s_nl, const int* s_prow, const int kp[16],
                                               float c2, int lane, int n) {
   float4_t sc[4];
-  scores(sc, kr, sq, 0, lane);
+  half8_t qb[4];
+  load_q(qb, sq, 0, lane);
+  mfma_scores(sc, kr, qb);
   float nl_c = s_nl[n];
   int pr_c = kMasked ? s_prow[n] : 0;
 #pragma unroll
@@ -586,9 +663,10 @@ __device__ __forceinline__ void chunk_refresh(float acc[16], const uint4 kr[4][4
     float nl_n = 0.0f;
     int pr_n = 0;
     if (rb + 1 < kRB) {
-      scores(sn, kr, sq, rb + 1, lane);
+      load_q(qb, sq, rb + 1, lane);
       nl_n = s_nl[(rb + 1) * 16 + n];
       if (kMasked) pr_n = s_prow[(rb + 1) * 16 + n];
+      mfma_scores(sn, kr, qb);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -728,11 +806,8 @@ struct TopShared {
 // Sum of two ints over the workgroup (every thread gets both totals).
 __device__ __forceinline__ void block_sum2(int& x, int& y, TopShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    x += __shfl_xor(x, o);
-    y += __shfl_xor(y, o);
-  }
+  x = wave_sum(x);
+  y = wave_sum(y);
   if (lane == 0) {
     sh.red[0][wave] = x;
     sh.red[1][wave] = y;
@@ -827,12 +902,7 @@ __device__ __forceinline__ void find_bin(int kk, TopShared& sh) {
     c[e] = sh.hist[0][255 - 4 * lane - e];        // lane l owns bins 255-4l .. 252-4l
     tot += c[e];
   }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(tot, lane);
   const int before = incl - tot;                  // keys in higher bins
   if (before < kk && incl >= kk) {
     int cum = before;
@@ -882,6 +952,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   uint32_t keys[kKeysPerThread];
   uint32_t thresh = 0;                 // keys > thresh are taken
   int take_eq = 0;                     // and this many keys == thresh, lowest positions first
+  bool eq_all = true;                  // known: every key == thresh is taken, or none is
   if (k_want > 0) {
     // unconditional loads (clamped index) so that all 32 are in flight at once
 #pragma unroll
@@ -904,11 +975,8 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
-        kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
-      }
+      kmin = wave_min(kmin);
+      kmax = wave_max(kmax);
       if (lane == 0) {
         sh.red[0][wave] = static_cast<int>(kmin);
         sh.red[1][wave] = static_cast<int>(kmax);
@@ -943,12 +1011,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
           c[e] = sh.hist[0][255 - 4 * lane - e];
           tot += c[e];
         }
-        int incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(tot, lane);
         int cum = incl - tot;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -982,12 +1045,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         if (c_in <= kListMax) {
           // the bracket's keys into LDS, in thread order: the radix passes
           // below then read c_in keys instead of all n
-          int incl = c_mine;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-          }
+          const int incl = wave_incl_scan(c_mine, lane);
           if (lane == 63) sh.red[0][wave] = incl;
           __syncthreads();
           int off = incl - c_mine;
@@ -1003,6 +1061,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
     }
 
     bool whole_bin = false;
+    int eq_total = -1;                 // keys == lo once the range is one value
     while (lo < hi) {
       const int shift = range_shift(lo, hi);
       if (list_n >= 0) hist_list(list_n, lo, hi, shift, sh);
@@ -1023,9 +1082,11 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       }
       lo = nlo;
       hi = nhi;
+      if (lo == hi) eq_total = cbin;
     }
     thresh = lo;
     take_eq = whole_bin ? 0 : kk;
+    eq_all = whole_bin || take_eq == eq_total;
   }
 
   // Flags and indices, segment by segment (position seg + tid + 1024 k).
@@ -1061,11 +1122,17 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         }
       }
     }
-    // how many threshold-equal keys the segment holds, in total
-    int eq_tot = __popc(eq), dummy = 0;
-    block_sum2(eq_tot, dummy, sh);
     uint32_t take = gt;
-    if (eq_seen + eq_tot <= take_eq) {
+    // how many threshold-equal keys the segment holds, in total (not needed
+    // when the radix select already knows that all or none are taken)
+    int eq_tot = 0, dummy = 0;
+    if (!eq_all) {
+      eq_tot = __popc(eq);
+      block_sum2(eq_tot, dummy, sh);
+    }
+    if (eq_all) {
+      if (take_eq > 0) take |= eq;       // whole_bin takes none of them
+    } else if (eq_seen + eq_tot <= take_eq) {
       take |= eq;                        // every equal key of the segment is taken
     } else {
       // ties at the cut-off: rank the equal keys in position order, row by row
@@ -1102,12 +1169,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         c[e] = sh.cnt[8 * lane + e];
         run += c[e];
       }
-      int incl = run;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-      }
+      const int incl = wave_incl_scan(run, lane);
       int acc = incl - run;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1131,9 +1193,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   }
   if (a.cut) {
     // the n_vl-th largest score: the smallest taken key (+inf when none)
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-      tmin = min(tmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(tmin), o)));
+    tmin = wave_min(tmin);
     if (lane == 0) sh.red[0][wave] = static_cast<int>(tmin);
     __syncthreads();
     if (tid == 0) {
