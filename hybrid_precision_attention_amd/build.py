@@ -23,10 +23,11 @@ SOURCES = ["hq_host.cpp", "quant_pack.hip", "decode_attn.hip", "select_vertical.
 PROBE_SOURCES = ["stream_probe.hip"]                # measurement helper, its own library
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# -fno-honor-nans: inputs are finite by contract, so fmaxf/fminf need no
-# canonicalising v_max per operand and chains fold into v_max3_f32
+# device code only: -fno-honor-nans (kernel inputs are finite by contract, so
+# fmaxf/fminf need no canonicalising v_max per operand and chains fold into
+# v_max3_f32); the host's argument checks keep their NaN tests
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-         "-Wno-unused-function", "-fno-honor-nans",
+         "-Wno-unused-function", "-Xarch_device", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
 
