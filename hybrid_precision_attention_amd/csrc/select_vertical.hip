@@ -794,14 +794,17 @@ constexpr int kSampleStride = 8;                // rows k = 0, 8, 16, 24 form th
 
 constexpr int kListMax = 4096;                  // keys of a confirmed bracket kept in LDS
 
+constexpr int kSegWords = kSeg / 32;            // bitmap words of one segment (one per thread)
+
 struct TopShared {
-  int hist[kTopWaves][256];
+  int hist[256];
   int red[2][kTopWaves];
   uint32_t sel[4];
-  int cnt[kKeysPerThread * kTopWaves];
-  int tot;
+  uint32_t gt[kSegWords];                       // bit p: position seg + p above the threshold
+  uint32_t eq[kSegWords];                       // bit p: equal to it; then: taken
   uint32_t list[kListMax];
 };
+static_assert(kSegWords == kTopThreads, "one bitmap word per thread");
 
 // Sum of two ints over the workgroup (every thread gets both totals).
 __device__ __forceinline__ void block_sum2(int& x, int& y, TopShared& sh) {
@@ -823,15 +826,33 @@ __device__ __forceinline__ void block_sum2(int& x, int& y, TopShared& sh) {
   __syncthreads();
 }
 
+// Exclusive prefix of x over the workgroup's threads, and the total.
+__device__ __forceinline__ void block_excl_scan(int x, int& excl, int& total, TopShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x, lane);
+  if (lane == 63) sh.red[1][wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopWaves; ++w) {
+    const int v = sh.red[1][w];
+    before += (w < wave) ? v : 0;
+    tot += v;
+  }
+  excl = before + incl - x;
+  total = tot;
+  __syncthreads();
+}
+
 // One histogram pass: keys in [lo, hi] counted into 256 bins of 2^shift keys
-// (per-wave LDS histograms; the lanes that share the first in-range lane's
-// bin add with one atomic, since same-address LDS atomics serialise), then
-// merged into hist[0].  Keys past the first segment are re-read.
+// in one LDS histogram (the lanes that share the first in-range lane's bin
+// add with one atomic, since same-address LDS atomics serialise).  Keys past
+// the first segment are re-read.
 __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], const float* sc, int n,
                                           uint32_t lo, uint32_t hi, int shift, bool sample,
                                           TopShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kTopWaves * 256; i += kTopThreads) (&sh.hist[0][0])[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 256) sh.hist[tid] = 0;
   __syncthreads();
   auto add = [&](uint32_t key, bool valid) {
     const bool in = valid && key >= lo && key <= hi;
@@ -841,8 +862,8 @@ __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], c
       const int leader = __builtin_ctzll(act);
       const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
       const uint64_t same = __ballot(in && bin == lbin);
-      if (lane == leader) atomicAdd(&sh.hist[wave][lbin], __popcll(same));
-      else if (in && bin != lbin) atomicAdd(&sh.hist[wave][bin], 1);
+      if (lane == leader) atomicAdd(&sh.hist[lbin], __popcll(same));
+      else if (in && bin != lbin) atomicAdd(&sh.hist[bin], 1);
     }
   };
 #pragma unroll
@@ -854,19 +875,12 @@ __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], c
     for (int i = kSeg + tid; i < n; i += kTopThreads) add(order_key(sc[i]), true);
   }
   __syncthreads();
-  if (tid < 256) {
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < kTopWaves; ++w) c += sh.hist[w][tid];
-    sh.hist[0][tid] = c;
-  }
-  __syncthreads();
 }
 
 // hist_pass over the compacted keys of a bracket (cnt <= kListMax).
 __device__ __forceinline__ void hist_list(int cnt, uint32_t lo, uint32_t hi, int shift, TopShared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kTopWaves * 256; i += kTopThreads) (&sh.hist[0][0])[i] = 0;
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid < 256) sh.hist[tid] = 0;
   __syncthreads();
   for (int i0 = 0; i0 < cnt; i0 += kTopThreads) {
     const int i = i0 + tid;
@@ -878,16 +892,9 @@ __device__ __forceinline__ void hist_list(int cnt, uint32_t lo, uint32_t hi, int
       const int leader = __builtin_ctzll(act);
       const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
       const uint64_t same = __ballot(in && bin == lbin);
-      if (lane == leader) atomicAdd(&sh.hist[wave][lbin], __popcll(same));
-      else if (in && bin != lbin) atomicAdd(&sh.hist[wave][bin], 1);
+      if (lane == leader) atomicAdd(&sh.hist[lbin], __popcll(same));
+      else if (in && bin != lbin) atomicAdd(&sh.hist[bin], 1);
     }
-  }
-  __syncthreads();
-  if (tid < 256) {
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < kTopWaves; ++w) c += sh.hist[w][tid];
-    sh.hist[0][tid] = c;
   }
   __syncthreads();
 }
@@ -899,7 +906,7 @@ __device__ __forceinline__ void find_bin(int kk, TopShared& sh) {
   int c[4], tot = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    c[e] = sh.hist[0][255 - 4 * lane - e];        // lane l owns bins 255-4l .. 252-4l
+    c[e] = sh.hist[255 - 4 * lane - e];        // lane l owns bins 255-4l .. 252-4l
     tot += c[e];
   }
   const int incl = wave_incl_scan(tot, lane);
@@ -1008,7 +1015,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         int c[4], tot = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          c[e] = sh.hist[0][255 - 4 * lane - e];
+          c[e] = sh.hist[255 - 4 * lane - e];
           tot += c[e];
         }
         const int incl = wave_incl_scan(tot, lane);
@@ -1089,108 +1096,82 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
     eq_all = whole_bin || take_eq == eq_total;
   }
 
-  // Flags and indices, segment by segment (position seg + tid + 1024 k).
-  // Keys equal to the threshold are taken lowest position first; when all of
-  // them are taken (no tie at the cut-off, the usual case) no ranking is
-  // needed.  Indices are compacted with per-(row, wave) ballot counts and one
-  // scan over them.
+  // Flags and indices, segment by segment of kSeg positions.  The rows of the
+  // coalesced layout (position seg + tid + 1024 k) leave their above- and
+  // equal-to-threshold bits in LDS bitmaps, one 64-bit ballot per (row, wave)
+  // covering 64 consecutive positions.  Thread t then owns bitmap word t
+  // (positions seg + 32 t .. + 31): equal keys are ranked in position order
+  // (only when some but not all of them are taken), and one scan of the
+  // threads' taken counts gives each thread the index of its first taken
+  // position.  Flags are written back in the coalesced layout.
   int base = 0;          // taken positions before the segment
   int eq_seen = 0;       // threshold-equal positions before the segment
   uint32_t tmin = 0xFFFFFFFFu;   // smallest taken key: the n_vl-th largest score
-  for (int seg = 0; seg < a.L; seg += kSeg) {
-    uint32_t gt = 0, eq = 0;            // bit k: row k of this thread
+  // segment 0 takes its keys from registers, later ones re-read them (the
+  // first call is separate so that the register keys die with it)
+  auto emit = [&](int seg, bool from_regs) {
     if (k_want > 0) {
-      if (seg == 0) {
 #pragma unroll
-        for (int k = 0; k < kKeysPerThread; ++k) {
-          if (tid + k * kTopThreads < n) {
-            gt |= static_cast<uint32_t>(keys[k] > thresh) << k;
-            eq |= static_cast<uint32_t>(keys[k] == thresh) << k;
-            if (keys[k] > thresh) tmin = min(tmin, keys[k]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kKeysPerThread; ++k) {
-          const int i = seg + tid + k * kTopThreads;
-          const uint32_t key = order_key(sc[min(i, max(n - 1, 0))]);
-          if (i < n) {
-            gt |= static_cast<uint32_t>(key > thresh) << k;
-            eq |= static_cast<uint32_t>(key == thresh) << k;
-            if (key > thresh) tmin = min(tmin, key);
-          }
-        }
-      }
-    }
-    uint32_t take = gt;
-    // how many threshold-equal keys the segment holds, in total (not needed
-    // when the radix select already knows that all or none are taken)
-    int eq_tot = 0, dummy = 0;
-    if (!eq_all) {
-      eq_tot = __popc(eq);
-      block_sum2(eq_tot, dummy, sh);
-    }
-    if (eq_all) {
-      if (take_eq > 0) take |= eq;       // whole_bin takes none of them
-    } else if (eq_seen + eq_tot <= take_eq) {
-      take |= eq;                        // every equal key of the segment is taken
-    } else {
-      // ties at the cut-off: rank the equal keys in position order, row by row
-      int seen = eq_seen;
       for (int k = 0; k < kKeysPerThread; ++k) {
-        const uint64_t bal = __ballot((eq >> k) & 1u);
-        if (lane == 0) sh.red[0][wave] = __popcll(bal);
-        __syncthreads();
-        int off = 0, tot = 0;
-        for (int w = 0; w < kTopWaves; ++w) {
-          off += (w < wave) ? sh.red[0][w] : 0;
-          tot += sh.red[0][w];
+        const int i = seg + tid + k * kTopThreads;
+        const uint32_t key = from_regs ? keys[k] : order_key(sc[min(i, n - 1)]);
+        const bool valid = i < n;
+        const bool g = valid && key > thresh, e = valid && key == thresh;
+        if (g) tmin = min(tmin, key);
+        const uint64_t bg = __ballot(g), be = __ballot(e);
+        if (lane == 0) {
+          // positions seg + 1024 k + 64 wave .. + 63 are words 32 k + 2 wave, + 1
+          const int w = 32 * k + 2 * wave;
+          sh.gt[w] = static_cast<uint32_t>(bg);
+          sh.gt[w + 1] = static_cast<uint32_t>(bg >> 32);
+          sh.eq[w] = static_cast<uint32_t>(be);
+          sh.eq[w + 1] = static_cast<uint32_t>(be >> 32);
         }
-        __syncthreads();
-        const int rank = seen + off + __popcll(bal & ((1ull << lane) - 1ull));
-        if (((eq >> k) & 1u) && rank < take_eq) take |= 1u << k;
-        seen += tot;
+        __builtin_amdgcn_sched_barrier(0);   // one row at a time: no ballot results piling up
       }
+    } else {
+      sh.gt[tid] = 0;
+      sh.eq[tid] = 0;
     }
-    eq_seen += eq_tot;
-    if (take & eq) tmin = min(tmin, thresh);
-    // per (row, wave) counts of taken positions, then their exclusive prefix
-#pragma unroll
+    __syncthreads();
+    const uint32_t e = sh.eq[tid];
+    uint32_t take = sh.gt[tid];
+    if (eq_all) {
+      if (take_eq > 0) take |= e;        // all of them (a whole-bin cut takes none)
+    } else {
+      // ties at the cut-off: the first take_eq equal keys in position order
+      int ex_e, tot_e;
+      block_excl_scan(__popc(e), ex_e, tot_e, sh);
+      int want = take_eq - (eq_seen + ex_e);
+      uint32_t m = e;
+      while (want > 0 && m) {
+        take |= m & (~m + 1u);
+        m &= m - 1u;
+        --want;
+      }
+      eq_seen += tot_e;
+    }
+    if (take & e) tmin = min(tmin, thresh);
+    // this thread's taken positions, ascending, after those of the threads before it
+    int ex_t, tot_t;
+    block_excl_scan(__popc(take), ex_t, tot_t, sh);
+    int o = base + ex_t;
+    for (uint32_t m = take; m; m &= m - 1u) {
+      if (o < k_want) idx[o] = seg + 32 * tid + __builtin_ctz(m);
+      ++o;
+    }
+    base += tot_t;
+    sh.eq[tid] = take;                   // the taken bitmap, for the flags
+    __syncthreads();
+#pragma unroll 4
     for (int k = 0; k < kKeysPerThread; ++k) {
-      const uint64_t bal = __ballot((take >> k) & 1u);
-      if (lane == 0) sh.cnt[k * kTopWaves + wave] = __popcll(bal);
+      const int pl = tid + k * kTopThreads;
+      if (seg + pl < a.L) flag[seg + pl] = static_cast<uint8_t>((sh.eq[pl >> 5] >> (pl & 31)) & 1u);
     }
-    __syncthreads();
-    if (wave == 0) {
-      // 512 counts in (row, wave) order = position order; 8 per lane
-      int c[8], run = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        c[e] = sh.cnt[8 * lane + e];
-        run += c[e];
-      }
-      const int incl = wave_incl_scan(run, lane);
-      int acc = incl - run;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = c[e];
-        sh.cnt[8 * lane + e] = acc;
-        acc += v;
-      }
-      if (lane == 63) sh.tot = incl;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kKeysPerThread; ++k) {
-      const int i = seg + tid + k * kTopThreads;
-      const bool t = (take >> k) & 1u;
-      if (i < a.L) flag[i] = static_cast<uint8_t>(t);
-      const uint64_t bal = __ballot(t);
-      if (t) idx[base + sh.cnt[k * kTopWaves + wave] + __popcll(bal & ((1ull << lane) - 1ull))] = i;
-    }
-    base += sh.tot;
-    __syncthreads();
-  }
+    __syncthreads();                     // before the next segment reuses the bitmaps
+  };
+  emit(0, true);
+  for (int seg = kSeg; seg < a.L; seg += kSeg) emit(seg, false);
   if (a.cut) {
     // the n_vl-th largest score: the smallest taken key (+inf when none)
     tmin = wave_min(tmin);

@@ -200,3 +200,50 @@ def test_select_workspace_reuse():
     for b in range(B):
         for g in range(Hkv):
             assert np.array_equal(i1[b, g, :n_vl], exact_topk(s1[b, g, :L - wl.W], n_vl))
+
+
+def test_select_two_segments():
+    """A prefix longer than one top-k segment (32768 positions): keys past the
+    first segment are re-read by the histogram passes and flagged segment by
+    segment, with indices continuing across the boundary."""
+    wl = workload("tiny", L=40000, n_plant=40)
+    print("case tiny L=40000", flush=True)
+    x = batch(wl, steps=1)
+    score_g, idx_g, flag_g, n_vl = gpu_select(x, wl)
+    score_o, _, _ = O.select_vertical(x["K"], x["qbuf"], wl.L, wl.W, wl.rho)
+    check(wl, x, score_g, idx_g, flag_g, n_vl, score_o)
+
+
+@pytest.mark.parametrize("L", [40000, 70000])
+def test_select_tied_across_segments(L):
+    """Every score equal over two or three segments: the equal keys are ranked
+    in position order across segments (the lowest n_vl positions)."""
+    wl = workload("tiny", L=L)
+    x = batch(wl, steps=1)
+    s_in = torch.full((wl.B, wl.Hkv, wl.L), 1.0e9, dtype=torch.float32, device="cuda")
+    score_g, idx_g, flag_g, n_vl = gpu_select(x, wl, score_in=s_in)
+    _own_topk_exact(wl, score_g, idx_g, flag_g, n_vl)
+    assert np.array_equal(idx_g[0, 0], np.arange(n_vl))
+
+
+def test_select_ties_at_the_cut():
+    """A block of equal scores straddling the cut-off: only the lowest of
+    them are taken, the higher ones not (ranking inside and across threads'
+    words)."""
+    wl = workload("llama31_8b", L=9000)
+    x = batch(wl, steps=1)
+    rng = np.random.default_rng(3)
+    n_nw = wl.L - wl.W
+    n_vl = O.n_vertical(wl.rho, n_nw)
+    base = rng.uniform(0.0, 1.0, size=(wl.B, wl.Hkv, wl.L)).astype(np.float32)
+    # n_vl - 100 positions clearly above, 400 tied at the cut, the rest below
+    perm = rng.permutation(n_nw)
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            base[b, g, perm[:n_vl - 100]] = 1.0e9 + 1.0e3
+            base[b, g, perm[n_vl - 100:n_vl + 300]] = 1.0e9
+            base[b, g, perm[n_vl + 300:]] = 1.0e6
+    s_in = torch.from_numpy(base).to("cuda")
+    score_g, idx_g, flag_g, n_vl2 = gpu_select(x, wl, score_in=s_in)
+    assert n_vl2 == n_vl
+    _own_topk_exact(wl, score_g, idx_g, flag_g, n_vl)
