@@ -9,9 +9,11 @@
 //
 // Work decomposition.  Grid = (splits, units).  A unit's work list is its
 // K4V4 slots in 32-token blocks followed by its FP16 sequence (vertical lines,
-// window slots, staging) in 32-token blocks; the unit's nsplit * 8 waves take
+// window slots, staging) in 32-token blocks; the unit's nsplit * 4 waves take
 // the items round-robin, so every wave gets the same number of blocks to
-// within one whatever the mix.  Each workgroup merges its eight waves'
+// within one whatever the mix.  Workgroups are four waves, so that two fit
+// on a CU at the register count of the scan and one's merge and ramp-up
+// overlap the other's streaming.  Each workgroup merges its four waves'
 // (max, sum, output) states through LDS into one partial record; the last
 // workgroup of the unit to arrive (an atomic counter in the workspace) merges
 // the unit's records by log-sum-exp and writes out/lse.
@@ -47,7 +49,7 @@ namespace hq {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
@@ -591,8 +593,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // the per-wave staging areas of the scan, the image of the waves' states
   // and the partials of the final merge share LDS (barriers separate them)
   __shared__ union {
-    K4Stage stage[kWaves];                         // 28 KB
-    WgImage img;                                   // 33 KB
+    K4Stage stage[kWaves];                         // 14 KB
+    WgImage img;                                   // 16.5 KB
     FinPart fin[kThreads];                         // 16 KB
   } s_lds;
   __shared__ int s_last;
@@ -822,7 +824,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < 8; ++i) ofin[i] = st.o[i];
   }
 
-  // Merge the eight waves' states and publish the workgroup's record.  The
+  // Merge the four waves' states and publish the workgroup's record.  The
   // waves write their states to LDS once; thread (head g, dims 4c..4c+3)
   // merges them and stores its part of the record with 16-byte device-scope
   // stores, at most eight heads per round.

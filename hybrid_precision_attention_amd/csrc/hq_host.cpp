@@ -19,12 +19,12 @@ namespace {
 
 constexpr int kMaxGroup = 16;      // query heads per KV head handled by one MFMA tile
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kDecodeWaves = 8;    // waves per decode workgroup
+constexpr int kDecodeWaves = 4;    // waves per decode workgroup (two workgroups per CU)
 constexpr int kBlk = 32;           // tokens per decode block
 constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most
 constexpr int kMaxSplit = 128;     // decode workgroups per unit, at most (LDS of the final merge)
 constexpr int kPartFloats = 132;   // m, l, 2 pad, o[128]
-constexpr double kWgBytes = 192.0 * 1024;  // bytes one decode workgroup streams at small batch
+constexpr double kWgBytes = 384.0 * 1024;  // bytes one decode workgroup streams at small batch
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
