@@ -166,9 +166,10 @@ using QStage = uint4[kRB][4][64];
 
 constexpr int kStageIters = kRG * 16 / kSThreads;   // 16-byte pieces per thread
 
-__device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t b, int h0, int rg) {
-  // all of the thread's loads are issued before any is stored
-  uint4 v[kStageIters];
+// In two halves, so that other loads can be in flight between them: all of
+// the thread's loads are issued before any is stored.
+__device__ __forceinline__ void stage_load(uint4 v[kStageIters], const SelArgs& a, int64_t b, int h0,
+                                           int rg) {
 #pragma unroll
   for (int i = 0; i < kStageIters; ++i) {
     const int idx = threadIdx.x + i * kSThreads;
@@ -177,12 +178,19 @@ __device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t
     const int g = r / a.nb, jq = r - g * a.nb;
     v[i] = ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
   }
+}
+__device__ __forceinline__ void stage_store(QStage& sq, const uint4 v[kStageIters]) {
 #pragma unroll
   for (int i = 0; i < kStageIters; ++i) {
     const int idx = threadIdx.x + i * kSThreads;
     const int rr = idx >> 4, ch = idx & 15;
     sq[rr >> 4][ch & 3][16 * (ch >> 2) + (rr & 15)] = v[i];
   }
+}
+__device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t b, int h0, int rg) {
+  uint4 v[kStageIters];
+  stage_load(v, a, b, h0, rg);
+  stage_store(sq, v);
 }
 
 __device__ __forceinline__ void load_q(half8_t qb[4], const QStage& sq, int rb, int lane) {
@@ -456,29 +464,31 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
   const int lim = a.n_nw;
   uint4 kr[4][4];
   load_keys(kr, kunit, wg0 + kChunk * wave, a.L, n, j);
-  stage_rows(s_q, a, b, h0, rg);
+  // keys, queries and the rows' statistics are all in flight before the first wait
+  uint4 qv[kStageIters];
+  stage_load(qv, a, b, h0, rg);
   if (a.lse_from_stats) {
     // merge each row's (max, sum exp2) over the pass-1 workgroups: thread
-    // pair (row, half) takes every other workgroup, eight loads in flight at
-    // a time, as running (max, sum) pairs; the halves then combine
+    // pair (row, half) takes every other workgroup, sixteen loads in flight
+    // at a time, as running (max, sum) pairs; the halves then combine
     static_assert(kSThreads == 2 * kRG, "two threads per row");
     const int rr = tid >> 1, half = tid & 1;
     const int r = rg * kRG + rr;
     const float2* st = a.stats + u * a.nwg1 * a.R + min(r, a.R - 1);
     float mx = -INFINITY, sum = 0.0f;
-    for (int t0 = half; t0 < a.nwg1; t0 += 16) {
-      float2 v[8];
+    for (int t0 = half; t0 < a.nwg1; t0 += 32) {
+      float2 v[16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 16; ++e)
         v[e] = st[static_cast<int64_t>(min(t0 + 2 * e, a.nwg1 - 1)) * a.R];
       float cm = mx;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 16; ++e)
         if (t0 + 2 * e < a.nwg1) cm = fmaxf(cm, v[e].x);
       if (cm != -INFINITY) {
         float s = sum * __builtin_amdgcn_exp2f((mx - cm) * a.c2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < 16; ++e)
           if (t0 + 2 * e < a.nwg1) s = fmaf(v[e].y, __builtin_amdgcn_exp2f((v[e].x - cm) * a.c2), s);
         sum = s;
         mx = cm;
@@ -501,6 +511,7 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
       s_nl[rr] = nl;
     }
   }
+  stage_store(s_q, qv);
   __syncthreads();
   float* sc = a.score + u * a.L;
   float* part = a.colpart + (static_cast<int64_t>(rg) * a.U + u) * a.n_nw;
@@ -730,7 +741,8 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       const int k0 = wg0 + kChunk * wave;
       if (k0 + kChunk <= h.nq) load_k4raw(raw, a, u, k0, n, j);
     }
-    stage_rows(s_q, a, b, h0, rg);
+    uint4 qv[kStageIters];
+    stage_load(qv, a, b, h0, rg);                          // in flight with the LSE loads
     for (int rr = tid; rr < kRG; rr += kSThreads) {
       const int r = rg * kRG + rr;
       float nl = -INFINITY;
@@ -743,6 +755,7 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       s_nl[rr] = nl;
       s_prow[rr] = pr;
     }
+    stage_store(s_q, qv);
     __syncthreads();
     for (int i = 0; i < a.C; ++i) {
       const int k0 = wg0 + kChunk * (wave + kSWaves * i);
@@ -800,8 +813,8 @@ struct TopShared {
   int hist[256];
   int red[2][kTopWaves];
   uint32_t sel[4];
-  uint32_t gt[kSegWords];                       // bit p: position seg + p above the threshold
-  uint32_t eq[kSegWords];                       // bit p: equal to it; then: taken
+  uint64_t gt[kSegWords / 2];                   // bit p: position seg + p above the threshold
+  uint64_t eq[kSegWords / 2];                   // bit p: equal to it; then: taken
   uint32_t list[kListMax];
 };
 static_assert(kSegWords == kTopThreads, "one bitmap word per thread");
@@ -1107,6 +1120,8 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   int base = 0;          // taken positions before the segment
   int eq_seen = 0;       // threshold-equal positions before the segment
   uint32_t tmin = 0xFFFFFFFFu;   // smallest taken key: the n_vl-th largest score
+  // flags may go out four to a store when the unit's flag row is 4-byte aligned
+  const bool flags4 = (reinterpret_cast<uintptr_t>(flag) & 3u) == 0;
   // segment 0 takes its keys from registers, later ones re-read them (the
   // first call is separate so that the register keys die with it)
   auto emit = [&](int seg, bool from_regs) {
@@ -1120,22 +1135,20 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         if (g) tmin = min(tmin, key);
         const uint64_t bg = __ballot(g), be = __ballot(e);
         if (lane == 0) {
-          // positions seg + 1024 k + 64 wave .. + 63 are words 32 k + 2 wave, + 1
-          const int w = 32 * k + 2 * wave;
-          sh.gt[w] = static_cast<uint32_t>(bg);
-          sh.gt[w + 1] = static_cast<uint32_t>(bg >> 32);
-          sh.eq[w] = static_cast<uint32_t>(be);
-          sh.eq[w + 1] = static_cast<uint32_t>(be >> 32);
+          // positions seg + 1024 k + 64 wave .. + 63 are 64-bit word 16 k + wave
+          sh.gt[16 * k + wave] = bg;
+          sh.eq[16 * k + wave] = be;
         }
-        __builtin_amdgcn_sched_barrier(0);   // one row at a time: no ballot results piling up
       }
-    } else {
+    } else if (tid < kSegWords / 2) {
       sh.gt[tid] = 0;
       sh.eq[tid] = 0;
     }
     __syncthreads();
-    const uint32_t e = sh.eq[tid];
-    uint32_t take = sh.gt[tid];
+    const uint32_t* gt32 = reinterpret_cast<const uint32_t*>(sh.gt);
+    uint32_t* eq32 = reinterpret_cast<uint32_t*>(sh.eq);
+    const uint32_t e = eq32[tid];
+    uint32_t take = gt32[tid];
     if (eq_all) {
       if (take_eq > 0) take |= e;        // all of them (a whole-bin cut takes none)
     } else {
@@ -1161,12 +1174,23 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       ++o;
     }
     base += tot_t;
-    sh.eq[tid] = take;                   // the taken bitmap, for the flags
+    eq32[tid] = take;                    // the taken bitmap, for the flags
     __syncthreads();
+    if (flags4 && seg + kSeg <= a.L) {
+      // four positions a store: flag word q = positions seg + 4q .. + 3
+#pragma unroll
+      for (int k = 0; k < kKeysPerThread / 4; ++k) {
+        const int q = tid + k * kTopThreads;
+        const uint32_t x = (eq32[q >> 3] >> (4 * (q & 7))) & 0xFu;
+        const uint32_t w = (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+        reinterpret_cast<uint32_t*>(flag + seg)[q] = w;
+      }
+    } else {
 #pragma unroll 4
-    for (int k = 0; k < kKeysPerThread; ++k) {
-      const int pl = tid + k * kTopThreads;
-      if (seg + pl < a.L) flag[seg + pl] = static_cast<uint8_t>((sh.eq[pl >> 5] >> (pl & 31)) & 1u);
+      for (int k = 0; k < kKeysPerThread; ++k) {
+        const int pl = tid + k * kTopThreads;
+        if (seg + pl < a.L) flag[seg + pl] = static_cast<uint8_t>((eq32[pl >> 5] >> (pl & 31)) & 1u);
+      }
     }
     __syncthreads();                     // before the next segment reuses the bitmaps
   };
