@@ -803,7 +803,7 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kKeysPerThread = 32;              // register-resident keys per thread
 constexpr int kSeg = kKeysPerThread * kTopThreads;
-constexpr int kSampleStride = 8;                // rows k = 0, 8, 16, 24 form the sample
+constexpr int kSampleStride = 16;               // rows k = 0 and 16 form the sample
 
 constexpr int kListMax = 4096;                  // keys of a confirmed bracket kept in LDS
 
