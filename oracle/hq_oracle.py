@@ -30,8 +30,11 @@ position; the K4V4 group layout is asymmetric uint4 over groups of 32
 consecutive head_dim elements of one token, fp16 {scale, min} per group,
 scale = fp16(range / 15), codes = round-half-even((x - min) / scale) clamped
 to [0, 15] (all codes 0 when the scale is 0), two codes per byte with the
-lower-index element in the low nibble; the decode token is not part of the
-window -- it sits in an FP16 staging slot and attends to itself.
+lower-index element in the low nibble; the other strict low-bit widths of
+the mode table (K8V8, K4V2, K2V4) use the same rule with 2^b - 1 steps and
+8/b codes per byte, lowest-index element in the lowest bits, K and V widths
+chosen independently; the decode token is not part of the window -- it sits
+in an FP16 staging slot and attends to itself.
 
 Parity unpinned: none of the functions below; every one has a pin in
 tests/test_oracle_*.py (closed forms, brute force, library routines).
@@ -45,6 +48,7 @@ import numpy as np
 
 GROUP = 32          # head_dim elements per quantisation group
 QMAX = 15           # largest 4-bit code
+KV_BITS = (2, 4, 8) # code widths of the strict low-bit caches [R Mode reference]
 NB_MAX = 64         # buffered queries for the column-mass estimate [D], [R Overhead]
 
 
@@ -144,26 +148,51 @@ def select_vertical_unit(K, qgrp, L, W, rho, score_in=None):
 # --------------------------------------------------------------------------
 # O4/O5: K4V4 quantisation and packing [R Overview item 3; H author comment]
 # --------------------------------------------------------------------------
-def quantize_groups(X: np.ndarray):
-    """Asymmetric 4-bit quantisation of tokens X [n][d] (fp16), one group per
-    32 consecutive head_dim elements.
+def quantize_groups(X: np.ndarray, bits: int = 4):
+    """Asymmetric b-bit quantisation of tokens X [n][d] (fp16), one group per
+    32 consecutive head_dim elements (b = 4 for K4V4; 2 and 8 for the other
+    strict low-bit caches of [R Mode reference], same rule with 2^b - 1
+    steps).
 
     min m and max M of the group; scale s = fp16(round-to-nearest-even of
-    (M - m) / 15); a zero minimum or a zero scale is stored as +0; code =
-    clamp(round-half-even((x - m) / s), 0, 15), all 0 when s == 0.  Every
-    step is exact in fp64 before its single rounding.
+    (M - m) / (2^b - 1)); a zero minimum or a zero scale is stored as +0;
+    code = clamp(round-half-even((x - m) / s), 0, 2^b - 1), all 0 when
+    s == 0.  Every step is exact in fp64 before its single rounding.
     Returns codes uint8 [n][d], scale fp16 [n][d/32], min fp16 [n][d/32].
     """
+    assert bits in KV_BITS
+    qmax = (1 << bits) - 1
     n, d = X.shape
     x = X.astype(np.float64).reshape(n, d // GROUP, GROUP)
     m = x.min(axis=2) + 0.0        # a zero minimum is stored as +0
     M = x.max(axis=2)
-    s16 = (((M - m) + 0.0) / QMAX).astype(np.float16)   # a zero range gives scale +0
+    s16 = (((M - m) + 0.0) / qmax).astype(np.float16)   # a zero range gives scale +0
     s = s16.astype(np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):
         q = np.rint((x - m[:, :, None]) / s[:, :, None])
-    q = np.where(s[:, :, None] > 0, np.clip(q, 0, QMAX), 0)
+    q = np.where(s[:, :, None] > 0, np.clip(q, 0, qmax), 0)
     return q.reshape(n, d).astype(np.uint8), s16, m.astype(np.float16)
+
+
+def pack_codes(codes: np.ndarray, bits: int = 4) -> np.ndarray:
+    """b-bit codes [n][d] into bytes [n][d*b/8]: 8/b codes per byte, the
+    lower-index element in the lower bits (element (8/b) j + r of byte j at
+    bits b r .. b r + b - 1)."""
+    per = 8 // bits
+    n, d = codes.shape
+    out = np.zeros((n, d // per), np.uint16)
+    for r in range(per):
+        out |= codes[:, r::per].astype(np.uint16) << (bits * r)
+    return out.astype(np.uint8)
+
+
+def unpack_codes(packed: np.ndarray, bits: int = 4) -> np.ndarray:
+    per = 8 // bits
+    n, h = packed.shape
+    out = np.empty((n, per * h), np.uint8)
+    for r in range(per):
+        out[:, r::per] = (packed >> (bits * r)) & ((1 << bits) - 1)
+    return out
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
@@ -184,26 +213,28 @@ def make_meta(scale: np.ndarray, mn: np.ndarray) -> np.ndarray:
     return np.stack([scale, mn], axis=-1).astype(np.float16)
 
 
-def dequantize(packed: np.ndarray, meta: np.ndarray) -> np.ndarray:
+def dequantize(packed: np.ndarray, meta: np.ndarray, bits: int = 4) -> np.ndarray:
     """x_hat = code * scale + min, in fp64: [n][d]."""
-    c = unpack_nibbles(packed).astype(np.float64)
+    c = unpack_codes(packed, bits).astype(np.float64)
     n, d = c.shape
     s = meta[:, :, 0].astype(np.float64)
     m = meta[:, :, 1].astype(np.float64)
     return (c.reshape(n, d // GROUP, GROUP) * s[:, :, None] + m[:, :, None]).reshape(n, d)
 
 
-def quantize_pack_tokens(X: np.ndarray):
-    codes, s, m = quantize_groups(X)
-    return pack_nibbles(codes), make_meta(s, m)
+def quantize_pack_tokens(X: np.ndarray, bits: int = 4):
+    codes, s, m = quantize_groups(X, bits)
+    return pack_codes(codes, bits), make_meta(s, m)
 
 
 # --------------------------------------------------------------------------
 # The hybrid cache of one (sequence, KV head) and its construction
 # --------------------------------------------------------------------------
-def empty_unit_cache(d: int, W: int) -> Dict:
+def empty_unit_cache(d: int, W: int, k_bits: int = 4, v_bits: int = 4) -> Dict:
+    """One unit's hybrid cache; the quantised region holds k_bits-bit keys
+    and v_bits-bit values (K4V4 by default)."""
     return {
-        "kq": np.zeros((0, d // 2), np.uint8), "vq": np.zeros((0, d // 2), np.uint8),
+        "kq": np.zeros((0, d * k_bits // 8), np.uint8), "vq": np.zeros((0, d * v_bits // 8), np.uint8),
         "kq_meta": np.zeros((0, d // GROUP, 2), np.float16),
         "vq_meta": np.zeros((0, d // GROUP, 2), np.float16),
         "q_pos": np.zeros(0, np.int32),
@@ -212,12 +243,12 @@ def empty_unit_cache(d: int, W: int) -> Dict:
         "kwin": np.zeros((W, d), np.float16), "vwin": np.zeros((W, d), np.float16),
         "kstg": np.zeros((0, d), np.float16), "vstg": np.zeros((0, d), np.float16),
         "stg_pos": np.zeros(0, np.int32),
-        "W": W, "d": d,
+        "W": W, "d": d, "k_bits": k_bits, "v_bits": v_bits,
     }
 
 
 def quant_pack_unit(K: np.ndarray, V: np.ndarray, L: int, W: int,
-                    vl_flag: np.ndarray) -> Dict:
+                    vl_flag: np.ndarray, k_bits: int = 4, v_bits: int = 4) -> Dict:
     """Build the hybrid cache of one unit after the prefill tail [D decode
     paragraph; R Overview item 3]: vertical-line tokens (flag set, non-window)
     keep FP16 K and V in ascending position; the window [L-W, L) goes to an
@@ -228,9 +259,9 @@ def quant_pack_unit(K: np.ndarray, V: np.ndarray, L: int, W: int,
     flag = np.asarray(vl_flag[:n_nw]).astype(bool)
     qpos = np.nonzero(~flag)[0].astype(np.int32)
     vpos = np.nonzero(flag)[0].astype(np.int32)
-    cache = empty_unit_cache(d, W)
-    cache["kq"], cache["kq_meta"] = quantize_pack_tokens(K[qpos])
-    cache["vq"], cache["vq_meta"] = quantize_pack_tokens(V[qpos])
+    cache = empty_unit_cache(d, W, k_bits, v_bits)
+    cache["kq"], cache["kq_meta"] = quantize_pack_tokens(K[qpos], k_bits)
+    cache["vq"], cache["vq_meta"] = quantize_pack_tokens(V[qpos], v_bits)
     cache["q_pos"] = qpos
     cache["kvl"], cache["vvl"], cache["vl_pos"] = K[vpos].copy(), V[vpos].copy(), vpos
     for p in win:
@@ -275,8 +306,8 @@ def _evict(cache, pos, k, v, to_vl):
         cache["vvl"] = np.concatenate([cache["vvl"], v[None]])
         cache["vl_pos"] = np.concatenate([cache["vl_pos"], np.array([pos], np.int32)])
     else:
-        kb, km = quantize_pack_tokens(k[None])
-        vb, vm = quantize_pack_tokens(v[None])
+        kb, km = quantize_pack_tokens(k[None], cache.get("k_bits", 4))
+        vb, vm = quantize_pack_tokens(v[None], cache.get("v_bits", 4))
         cache["kq"] = np.concatenate([cache["kq"], kb])
         cache["kq_meta"] = np.concatenate([cache["kq_meta"], km])
         cache["vq"] = np.concatenate([cache["vq"], vb])
@@ -294,8 +325,8 @@ def hybrid_regions(cache: Dict, L: int):
     [max(0, L-W), L)), staging.  Returns a list of (name, positions, K, V)."""
     W = cache["W"]
     out = [("k4", cache["q_pos"].astype(np.int64),
-            dequantize(cache["kq"], cache["kq_meta"]),
-            dequantize(cache["vq"], cache["vq_meta"])),
+            dequantize(cache["kq"], cache["kq_meta"], cache.get("k_bits", 4)),
+            dequantize(cache["vq"], cache["vq_meta"], cache.get("v_bits", 4))),
            ("vl", cache["vl_pos"].astype(np.int64),
             cache["kvl"].astype(np.float64), cache["vvl"].astype(np.float64))]
     if W > 0:
@@ -346,8 +377,8 @@ def decode_fused(cache: Dict, q: np.ndarray, L: int, tile: int = 256):
     n_q = cache["kq"].shape[0]
     for t0 in range(0, n_q, tile):
         sl = slice(t0, min(n_q, t0 + tile))
-        absorb(dequantize(cache["kq"][sl], cache["kq_meta"][sl]),
-               dequantize(cache["vq"][sl], cache["vq_meta"][sl]))
+        absorb(dequantize(cache["kq"][sl], cache["kq_meta"][sl], cache.get("k_bits", 4)),
+               dequantize(cache["vq"][sl], cache["vq_meta"][sl], cache.get("v_bits", 4)))
     for name, _, Kr, Vr in hybrid_regions(cache, L)[1:]:
         absorb(Kr, Vr)
     return acc / l[:, None], m + np.log(l)
@@ -372,10 +403,10 @@ def select_vertical(K, qbuf, L, W, rho, score_in=None):
     return score, idx, flags
 
 
-def quant_pack(K, V, L, W, vl_flag) -> List[List[Dict]]:
+def quant_pack(K, V, L, W, vl_flag, k_bits: int = 4, v_bits: int = 4) -> List[List[Dict]]:
     B, Hkv = K.shape[:2]
-    return [[quant_pack_unit(K[b, g], V[b, g], L, W, vl_flag[b, g]) for g in range(Hkv)]
-            for b in range(B)]
+    return [[quant_pack_unit(K[b, g], V[b, g], L, W, vl_flag[b, g], k_bits, v_bits)
+             for g in range(Hkv)] for b in range(B)]
 
 
 def append_merge(caches, t, k_new, v_new, evict_is_vl=None) -> None:
