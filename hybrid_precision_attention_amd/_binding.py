@@ -31,7 +31,7 @@ class hq_dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("W", ctypes.c_int32), ("rho", ctypes.c_double),
                 ("cap_q", ctypes.c_int32), ("cap_vl", ctypes.c_int32),
-                ("cap_stg", ctypes.c_int32)]
+                ("cap_stg", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32)]
 
 
 class hq_cache(ctypes.Structure):
@@ -78,8 +78,8 @@ def n_vertical(rho: float, n_nw: int) -> int:
     return int(math.floor(rho * n_nw + 1e-6)) if n_nw > 0 else 0
 
 
-def make_dims(B, Hq, Hkv, W, rho, cap_q=0, cap_vl=0, cap_stg=1, d=D) -> hq_dims:
-    return hq_dims(B, Hq, Hkv, d, W, float(rho), cap_q, cap_vl, cap_stg)
+def make_dims(B, Hq, Hkv, W, rho, cap_q=0, cap_vl=0, cap_stg=1, d=D, k_bits=4, v_bits=4) -> hq_dims:
+    return hq_dims(B, Hq, Hkv, d, W, float(rho), cap_q, cap_vl, cap_stg, k_bits, v_bits)
 
 
 def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
@@ -111,19 +111,20 @@ class HybridCache:
     t: dict
 
     @staticmethod
-    def allocate(B, Hq, Hkv, W, rho, L_max, extra_vl=0, cap_stg=1, device="cuda"):
+    def allocate(B, Hq, Hkv, W, rho, L_max, extra_vl=0, cap_stg=1, device="cuda", k_bits=4, v_bits=4):
         """Capacities for prefixes up to L_max tokens: every non-window
         position may be quantised; the vertical-line region holds the top-rho
-        set of L_max plus ``extra_vl`` promotions."""
+        set of L_max plus ``extra_vl`` promotions.  Quantised keys and values
+        use k_bits / v_bits codes (2, 4 or 8)."""
         n_nw = max(0, L_max - W)
         cap_q = max(1, n_nw)
         cap_vl = max(1, n_vertical(rho, n_nw) + extra_vl)
-        dims = make_dims(B, Hq, Hkv, W, rho, cap_q, cap_vl, max(1, cap_stg))
+        dims = make_dims(B, Hq, Hkv, W, rho, cap_q, cap_vl, max(1, cap_stg), k_bits=k_bits, v_bits=v_bits)
         dev = torch.device(device)
         u8, f16, i32 = torch.uint8, torch.float16, torch.int32
         t = {
-            "kq": torch.zeros((B, Hkv, cap_q, D // 2), dtype=u8, device=dev),
-            "vq": torch.zeros((B, Hkv, cap_q, D // 2), dtype=u8, device=dev),
+            "kq": torch.zeros((B, Hkv, cap_q, D * k_bits // 8), dtype=u8, device=dev),
+            "vq": torch.zeros((B, Hkv, cap_q, D * v_bits // 8), dtype=u8, device=dev),
             "kq_meta": torch.zeros((B, Hkv, cap_q, D // 32, 2), dtype=f16, device=dev),
             "vq_meta": torch.zeros((B, Hkv, cap_q, D // 32, 2), dtype=f16, device=dev),
             "q_pos": torch.zeros((B, Hkv, cap_q), dtype=i32, device=dev),

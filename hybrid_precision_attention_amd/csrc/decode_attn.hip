@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "hq_device.h"
 #include "hq_launch.h"
 
@@ -298,14 +300,11 @@ __device__ __forceinline__ void load_f16_k(uint4 kr[8], const F16Rows& f, int tb
   }
 }
 
-__device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], const F16Rows& f,
-                                            const uint4 kr[8], int tb, int n, int j, float c2) {
-  uint4 vr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = min(k4_token(tb, j, e), f.nf - 1);
-    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * n);
-  }
+// One block of fp16 K and V operands (kr: lane (t, j) holds dims 32j ..
+// 32j + 31 of tokens t and 16 + t; vr: dims 8n .. 8n + 7 of the lane's eight
+// tokens), tokens from `valid` on masked.
+__device__ __forceinline__ void f16_compute(SoftState& st, const half8_t qn[4], const uint4 kr[8],
+                                            const uint4 vr[8], int valid, int j, float c2) {
   float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -313,11 +312,11 @@ __device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], 
     sb = mfma(as_half8(kr[4 + kk]), qn[kk], sb);
   }
   float s[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-  if (tb + kBlk > f.nf) {
+  if (valid < kBlk) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (tb + 4 * j + e >= f.nf) s[e] = -INFINITY;
-      if (tb + 16 + 4 * j + e >= f.nf) s[4 + e] = -INFINITY;
+      if (4 * j + e >= valid) s[e] = -INFINITY;
+      if (16 + 4 * j + e >= valid) s[4 + e] = -INFINITY;
     }
   }
   const half8_t pb = softmax_block(st, s, c2);
@@ -333,6 +332,17 @@ __device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], 
     }
     st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pb, st.o[i]);
   }
+}
+
+__device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], const F16Rows& f,
+                                            const uint4 kr[8], int tb, int n, int j, float c2) {
+  uint4 vr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = min(k4_token(tb, j, e), f.nf - 1);
+    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * n);
+  }
+  f16_compute(st, qn, kr, vr, f.nf - tb, j, c2);
 }
 
 // ---------------------------------------------------------------------------
@@ -511,14 +521,8 @@ __device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Mas
 // One FP16 block in the grouped layout: the same columns (no bias, no
 // scale), P for even and 16 P for odd output dims, so that the FP16 and
 // K4V4 contributions share one accumulator under O = (o - corr) (1 or 1/16) + mt.
-__device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], const F16Rows& f,
-                                              const uint4 kr[8], int tb, int c, int j, float c2) {
-  uint4 vr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = min(k4_token(tb, j, e), f.nf - 1);
-    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * c);
-  }
+__device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], const uint4 kr[8],
+                                              const uint4 vr[8], int valid, int j, float c2) {
   float4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -528,11 +532,11 @@ __device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], c
   float s[8] = {da[0], da[1], da[2], da[3], db[0], db[1], db[2], db[3]};
 #pragma unroll
   for (int e = 0; e < 8; ++e) s[e] = quad_sum(s[e]);
-  if (tb + kBlk > f.nf) {
+  if (valid < kBlk) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (tb + 4 * j + e >= f.nf) s[e] = -INFINITY;
-      if (tb + 16 + 4 * j + e >= f.nf) s[4 + e] = -INFINITY;
+      if (4 * j + e >= valid) s[e] = -INFINITY;
+      if (16 + 4 * j + e >= valid) s[4 + e] = -INFINITY;
     }
   }
   float pr[8];
@@ -555,6 +559,100 @@ __device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], c
     }
     st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), (i & 1) ? p16x : p1, st.o[i]);
   }
+}
+
+__device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], const F16Rows& f,
+                                              const uint4 kr[8], int tb, int c, int j, float c2) {
+  uint4 vr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = min(k4_token(tb, j, e), f.nf - 1);
+    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * c);
+  }
+  f16_compute_g(st, qf, kr, vr, f.nf - tb, j, c2);
+}
+
+
+// ---------------------------------------------------------------------------
+// Other code widths (K8V8, K4V2, K2V4, ...: b-bit keys and values, 8/b codes
+// a byte).  A 32-token block of the quantised region is dequantised into a
+// per-wave LDS tile of fp16 rows, then attended exactly like an FP16 block.
+// Lane l owns half a row: token l / 2, elements 64 (l & 1) .. + 63 (two
+// groups), whose codes and {scale, min} words it loads with wide loads.
+// ---------------------------------------------------------------------------
+constexpr int kTileStride = kD + 8;               // halves a row: 16-byte reads spread over banks
+struct DqTile {
+  uint16_t k[kBlk][kTileStride];
+  uint16_t v[kBlk][kTileStride];
+};
+
+template <int kKB, int kVB>
+struct GenRaw {
+  uint4 k[kKB / 2];                 // 8 kKB code bytes of the lane's half row of K
+  uint4 v[kVB / 2];
+  uint2 km, vm;                     // {scale, min} of the half row's two groups
+};
+
+template <int kKB, int kVB>
+__device__ __forceinline__ void load_gen(GenRaw<kKB, kVB>& r, const uint8_t* kq, const uint32_t* kmeta,
+                                         const uint8_t* vq, const uint32_t* vmeta, int tb, int nq,
+                                         int lane) {
+  // rows past the unit's last token re-read it (masked below)
+  const uint32_t t = static_cast<uint32_t>(min(tb + (lane >> 1), nq - 1));
+  const uint32_t h = lane & 1;
+  const uint8_t* kp = kq + t * (16 * kKB) + h * (8 * kKB);
+  const uint8_t* vp = vq + t * (16 * kVB) + h * (8 * kVB);
+#pragma unroll
+  for (int i = 0; i < kKB / 2; ++i) r.k[i] = ld16(kp + 16 * i);
+#pragma unroll
+  for (int i = 0; i < kVB / 2; ++i) r.v[i] = ld16(vp + 16 * i);
+  r.km = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kmeta) + t * 16 + h * 8);
+  r.vm = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vmeta) + t * 16 + h * 8);
+}
+
+// 64 b-bit codes (element e at bits b e .. of the little-endian words w) of
+// two groups to 64 fp16 code * scale + min, each rounded once: a code goes
+// under the exponent of 1024 (exactly 1024 + code, codes < 1024), 1024 is
+// taken off, then one fused multiply-add.
+template <int kB>
+__device__ __forceinline__ void dq_half_row(uint16_t* dst, const uint32_t* w, uint2 meta) {
+  constexpr uint32_t kMask = (1u << kB) - 1u;
+  const half2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const half2_t sm = as_half2(g ? meta.y : meta.x);
+    const half2_t s2 = {sm[0], sm[0]}, m2 = {sm[1], sm[1]};
+    uint32_t o[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e = 32 * g + 2 * p;
+      const uint32_t c0 = (w[(kB * e) >> 5] >> ((kB * e) & 31)) & kMask;
+      const uint32_t c1 = (w[(kB * (e + 1)) >> 5] >> ((kB * (e + 1)) & 31)) & kMask;
+      const half2_t c = as_half2(c0 | (c1 << 16) | 0x64006400u) - k1024;
+      o[p] = as_u32(__builtin_elementwise_fma(c, s2, m2));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      st16(dst + 32 * g + 8 * q, make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]));
+  }
+}
+
+// The block's K and V as fp16 operands of the FP16-block code.
+template <int kKB, int kVB>
+__device__ __forceinline__ void gen_operands(uint4 kr[8], uint4 vr[8], const GenRaw<kKB, kVB>& r,
+                                             DqTile& tl, int lane, int n, int j) {
+  wave_sync();                                     // the previous block's reads are done
+  const int t = lane >> 1, h = lane & 1;
+  dq_half_row<kKB>(&tl.k[t][64 * h], reinterpret_cast<const uint32_t*>(r.k), r.km);
+  dq_half_row<kVB>(&tl.v[t][64 * h], reinterpret_cast<const uint32_t*>(r.v), r.vm);
+  wave_sync();
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    kr[kk] = ld16(&tl.k[n][32 * j + 8 * kk]);
+    kr[4 + kk] = ld16(&tl.k[16 + n][32 * j + 8 * kk]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vr[e] = ld16(&tl.v[k4_token(0, j, e)][8 * n]);
 }
 
 // LDS image of the waves' states for up to eight heads at a time:
@@ -588,14 +686,18 @@ __device__ __forceinline__ void st4_agent(float* p, float4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
-template <bool kG4>
+template <bool kG4, int kKB, int kVB>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  // K4V4 takes the grouped-code paths; other widths dequantise each block
+  // into an LDS tile and use the FP16-block code
+  constexpr bool kK4V4 = kKB == 4 && kVB == 4;
+  using Stage = std::conditional_t<kK4V4, K4Stage, DqTile>;
   // the per-wave staging areas of the scan, the image of the waves' states
   // and the partials of the final merge share LDS (barriers separate them)
   __shared__ union {
-    K4Stage stage[kWaves];                         // 14 KB
+    Stage stage[kWaves];                           // 14 KB (K4V4), 68 KB (tiles)
     WgImage img;                                   // 16.5 KB
-    FinPart fin[kThreads];                         // 16 KB
+    FinPart fin[kThreads];                         // 8 KB
   } s_lds;
   __shared__ int s_last;
 
@@ -667,25 +769,41 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int nq = min(a.c.n_q[u], a.cap_q);
     const int nblk_q = (nq + kBlk - 1) / kBlk;
     if (gw < nblk_q) {
-      const uint8_t* kq = a.c.kq + u * a.cap_q * kRowBytes;
-      const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
+      const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
+      const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
       const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
       const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
-      K4Stage& sg = s_lds.stage[wave];
-      const Masks km = make_masks();
       const int last = nblk_q - 1;
-      K4Raw ra, rb;
-      K4Mid x;
       int blk = gw;
-      load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
-      for (; blk < nblk_q; blk += 2 * nwaves) {
-        load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
-        k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
-        k4_phase_b(st, x, km, c2);
-        if (blk + nwaves >= nblk_q) break;
-        load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
-        k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + nwaves) * kBlk, nq, lane, n, j);
-        k4_phase_b(st, x, km, c2);
+      if constexpr (kK4V4) {
+        K4Stage& sg = s_lds.stage[wave];
+        const Masks km = make_masks();
+        K4Raw ra, rb;
+        K4Mid x;
+        load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+        for (; blk < nblk_q; blk += 2 * nwaves) {
+          load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+          k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
+          k4_phase_b(st, x, km, c2);
+          if (blk + nwaves >= nblk_q) break;
+          load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+          k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + nwaves) * kBlk, nq, lane, n, j);
+          k4_phase_b(st, x, km, c2);
+        }
+      } else {
+        DqTile& tl = s_lds.stage[wave];
+        GenRaw<kKB, kVB> ra, rb;
+        load_gen(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane);
+        for (; blk < nblk_q; blk += 2 * nwaves) {
+          uint4 kr[8], vr[8];
+          load_gen(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane);
+          gen_operands(kr, vr, ra, tl, lane, n, j);
+          f16_compute_g(st, qf, kr, vr, nq - blk * kBlk, j, c2);
+          if (blk + nwaves >= nblk_q) break;
+          load_gen(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane);
+          gen_operands(kr, vr, rb, tl, lane, n, j);
+          f16_compute_g(st, qf, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
+        }
       }
     }
     {
@@ -755,31 +873,50 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int nq = min(a.c.n_q[u], a.cap_q);
     const int nblk_q = (nq + kBlk - 1) / kBlk;
     if (gw < nblk_q) {
-      half8_t qb[4];
-  #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const half8_t nat = as_half8(qraw[kk]);
-        qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
-      }
-      const uint8_t* kq = a.c.kq + u * a.cap_q * kRowBytes;
-      const uint8_t* vq = a.c.vq + u * a.cap_q * kRowBytes;
+      const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
+      const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
       const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
       const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
       // one block of prefetch in two alternating buffers (no register copies);
       // the loads are unconditional (past the end they re-read the last block)
       // so that the wait before a compute only covers its own loads
-      K4Stage& sg = s_lds.stage[wave];
-      const Masks km = make_masks();
       const int last = nblk_q - 1;
-      K4Raw ra, rb;
       int blk = gw;
-      load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
-      for (; blk < nblk_q; blk += 2 * nwaves) {
-        load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
-        compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
-        if (blk + nwaves >= nblk_q) break;
-        load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
-        compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
+      if constexpr (kK4V4) {
+        half8_t qb[4];
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8_t nat = as_half8(qraw[kk]);
+          qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
+        }
+        K4Stage& sg = s_lds.stage[wave];
+        const Masks km = make_masks();
+        K4Raw ra, rb;
+        load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+        for (; blk < nblk_q; blk += 2 * nwaves) {
+          load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+          compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
+          if (blk + nwaves >= nblk_q) break;
+          load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+          compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
+        }
+      } else {
+        half8_t qn[4];
+  #pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
+        DqTile& tl = s_lds.stage[wave];
+        GenRaw<kKB, kVB> ra, rb;
+        load_gen(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane);
+        for (; blk < nblk_q; blk += 2 * nwaves) {
+          uint4 kr[8], vr[8];
+          load_gen(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane);
+          gen_operands(kr, vr, ra, tl, lane, n, j);
+          f16_compute(st, qn, kr, vr, nq - blk * kBlk, j, c2);
+          if (blk + nwaves >= nblk_q) break;
+          load_gen(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane);
+          gen_operands(kr, vr, rb, tl, lane, n, j);
+          f16_compute(st, qn, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
+        }
       }
     }
     {
@@ -981,10 +1118,23 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
   (void)L;
   dim3 grid(plan.nsplit, d.B * d.Hkv);
-  if (a.G <= 4)
-    hipLaunchKernelGGL(decode_kernel<true>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<false>, grid, dim3(kThreads), 0, s, a);
+  const int kb = kv_bits(d.k_bits), vb = kv_bits(d.v_bits);
+  auto launch = [&](auto g4, auto kbc, auto vbc) {
+    hipLaunchKernelGGL((decode_kernel<decltype(g4)::value, decltype(kbc)::value, decltype(vbc)::value>),
+                       grid, dim3(kThreads), 0, s, a);
+  };
+  auto by_v = [&](auto g4, auto kbc) {
+    if (vb == 2) launch(g4, kbc, std::integral_constant<int, 2>{});
+    else if (vb == 8) launch(g4, kbc, std::integral_constant<int, 8>{});
+    else launch(g4, kbc, std::integral_constant<int, 4>{});
+  };
+  auto by_k = [&](auto g4) {
+    if (kb == 2) by_v(g4, std::integral_constant<int, 2>{});
+    else if (kb == 8) by_v(g4, std::integral_constant<int, 8>{});
+    else by_v(g4, std::integral_constant<int, 4>{});
+  };
+  if (a.G <= 4) by_k(std::true_type{});
+  else by_k(std::false_type{});
   return hipGetLastError();
 }
 

@@ -1,12 +1,15 @@
 // Device-side helpers shared by the gfx950 kernels of libhq.
 //
-// The K4V4 group rule (per token, per 32 consecutive head_dim elements):
-// min m, max M, scale s = fp16_rne((M - m) / 15), code = clamp(rne((x - m)/s),
-// 0, 15), all codes 0 when s == 0; two codes per byte, lower element in the
-// low nibble.  The decision is taken in fp64: x - m and M - m are exact there
-// (fp16 differences need at most 41 significant bits), and the single
-// correctly-rounded fp64 division cannot move a quotient across a half-integer
-// boundary, so the codes equal the exact-arithmetic definition.
+// The group rule (per token, per 32 consecutive head_dim elements), for
+// b-bit codes (b = 4 for K4V4; 2 and 8 for the other strict low-bit caches):
+// min m, max M, scale s = fp16_rne((M - m) / (2^b - 1)), code =
+// clamp(rne((x - m)/s), 0, 2^b - 1), all codes 0 when s == 0; 8/b codes per
+// byte, the lower element in the lower bits.  The decision is taken in fp64:
+// x - m and M - m are exact there (fp16 differences need at most 41
+// significant bits), and the single correctly-rounded fp64 division cannot
+// move a quotient across a half-integer boundary or an fp16 rounding
+// midpoint (the divisors are at most 255), so the codes equal the
+// exact-arithmetic definition.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,7 +19,9 @@ namespace hq {
 
 constexpr int kD = 128;        // head_dim
 constexpr int kGroup = 32;     // elements per quantisation group
-constexpr int kRowBytes = kD / 2;        // packed code bytes per token
+constexpr int kRowBytes = kD / 2;        // packed 4-bit code bytes per token
+template <int kBits>
+constexpr int row_bytes() { return kD * kBits / 8; }   // packed b-bit code bytes per token
 constexpr int kMetaWords = kD / kGroup;  // {scale, min} words per token
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -39,10 +44,13 @@ __device__ __forceinline__ uint16_t d2h_rne_nonneg(double x) {
 }
 
 // Quantise one group of 32 fp16 values held as 16 dwords (two per dword,
-// element 2i in the low half).  Returns the 16 code bytes in codes[4] and
+// element 2i in the low half) to b-bit codes.  Returns the 4 b code bytes in
+// codes[kBits] (element e at bits b e .. of the little-endian group) and
 // {scale, min} packed as scale | min << 16 in *meta.
-__device__ __forceinline__ void quant_group32(const uint32_t in[16], uint32_t codes[4],
+template <int kBits = 4>
+__device__ __forceinline__ void quant_group32(const uint32_t in[16], uint32_t codes[kBits],
                                               uint32_t* meta) {
+  constexpr int kQmax = (1 << kBits) - 1;
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -52,13 +60,13 @@ __device__ __forceinline__ void quant_group32(const uint32_t in[16], uint32_t co
     mx = fmaxf(mx, fmaxf(a, b));
   }
   const double m = static_cast<double>(mn) + 0.0;    // canonical +0 for a zero min
-  const uint16_t s_bits = d2h_rne_nonneg((static_cast<double>(mx) - m) / 15.0);
+  const uint16_t s_bits = d2h_rne_nonneg((static_cast<double>(mx) - m) / static_cast<double>(kQmax));
   const double s = static_cast<double>(h2f(s_bits));
   const _Float16 m_h = static_cast<_Float16>(static_cast<float>(m));
   *meta = static_cast<uint32_t>(s_bits) |
           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, m_h)) << 16);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) codes[w] = 0;
+  for (int w = 0; w < kBits; ++w) codes[w] = 0;
   if (s_bits == 0) return;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -66,11 +74,35 @@ __device__ __forceinline__ void quant_group32(const uint32_t in[16], uint32_t co
     for (int h = 0; h < 2; ++h) {
       const double x = static_cast<double>(h2f(static_cast<uint16_t>(in[i] >> (16 * h))));
       double c = rint((x - m) / s);
-      c = c < 0.0 ? 0.0 : (c > 15.0 ? 15.0 : c);
+      c = c < 0.0 ? 0.0 : (c > static_cast<double>(kQmax) ? static_cast<double>(kQmax) : c);
       const int e = 2 * i + h;                 // element index in the group
-      codes[e >> 3] |= static_cast<uint32_t>(c) << (4 * (e & 7));
+      codes[(kBits * e) >> 5] |= static_cast<uint32_t>(c) << ((kBits * e) & 31);
     }
   }
+}
+
+// Quantise one group and store its codes (4 b bytes at `dst`, 8-byte
+// aligned) and {scale, min} word.
+template <int kBits>
+__device__ __forceinline__ void quant_store_group(const uint32_t in[16], uint8_t* dst, uint32_t* meta_dst) {
+  uint32_t codes[kBits], meta;
+  quant_group32<kBits>(in, codes, &meta);
+  if constexpr (kBits == 2) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(codes[0], codes[1]);
+  } else {
+#pragma unroll
+    for (int w = 0; w < kBits; w += 4)
+      *reinterpret_cast<uint4*>(dst + 4 * w) = make_uint4(codes[w], codes[w + 1], codes[w + 2], codes[w + 3]);
+  }
+  *meta_dst = meta;
+}
+
+// Width chosen at run time (K and V may differ): 2, 4 or 8 bits.
+__device__ __forceinline__ void quant_store_group_bits(int bits, const uint32_t in[16], uint8_t* dst,
+                                                       uint32_t* meta_dst) {
+  if (bits == 2) quant_store_group<2>(in, dst, meta_dst);
+  else if (bits == 8) quant_store_group<8>(in, dst, meta_dst);
+  else quant_store_group<4>(in, dst, meta_dst);
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) {

@@ -34,6 +34,8 @@ int check_dims(const hq_dims* d) {
   if (d->W < 0 || d->cap_q < 0 || d->cap_vl < 0 || d->cap_stg < 0) return HQ_ERR_ARG;
   if (!(d->rho >= 0.0 && d->rho <= 1.0)) return HQ_ERR_ARG;
   if (d->d != 128) return HQ_ERR_UNSUPPORTED;
+  for (const int32_t b : {d->k_bits, d->v_bits})
+    if (b != 0 && b != 2 && b != 4 && b != 8) return HQ_ERR_UNSUPPORTED;
   if (d->Hq / d->Hkv > kMaxGroup) return HQ_ERR_UNSUPPORTED;
   // keep every flat index comfortably inside int64 and every per-unit row
   // count inside int32
@@ -65,7 +67,7 @@ int32_t n_vertical(double rho, int32_t n_nw) {
 }
 
 // Splits per unit for the decode: workgroups carry about equal bytes (160 per
-// K4V4 token, 512 per FP16 token).  Small problems get one workgroup per CU;
+// K4V4 token, 16 (k_bits + v_bits) + 32 at other widths, 512 per FP16 token).  Small problems get one workgroup per CU;
 // large ones up to eight per CU so that uneven finishing times average out.
 static int64_t max_splits(int64_t units) {
   return std::min<int64_t>(kMaxSplit, cdiv(kMaxWG, units) + 3);
@@ -82,7 +84,8 @@ DecodePlan plan_decode(const hq_dims& d, int32_t L) {
   const int64_t n_q = std::max<int32_t>(0, n_nw - n_vl);
   const int32_t n_win = std::min(d.W, L);
   const int64_t n_f = static_cast<int64_t>(n_vl) + n_win + d.cap_stg;
-  const double per_unit = 160.0 * static_cast<double>(n_q) + 512.0 * static_cast<double>(n_f);
+  const double q_tok = 16.0 * (kv_bits(d.k_bits) + kv_bits(d.v_bits)) + 32.0;
+  const double per_unit = q_tok * static_cast<double>(n_q) + 512.0 * static_cast<double>(n_f);
   const double total = static_cast<double>(units) * per_unit;
   const double per_cu = std::min(8.0, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
   const double wg_bytes = std::max(total / (kCUs * per_cu), 1.0);
@@ -116,13 +119,13 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 2; }
+int hq_abi_version(void) { return 3; }
 
 const char* hq_status_string(int status) {
   switch (status) {
     case HQ_OK: return "ok";
     case HQ_ERR_ARG: return "invalid argument (null pointer, shape or range)";
-    case HQ_ERR_UNSUPPORTED: return "unsupported shape (head_dim must be 128, Hq/Hkv <= 16)";
+    case HQ_ERR_UNSUPPORTED: return "unsupported shape (head_dim 128, Hq/Hkv <= 16, code widths 2/4/8)";
     case HQ_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case HQ_ERR_CAPACITY: return "cache region capacity too small";
     case HQ_ERR_WORKSPACE: return "workspace missing or too small";

@@ -49,6 +49,9 @@ hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32
                                       const float* score, int32_t score_ld, const float* cut,
                                       hipStream_t s);
 
+// Code width of a quantised region: 0 (unset) means 4.
+inline int kv_bits(int32_t b) { return b == 0 ? 4 : b; }
+
 // floor(rho * n_nw + 1e-6): size of the vertical-line set of n_nw candidates.
 int32_t n_vertical(double rho, int32_t n_nw);
 

@@ -24,6 +24,7 @@ struct PackArgs {
   const uint8_t* flag;
   hq_cache c;
   int32_t L, W, cap_q, cap_vl;
+  int32_t k_bits, v_bits;           // code widths of the quantised region
 };
 
 __device__ __forceinline__ int wave_sum(int x) {
@@ -112,12 +113,10 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
       x[4 * i + 0] = w4.x; x[4 * i + 1] = w4.y; x[4 * i + 2] = w4.z; x[4 * i + 3] = w4.w;
     }
     if (knd == 1) {
-      uint32_t codes[4], meta;
-      quant_group32(x, codes, &meta);
-      uint8_t* dst = (kv ? a.c.vq : a.c.kq) + (u * a.cap_q + sl) * kRowBytes + g * 16;
-      st16(dst, make_uint4(codes[0], codes[1], codes[2], codes[3]));
+      const int bits = kv ? a.v_bits : a.k_bits;
+      uint8_t* dst = (kv ? a.c.vq : a.c.kq) + (u * a.cap_q + sl) * (kD * bits / 8) + g * (4 * bits);
       uint32_t* md = reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta);
-      md[(u * a.cap_q + sl) * kMetaWords + g] = meta;
+      quant_store_group_bits(bits, x, dst, &md[(u * a.cap_q + sl) * kMetaWords + g]);
     } else {
       uint16_t* dst;
       if (knd == 2) dst = (kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + sl) * kD + g * kGroup;
@@ -131,6 +130,7 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
 
 struct MergeArgs {
   hq_cache c;
+  int32_t k_bits, v_bits;
   const uint16_t* k_new;
   const uint16_t* v_new;
   const uint8_t* evict_is_vl;
@@ -192,14 +192,14 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
         __syncthreads();
         if (lane < 8) {
           const int qkv = lane >> 2, g = lane & 3;
-          uint32_t x[16], codes[4], meta;
+          const int bits = qkv ? a.v_bits : a.k_bits;
+          uint32_t x[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[i] = s_row[qkv][16 * g + i];
-          quant_group32(x, codes, &meta);
-          st16((qkv ? a.c.vq : a.c.kq) + (u * a.cap_q + nq) * kRowBytes + g * 16,
-               make_uint4(codes[0], codes[1], codes[2], codes[3]));
-          reinterpret_cast<uint32_t*>(qkv ? a.c.vq_meta : a.c.kq_meta)
-              [(u * a.cap_q + nq) * kMetaWords + g] = meta;
+          quant_store_group_bits(bits, x,
+                                 (qkv ? a.c.vq : a.c.kq) + (u * a.cap_q + nq) * (kD * bits / 8) + g * (4 * bits),
+                                 &reinterpret_cast<uint32_t*>(qkv ? a.c.vq_meta : a.c.kq_meta)
+                                     [(u * a.cap_q + nq) * kMetaWords + g]);
         }
         if (lane == 0) {
           a.c.q_pos[u * a.cap_q + nq] = ev;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
 
 hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t* v, int32_t L,
                              const uint8_t* vl_flag, const hq_cache& c, hipStream_t s) {
-  PackArgs a{k, v, vl_flag, c, L, d.W, d.cap_q, d.cap_vl};
+  PackArgs a{k, v, vl_flag, c, L, d.W, d.cap_q, d.cap_vl, kv_bits(d.k_bits), kv_bits(d.v_bits)};
   const int chunks = L > 0 ? (L + kChunk - 1) / kChunk : 1;
   dim3 grid(chunks, d.B * d.Hkv);
   hipLaunchKernelGGL(quant_pack_kernel, grid, dim3(kPackThreads), 0, s, a);
@@ -227,7 +227,8 @@ hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t
 hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
                                const uint16_t* k_new, const uint16_t* v_new,
                                const uint8_t* evict_is_vl, hipStream_t s) {
-  MergeArgs a{c, k_new, v_new, evict_is_vl, nullptr, nullptr, 0, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+  MergeArgs a{c, kv_bits(d.k_bits), kv_bits(d.v_bits), k_new, v_new, evict_is_vl, nullptr, nullptr, 0,
+              t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
   hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }
@@ -236,7 +237,8 @@ hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32
                                       const uint16_t* k_new, const uint16_t* v_new,
                                       const float* score, int32_t score_ld, const float* cut,
                                       hipStream_t s) {
-  MergeArgs a{c, k_new, v_new, nullptr, score, cut, score_ld, t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+  MergeArgs a{c, kv_bits(d.k_bits), kv_bits(d.v_bits), k_new, v_new, nullptr, score, cut, score_ld,
+              t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
   hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }

@@ -576,17 +576,39 @@ constexpr int kNoPos = 0x7FFFFFFF;   // list entries past the last key
 
 // K4V4 entries k0 + 16x + n (all of them below nq) for lane (n, j): the
 // group-j codes, {scale, min} and position of each.
-struct K4Raw {
-  uint4 codes[4];
+// (kKB-bit key codes: group j of a token is 4 kKB bytes at byte 4 kKB j of
+// its 16 kKB-byte row.)
+template <int kKB>
+struct KRaw {
+  uint32_t codes[4][kKB];
   uint32_t meta[4];
   int pos[4];
 };
 
-__device__ __forceinline__ void load_k4raw(K4Raw& r, const SelArgs& a, int64_t u, int k0, int n, int j) {
+template <int kKB>
+__device__ __forceinline__ void load_group_codes(uint32_t w[kKB], const uint8_t* p) {
+  if constexpr (kKB == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kKB; i += 4) {
+      const uint4 v = ld16(p + 4 * i);
+      w[i] = v.x;
+      w[i + 1] = v.y;
+      w[i + 2] = v.z;
+      w[i + 3] = v.w;
+    }
+  }
+}
+
+template <int kKB>
+__device__ __forceinline__ void load_k4raw(KRaw<kKB>& r, const SelArgs& a, int64_t u, int k0, int n, int j) {
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int64_t sl = u * a.cap_q + k0 + 16 * x + n;
-    r.codes[x] = ld16(a.c.kq + sl * kRowBytes + 16 * j);
+    load_group_codes<kKB>(r.codes[x], a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
     r.meta[x] = reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j];
     r.pos[x] = a.c.q_pos[sl];
   }
@@ -611,19 +633,38 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t m2) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-__device__ __forceinline__ void dequant_group(uint4 out[4], uint4 codes, uint32_t meta) {
+template <int kKB>
+__device__ __forceinline__ void dequant_group(uint4 out[4], const uint32_t w[kKB], uint32_t meta) {
   const half2_t sm = __builtin_bit_cast(half2_t, meta);
   const half2_t s2 = {sm[0], sm[0]}, m2 = {sm[1], sm[1]};
-  out[0] = dequant8(codes.x, s2, m2);
-  out[1] = dequant8(codes.y, s2, m2);
-  out[2] = dequant8(codes.z, s2, m2);
-  out[3] = dequant8(codes.w, s2, m2);
+  if constexpr (kKB == 4) {
+    out[0] = dequant8(w[0], s2, m2);
+    out[1] = dequant8(w[1], s2, m2);
+    out[2] = dequant8(w[2], s2, m2);
+    out[3] = dequant8(w[3], s2, m2);
+  } else {
+    // element e at bits kKB e of the group, in pairs under the exponent of 1024
+    constexpr uint32_t kMask = (1u << kKB) - 1u;
+    const half2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+    uint32_t o[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int e = 2 * p;
+      const uint32_t c0 = (w[(kKB * e) >> 5] >> ((kKB * e) & 31)) & kMask;
+      const uint32_t c1 = (w[(kKB * (e + 1)) >> 5] >> ((kKB * (e + 1)) & 31)) & kMask;
+      const half2_t c = __builtin_bit_cast(half2_t, c0 | (c1 << 16) | 0x64006400u) - k1024;
+      o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, m2));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
 }
 
 // fp16 operands of any 64 list entries, lane (n, j) holding dims
 // 32j .. 32j + 31 of entry k0 + 16x + n in kr[x] (zeros past the list) and its
 // position in pos[x] (kNoPos past the list).  Used for the few chunks that
 // are not all K4V4, so the loads are simply issued in order.
+template <int kKB>
 __device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelArgs& a,
                                          const HybridList& h, int64_t u, int k0, int n, int j) {
 #pragma unroll
@@ -631,8 +672,9 @@ __device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelAr
     const int ki = k0 + 16 * x + n;
     if (ki < h.nq) {
       const int64_t sl = u * a.cap_q + ki;
-      dequant_group(kr[x], ld16(a.c.kq + sl * kRowBytes + 16 * j),
-                    reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j]);
+      uint32_t w[kKB];
+      load_group_codes<kKB>(w, a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
+      dequant_group<kKB>(kr[x], w, reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j]);
       pos[x] = a.c.q_pos[sl];
     } else {
       int e = ki - h.nq;
@@ -709,6 +751,7 @@ __device__ __forceinline__ void chunk_refresh(float acc[16], const uint4 kr[4][4
 // K4V4 codes are in flight (the other chunks, a few per unit, load in place).
 // Row groups (G * nb > 256) run one after another inside the workgroup, each
 // adding its mass to the score entries it owns.
+template <int kKB>
 __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
   __shared__ QStage s_q;                                    // 64 KB
   __shared__ float s_nl[kRG];                               // -lse * log2(e), -inf for padding
@@ -736,7 +779,7 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       __syncthreads();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    K4Raw raw;
+    KRaw<kKB> raw;
     {
       const int k0 = wg0 + kChunk * wave;
       if (k0 + kChunk <= h.nq) load_k4raw(raw, a, u, k0, n, j);
@@ -765,11 +808,11 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       if (k0 + kChunk <= h.nq) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          dequant_group(kr[x], raw.codes[x], raw.meta[x]);
+          dequant_group<kKB>(kr[x], raw.codes[x], raw.meta[x]);
           kpos[x] = raw.pos[x];
         }
       } else {
-        load_any(kr, kpos, a, h, u, k0, n, j);
+        load_any<kKB>(kr, kpos, a, h, u, k0, n, j);
       }
       // positions through LDS: lane (n, j) needs those of entries 16x + 4j + e
 #pragma unroll
@@ -1310,7 +1353,10 @@ hipError_t launch_refresh(const hq_dims& d, const hq_cache& c, int32_t t, const 
   a.wg_keys = kChunk * kSWaves * a.C;
   const unsigned nwg = static_cast<unsigned>((nk + a.wg_keys - 1) / a.wg_keys);
   const unsigned U = static_cast<unsigned>(units);
-  hipLaunchKernelGGL(refresh_mass_kernel, dim3(nwg, U), dim3(kSThreads), 0, s, a);
+  const int kb = kv_bits(d.k_bits);
+  if (kb == 2) hipLaunchKernelGGL(refresh_mass_kernel<2>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
+  else if (kb == 8) hipLaunchKernelGGL(refresh_mass_kernel<8>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
+  else hipLaunchKernelGGL(refresh_mass_kernel<4>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
   a.nrg = 1;                       // the scores are complete: nothing to fold
   hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();

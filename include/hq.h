@@ -23,7 +23,9 @@
  * with an fp16 {scale, min}: scale = fp16_rne((max - min) / 15), code =
  * clamp(round_half_even((x - min) / scale), 0, 15) (all 0 when scale == 0),
  * x_hat = code * scale + min.  Byte j of a packed row holds element 2j in the
- * low nibble and element 2j+1 in the high nibble.
+ * low nibble and element 2j+1 in the high nibble.  b-bit codes (b = 2, 8)
+ * follow the same rule with 2^b - 1 in place of 15, 8/b codes per byte, the
+ * lower element in the lower bits.
  *
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
@@ -53,24 +55,31 @@ extern "C" {
 
 #define HQ_OK               0
 #define HQ_ERR_ARG         -1   /* null pointer, bad shape or out-of-range scalar */
-#define HQ_ERR_UNSUPPORTED -2   /* head_dim other than 128 */
+#define HQ_ERR_UNSUPPORTED -2   /* head_dim other than 128, or a code width other than 2/4/8 */
 #define HQ_ERR_ALIGN       -3   /* a tensor pointer not 16-byte aligned */
 #define HQ_ERR_CAPACITY    -4   /* a cache region too small for the request */
 #define HQ_ERR_WORKSPACE   -5   /* workspace missing or smaller than required */
 #define HQ_ERR_HIP         -6   /* a HIP launch or runtime call failed */
 
 /* Problem shape: batch, query/KV heads, head_dim, window W, vertical-line
- * ratio rho in [0, 1], and the capacities (tokens per unit) of the K4V4,
- * vertical-line and staging regions of a cache. */
+ * ratio rho in [0, 1], the capacities (tokens per unit) of the quantised,
+ * vertical-line and staging regions of a cache, and the code widths of the
+ * quantised keys and values: 2, 4 or 8 bits each (0 means 4).  K4V4 is the
+ * method's cache; K8V8, K4V2 and K2V4 are the other strict low-bit caches of
+ * the README's mode table, with or without vertical lines.  A caller with
+ * per-layer value widths passes each layer's dims. */
 typedef struct {
   int32_t B, Hq, Hkv, d;
   int32_t W;
   double rho;
   int32_t cap_q, cap_vl, cap_stg;
+  int32_t k_bits, v_bits;
 } hq_dims;
 
 /* One layer's hybrid cache.  u = b * Hkv + kv_head indexes the units.
- *   kq, vq        [B][Hkv][cap_q][d/2]     packed 4-bit K and V codes
+ *   kq, vq        [B][Hkv][cap_q][d*k_bits/8], [..][d*v_bits/8]
+ *                                          packed K and V codes (d/2 bytes
+ *                                          a token at 4 bits)
  *   kq_meta,      [B][Hkv][cap_q][d/32][2] fp16 {scale, min} per group
  *   vq_meta
  *   q_pos         [B][Hkv][cap_q]          source position of each K4V4 slot;

@@ -16,12 +16,12 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def gpu_pack(x, L, W, rho, flags, L_max=None, extra_vl=0):
+def gpu_pack(x, L, W, rho, flags, L_max=None, extra_vl=0, k_bits=4, v_bits=4):
     """Pack the prefix with the HIP kernel; returns the HybridCache."""
     B, Hkv = x["K"].shape[:2]
     Hq = x["qbuf"].shape[1]
     cache = H.HybridCache.allocate(B, Hq, Hkv, W, rho, L_max if L_max is not None else L,
-                                   extra_vl=extra_vl)
+                                   extra_vl=extra_vl, k_bits=k_bits, v_bits=v_bits)
     K = dev(x["K"][:, :, :L]) if L else None
     V = dev(x["V"][:, :, :L]) if L else None
     F = dev(flags[:, :, :L]) if L else None
@@ -35,7 +35,7 @@ def unit_from_gpu(cache, b, g):
     t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()}
     n_q, n_vl, n_stg = int(t["n_q"]), int(t["n_vl"]), int(t["n_stg"])
     W = cache.dims.W
-    c = O.empty_unit_cache(128, W)
+    c = O.empty_unit_cache(128, W, cache.dims.k_bits, cache.dims.v_bits)
     c["kq"], c["vq"] = t["kq"][:n_q], t["vq"][:n_q]
     c["kq_meta"], c["vq_meta"] = t["kq_meta"][:n_q], t["vq_meta"][:n_q]
     c["q_pos"] = t["q_pos"][:n_q]

@@ -32,7 +32,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 2
+    assert H.lib.hq_abi_version() == 3
 
 
 def _fake_cache(W=128, base=1 << 20):
