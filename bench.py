@@ -323,11 +323,12 @@ def main():
         cpu = cpu_baseline(wl, base, H, torch)
 
     # ---- the metric's batch sweep and the measured read ceiling -----------
-    sweep, ceiling = None, None
+    sweep, ceiling, widths = None, None, None
     if not args.no_sweep:
         del caches, ws, K_rep, base, spare
         torch.cuda.empty_cache()
         sweep = decode_sweep(H, torch, workload)
+        widths = width_sweep(H, torch, workload)
         ceiling = read_ceiling(torch, 4 << 30)
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
 
@@ -352,6 +353,7 @@ def main():
         "select_util": sel_util,
         "decode_time_refresh": refresh,
         "b_sweep": sweep,
+        "kv_width_sweep": widths,
         "read_ceiling": ceiling,
         "replicas": R, "input_gen_s": round(gen_s, 1),
     }
@@ -436,9 +438,19 @@ def decode_sweep(H, torch, workload, Bs=(1, 4, 16, 32)):
     L = 32768, W = 128, rho = 5 %): decode launches only, caches built on the
     device from bf16-rounded N(0,1) keys and values (timing inputs; parity is
     covered by the tests), each then holding one staged token as in a step."""
-    res = []
+    return [decode_point(H, torch, workload, B) for B in Bs]
+
+
+def width_sweep(H, torch, workload, points=((1, 8, 8), (1, 4, 2), (1, 2, 4), (32, 8, 8), (32, 4, 2), (32, 2, 4))):
+    """Decode of the other strict low-bit caches (K8V8, K4V2, K2V4, with
+    vertical lines and window) on the same layer: µs and GB/s of each width's
+    own algorithmic bytes (16 (k_bits + v_bits) + 32 per quantised token)."""
+    return [decode_point(H, torch, workload, B, kb, vb) for B, kb, vb in points]
+
+
+def decode_point(H, torch, workload, B, kb=4, vb=4):
     d = 128
-    for B in Bs:
+    if True:
         wl = workload("qwen3_8b", B=B)
         Hq, Hkv, L, W, rho = wl.Hq, wl.Hkv, wl.L, wl.W, wl.rho
         U = B * Hkv
@@ -453,21 +465,24 @@ def decode_sweep(H, torch, workload, Bs=(1, 4, 16, 32)):
         idx = torch.zeros((B, Hkv, n_vl), dtype=torch.int32, device="cuda")
         flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device="cuda")
         H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, H.workspace(dims_s, H.HQ_OP_SELECT, L))
-        base = H.HybridCache.allocate(B, Hq, Hkv, W, rho, L + 8)
+        base = H.HybridCache.allocate(B, Hq, Hkv, W, rho, L + 8, k_bits=kb, v_bits=vb)
         H.hq_quant_pack(base.dims, K, V, L, flag, base)
         H.hq_append_merge(base.dims, base, L, K[:, :, 0].contiguous(), V[:, :, 0].contiguous())
         del K, V, qb, score, idx, flag
-        footprint = U * (160 * (n_nw - n_vl) + 512 * (n_vl + W + 1))
+        q_tok = 16 * (kb + vb) + 32
+        footprint = U * (q_tok * (n_nw - n_vl) + 512 * (n_vl + W + 1))
         R = max(1, math.ceil((1 << 30) / footprint))
         caches = [base] + [base.clone() for _ in range(R - 1)]
         wss = [H.workspace(base.dims, H.HQ_OP_DECODE, L + 8) for _ in range(R)]
         q = torch.randn((B, Hq, d), generator=g, device="cuda").half()
         out = torch.empty_like(q)
         us = graph_decode_us(H, torch, base.dims, caches, wss, L + 1, q, out, max(2 * R, 32))
-        nbytes = U * (160 * (n_nw - n_vl) + 512 * (n_vl + W + 1)) + B * Hq * d * 4
+        nbytes = U * (q_tok * (n_nw - n_vl) + 512 * (n_vl + W + 1)) + B * Hq * d * 4
         gbs = nbytes / (us * 1e-6) / 1e9
-        res.append({"B": B, "decode_us": round(us, 2), "GBs": round(gbs, 1),
-                    "frac": round(gbs / PEAK_GBS, 4), "bytes": nbytes, "replicas": R})
+        res = {"B": B, "decode_us": round(us, 2), "GBs": round(gbs, 1),
+               "frac": round(gbs / PEAK_GBS, 4), "bytes": nbytes, "replicas": R}
+        if (kb, vb) != (4, 4):
+            res["kv_bits"] = f"K{kb}V{vb}"
         del caches, wss, base
         torch.cuda.empty_cache()
     return res

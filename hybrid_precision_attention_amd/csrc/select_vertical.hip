@@ -990,7 +990,7 @@ __device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
 // by a radix select over order-preserving integer keys, then flags and
 // ascending indices, ties at the threshold taken from the lowest positions.
 // Thread t holds the keys of positions t + 1024 k (k < 32) in registers.
-// Before the radix passes, a 1/8 sample brackets the cut-off; one exact count
+// Before the radix passes, a 1/16 sample brackets the cut-off; one exact count
 // checks the bracket (else the full range is used), so the passes then see
 // a few hundred keys instead of all of them.
 __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
