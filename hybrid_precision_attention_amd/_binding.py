@@ -53,13 +53,18 @@ lib.hq_refresh_hybrid.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cac
                                   _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p]
 lib.hq_append_merge_scored.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache),
                                        ctypes.c_int32, _p, _p, _p, ctypes.c_int32, _p, _p]
+lib.hq_append_merge_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), _p,
+                                       ctypes.c_int32, _p, _p, _p, _p]
+lib.hq_decode_attn_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), _p,
+                                      ctypes.c_int32, _p, _p, _p, _p, ctypes.c_size_t, _p]
 lib.hq_workspace_bytes.argtypes = [ctypes.POINTER(hq_dims), ctypes.c_int, ctypes.c_int32]
 lib.hq_workspace_bytes.restype = ctypes.c_size_t
 lib.hq_status_string.argtypes = [ctypes.c_int]
 lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
-           "hq_refresh_hybrid", "hq_append_merge_scored"):
+           "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
+           "hq_decode_attn_ragged"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -150,6 +155,16 @@ class HybridCache:
             self._struct = cs
         return cs
 
+    def view(self, b: int) -> "HybridCache":
+        """Sequence b alone, as a B = 1 cache over the same memory (for
+        building the caches of a ragged batch one sequence at a time)."""
+        d = hq_dims.from_buffer_copy(self.dims)
+        d.B = 1
+        return HybridCache(d, {k: (v[b:b + 1] if v is not None else None) for k, v in self.t.items()})
+
+    def nbytes(self) -> int:
+        return sum(v.numel() * v.element_size() for v in self.t.values() if v is not None)
+
     def clone(self) -> "HybridCache":
         return HybridCache(hq_dims.from_buffer_copy(self.dims),
                            {k: (v.clone() if v is not None else None) for k, v in self.t.items()})
@@ -223,6 +238,27 @@ def hq_append_merge_scored(dims, cache: HybridCache, t, k_new, v_new, score, cut
                                     _ptr(score, torch.float32, "score"), score.shape[-1],
                                     _ptr(cut, torch.float32, "cut"), _stream(stream))
     _check(st, "hq_append_merge_scored")
+
+
+def hq_append_merge_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new, evict_is_vl=None,
+                           stream=None):
+    """t_seq: [B] int32 device tensor of per-sequence positions (<= t_max)."""
+    cs = cache.struct()
+    st = lib.hq_append_merge_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(t_seq, torch.int32, "t_seq"),
+                                    t_max, _ptr(k_new, torch.float16, "k_new"),
+                                    _ptr(v_new, torch.float16, "v_new"),
+                                    _ptr(evict_is_vl, torch.uint8, "evict_is_vl"), _stream(stream))
+    _check(st, "hq_append_merge_ragged")
+
+
+def hq_decode_attn_ragged(dims, cache: HybridCache, L_seq, L_max, q, out, ws, lse=None, stream=None):
+    """L_seq: [B] int32 device tensor of per-sequence query positions (<= L_max)."""
+    cs = cache.struct()
+    st = lib.hq_decode_attn_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(L_seq, torch.int32, "L_seq"),
+                                   L_max, _ptr(q, torch.float16, "q"), _ptr(out, torch.float16, "out"),
+                                   _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "hq_decode_attn_ragged")
 
 
 # --------------------------------------------------------------------------

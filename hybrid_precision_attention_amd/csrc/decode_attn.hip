@@ -66,11 +66,21 @@ struct DecodeArgs {
   int32_t* counters;
   int32_t Hq, Hkv, G, W, cap_q, cap_vl, cap_stg;
   int32_t n_win;
+  const int32_t* L_seq;             // [B] per-sequence query positions (ragged batch), or null
+  int32_t L_max;
   int32_t nsplit;                   // workgroups per unit
   float c2;                         // log2(e) / sqrt(d)
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+
+// Valid window slots of sequence b: min(W, L) at its own position L in a
+// ragged batch (clamped to [0, L_max]), else the batch's common count.
+__device__ __forceinline__ int unit_n_win(const DecodeArgs& a, int64_t b) {
+  if (!a.L_seq) return a.n_win;
+  const int L = min(max(a.L_seq[b], 0), a.L_max);
+  return min(a.W, L);
+}
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -809,7 +819,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     {
       const int nvl = min(a.c.n_vl[u], a.cap_vl);
       const int nst = min(a.c.n_stg[u], a.cap_stg);
-      const int nwin = a.n_win;
+      const int nwin = unit_n_win(a, b);
       const int nf = nvl + nwin + nst;
       const int nblk_f = (nf + kBlk - 1) / kBlk;
       const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
@@ -922,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     {
       const int nvl = min(a.c.n_vl[u], a.cap_vl);
       const int nst = min(a.c.n_stg[u], a.cap_stg);
-      const int nwin = a.n_win;
+      const int nwin = unit_n_win(a, b);
       const int nf = nvl + nwin + nst;
       const int nblk_f = (nf + kBlk - 1) / kBlk;
       // this wave's first item past the K4 blocks
@@ -1098,8 +1108,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const DecodePlan& plan,
-                         const uint16_t* q, uint16_t* out, float* lse, void* ws, hipStream_t s) {
+                         const uint16_t* q, uint16_t* out, float* lse, void* ws, hipStream_t s,
+                         const int32_t* L_seq) {
   DecodeArgs a;
+  a.L_seq = L_seq;
+  a.L_max = L;
   a.c = c;
   a.q = q;
   a.out = out;

@@ -51,8 +51,13 @@ int check_cache(const hq_dims& d, const hq_cache* c) {
   for (const void* p : must)
     if (!p) return HQ_ERR_ARG;
   if (d.W > 0 && (!c->kwin || !c->vwin)) return HQ_ERR_ARG;
-  for (const void* p : must)
+  // rows are read with 16-byte loads; positions and counters one int32 at a time
+  const void* rows[] = {c->kq, c->vq, c->kq_meta, c->vq_meta, c->kvl, c->vvl, c->kstg, c->vstg};
+  for (const void* p : rows)
     if (!aligned16(p)) return HQ_ERR_ALIGN;
+  const void* words[] = {c->q_pos, c->vl_pos, c->n_q, c->n_vl, c->n_stg};
+  for (const void* p : words)
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return HQ_ERR_ALIGN;
   if (d.W > 0 && (!aligned16(c->kwin) || !aligned16(c->vwin))) return HQ_ERR_ALIGN;
   return HQ_OK;
 }
@@ -119,7 +124,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 3; }
+int hq_abi_version(void) { return 4; }
 
 const char* hq_status_string(int status) {
   switch (status) {
@@ -243,6 +248,40 @@ int hq_append_merge_scored(const hq_dims* dims, const hq_cache* cache, int32_t t
   if (dims->cap_q < std::max(0, t - dims->W)) return HQ_ERR_CAPACITY;
   if (launch_append_merge_scored(*dims, *cache, t, k_new, v_new, score, score_ld, cut, stream) !=
       hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_append_merge_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* t_seq,
+                           int32_t t_max, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint8_t* evict_is_vl_or_null, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t_max < 0 || !t_seq || !k_new || !v_new) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(t_seq) || !aligned16(k_new) || !aligned16(v_new)) return HQ_ERR_ALIGN;
+  if (evict_is_vl_or_null && !aligned16(evict_is_vl_or_null)) return HQ_ERR_ALIGN;
+  if (dims->cap_stg < 1) return HQ_ERR_CAPACITY;
+  if (dims->cap_q < std::max(0, t_max - dims->W)) return HQ_ERR_CAPACITY;
+  if (launch_append_merge(*dims, *cache, t_max, k_new, v_new, evict_is_vl_or_null, stream, t_seq) !=
+      hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* L_seq,
+                          int32_t L_max, const uint16_t* q, uint16_t* out, float* lse_or_null,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L_max < 0 || !L_seq || !q || !out) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(L_seq) || !aligned16(q) || !aligned16(out)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  if (!ws || ws_bytes < decode_ws_bytes(*dims, L_max)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  const DecodePlan plan = plan_decode(*dims, L_max);
+  if (launch_decode(*dims, *cache, L_max, plan, q, out, lse_or_null, ws, stream, L_seq) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }

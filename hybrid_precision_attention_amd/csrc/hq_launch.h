@@ -29,11 +29,12 @@ hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t
 
 hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
                                const uint16_t* k_new, const uint16_t* v_new,
-                               const uint8_t* evict_is_vl, hipStream_t s);
+                               const uint8_t* evict_is_vl, hipStream_t s,
+                               const int32_t* t_seq = nullptr);
 
 hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L,
                          const DecodePlan& plan, const uint16_t* q, uint16_t* out,
-                         float* lse, void* ws, hipStream_t s);
+                         float* lse, void* ws, hipStream_t s, const int32_t* L_seq = nullptr);
 
 hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb,
                          const uint16_t* k, int32_t L, const float* lse_in,

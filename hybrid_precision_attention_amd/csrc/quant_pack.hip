@@ -140,6 +140,8 @@ struct MergeArgs {
   const float* cut;                 // [U]
   int32_t score_ld;
   int32_t t, W, cap_q, cap_vl, cap_stg;
+  const int32_t* t_seq;             // [B] per-sequence positions (ragged batch), or null
+  int32_t Hkv;
 };
 
 // One wave per unit.  Lanes 0-15 carry the K row, lanes 16-31 the V row, 16
@@ -152,7 +154,10 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
   const int64_t u = blockIdx.x;
   const bool mover = lane < 32;
   const int kv = (lane >> 4) & 1, part = lane & 15;
-  const int W = a.W, t = a.t;
+  const int W = a.W;
+  // the new token's position: its sequence's own in a ragged batch (clamped
+  // to [0, t_max]), else the batch's common one
+  const int t = a.t_seq ? min(max(a.t_seq[u / a.Hkv], 0), a.t) : a.t;
   // Every address is known from the arguments, so all loads are issued
   // before any is used: the counters, the staged row, the ring slot the
   // staged token goes to (its old token is the evictee) and the new token.
@@ -226,9 +231,9 @@ hipError_t launch_quant_pack(const hq_dims& d, const uint16_t* k, const uint16_t
 
 hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
                                const uint16_t* k_new, const uint16_t* v_new,
-                               const uint8_t* evict_is_vl, hipStream_t s) {
+                               const uint8_t* evict_is_vl, hipStream_t s, const int32_t* t_seq) {
   MergeArgs a{c, kv_bits(d.k_bits), kv_bits(d.v_bits), k_new, v_new, evict_is_vl, nullptr, nullptr, 0,
-              t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+              t, d.W, d.cap_q, d.cap_vl, d.cap_stg, t_seq, d.Hkv};
   hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }
@@ -238,7 +243,7 @@ hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32
                                       const float* score, int32_t score_ld, const float* cut,
                                       hipStream_t s) {
   MergeArgs a{c, kv_bits(d.k_bits), kv_bits(d.v_bits), k_new, v_new, nullptr, score, cut, score_ld,
-              t, d.W, d.cap_q, d.cap_vl, d.cap_stg};
+              t, d.W, d.cap_q, d.cap_vl, d.cap_stg, nullptr, d.Hkv};
   hipLaunchKernelGGL(append_merge_kernel, dim3(d.B * d.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }

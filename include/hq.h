@@ -29,7 +29,10 @@
  *
  * Conventions shared by every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major,
- *     16-byte aligned (HQ_ERR_ALIGN otherwise).  fp16 data is passed as the
+ *     16-byte aligned (HQ_ERR_ALIGN otherwise), except the cache's int32
+ *     position arrays and counters (q_pos, vl_pos, n_q, n_vl, n_stg), which
+ *     need 4 bytes, so that one sequence's slice of a batch cache is a
+ *     valid B = 1 cache.  fp16 data is passed as the
  *     raw uint16_t bit patterns.  The library allocates nothing and keeps no
  *     state between calls.
  *   - Calls are asynchronous on `stream`.  All argument checks run on the host
@@ -244,6 +247,29 @@ int hq_append_merge_scored(const hq_dims* dims, const hq_cache* cache, int32_t t
                            const uint16_t* k_new, const uint16_t* v_new,
                            const float* score, int32_t score_ld, const float* cut,
                            hipStream_t stream);
+
+/*
+ * hq_append_merge_ragged, hq_decode_attn_ragged -- the per-step operations
+ * of a ragged batch, each sequence at its own position (a serving batch of
+ * sequences of different lengths; the 32K-prefix batch-capacity runs of the
+ * agihunt digest, results paragraph, and the HyQuant README, Highlights).
+ *
+ *   t_seq / L_seq  [B] int32 DEVICE array: sequence b's new token / query
+ *                  position; values are clamped to [0, t_max] / [0, L_max]
+ *   t_max / L_max  host bound on every sequence's position: the capacity
+ *                  checks and the decode's split plan use it
+ * Otherwise exactly hq_append_merge / hq_decode_attn (the decode's workspace
+ * is hq_workspace_bytes(dims, HQ_OP_DECODE, L_max)).  Sequences shorter than
+ * their cache's capacity simply use fewer slots; to build the cache of a
+ * ragged batch, hq_quant_pack (and hq_select_vertical) run per sequence on
+ * B = 1 views of the cache (pointers advanced by b * Hkv units).
+ */
+int hq_append_merge_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* t_seq,
+                           int32_t t_max, const uint16_t* k_new, const uint16_t* v_new,
+                           const uint8_t* evict_is_vl_or_null, hipStream_t stream);
+int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* L_seq,
+                          int32_t L_max, const uint16_t* q, uint16_t* out, float* lse_or_null,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes an operation needs for any prefix length up to L_max;
  * 0 for an invalid request. */

@@ -32,7 +32,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 3
+    assert H.lib.hq_abi_version() == 4
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -83,6 +83,9 @@ def test_pack_validation():
     assert _pack(d, cache=c) == -1
     c = _fake_cache()
     c.kq_meta = (1 << 20) + 8
+    assert _pack(d, cache=c) == -3
+    c = _fake_cache()
+    c.q_pos = (1 << 20) + 2                             # positions need 4 bytes
     assert _pack(d, cache=c) == -3
     assert _pack(_dims(W=128), cache=_fake_cache(W=0)) == -1   # W > 0 needs a ring
 
