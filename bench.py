@@ -52,6 +52,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--decode-only", action="store_true",
                    help="time only hq_decode_attn launches (profiling runs)")
+    p.add_argument("--no-capacity", action="store_true",
+                   help="skip the whole-model capacity run (36 layers at the largest 32K batch)")
+    p.add_argument("--capacity-only", action="store_true",
+                   help="print only the capacity run's JSON object")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the decode batch sweep and the streaming-read ceiling")
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -119,6 +123,10 @@ def main():
 
     import hybrid_precision_attention_amd as H
     from hq_inputs import workload, batch
+
+    if args.capacity_only:
+        print(json.dumps({"capacity": capacity_run(H, torch)}))
+        return
 
     over = {}
     if args.B is not None:
@@ -331,6 +339,11 @@ def main():
         widths = width_sweep(H, torch, workload)
         ceiling = read_ceiling(torch, 4 << 30)
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
+    capacity = None
+    if not args.no_capacity:
+        if args.no_sweep:
+            del caches, ws, K_rep, base, spare
+        capacity = capacity_run(H, torch)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -355,6 +368,7 @@ def main():
         "b_sweep": sweep,
         "kv_width_sweep": widths,
         "read_ceiling": ceiling,
+        "capacity": capacity,
         "replicas": R, "input_gen_s": round(gen_s, 1),
     }
     if ceiling:
@@ -485,6 +499,124 @@ def decode_point(H, torch, workload, B, kb=4, vb=4):
             res["kv_bits"] = f"K{kb}V{vb}"
         del caches, wss, base
         torch.cuda.empty_cache()
+    return res
+
+
+def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n_var=4):
+    """Attention of a whole Qwen3-8B-shaped model (36 layers, 32/8 heads) at
+    the largest batch of 32K-token prefixes whose hybrid caches fit this GPU
+    beside the model's 16-bit weights and a reserve.  The weights are not
+    allocated (only the attention path runs).  Each layer's cache is built by
+    hq_select_vertical + hq_quant_pack one sequence at a time, from n_var
+    independent bf16-rounded N(0,1) prefixes.  A token step is
+    hq_append_merge + hq_decode_attn in every layer for the whole batch; K
+    steps are captured in one graph and replayed once between HIP events, and
+    a graph of one step's decodes gives the decode share."""
+    from hybrid_precision_attention_amd.model_cache import QWEN3_8B as shape, ModelCache, plan_capacity
+    d, Hq, Hkv = shape.d, shape.Hq, shape.Hkv
+    torch.cuda.empty_cache()
+    free, total = torch.cuda.mem_get_info()
+    L_max = L + steps + 1
+    plan = plan_capacity(shape, L_max, W, rho, total, reserve_bytes=reserve)
+    per_seq = plan["hybrid_bytes_per_seq"]
+    B = int(min(plan["max_batch_hybrid"], (free - (6 << 30)) // per_seq))
+    res = {"model": f"{shape.name} attention, {shape.layers} layers", "L": L, "W": W, "rho": rho,
+           "hbm_bytes": total, "weights_bytes_set_aside": shape.weight_bytes, "reserve_bytes": reserve,
+           "hybrid_bytes_per_seq": per_seq, "fp16_bytes_per_seq": plan["fp16_bytes_per_seq"],
+           "max_batch_hybrid": plan["max_batch_hybrid"], "max_batch_fp16": plan["max_batch_fp16"]}
+    if B < 1:
+        res["skipped"] = "no room for one sequence"
+        return res
+    t0 = time.time()
+    g = torch.Generator(device="cuda").manual_seed(77)
+    dims1 = H.make_dims(1, Hq, Hkv, W, rho)
+    n_nw = L - W
+    n_vl = H.n_vertical(rho, n_nw)
+    ws_sel = H.workspace(dims1, H.HQ_OP_SELECT, L)
+    variants = []
+    for _ in range(n_var):
+        K = torch.randn((1, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+        V = torch.randn((1, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+        qb = torch.randn((1, Hq, 64, d), generator=g, device="cuda").half()
+        score = torch.zeros((1, Hkv, L), device="cuda")
+        idx = torch.zeros((1, Hkv, n_vl), dtype=torch.int32, device="cuda")
+        flag = torch.zeros((1, Hkv, L), dtype=torch.uint8, device="cuda")
+        H.hq_select_vertical(dims1, qb, K, L, score, idx, flag, ws_sel)
+        variants.append((K, V, flag))
+    mc = ModelCache(shape, B, L_max, W, rho)
+    for l, c in enumerate(mc.layers):
+        for b in range(B):
+            K, V, flag = variants[(l + b) % n_var]
+            v = c.view(b)
+            H.hq_quant_pack(v.dims, K, V, L, flag, v)
+    torch.cuda.synchronize()
+    del variants, ws_sel
+    build_s = time.time() - t0
+
+    k_new = [torch.randn((B, Hkv, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    v_new = [torch.randn((B, Hkv, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    q = [torch.randn((B, Hq, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device="cuda")
+    ws = H.workspace(mc[0].dims, H.HQ_OP_DECODE, L_max)
+
+    def binds(stream):
+        dec = [H.bind_decode(c.dims, c, q[l], out, ws, stream=stream) for l, c in enumerate(mc.layers)]
+        mrg = [H.bind_merge(c.dims, c, stream=stream) for c in mc.layers]
+        return dec, mrg
+
+    dec, _ = binds(torch.cuda.current_stream())
+    for f in dec:                   # warm-up: one decode per layer over the packed prefix
+        f(L)
+    torch.cuda.synchronize()
+
+    def capture(body):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            body(torch.cuda.current_stream())
+        graph_upload(gr, torch)
+        return gr
+
+    def token_steps(stream):
+        dec_s, mrg_s = binds(stream)
+        for s in range(steps):
+            for l in range(shape.layers):
+                mrg_s[l](L + s, k_new[l].data_ptr(), v_new[l].data_ptr())
+                dec_s[l](L + s)
+
+    def decode_step(stream):
+        dec_s, _ = binds(stream)
+        for l in range(shape.layers):
+            dec_s[l](L + steps - 1)
+
+    g_steps = capture(token_steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g_steps.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    g_dec = capture(decode_step)
+    g_dec.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    g_dec.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1)
+    U = B * Hkv
+    n_q = n_nw - n_vl + steps
+    dec_bytes = shape.layers * (U * (160 * n_q + 512 * (n_vl + W + 1)) + B * Hq * d * 4)
+    res.update({"batch": B, "cache_bytes": mc.nbytes(), "build_s": round(build_s, 1), "steps": steps,
+                "token_step_ms": round(step_ms, 3), "decode_ms": round(dec_ms, 3),
+                "merge_ms": round(step_ms - dec_ms, 3),
+                "attn_tokens_per_s": round(B / (step_ms * 1e-3), 1),
+                "decode_bytes": dec_bytes,
+                "decode_GBs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+                "timing": "K token steps (merge + decode in every layer) as one graph, replayed once"})
+    del g_steps, g_dec, mc, ws, k_new, v_new, q, out
+    torch.cuda.empty_cache()
     return res
 
 
