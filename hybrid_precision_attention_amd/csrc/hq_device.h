@@ -105,6 +105,53 @@ __device__ __forceinline__ void quant_store_group_bits(int bits, const uint32_t 
   else quant_store_group<4>(in, dst, meta_dst);
 }
 
+// The same rule for a group spread over the four lanes of a lane quad, 8
+// values each (quad lane i holds elements 8i .. 8i+7 of the group, two per
+// dword, the lower element in the low half).  The min and max are reduced
+// across the quad, so every lane of the wave must make the call.  Returns
+// this lane's 8 codes in the low 8 b bits (element 8i + j at bit b j), and
+// the group's {scale, min} word in *meta.
+__device__ __forceinline__ uint64_t quant_quad8(const uint4 v, int bits, uint32_t* meta) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+    const float b = h2f(static_cast<uint16_t>(w[i] >> 16));
+    mn = fminf(mn, fminf(a, b));
+    mx = fmaxf(mx, fmaxf(a, b));
+  }
+  mn = fminf(mn, __shfl_xor(mn, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mn = fminf(mn, __shfl_xor(mn, 2));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  const double qmax = static_cast<double>((1 << bits) - 1);
+  const double m = static_cast<double>(mn) + 0.0;    // canonical +0 for a zero min
+  const uint16_t s_bits = d2h_rne_nonneg((static_cast<double>(mx) - m) / qmax);
+  const double s = static_cast<double>(h2f(s_bits));
+  const _Float16 m_h = static_cast<_Float16>(static_cast<float>(m));
+  *meta = static_cast<uint32_t>(s_bits) |
+          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, m_h)) << 16);
+  uint64_t codes = 0;
+  if (s_bits == 0) return codes;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const double x = static_cast<double>(h2f(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)))));
+    double c = rint((x - m) / s);
+    c = c < 0.0 ? 0.0 : (c > qmax ? qmax : c);
+    codes |= static_cast<uint64_t>(c) << (bits * j);
+  }
+  return codes;
+}
+
+// Store a lane's 8 b-bit codes (b bytes) at `dst`, b-byte aligned.
+__device__ __forceinline__ void store_codes8(uint8_t* dst, uint64_t codes, int bits) {
+  if (bits == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(codes);
+  else if (bits == 8) *reinterpret_cast<uint2*>(dst) =
+      make_uint2(static_cast<uint32_t>(codes), static_cast<uint32_t>(codes >> 32));
+  else *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(codes);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

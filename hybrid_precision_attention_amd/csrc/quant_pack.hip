@@ -146,10 +146,8 @@ struct MergeArgs {
 
 // One wave per unit.  Lanes 0-15 carry the K row, lanes 16-31 the V row, 16
 // bytes each.  The token leaving the window is either copied to the
-// vertical-line region or quantised by eight lanes (K/V x four groups) after
-// a pass through LDS.
+// vertical-line region or quantised in place, four lanes per group.
 __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
-  __shared__ uint32_t s_row[2][kD / 2];
   const int lane = threadIdx.x;
   const int64_t u = blockIdx.x;
   const bool mover = lane < 32;
@@ -188,23 +186,17 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
           a.c.n_vl[u] = nvl + 1;
         }
       } else if (nq < a.cap_q) {
+        // the row is already spread 8 values per lane, so a group is the
+        // four lanes of a quad: K groups in lanes 0-15, V groups in 16-31
+        // (lanes 32-63 quantise zeros and store nothing)
+        const int bits = kv ? a.v_bits : a.k_bits;
+        uint32_t meta;
+        const uint64_t codes = quant_quad8(evv, bits, &meta);
         if (mover) {
-          s_row[kv][4 * part + 0] = evv.x;
-          s_row[kv][4 * part + 1] = evv.y;
-          s_row[kv][4 * part + 2] = evv.z;
-          s_row[kv][4 * part + 3] = evv.w;
-        }
-        __syncthreads();
-        if (lane < 8) {
-          const int qkv = lane >> 2, g = lane & 3;
-          const int bits = qkv ? a.v_bits : a.k_bits;
-          uint32_t x[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = s_row[qkv][16 * g + i];
-          quant_store_group_bits(bits, x,
-                                 (qkv ? a.c.vq : a.c.kq) + (u * a.cap_q + nq) * (kD * bits / 8) + g * (4 * bits),
-                                 &reinterpret_cast<uint32_t*>(qkv ? a.c.vq_meta : a.c.kq_meta)
-                                     [(u * a.cap_q + nq) * kMetaWords + g]);
+          const int64_t slot = u * a.cap_q + nq;
+          store_codes8((kv ? a.c.vq : a.c.kq) + slot * (kD * bits / 8) + bits * part, codes, bits);
+          if ((part & 3) == 0)
+            reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta)[slot * kMetaWords + (part >> 2)] = meta;
         }
         if (lane == 0) {
           a.c.q_pos[u * a.cap_q + nq] = ev;
