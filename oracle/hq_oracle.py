@@ -34,7 +34,10 @@ lower-index element in the low nibble; the other strict low-bit widths of
 the mode table (K8V8, K4V2, K2V4) use the same rule with 2^b - 1 steps and
 8/b codes per byte, lowest-index element in the lowest bits, K and V widths
 chosen independently; the decode token is not part of the window -- it sits
-in an FP16 staging slot and attends to itself.
+in an FP16 staging slot and attends to itself; the prefill's low-bit QK is
+symmetric INT8 per token row (scale fp32(amax/127), code round-half-even of
+127 x / amax), its FP16 keys are the vertical lines and each query's own
+W-window, and its P V is FP16 for every key.
 
 Parity unpinned: none of the functions below; every one has a pin in
 tests/test_oracle_*.py (closed forms, brute force, library routines).
@@ -494,6 +497,87 @@ def append_merge_scored_unit(cache: Dict, t: int, k_new: np.ndarray, v_new: np.n
     promote = ev >= 0 and bool(score[ev] >= cut)
     append_merge_unit(cache, t, k_new, v_new, promote)
     return promote
+
+
+# --------------------------------------------------------------------------
+# Prefill: one fused hybrid-precision attention [D method paragraph, the
+# prefill sentences; R Overview item 2; R repository layout, the ops listing
+# (INT8-QK + FP16-PV prefill attention with window / vertical variants)].
+# Readings: the low-bit path quantises Q and K to symmetric INT8 per token
+# row (one scale per row of d elements): scale = fp32(amax / 127), code =
+# round-half-even(x / (amax / 127)) in exact arithmetic, i.e. of 127 x / amax
+# (all codes 0 and scale 0 when amax = 0); a key is kept in FP16 for query p
+# when it is a vertical line or lies in the query's own window (p - i < W),
+# else its logit is tau * (q8 . k8) * scale_q * scale_k; causal (i <= p);
+# P V runs in FP16 for every key, so the oracle takes the exact softmax times
+# V; the LSE (natural log) is over the hybrid logits.
+# --------------------------------------------------------------------------
+def int8_quantize_rows(X: np.ndarray):
+    """Symmetric per-row INT8 of fp16 rows X [..][d].  Returns (codes int8
+    [..][d], scales float32 [..]).  127 x is exact in float64 and a single
+    correctly rounded division cannot cross a half-integer (the exact
+    quotient is a ratio of 18- and 11-bit integers), so rint gives the exact
+    round-half-even code."""
+    Xd = X.astype(np.float64)
+    amax = np.abs(Xd).max(axis=-1, keepdims=True)
+    safe = np.where(amax > 0.0, amax, 1.0)
+    codes = np.where(amax > 0.0, np.rint(127.0 * Xd / safe), 0.0) + 0.0
+    scales = (amax[..., 0] / 127.0).astype(np.float32)
+    return codes.astype(np.int8), scales
+
+
+def prefill_fp16_mask(L: int, W: int, vl_flag: np.ndarray) -> np.ndarray:
+    """[L][L] bool: key i is taken in FP16 by query p (i <= p, and i is a
+    vertical line or p - i < W)."""
+    p = np.arange(L)[:, None]
+    i = np.arange(L)[None, :]
+    return (i <= p) & (((p - i) < W) | (np.asarray(vl_flag)[None, :L] != 0))
+
+
+def prefill_hybrid_unit(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                        vl_flag: Optional[np.ndarray], W: int):
+    """Causal prefill attention of one unit.  Q [G][L][d], K, V [L][d] fp16,
+    vl_flag [L] (or None: no vertical lines).  Returns (O [G][L][d],
+    lse [G][L]) in float64."""
+    G, L, d = Q.shape
+    tau = softmax_scale(d)
+    flag = np.zeros(L, np.uint8) if vl_flag is None else np.asarray(vl_flag)
+    q8, sq = int8_quantize_rows(Q)
+    k8, sk = int8_quantize_rows(K)
+    hi = prefill_fp16_mask(L, W, flag)
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    Kd, Vd = K.astype(np.float64), V.astype(np.float64)
+    k8d = k8.astype(np.float64)
+    O = np.zeros((G, L, d))
+    lse = np.zeros((G, L))
+    for h in range(G):
+        z_hi = tau * (Q[h].astype(np.float64) @ Kd.T)
+        z_lo = tau * (q8[h].astype(np.float64) @ k8d.T) * sq[h].astype(np.float64)[:, None] \
+            * sk.astype(np.float64)[None, :]
+        z = np.where(hi, z_hi, z_lo)
+        z[~causal] = -np.inf
+        m = z.max(axis=1)
+        e = np.exp(z - m[:, None])
+        s = e.sum(axis=1)
+        O[h] = (e @ Vd) / s[:, None]
+        lse[h] = m + np.log(s)
+    return O, lse
+
+
+def prefill_hybrid(Q, K, V, vl_flag, W):
+    """Batch driver: Q [B][Hq][L][d], K, V [B][Hkv][L][d], vl_flag
+    [B][Hkv][L] or None.  Query head h uses KV head h // (Hq / Hkv)."""
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    O = np.zeros((B, Hq, L, d))
+    lse = np.zeros((B, Hq, L))
+    for b in range(B):
+        for g in range(Hkv):
+            f = None if vl_flag is None else vl_flag[b, g]
+            O[b, g * G:(g + 1) * G], lse[b, g * G:(g + 1) * G] = prefill_hybrid_unit(
+                Q[b, g * G:(g + 1) * G], K[b, g], V[b, g], f, W)
+    return O, lse
 
 
 # --------------------------------------------------------------------------
