@@ -6,7 +6,7 @@ the GPU path consume the arrays it returns, so that the two sides are compared
 on identical inputs.
 """
 from .gen import (WORKLOADS, Workload, workload, sequence, batch, unit_vectors,
-                  bf16_round)
+                  bf16_round, prefill_queries)
 
 __all__ = ["WORKLOADS", "Workload", "workload", "sequence", "batch",
-           "unit_vectors", "bf16_round"]
+           "unit_vectors", "bf16_round", "prefill_queries"]

@@ -19,6 +19,10 @@ Recipe (one sequence b of workload number c):
   * values are float32 N(0,1); planting is applied in float32; the result is
     rounded to fp16 (round to nearest even).  Workloads flagged ``bf16`` are
     rounded to bf16 first, then to fp16.
+  * prefill queries of every prefix position (``prefill_queries``): their own
+    stream, ``PCG64(SeedSequence([number, b, 7]))``, drawn as Q [Hq][L][d]
+    N(0,1) plus 1.5 u of the query's KV head (u as above), then rounded the
+    same way.
 """
 from __future__ import annotations
 
@@ -180,3 +184,15 @@ def batch(wl: Workload, steps: Optional[int] = None,
     out["plant"] = [p["plant"] for p in per]
     out["strength"] = [p["strength"] for p in per]
     return out
+
+
+def prefill_queries(wl: Workload, b: int) -> np.ndarray:
+    """Queries of every prefix position of sequence ``b``, fp16 [Hq][L][d]:
+    N(0,1) from their own stream plus 1.5 u of the KV head (the vector the
+    planted keys carry), so that the planted lines draw attention in the
+    prefill as in decode."""
+    u = unit_vectors(np.random.Generator(np.random.PCG64(10000 * wl.number + b)), wl.Hkv, wl.d)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.number, b, 7])))
+    Q = rng.standard_normal((wl.Hq, wl.L, wl.d), dtype=np.float32)
+    Q += 1.5 * np.repeat(u, wl.G, axis=0)[:, None, :]
+    return _to_fp16(Q, wl.bf16)

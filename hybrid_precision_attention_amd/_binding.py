@@ -24,6 +24,7 @@ lib = ctypes.CDLL(_LIB_PATH)
 HQ_OK = 0
 HQ_OP_SELECT = 1
 HQ_OP_DECODE = 2
+HQ_OP_PREFILL = 3
 D = 128
 
 
@@ -57,6 +58,9 @@ lib.hq_append_merge_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(h
                                        ctypes.c_int32, _p, _p, _p, _p]
 lib.hq_decode_attn_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), _p,
                                       ctypes.c_int32, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.hq_quant_int8.argtypes = [_p, ctypes.c_int64, _p, _p, _p]
+lib.hq_prefill_attn.argtypes = [ctypes.POINTER(hq_dims), _p, _p, _p, ctypes.c_int32, _p, _p, _p, _p,
+                                ctypes.c_size_t, _p]
 lib.hq_workspace_bytes.argtypes = [ctypes.POINTER(hq_dims), ctypes.c_int, ctypes.c_int32]
 lib.hq_workspace_bytes.restype = ctypes.c_size_t
 lib.hq_status_string.argtypes = [ctypes.c_int]
@@ -64,7 +68,7 @@ lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
-           "hq_decode_attn_ragged"):
+           "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -259,6 +263,27 @@ def hq_decode_attn_ragged(dims, cache: HybridCache, L_seq, L_max, q, out, ws, ls
                                    _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_attn_ragged")
+
+
+def hq_quant_int8(x, codes, scales, stream=None):
+    """x [..][128] fp16 rows -> codes [..][128] int8, scales [..] fp32."""
+    rows = x.numel() // 128
+    if x.shape[-1] != 128 or codes.numel() != rows * 128 or scales.numel() != rows:
+        raise ValueError("hq_quant_int8: x [..][128], codes of x's shape, scales [rows]")
+    st = lib.hq_quant_int8(_ptr(x, torch.float16, "x"), rows, _ptr(codes, torch.int8, "codes"),
+                           _ptr(scales, torch.float32, "scales"), _stream(stream))
+    _check(st, "hq_quant_int8")
+
+
+def hq_prefill_attn(dims, q, k, v, L, vl_flag, out, ws, lse=None, stream=None):
+    """q [B][Hq][L][128], k, v [B][Hkv][L][128] fp16; vl_flag [B][Hkv][L] uint8
+    or None; out like q; lse [B][Hq][L] fp32 or None; ws from
+    workspace(dims, HQ_OP_PREFILL, L)."""
+    st = lib.hq_prefill_attn(ctypes.byref(dims), _ptr(q, torch.float16, "q"), _ptr(k, torch.float16, "k"),
+                             _ptr(v, torch.float16, "v"), L, _ptr(vl_flag, torch.uint8, "vl_flag"),
+                             _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
+                             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "hq_prefill_attn")
 
 
 # --------------------------------------------------------------------------

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhq.so")
 PROBE_LIB = os.path.join(PKG, "libhq_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["hq_host.cpp", "quant_pack.hip", "decode_attn.hip", "select_vertical.hip"]
+SOURCES = ["hq_host.cpp", "quant_pack.hip", "decode_attn.hip", "select_vertical.hip",
+           "prefill_attn.hip"]
 PROBE_SOURCES = ["stream_probe.hip"]                # measurement helper, its own library
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -124,7 +124,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 4; }
+int hq_abi_version(void) { return 5; }
 
 const char* hq_status_string(int status) {
   switch (status) {
@@ -143,6 +143,7 @@ size_t hq_workspace_bytes(const hq_dims* dims, int op, int32_t L_max) {
   if (check_dims(dims) != HQ_OK || L_max < 0) return 0;
   if (op == HQ_OP_DECODE) return decode_ws_bytes(*dims, L_max);
   if (op == HQ_OP_SELECT) return L_max >= 1 ? select_ws_bytes(*dims, L_max) : 0;
+  if (op == HQ_OP_PREFILL) return prefill_ws_bytes(*dims, L_max);
   return 0;
 }
 
@@ -282,6 +283,34 @@ int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int3
   if (!aligned16(ws)) return HQ_ERR_ALIGN;
   const DecodePlan plan = plan_decode(*dims, L_max);
   if (launch_decode(*dims, *cache, L_max, plan, q, out, lse_or_null, ws, stream, L_seq) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales, hipStream_t stream) {
+  if (rows < 0 || (rows > 0 && (!x || !codes || !scales))) return HQ_ERR_ARG;
+  if (rows > (int64_t{1} << 36)) return HQ_ERR_ARG;
+  if (rows > 0 && (!aligned16(x) || !aligned16(codes) || !aligned16(scales))) return HQ_ERR_ALIGN;
+  if (launch_quant_int8(x, rows, codes, scales, stream) != hipSuccess) return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_prefill_attn(const hq_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    int32_t L, const uint8_t* vl_flag_or_null, uint16_t* out, float* lse_or_null,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L < 0) return HQ_ERR_ARG;
+  if (L == 0) return HQ_OK;
+  if (!q || !k || !v || !out) return HQ_ERR_ARG;
+  // positions, and rows of one unit, stay inside int32 in the kernels
+  if (static_cast<int64_t>(L) * 128 > (int64_t{1} << 31) - 1) return HQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HQ_ERR_ALIGN;
+  if (vl_flag_or_null && !aligned16(vl_flag_or_null)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  if (!ws || ws_bytes < prefill_ws_bytes(*dims, L)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  if (launch_prefill(*dims, q, k, v, L, vl_flag_or_null, out, lse_or_null, ws, stream) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }

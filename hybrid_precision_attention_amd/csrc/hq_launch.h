@@ -51,6 +51,13 @@ hipError_t launch_append_merge_scored(const hq_dims& d, const hq_cache& c, int32
                                       hipStream_t s);
 
 // Code width of a quantised region: 0 (unset) means 4.
+size_t prefill_ws_bytes(const hq_dims& d, int32_t L_max);
+hipError_t launch_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales,
+                             hipStream_t s);
+hipError_t launch_prefill(const hq_dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int32_t L, const uint8_t* vl_flag, uint16_t* out, float* lse, void* ws,
+                          hipStream_t s);
+
 inline int kv_bits(int32_t b) { return b == 0 ? 4 : b; }
 
 // floor(rho * n_nw + 1e-6): size of the vertical-line set of n_nw candidates.

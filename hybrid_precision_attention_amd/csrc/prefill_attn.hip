@@ -1,0 +1,484 @@
+// hq_quant_int8 and hq_prefill_attn kernels for gfx950.
+//
+// The prefill's fused hybrid-precision attention (agihunt digest "HyQuant:
+// Hybrid-Precision Quantization for LLM Attention", method paragraph, the
+// prefill sentences; HyQuant README, Overview item 2 and the ops listing of
+// the repository layout, INT8-QK + FP16-PV prefill attention with window and
+// vertical variants): causal attention of every prefix query in one online
+// softmax.  A logit comes from symmetric per-token INT8 codes of q and k,
+// except for the vertical lines and the query's own W-window, which use the
+// FP16 values; P V is FP16 for every key.
+//
+// Layout of the work: one workgroup of four waves takes four (query head,
+// 32-position block) pairs of one KV unit -- four heads of the GQA group at
+// the same positions when G >= 4 -- so that every 64-key tile staged in LDS
+// serves all of them.  Per wave S^T = K Q^T (keys as MFMA rows, the wave's 32
+// queries as two 16-column blocks) and O^T += V^T P^T with
+// v_mfma_f32_16x16x32_f16.  The INT8 product runs on the same instruction
+// with the codes as integer-valued fp16: every product is an integer below
+// 2^14 and every partial sum below 2^24, so the f32 accumulation is exact.
+// Tiles come in three kinds:
+//   far   (every key at least W before every query of the workgroup): INT8
+//         logits, vertical lines masked out (their FP16 turn comes below);
+//   near  (the rest, up to the diagonal): FP16 and INT8 products both, the
+//         choice made per (query, key); causal mask;
+//   lines (the unit's vertical lines at least W before some query, gathered
+//         from their ascending list): FP16 logits where key <= query - W.
+#include <hip/hip_runtime.h>
+
+#include "hq_device.h"
+#include "hq_launch.h"
+
+namespace hq {
+
+namespace {
+
+constexpr int kTile = 64;          // keys per tile
+constexpr int kKP = kD + 8;        // K tile row pitch in halves (272-byte rows)
+constexpr int kVP = kTile + 4;     // V^T row pitch in halves (136-byte rows)
+constexpr int kQW = 32;            // query positions per wave
+constexpr int kPThreads = 256;
+
+__device__ __forceinline__ half8_t as_h8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Eight signed INT8 codes -> eight fp16 integers: each byte, offset by 128,
+// sits under the exponent of 1024 (0x64 high byte), and 1152 is taken off.
+__device__ __forceinline__ uint4 i8x8_to_h8(uint2 c) {
+  const uint32_t a = c.x ^ 0x80808080u, b = c.y ^ 0x80808080u;
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(0u, a, 0x0C010C00u) | 0x64006400u;
+  r.y = __builtin_amdgcn_perm(0u, a, 0x0C030C02u) | 0x64006400u;
+  r.z = __builtin_amdgcn_perm(0u, b, 0x0C010C00u) | 0x64006400u;
+  r.w = __builtin_amdgcn_perm(0u, b, 0x0C030C02u) | 0x64006400u;
+  const half8_t h = as_h8(r) - (half8_t){1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
+  return __builtin_bit_cast(uint4, h);
+}
+
+// ---------------------------------------------------------------------------
+// Symmetric INT8 of 128-element fp16 rows: scale = fp32(amax / 127), code =
+// round-half-even(127 x / amax), decided in fp64 (127 x is exact there, and
+// one correctly rounded division cannot cross a half-integer: the exact
+// quotient is a ratio of 18- and 11-bit integers).  16 lanes per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void int8_rows_kernel(const uint16_t* x, int64_t rows,
+                                                        int8_t* codes, float* scales) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  const bool ok = row < rows;
+  const uint4 v = ok ? ld16(x + row * kD + 8 * part) : make_uint4(0, 0, 0, 0);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    amax = fmaxf(amax, fabsf(h2f(static_cast<uint16_t>(w[i] & 0xFFFFu))));
+    amax = fmaxf(amax, fabsf(h2f(static_cast<uint16_t>(w[i] >> 16))));
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  uint32_t c[2] = {0u, 0u};
+  if (amax > 0.0f) {
+    const double a = static_cast<double>(amax);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const double xv = static_cast<double>(h2f(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)))));
+      const int q = static_cast<int>(rint(xv * 127.0 / a));
+      c[j >> 2] |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * (j & 3));
+    }
+  }
+  if (ok) {
+    *reinterpret_cast<uint2*>(codes + row * kD + 8 * part) = make_uint2(c[0], c[1]);
+    if (part == 0) scales[row] = static_cast<float>(static_cast<double>(amax) / 127.0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The flagged positions of each unit, ascending, and their count.  One
+// 1024-thread workgroup per unit; thread t takes a run of consecutive
+// positions.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void vl_list_kernel(const uint8_t* flag, int32_t L, int32_t* list,
+                                                       int32_t* count) {
+  __shared__ int s_w[16];
+  const int64_t u = blockIdx.x;
+  const uint8_t* f = flag + u * L;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (L + 1023) / 1024;
+  const int a0 = min(L, tid * per), a1 = min(L, a0 + per);
+  int c = 0;
+  for (int i = a0; i < a1; ++i) c += f[i] != 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int off = incl - c;
+  for (int w = 0; w < wave; ++w) off += s_w[w];
+  int32_t* out = list + u * L;
+  for (int i = a0; i < a1; ++i)
+    if (f[i] != 0) out[off++] = i;
+  if (tid == 1023) {
+    int tot = 0;
+    for (int w = 0; w < 16; ++w) tot += s_w[w];
+    count[u] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------
+struct PrefillArgs {
+  const uint16_t* q;       // [B][Hq][L][d]
+  const uint16_t* k;       // [B][Hkv][L][d]
+  const uint16_t* v;
+  const int8_t* q8;        // [B][Hq][L][d]
+  const float* sq;         // [B][Hq][L]
+  const int8_t* k8;        // [B][Hkv][L][d]
+  const float* sk;         // [B][Hkv][L]
+  const uint8_t* flag;     // [B][Hkv][L] or null
+  const int32_t* vl_list;  // [B][Hkv][L] ascending, or null
+  const int32_t* vl_cnt;   // [B][Hkv]
+  uint16_t* out;           // [B][Hq][L][d]
+  float* lse;              // [B][Hq][L] or null
+  int32_t L, W, Hq, Hkv, G, gw, pos_wg, n_qblk;
+  float c2;                // log2(e) / sqrt(d)
+};
+
+struct PrefillShared {
+  uint16_t kf[kTile][kKP];   // FP16 keys (near and line tiles)
+  uint16_t kc[kTile][kKP];   // INT8 key codes as fp16 integers
+  uint16_t vt[kD][kVP];      // values, transposed: vt[dim][key]
+  float sk[kTile];           // key scales
+  int32_t pos[kTile];        // key positions
+  uint8_t vl[kTile];         // vertical-line flags of the tile's keys
+  // each wave's INT8 query codes in B-operand order (8 codes a lane, turned
+  // into fp16 integers when read): [wave][column block][32-dim step][lane]
+  uint2 qc[4][2][4][64];
+};
+
+enum TileKind { kFar = 0, kNear = 1, kLines = 2 };
+
+// Stage one tile: keys pos[0..n) of the unit (n <= 64; the rest are zero).
+// Thread t: key t / 4, a quarter row (32 dims) of K and of the codes; for V,
+// keys 4 (t / 16) .. + 3 and dims 8 (t % 16) .. + 7, transposed on the way.
+__device__ __forceinline__ void stage_tile(PrefillShared& sh, const PrefillArgs& a, int64_t u, int kind,
+                                           int base, int n, const int32_t* list) {
+  const int tid = threadIdx.x;
+  const uint16_t* kunit = a.k + u * a.L * kD;
+  const uint16_t* vunit = a.v + u * a.L * kD;
+  if (tid < kTile) {
+    const int j = tid;
+    int p = -1;
+    if (j < n) p = kind == kLines ? list[base + j] : base + j;
+    sh.pos[j] = p;
+    sh.sk[j] = (p >= 0 && kind != kLines) ? a.sk[u * a.L + p] : 0.0f;
+    sh.vl[j] = (p >= 0 && a.flag && kind != kLines) ? a.flag[u * a.L + p] : 0;
+  }
+  {
+    const int j = tid >> 2, qt = tid & 3;
+    int p = -1;
+    if (j < n) p = kind == kLines ? list[base + j] : base + j;
+    if (kind != kFar) {
+      const uint16_t* src = kunit + static_cast<int64_t>(max(p, 0)) * kD + 32 * qt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 x = p >= 0 ? ld16(src + 8 * i) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sh.kf[j][32 * qt + 8 * i]) = x;
+      }
+    }
+    if (kind != kLines) {
+      const int8_t* src = a.k8 + (u * a.L + max(p, 0)) * kD + 32 * qt;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint4 x = p >= 0 ? *reinterpret_cast<const uint4*>(src + 16 * i) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i]) = i8x8_to_h8(make_uint2(x.x, x.y));
+        *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i + 8]) = i8x8_to_h8(make_uint2(x.z, x.w));
+      }
+    }
+  }
+  {
+    const int kq = tid >> 4, oct = tid & 15;
+    uint4 r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * kq + e;
+      int p = -1;
+      if (j < n) p = kind == kLines ? list[base + j] : base + j;
+      r[e] = p >= 0 ? ld16(vunit + static_cast<int64_t>(p) * kD + 8 * oct) : make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w}, {r[1].x, r[1].y, r[1].z, r[1].w},
+                              {r[2].x, r[2].y, r[2].z, r[2].w}, {r[3].x, r[3].y, r[3].z, r[3].w}};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint2 lo = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                                  __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
+      const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                                  __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
+      *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m][4 * kq]) = lo;
+      *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m + 1][4 * kq]) = hi;
+    }
+  }
+}
+
+struct WaveState {
+  half8_t qf[2][4];     // FP16 query operand: column block cb, 32-dim step kk
+  float qs2[2];         // query scale * c2 of this lane's query, per column block
+  float4_t o[2][8];     // O^T: rows = dims 16 db + 4 g + r, column = query
+  float m[2], l[2];     // running max (log2 units) and this lane's partial sum
+};
+
+// S^T of one 16-key block: rows = keys 16 kb + lane % 16 of the tile; the
+// column block's queries as B.
+__device__ __forceinline__ float4_t s_block(const uint16_t (*tile)[kKP], const half8_t qop[4], int kb,
+                                            int lane) {
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* row = tile[16 * kb + (lane & 15)] + 8 * (lane >> 4);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) s = mfma16(as_h8(*reinterpret_cast<const uint4*>(row + 32 * kk)), qop[kk], s);
+  return s;
+}
+
+__device__ __forceinline__ void wave_tile(WaveState& ws, const PrefillShared& sh, const PrefillArgs& a,
+                                          int kind, int pos0, int lane, int wave) {
+  const int g = lane >> 4;
+  uint4 pb[2][2];
+  // one column block at a time: logits, then the online softmax per query
+  // column (the lane's 16 keys, then the four lanes g = 0..3 sharing it)
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int p = pos0 + 16 * cb + (lane & 15);
+    float z[4][4];
+    half8_t qc[4];
+    if (kind != kLines) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qc[kk] = as_h8(i8x8_to_h8(sh.qc[wave][cb][kk][lane]));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float4_t si = {0.f, 0.f, 0.f, 0.f}, sf = {0.f, 0.f, 0.f, 0.f};
+      if (kind != kLines) si = s_block(sh.kc, qc, kb, lane);
+      if (kind != kFar) sf = s_block(sh.kf, ws.qf[cb], kb, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * g + r;
+        const int i = sh.pos[j];
+        const float zi = sh.vl[j] ? -INFINITY : si[r] * ws.qs2[cb] * sh.sk[j];
+        float zz;
+        if (kind == kFar) {
+          zz = zi;
+        } else if (kind == kNear) {
+          zz = (i < 0 || i > p) ? -INFINITY : (p - i < a.W ? sf[r] * a.c2 : zi);
+        } else {
+          zz = (i < 0 || i > p - a.W) ? -INFINITY : sf[r] * a.c2;
+        }
+        z[kb][r] = zz;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(ws.m[cb], mx);
+    const float mu = m_new == -INFINITY ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(ws.m[cb] - mu);
+    float ps = 0.0f;
+    float pv[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[kb][r] = __builtin_amdgcn_exp2f(z[kb][r] - mu);
+        ps += pv[kb][r];
+      }
+    ws.l[cb] = ws.l[cb] * alpha + ps;
+    ws.m[cb] = m_new;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ws.o[cb][db] *= alpha;
+    // P^T operand of the 32-key step kk: keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g + r
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      half8_t h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        h[r] = static_cast<_Float16>(pv[2 * kk][r]);
+        h[4 + r] = static_cast<_Float16>(pv[2 * kk + 1][r]);
+      }
+      pb[cb][kk] = __builtin_bit_cast(uint4, h);
+    }
+  }
+  // O^T += V^T P^T; the V^T operand of dims 16 db + lane % 16 holds the same
+  // key order as the P^T operand
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint16_t* row = sh.vt[16 * db + (lane & 15)] + 32 * kk + 4 * g;
+      const uint2 lo = *reinterpret_cast<const uint2*>(row);
+      const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+      const half8_t va = as_h8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) ws.o[cb][db] = mfma16(va, as_h8(pb[cb][kk]), ws.o[cb][db]);
+    }
+}
+
+__global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ PrefillShared sh;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hgroups = a.G / a.gw;
+  const int64_t u = blockIdx.x / hgroups;            // unit (b, kv head): fastest, one XCD each
+  const int hg = blockIdx.x % hgroups;
+  const int64_t b = u / a.Hkv;
+  const int h = static_cast<int>(u % a.Hkv) * a.G + hg * a.gw + wave % a.gw;
+  const int qblk = a.n_qblk - 1 - static_cast<int>(blockIdx.y);   // the longest rows first
+  const int m0 = qblk * a.pos_wg;
+  const int pos0 = m0 + (wave / a.gw) * kQW;                      // this wave's first query
+  const int pmax = min(a.L, m0 + a.pos_wg) - 1;                   // the workgroup's last query
+  const int64_t bh = b * a.Hq + h;
+
+  WaveState ws;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int p = pos0 + 16 * cb + (lane & 15);
+    const bool ok = p < a.L;
+    const int64_t row = (bh * a.L + min(p, a.L - 1)) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ws.qf[cb][kk] = as_h8(ok ? ld16(a.q + row + 32 * kk) : make_uint4(0, 0, 0, 0));
+      const uint2 c = ok ? *reinterpret_cast<const uint2*>(a.q8 + row + 32 * kk) : make_uint2(0, 0);
+      sh.qc[wave][cb][kk][lane] = c;
+    }
+    ws.qs2[cb] = ok ? a.sq[bh * a.L + p] * a.c2 : 0.0f;
+    ws.m[cb] = -INFINITY;
+    ws.l[cb] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ws.o[cb][db] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // key tiles up to the workgroup's last query, then the vertical lines
+  const int n_tiles = pmax / kTile + 1;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int base = t * kTile;
+    const int kind = (base + kTile - 1 <= m0 - a.W) ? kFar : kNear;
+    stage_tile(sh, a, u, kind, base, min(kTile, a.L - base), nullptr);
+    __syncthreads();
+    if (base <= pos0 + kQW - 1) wave_tile(ws, sh, a, kind, pos0, lane, wave);
+    __syncthreads();
+  }
+  if (a.vl_list) {
+    const int32_t* list = a.vl_list + u * a.L;
+    const int cnt = a.vl_cnt[u];
+    for (int base = 0; base < cnt; base += kTile) {
+      if (list[base] > pmax - a.W) break;      // ascending: nothing further is W before a query
+      stage_tile(sh, a, u, kLines, base, min(kTile, cnt - base), list);
+      __syncthreads();
+      if (list[base] <= pos0 + kQW - 1 - a.W) wave_tile(ws, sh, a, kLines, pos0, lane, wave);
+      __syncthreads();
+    }
+  }
+
+  // normalise and store: lane holds dims 16 db + 4 g + r of query 16 cb + lane % 16
+  const int g = lane >> 4;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    float lt = ws.l[cb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int p = pos0 + 16 * cb + (lane & 15);
+    if (p < a.L) {
+      const float inv = 1.0f / lt;
+      uint16_t* dst = a.out + (bh * a.L + p) * kD + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        half2_t h01 = {static_cast<_Float16>(ws.o[cb][db][0] * inv), static_cast<_Float16>(ws.o[cb][db][1] * inv)};
+        half2_t h23 = {static_cast<_Float16>(ws.o[cb][db][2] * inv), static_cast<_Float16>(ws.o[cb][db][3] * inv)};
+        *reinterpret_cast<uint2*>(dst + 16 * db) =
+            make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+      }
+      if (a.lse && g == 0) a.lse[bh * a.L + p] = (ws.m[cb] + __log2f(lt)) * 0.69314718055994531f;
+    }
+  }
+}
+
+}  // namespace
+
+static size_t round256p(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t prefill_ws_bytes(const hq_dims& d, int32_t L_max) {
+  const size_t L = static_cast<size_t>(L_max);
+  const size_t rq = static_cast<size_t>(d.B) * d.Hq * L, rk = static_cast<size_t>(d.B) * d.Hkv * L;
+  return round256p(rq * kD) + round256p(rq * 4) + round256p(rk * kD) + round256p(rk * 4) +
+         round256p(rk * 4) + round256p(static_cast<size_t>(d.B) * d.Hkv * 4);
+}
+
+hipError_t launch_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(int8_rows_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, x,
+                     rows, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(const hq_dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          int32_t L, const uint8_t* vl_flag, uint16_t* out, float* lse, void* ws,
+                          hipStream_t s) {
+  if (L <= 0) return hipSuccess;
+  const size_t Ls = static_cast<size_t>(L);
+  const size_t rq = static_cast<size_t>(d.B) * d.Hq * Ls, rk = static_cast<size_t>(d.B) * d.Hkv * Ls;
+  char* p = static_cast<char*>(ws);
+  int8_t* q8 = reinterpret_cast<int8_t*>(p);
+  p += round256p(rq * kD);
+  float* sq = reinterpret_cast<float*>(p);
+  p += round256p(rq * 4);
+  int8_t* k8 = reinterpret_cast<int8_t*>(p);
+  p += round256p(rk * kD);
+  float* sk = reinterpret_cast<float*>(p);
+  p += round256p(rk * 4);
+  int32_t* list = reinterpret_cast<int32_t*>(p);
+  p += round256p(rk * 4);
+  int32_t* cnt = reinterpret_cast<int32_t*>(p);
+
+  hipError_t e = launch_quant_int8(q, static_cast<int64_t>(rq), q8, sq, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch_quant_int8(k, static_cast<int64_t>(rk), k8, sk, s)) != hipSuccess) return e;
+  const int units = d.B * d.Hkv;
+  if (vl_flag) {
+    hipLaunchKernelGGL(vl_list_kernel, dim3(units), dim3(1024), 0, s, vl_flag, L, list, cnt);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.q8 = q8;
+  a.sq = sq;
+  a.k8 = k8;
+  a.sk = sk;
+  a.flag = vl_flag;
+  a.vl_list = vl_flag ? list : nullptr;
+  a.vl_cnt = vl_flag ? cnt : nullptr;
+  a.out = out;
+  a.lse = lse;
+  a.L = L;
+  a.W = d.W;
+  a.Hq = d.Hq;
+  a.Hkv = d.Hkv;
+  a.G = d.Hq / d.Hkv;
+  a.gw = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);   // heads per workgroup, a divisor of G
+  a.pos_wg = kQW * (4 / a.gw);
+  a.n_qblk = (L + a.pos_wg - 1) / a.pos_wg;
+  a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(kD)));
+  dim3 grid(static_cast<unsigned>(units * (a.G / a.gw)), static_cast<unsigned>(a.n_qblk));
+  hipLaunchKernelGGL(prefill_attn_kernel, grid, dim3(kPThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hq

@@ -109,6 +109,7 @@ typedef struct {
 /* Operation ids for hq_workspace_bytes. */
 #define HQ_OP_SELECT 1
 #define HQ_OP_DECODE 2
+#define HQ_OP_PREFILL 3
 
 /*
  * hq_select_vertical -- column-mass score and top-rho vertical-line set
@@ -270,6 +271,47 @@ int hq_append_merge_ragged(const hq_dims* dims, const hq_cache* cache, const int
 int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* L_seq,
                           int32_t L_max, const uint16_t* q, uint16_t* out, float* lse_or_null,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hq_quant_int8 -- symmetric INT8 of 128-element fp16 rows, the low-bit
+ * operand of the prefill's QK product (agihunt digest on HyQuant, method
+ * paragraph, prefill sentences; HyQuant README, Overview item 2, and the ops
+ * listing's INT8-QK + FP16-PV prefill attention).
+ *
+ *   x       [rows][128] fp16
+ *   codes   [rows][128] int8 out: round-half-even(127 x / amax) of the row
+ *           (the decision is exact); all 0 when amax = 0
+ *   scales  [rows] fp32 out: fp32(amax / 127), 0 for an all-zero row
+ * rows may be 0 (nothing happens).  Errors: HQ_ERR_ARG (negative rows, null
+ * pointers), HQ_ERR_ALIGN.
+ */
+int hq_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales, hipStream_t stream);
+
+/*
+ * hq_prefill_attn -- causal prefill attention of the whole prefix in one
+ * online softmax with hybrid-precision logits (same passages as above).
+ *
+ *   q            [B][Hq][L][d] fp16 queries of positions 0..L-1
+ *   k, v         [B][Hkv][L][d] fp16 keys and values
+ *   vl_flag_or_null [B][Hkv][L] u8: nonzero marks a vertical-line key
+ *                position (e.g. hq_select_vertical's vl_flag); null: none
+ *   out          [B][Hq][L][d] fp16 out
+ *   lse_or_null  [B][Hq][L] fp32 out: natural-log log-sum-exp of each
+ *                query's logits (hq_select_vertical accepts the last nb rows
+ *                of a unit's heads as its lse)
+ *   ws           hq_workspace_bytes(dims, HQ_OP_PREFILL, L) bytes (INT8
+ *                codes and scales of q and k, the vertical-line lists)
+ * Query p (query head h, KV head h / G) attends to keys 0..p.  The logit of
+ * key i is tau q.k in FP16 when i is a vertical line or p - i < W (the
+ * query's own window, itself included), else tau (q8 . k8) s_q s_k with the
+ * hq_quant_int8 codes and scales of the two rows; tau = 1/sqrt(d).  P V uses
+ * the FP16 values of every key.  dims->rho, cap_* and the bit widths are not
+ * used.  L = 0 does nothing.  Errors: HQ_ERR_ARG, HQ_ERR_UNSUPPORTED (d),
+ * HQ_ERR_ALIGN, HQ_ERR_WORKSPACE, HQ_ERR_HIP.
+ */
+int hq_prefill_attn(const hq_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    int32_t L, const uint8_t* vl_flag_or_null, uint16_t* out, float* lse_or_null,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes an operation needs for any prefix length up to L_max;
  * 0 for an invalid request. */

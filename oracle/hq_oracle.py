@@ -526,32 +526,35 @@ def int8_quantize_rows(X: np.ndarray):
     return codes.astype(np.int8), scales
 
 
-def prefill_fp16_mask(L: int, W: int, vl_flag: np.ndarray) -> np.ndarray:
-    """[L][L] bool: key i is taken in FP16 by query p (i <= p, and i is a
-    vertical line or p - i < W)."""
-    p = np.arange(L)[:, None]
+def prefill_fp16_mask(pos: np.ndarray, L: int, W: int, vl_flag: np.ndarray) -> np.ndarray:
+    """[n][L] bool: key i is taken in FP16 by the query at position pos[r]
+    (i <= pos[r], and i is a vertical line or pos[r] - i < W)."""
+    p = np.asarray(pos, np.int64)[:, None]
     i = np.arange(L)[None, :]
     return (i <= p) & (((p - i) < W) | (np.asarray(vl_flag)[None, :L] != 0))
 
 
-def prefill_hybrid_unit(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
-                        vl_flag: Optional[np.ndarray], W: int):
-    """Causal prefill attention of one unit.  Q [G][L][d], K, V [L][d] fp16,
-    vl_flag [L] (or None: no vertical lines).  Returns (O [G][L][d],
-    lse [G][L]) in float64."""
-    G, L, d = Q.shape
+def prefill_rows_unit(Qr: np.ndarray, pos: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      vl_flag: Optional[np.ndarray], W: int):
+    """Causal prefill attention of one unit for the queries at positions pos
+    (Qr [G][n][d], the queries of those positions; K, V [L][d] fp16; vl_flag
+    [L] or None: no vertical lines).  Returns (O [G][n][d], lse [G][n]) in
+    float64."""
+    G, n, d = Qr.shape
+    L = K.shape[0]
     tau = softmax_scale(d)
+    pos = np.asarray(pos, np.int64)
     flag = np.zeros(L, np.uint8) if vl_flag is None else np.asarray(vl_flag)
-    q8, sq = int8_quantize_rows(Q)
+    q8, sq = int8_quantize_rows(Qr)
     k8, sk = int8_quantize_rows(K)
-    hi = prefill_fp16_mask(L, W, flag)
-    causal = np.tril(np.ones((L, L), dtype=bool))
+    hi = prefill_fp16_mask(pos, L, W, flag)
+    causal = np.arange(L)[None, :] <= pos[:, None]
     Kd, Vd = K.astype(np.float64), V.astype(np.float64)
     k8d = k8.astype(np.float64)
-    O = np.zeros((G, L, d))
-    lse = np.zeros((G, L))
+    O = np.zeros((G, n, d))
+    lse = np.zeros((G, n))
     for h in range(G):
-        z_hi = tau * (Q[h].astype(np.float64) @ Kd.T)
+        z_hi = tau * (Qr[h].astype(np.float64) @ Kd.T)
         z_lo = tau * (q8[h].astype(np.float64) @ k8d.T) * sq[h].astype(np.float64)[:, None] \
             * sk.astype(np.float64)[None, :]
         z = np.where(hi, z_hi, z_lo)
@@ -562,6 +565,13 @@ def prefill_hybrid_unit(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
         O[h] = (e @ Vd) / s[:, None]
         lse[h] = m + np.log(s)
     return O, lse
+
+
+def prefill_hybrid_unit(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                        vl_flag: Optional[np.ndarray], W: int):
+    """Every query of the prefix: Q [G][L][d].  Returns (O [G][L][d],
+    lse [G][L])."""
+    return prefill_rows_unit(Q, np.arange(Q.shape[1]), K, V, vl_flag, W)
 
 
 def prefill_hybrid(Q, K, V, vl_flag, W):

@@ -16,13 +16,14 @@ def _declared():
     with open(os.path.join(ROOT, "include", "hq.h")) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(hq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(hq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
-            "hq_refresh_hybrid", "hq_append_merge_scored",
+            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
+            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn",
             "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
@@ -32,7 +33,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 4
+    assert H.lib.hq_abi_version() == 5
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -165,6 +166,31 @@ def test_scored_merge_validation():
     assert f(*args(ld=99)) == -1                         # the leaving position may be t - 1
     assert f(*args(k=P + 2)) == -3
     assert f(ctypes.byref(_dims(cap_stg=0)), ctypes.byref(c), 100, P, P, P, 100, P, None) == -4
+
+
+def test_prefill_validation():
+    d = _dims()
+    L = 4096
+    need = H.hq_workspace_bytes(d, H.HQ_OP_PREFILL, L)
+    assert need > 0
+    f = H.lib.hq_prefill_attn
+    args = lambda L=L, q=P, k=P, flag=None, out=P, lse=None, ws=P, wsb=need: (
+        ctypes.byref(d), q, k, P, L, flag, out, lse, ws, wsb, None)
+    assert f(*args(L=-1)) == -1
+    assert f(*args(L=0, q=None)) == 0                   # nothing to do
+    assert f(*args(q=None)) == -1
+    assert f(*args(k=P + 2)) == -3
+    assert f(*args(flag=P + 1)) == -3
+    assert f(*args(lse=P + 4)) == -3
+    assert f(*args(ws=None)) == -5
+    assert f(*args(wsb=need - 1)) == -5
+    assert f(ctypes.byref(_dims(d=64)), P, P, P, L, None, P, None, P, need, None) == -2
+    assert H.hq_workspace_bytes(d, H.HQ_OP_PREFILL, 8192) > need
+    g = H.lib.hq_quant_int8
+    assert g(P, -1, P, P, None) == -1
+    assert g(None, 4, P, P, None) == -1
+    assert g(P, 4, P + 8, P, None) == -3
+    assert g(None, 0, None, None, None) == 0            # no rows
 
 
 def test_workspace_bytes():

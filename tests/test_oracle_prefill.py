@@ -119,6 +119,10 @@ def test_brute_force_mixed():
     V = rng.standard_normal((L, d)).astype(np.float16)
     flag = (rng.random(L) < 0.3).astype(np.uint8)
     o, lse = O.prefill_hybrid_unit(Q, K, V, flag, W)
+    # the row form on a scattered subset of positions gives the same rows
+    sub = np.array([22, 3, 0, 17, 9])
+    o_s, l_s = O.prefill_rows_unit(Q[:, sub], sub, K, V, flag, W)
+    assert np.abs(o_s - o[:, sub]).max() < 1e-12 and np.abs(l_s - lse[:, sub]).max() < 1e-12
     tau = 1.0 / math.sqrt(d)
 
     def q8row(r):
