@@ -13,11 +13,12 @@
 // 32-position block) pairs of one KV unit -- four heads of the GQA group at
 // the same positions when G >= 4 -- so that every 64-key tile staged in LDS
 // serves all of them.  Per wave S^T = K Q^T (keys as MFMA rows, the wave's 32
-// queries as two 16-column blocks) and O^T += V^T P^T with
-// v_mfma_f32_16x16x32_f16.  The INT8 product runs on the same instruction
-// with the codes as integer-valued fp16: every product is an integer below
-// 2^14 and every partial sum below 2^24, so the f32 accumulation is exact.
-// Tiles come in three kinds:
+// queries as two 16-column blocks): v_mfma_i32_16x16x64_i8 on the codes (an
+// exact int32 dot product, scaled by s_q s_k afterwards) or
+// v_mfma_f32_16x16x32_f16 on the FP16 values; then O^T += V^T P^T with the
+// FP16 instruction.  The INT8 operands of A and B take the same bytes of the
+// same lane groups, so the dot product does not depend on the order in which
+// the instruction walks them.  Tiles come in three kinds:
 //   far   (every key at least W before every query of the workgroup): INT8
 //         logits, vertical lines masked out (their FP16 turn comes below);
 //   near  (the rest, up to the diagonal): FP16 and INT8 products both, the
@@ -43,19 +44,6 @@ __device__ __forceinline__ half8_t as_h8(uint4 v) { return __builtin_bit_cast(ha
 
 __device__ __forceinline__ float4_t mfma16(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// Eight signed INT8 codes -> eight fp16 integers: each byte, offset by 128,
-// sits under the exponent of 1024 (0x64 high byte), and 1152 is taken off.
-__device__ __forceinline__ uint4 i8x8_to_h8(uint2 c) {
-  const uint32_t a = c.x ^ 0x80808080u, b = c.y ^ 0x80808080u;
-  uint4 r;
-  r.x = __builtin_amdgcn_perm(0u, a, 0x0C010C00u) | 0x64006400u;
-  r.y = __builtin_amdgcn_perm(0u, a, 0x0C030C02u) | 0x64006400u;
-  r.z = __builtin_amdgcn_perm(0u, b, 0x0C010C00u) | 0x64006400u;
-  r.w = __builtin_amdgcn_perm(0u, b, 0x0C030C02u) | 0x64006400u;
-  const half8_t h = as_h8(r) - (half8_t){1152, 1152, 1152, 1152, 1152, 1152, 1152, 1152};
-  return __builtin_bit_cast(uint4, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -133,6 +121,8 @@ __global__ __launch_bounds__(1024) void vl_list_kernel(const uint8_t* flag, int3
 // ---------------------------------------------------------------------------
 // Attention
 // ---------------------------------------------------------------------------
+typedef int32_t int4_t __attribute__((ext_vector_type(4)));
+
 struct PrefillArgs {
   const uint16_t* q;       // [B][Hq][L][d]
   const uint16_t* k;       // [B][Hkv][L][d]
@@ -150,173 +140,166 @@ struct PrefillArgs {
   float c2;                // log2(e) / sqrt(d)
 };
 
+constexpr int kCP = kD + 16;       // INT8 code tile row pitch in bytes
+
 struct PrefillShared {
   uint16_t kf[kTile][kKP];   // FP16 keys (near and line tiles)
-  uint16_t kc[kTile][kKP];   // INT8 key codes as fp16 integers
   uint16_t vt[kD][kVP];      // values, transposed: vt[dim][key]
+  int8_t kc[kTile][kCP];     // INT8 key codes
   float sk[kTile];           // key scales
-  int32_t pos[kTile];        // key positions
+  float bias[kTile];         // far tiles: -inf at a vertical line (its FP16 turn comes later), else 0
+  int32_t pos[kTile];        // key positions (-1: no key)
   uint8_t vl[kTile];         // vertical-line flags of the tile's keys
-  // each wave's INT8 query codes in B-operand order (8 codes a lane, turned
-  // into fp16 integers when read): [wave][column block][32-dim step][lane]
-  uint2 qc[4][2][4][64];
 };
 
 enum TileKind { kFar = 0, kNear = 1, kLines = 2 };
 
-// Stage one tile: keys pos[0..n) of the unit (n <= 64; the rest are zero).
-// Thread t: key t / 4, a quarter row (32 dims) of K and of the codes; for V,
-// keys 4 (t / 16) .. + 3 and dims 8 (t % 16) .. + 7, transposed on the way.
-__device__ __forceinline__ void stage_tile(PrefillShared& sh, const PrefillArgs& a, int64_t u, int kind,
-                                           int base, int n, const int32_t* list) {
+__device__ __forceinline__ float4_t mfma_i8(uint4 a, uint4 b, float4_t c_as_int) {
+  const int4_t r = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(int4_t, a),
+                                                         __builtin_bit_cast(int4_t, b),
+                                                         __builtin_bit_cast(int4_t, c_as_int), 0, 0, 0);
+  return __builtin_bit_cast(float4_t, r);
+}
+
+// The global half of staging a tile, into registers: thread t takes key t / 4
+// (a quarter row: 32 dims of K, 32 codes) and, for V, keys 4 (t / 16) .. + 3
+// at dims 8 (t % 16) .. + 7.
+struct TileRegs {
+  uint4 kf[4];
+  uint4 kc[2];
+  uint4 v[4];
+  int32_t pos;       // threads < 64: key position of slot t (or -1)
+  float sk;
+  uint8_t vl;
+};
+
+__device__ __forceinline__ int slot_pos(int kind, int base, int n, int j, const int32_t* list) {
+  if (j >= n) return -1;
+  return kind == kLines ? list[base + j] : base + j;
+}
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, int64_t u, int kind, int base,
+                                          int n, const int32_t* list) {
   const int tid = threadIdx.x;
-  const uint16_t* kunit = a.k + u * a.L * kD;
-  const uint16_t* vunit = a.v + u * a.L * kD;
   if (tid < kTile) {
-    const int j = tid;
-    int p = -1;
-    if (j < n) p = kind == kLines ? list[base + j] : base + j;
-    sh.pos[j] = p;
-    sh.sk[j] = (p >= 0 && kind != kLines) ? a.sk[u * a.L + p] : 0.0f;
-    sh.vl[j] = (p >= 0 && a.flag && kind != kLines) ? a.flag[u * a.L + p] : 0;
+    const int p = slot_pos(kind, base, n, tid, list);
+    r.pos = p;
+    r.sk = (p >= 0 && kind != kLines) ? a.sk[u * a.L + p] : 0.0f;
+    r.vl = (p >= 0 && a.flag && kind != kLines) ? a.flag[u * a.L + p] : 0;
   }
-  {
-    const int j = tid >> 2, qt = tid & 3;
-    int p = -1;
-    if (j < n) p = kind == kLines ? list[base + j] : base + j;
-    if (kind != kFar) {
-      const uint16_t* src = kunit + static_cast<int64_t>(max(p, 0)) * kD + 32 * qt;
+  const int j = tid >> 2, qt = tid & 3;
+  const int p = slot_pos(kind, base, n, j, list);
+  if (kind != kFar) {
+    const uint16_t* src = a.k + (u * a.L + max(p, 0)) * kD + 32 * qt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 x = p >= 0 ? ld16(src + 8 * i) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sh.kf[j][32 * qt + 8 * i]) = x;
-      }
-    }
-    if (kind != kLines) {
-      const int8_t* src = a.k8 + (u * a.L + max(p, 0)) * kD + 32 * qt;
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint4 x = p >= 0 ? *reinterpret_cast<const uint4*>(src + 16 * i) : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i]) = i8x8_to_h8(make_uint2(x.x, x.y));
-        *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i + 8]) = i8x8_to_h8(make_uint2(x.z, x.w));
-      }
-    }
+    for (int i = 0; i < 4; ++i) r.kf[i] = p >= 0 ? ld16(src + 8 * i) : make_uint4(0, 0, 0, 0);
   }
-  {
-    const int kq = tid >> 4, oct = tid & 15;
-    uint4 r[4];
+  if (kind != kLines) {
+    const int8_t* src = a.k8 + (u * a.L + max(p, 0)) * kD + 32 * qt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 4 * kq + e;
-      int p = -1;
-      if (j < n) p = kind == kLines ? list[base + j] : base + j;
-      r[e] = p >= 0 ? ld16(vunit + static_cast<int64_t>(p) * kD + 8 * oct) : make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w}, {r[1].x, r[1].y, r[1].z, r[1].w},
-                              {r[2].x, r[2].y, r[2].z, r[2].w}, {r[3].x, r[3].y, r[3].z, r[3].w}};
+    for (int i = 0; i < 2; ++i)
+      r.kc[i] = p >= 0 ? *reinterpret_cast<const uint4*>(src + 16 * i) : make_uint4(0, 0, 0, 0);
+  }
+  const int kq = tid >> 4, oct = tid & 15;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint2 lo = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
-                                  __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
-      const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
-                                  __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
-      *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m][4 * kq]) = lo;
-      *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m + 1][4 * kq]) = hi;
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int pe = slot_pos(kind, base, n, 4 * kq + e, list);
+    r.v[e] = pe >= 0 ? ld16(a.v + (u * a.L + pe) * kD + 8 * oct) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_tile(PrefillShared& sh, const TileRegs& r, int kind) {
+  const int tid = threadIdx.x;
+  if (tid < kTile) {
+    sh.pos[tid] = r.pos;
+    sh.sk[tid] = r.sk;
+    sh.vl[tid] = r.vl;
+    sh.bias[tid] = r.vl ? -INFINITY : 0.0f;
+  }
+  const int j = tid >> 2, qt = tid & 3;
+  if (kind != kFar) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sh.kf[j][32 * qt + 8 * i]) = r.kf[i];
+  }
+  if (kind != kLines) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i]) = r.kc[i];
+  }
+  const int kq = tid >> 4, oct = tid & 15;
+  const uint32_t w[4][4] = {{r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w}, {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w},
+                            {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w}, {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w}};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint2 lo = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u),
+                                __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
+    const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
+                                __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
+    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m][4 * kq]) = lo;
+    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m + 1][4 * kq]) = hi;
   }
 }
 
 struct WaveState {
-  half8_t qf[2][4];     // FP16 query operand: column block cb, 32-dim step kk
+  uint4 q8[2][2];       // INT8 query operand: column block cb, 64-dim step
   float qs2[2];         // query scale * c2 of this lane's query, per column block
   float4_t o[2][8];     // O^T: rows = dims 16 db + 4 g + r, column = query
   float m[2], l[2];     // running max (log2 units) and this lane's partial sum
 };
 
-// S^T of one 16-key block: rows = keys 16 kb + lane % 16 of the tile; the
-// column block's queries as B.
-__device__ __forceinline__ float4_t s_block(const uint16_t (*tile)[kKP], const half8_t qop[4], int kb,
-                                            int lane) {
-  float4_t s = {0.f, 0.f, 0.f, 0.f};
-  const uint16_t* row = tile[16 * kb + (lane & 15)] + 8 * (lane >> 4);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) s = mfma16(as_h8(*reinterpret_cast<const uint4*>(row + 32 * kk)), qop[kk], s);
-  return s;
+// the maximum / sum over the four lanes g = 0..3 that share a query column
+__device__ __forceinline__ float max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ void wave_tile(WaveState& ws, const PrefillShared& sh, const PrefillArgs& a,
-                                          int kind, int pos0, int lane, int wave) {
-  const int g = lane >> 4;
-  uint4 pb[2][2];
-  // one column block at a time: logits, then the online softmax per query
-  // column (the lane's 16 keys, then the four lanes g = 0..3 sharing it)
+// Online softmax of one column block's 16 logits per lane (keys 16 kb + 4 g
+// + r), then its P^T operands for the two 32-key steps.
+__device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&z)[4][4], uint4 (&pb)[2]) {
+  float mx = -INFINITY;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int p = pos0 + 16 * cb + (lane & 15);
-    float z[4][4];
-    half8_t qc[4];
-    if (kind != kLines) {
+  for (int kb = 0; kb < 4; ++kb)
+    mx = fmaxf(mx, fmaxf(fmaxf(z[kb][0], z[kb][1]), fmaxf(z[kb][2], z[kb][3])));
+  mx = max4(mx);
+  const float m_new = fmaxf(ws.m[cb], mx);
+  const float mu = m_new == -INFINITY ? 0.0f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(ws.m[cb] - mu);
+  float ps = 0.0f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) qc[kk] = as_h8(i8x8_to_h8(sh.qc[wave][cb][kk][lane]));
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      z[kb][r] = __builtin_amdgcn_exp2f(z[kb][r] - mu);
+      ps += z[kb][r];
     }
+  ws.l[cb] = ws.l[cb] * alpha + ps;
+  ws.m[cb] = m_new;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float4_t si = {0.f, 0.f, 0.f, 0.f}, sf = {0.f, 0.f, 0.f, 0.f};
-      if (kind != kLines) si = s_block(sh.kc, qc, kb, lane);
-      if (kind != kFar) sf = s_block(sh.kf, ws.qf[cb], kb, lane);
+  for (int db = 0; db < 8; ++db) ws.o[cb][db] *= alpha;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * kb + 4 * g + r;
-        const int i = sh.pos[j];
-        const float zi = sh.vl[j] ? -INFINITY : si[r] * ws.qs2[cb] * sh.sk[j];
-        float zz;
-        if (kind == kFar) {
-          zz = zi;
-        } else if (kind == kNear) {
-          zz = (i < 0 || i > p) ? -INFINITY : (p - i < a.W ? sf[r] * a.c2 : zi);
-        } else {
-          zz = (i < 0 || i > p - a.W) ? -INFINITY : sf[r] * a.c2;
-        }
-        z[kb][r] = zz;
-      }
+  for (int kk = 0; kk < 2; ++kk) {
+    half8_t h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      h[r] = static_cast<_Float16>(z[2 * kk][r]);
+      h[4 + r] = static_cast<_Float16>(z[2 * kk + 1][r]);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, z[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(ws.m[cb], mx);
-    const float mu = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(ws.m[cb] - mu);
-    float ps = 0.0f;
-    float pv[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[kb][r] = __builtin_amdgcn_exp2f(z[kb][r] - mu);
-        ps += pv[kb][r];
-      }
-    ws.l[cb] = ws.l[cb] * alpha + ps;
-    ws.m[cb] = m_new;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) ws.o[cb][db] *= alpha;
-    // P^T operand of the 32-key step kk: keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g + r
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      half8_t h;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        h[r] = static_cast<_Float16>(pv[2 * kk][r]);
-        h[4 + r] = static_cast<_Float16>(pv[2 * kk + 1][r]);
-      }
-      pb[cb][kk] = __builtin_bit_cast(uint4, h);
-    }
+    pb[kk] = __builtin_bit_cast(uint4, h);
   }
-  // O^T += V^T P^T; the V^T operand of dims 16 db + lane % 16 holds the same
-  // key order as the P^T operand
+}
+
+// O^T += V^T P^T; the V^T operand of dims 16 db + lane % 16 holds the same
+// key order as the P^T operand (keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g + r)
+__device__ __forceinline__ void pv_tile(WaveState& ws, const PrefillShared& sh, const uint4 (&pb)[2][2],
+                                        int lane) {
+  const int g = lane >> 4;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -328,6 +311,99 @@ __device__ __forceinline__ void wave_tile(WaveState& ws, const PrefillShared& sh
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) ws.o[cb][db] = mfma16(va, as_h8(pb[cb][kk]), ws.o[cb][db]);
     }
+}
+
+// INT8 S^T of the tile for both column blocks: rows = keys 16 kb + lane % 16
+__device__ __forceinline__ void s_int8(float4_t (&si)[2][4], const WaveState& ws, const PrefillShared& sh,
+                                       int lane) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int8_t* row = sh.kc[16 * kb + (lane & 15)] + 16 * (lane >> 4);
+    const uint4 a0 = *reinterpret_cast<const uint4*>(row);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(row + 64);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_i8(a0, ws.q8[cb][0], acc);
+      si[cb][kb] = mfma_i8(a1, ws.q8[cb][1], acc);
+    }
+  }
+}
+
+// FP16 S^T of the tile for both column blocks
+__device__ __forceinline__ void s_fp16(float4_t (&sf)[2][4], const half8_t (&qf)[2][4], const PrefillShared& sh,
+                                       int lane) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint16_t* row = sh.kf[16 * kb + (lane & 15)] + 8 * (lane >> 4);
+    half8_t ar[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) ar[kk] = as_h8(*reinterpret_cast<const uint4*>(row + 32 * kk));
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma16(ar[kk], qf[cb][kk], acc);
+      sf[cb][kb] = acc;
+    }
+  }
+}
+
+// A far tile: INT8 logits, vertical lines masked (bias), no causal mask.
+__device__ __forceinline__ void far_tile(WaveState& ws, const PrefillShared& sh, int lane) {
+  const int g = lane >> 4;
+  float4_t si[2][4];
+  s_int8(si, ws, sh, lane);
+  uint4 pb[2][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    float z[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * g + r;
+        const float acc = static_cast<float>(__builtin_bit_cast(int4_t, si[cb][kb])[r]);
+        z[kb][r] = fmaf(acc, ws.qs2[cb] * sh.sk[j], sh.bias[j]);
+      }
+    softmax_block(ws, cb, z, pb[cb]);
+  }
+  pv_tile(ws, sh, pb, lane);
+}
+
+// A near-diagonal tile (INT8 and FP16 logits chosen per element, causal) or
+// a tile of gathered vertical lines (FP16, key <= query - W).
+__device__ __forceinline__ void mixed_tile(WaveState& ws, const half8_t (&qf)[2][4], const PrefillShared& sh,
+                                           const PrefillArgs& a, int kind, int pos0, int lane) {
+  const int g = lane >> 4;
+  float4_t si[2][4], sf[2][4];
+  if (kind == kNear) s_int8(si, ws, sh, lane);
+  s_fp16(sf, qf, sh, lane);
+  uint4 pb[2][2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int p = pos0 + 16 * cb + (lane & 15);
+    float z[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * kb + 4 * g + r;
+        const int i = sh.pos[j];
+        float zz;
+        if (kind == kNear) {
+          const float zi = sh.vl[j] ? -INFINITY
+                                    : static_cast<float>(__builtin_bit_cast(int4_t, si[cb][kb])[r]) *
+                                          ws.qs2[cb] * sh.sk[j];
+          zz = (i < 0 || i > p) ? -INFINITY : (p - i < a.W ? sf[cb][kb][r] * a.c2 : zi);
+        } else {
+          zz = (i < 0 || i > p - a.W) ? -INFINITY : sf[cb][kb][r] * a.c2;
+        }
+        z[kb][r] = zz;
+      }
+    softmax_block(ws, cb, z, pb[cb]);
+  }
+  pv_tile(ws, sh, pb, lane);
 }
 
 __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs a) {
@@ -350,13 +426,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
   for (int cb = 0; cb < 2; ++cb) {
     const int p = pos0 + 16 * cb + (lane & 15);
     const bool ok = p < a.L;
-    const int64_t row = (bh * a.L + min(p, a.L - 1)) * kD + 8 * (lane >> 4);
+    const int8_t* row = a.q8 + (bh * a.L + min(p, a.L - 1)) * kD + 16 * (lane >> 4);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      ws.qf[cb][kk] = as_h8(ok ? ld16(a.q + row + 32 * kk) : make_uint4(0, 0, 0, 0));
-      const uint2 c = ok ? *reinterpret_cast<const uint2*>(a.q8 + row + 32 * kk) : make_uint2(0, 0);
-      sh.qc[wave][cb][kk][lane] = c;
-    }
+    for (int c = 0; c < 2; ++c)
+      ws.q8[cb][c] = ok ? *reinterpret_cast<const uint4*>(row + 64 * c) : make_uint4(0, 0, 0, 0);
     ws.qs2[cb] = ok ? a.sq[bh * a.L + p] * a.c2 : 0.0f;
     ws.m[cb] = -INFINITY;
     ws.l[cb] = 0.0f;
@@ -364,24 +437,48 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
     for (int db = 0; db < 8; ++db) ws.o[cb][db] = (float4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  // key tiles up to the workgroup's last query, then the vertical lines
+  // far tiles: every key at least W before every query of the workgroup;
+  // the next tile's loads are in flight while this one is computed
   const int n_tiles = pmax / kTile + 1;
-  for (int t = 0; t < n_tiles; ++t) {
-    const int base = t * kTile;
-    const int kind = (base + kTile - 1 <= m0 - a.W) ? kFar : kNear;
-    stage_tile(sh, a, u, kind, base, min(kTile, a.L - base), nullptr);
+  const int n_far = min(n_tiles, max(0, (m0 - a.W + 1) / kTile));
+  TileRegs tr;
+  if (n_far > 0) load_tile(tr, a, u, kFar, 0, kTile, nullptr);
+  for (int t = 0; t < n_far; ++t) {
+    store_tile(sh, tr, kFar);
     __syncthreads();
-    if (base <= pos0 + kQW - 1) wave_tile(ws, sh, a, kind, pos0, lane, wave);
+    if (t + 1 < n_far) load_tile(tr, a, u, kFar, (t + 1) * kTile, kTile, nullptr);
+    far_tile(ws, sh, lane);
+    __syncthreads();
+  }
+
+  // near-diagonal tiles and the vertical lines, with the FP16 queries
+  half8_t qf[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int p = pos0 + 16 * cb + (lane & 15);
+    const bool ok = p < a.L;
+    const uint16_t* row = a.q + (bh * a.L + min(p, a.L - 1)) * kD + 8 * (lane >> 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[cb][kk] = as_h8(ok ? ld16(row + 32 * kk) : make_uint4(0, 0, 0, 0));
+  }
+  for (int t = n_far; t < n_tiles; ++t) {
+    const int base = t * kTile;
+    load_tile(tr, a, u, kNear, base, min(kTile, a.L - base), nullptr);
+    store_tile(sh, tr, kNear);
+    __syncthreads();
+    if (base <= pos0 + kQW - 1) mixed_tile(ws, qf, sh, a, kNear, pos0, lane);
     __syncthreads();
   }
   if (a.vl_list) {
     const int32_t* list = a.vl_list + u * a.L;
     const int cnt = a.vl_cnt[u];
     for (int base = 0; base < cnt; base += kTile) {
-      if (list[base] > pmax - a.W) break;      // ascending: nothing further is W before a query
-      stage_tile(sh, a, u, kLines, base, min(kTile, cnt - base), list);
+      const int first = list[base];
+      if (first > pmax - a.W) break;      // ascending: nothing further is W before a query
+      load_tile(tr, a, u, kLines, base, min(kTile, cnt - base), list);
+      store_tile(sh, tr, kLines);
       __syncthreads();
-      if (list[base] <= pos0 + kQW - 1 - a.W) wave_tile(ws, sh, a, kLines, pos0, lane, wave);
+      if (first <= pos0 + kQW - 1 - a.W) mixed_tile(ws, qf, sh, a, kLines, pos0, lane);
       __syncthreads();
     }
   }
@@ -390,9 +487,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
   const int g = lane >> 4;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    float lt = ws.l[cb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = sum4(ws.l[cb]);
     const int p = pos0 + 16 * cb + (lane & 15);
     if (p < a.L) {
       const float inv = 1.0f / lt;
