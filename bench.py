@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = "hybrid K4V4 decode-attn µs/step + HBM GB/s (% of peak) at L=32K, B=1..32"
 PEAK_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0
+PEAK_I8_TOPS = 5000.0
 REFRESH = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
 
@@ -56,6 +57,7 @@ def parse():
                    help="skip the whole-model capacity run (36 layers at the largest 32K batch)")
     p.add_argument("--capacity-only", action="store_true",
                    help="print only the capacity run's JSON object")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill attention timing")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the decode batch sweep and the streaming-read ceiling")
     p.add_argument("--copy-bytes", type=int, default=0,
@@ -330,20 +332,19 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, base, H, torch)
 
-    # ---- the metric's batch sweep and the measured read ceiling -----------
-    sweep, ceiling, widths = None, None, None
-    if not args.no_sweep:
+    # ---- the metric's batch sweep, the read ceiling, prefill, capacity ----
+    # (the step's own buffers are released first)
+    if not (args.no_sweep and args.no_prefill and args.no_capacity):
         del caches, ws, K_rep, base, spare
         torch.cuda.empty_cache()
+    sweep, ceiling, widths = None, None, None
+    if not args.no_sweep:
         sweep = decode_sweep(H, torch, workload)
         widths = width_sweep(H, torch, workload)
         ceiling = read_ceiling(torch, 4 << 30)
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
-    capacity = None
-    if not args.no_capacity:
-        if args.no_sweep:
-            del caches, ws, K_rep, base, spare
-        capacity = capacity_run(H, torch)
+    prefill = None if args.no_prefill else prefill_timing(H, torch)
+    capacity = None if args.no_capacity else capacity_run(H, torch)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -368,6 +369,7 @@ def main():
         "b_sweep": sweep,
         "kv_width_sweep": widths,
         "read_ceiling": ceiling,
+        "prefill": prefill,
         "capacity": capacity,
         "replicas": R, "input_gen_s": round(gen_s, 1),
     }
@@ -499,6 +501,59 @@ def decode_point(H, torch, workload, B, kb=4, vb=4):
             res["kv_bits"] = f"K{kb}V{vb}"
         del caches, wss, base
         torch.cuda.empty_cache()
+    return res
+
+
+def prefill_timing(H, torch, L=32768, n=3):
+    """hq_prefill_attn on the Llama-3.1-8B-shaped layer (B = 1, 32/8 heads,
+    d = 128, W = 128) at a 32K prefix: bf16-rounded N(0,1) device inputs,
+    the vertical lines chosen by hq_select_vertical from the last 64 queries
+    (rho = 5 %), n calls captured in a graph and replayed once between HIP
+    events.  Algorithmic work: the causal QK and PV products, 4 d Hq L (L+1)/2
+    flop; QK runs on INT8 codes for all but the window and line keys, PV on
+    FP16, so the ceiling is between the FP16 peak (2.5 PFLOP/s) and, with
+    every QK product at the INT8 rate, 1 / (0.5/5.0 + 0.5/2.5) = 3.33 P/s."""
+    B, Hq, Hkv, d, W, rho = 1, 32, 8, 128, 128, 0.05
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    q = torch.randn((B, Hq, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    k = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    v = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    dims = H.make_dims(B, Hq, Hkv, W, rho)
+    n_vl = H.n_vertical(rho, L - W)
+    score = torch.zeros((B, Hkv, L), device="cuda")
+    idx = torch.zeros((B, Hkv, n_vl), dtype=torch.int32, device="cuda")
+    flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device="cuda")
+    qtail = q[:, :, L - 64:].contiguous()
+    H.hq_select_vertical(dims, qtail, k, L, score, idx, flag, H.workspace(dims, H.HQ_OP_SELECT, L))
+    ws = H.workspace(dims, H.HQ_OP_PREFILL, L)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, L), device="cuda")
+    H.hq_prefill_attn(dims, q, k, v, L, flag, out, ws, lse=lse)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        st = torch.cuda.current_stream()
+        for _ in range(n):
+            H.hq_prefill_attn(dims, q, k, v, L, flag, out, ws, lse=lse, stream=st)
+    graph_upload(gr, torch)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 4.0 * d * Hq * B * L * (L + 1) / 2
+    tf = flops / (ms * 1e-3) / 1e12
+    mixed_peak = 1.0 / (0.5 / PEAK_I8_TOPS + 0.5 / PEAK_F16_TFLOPS)
+    res = {"workload": "Llama-3.1-8B-shaped layer, B=1", "L": L, "W": W, "rho": rho,
+           "n_vertical_per_head": n_vl, "ms": round(ms, 3), "flop": flops, "tflops": round(tf, 1),
+           "frac_of_fp16_peak": round(tf / PEAK_F16_TFLOPS, 4),
+           "frac_of_int8_qk_fp16_pv_peak": round(tf / mixed_peak, 4),
+           "timing": f"{n} calls (INT8 rows of q and k, line lists, attention) in one graph, replayed once"}
+    del gr, q, k, v, out, lse, ws, score, idx, flag
+    torch.cuda.empty_cache()
     return res
 
 
