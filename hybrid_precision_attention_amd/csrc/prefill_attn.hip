@@ -142,14 +142,20 @@ struct PrefillArgs {
 
 constexpr int kCP = kD + 16;       // INT8 code tile row pitch in bytes
 
-struct PrefillShared {
-  uint16_t kf[kTile][kKP];   // FP16 keys (near and line tiles)
+struct TileBuf {
   uint16_t vt[kD][kVP];      // values, transposed: vt[dim][key]
   int8_t kc[kTile][kCP];     // INT8 key codes
   float sk[kTile];           // key scales
-  float bias[kTile];         // far tiles: -inf at a vertical line (its FP16 turn comes later), else 0
+  float bias[kTile];         // -inf at a vertical line (its FP16 turn comes later), else 0
   int32_t pos[kTile];        // key positions (-1: no key)
   uint8_t vl[kTile];         // vertical-line flags of the tile's keys
+};
+
+// Two tile buffers (the far tiles alternate between them, one barrier a
+// tile) and the FP16 keys of the near and line tiles.
+struct PrefillShared {
+  TileBuf tb[2];
+  uint16_t kf[kTile][kKP];
 };
 
 enum TileKind { kFar = 0, kNear = 1, kLines = 2 };
@@ -208,7 +214,7 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, int
   }
 }
 
-__device__ __forceinline__ void store_tile(PrefillShared& sh, const TileRegs& r, int kind) {
+__device__ __forceinline__ void store_tile(TileBuf& sh, uint16_t (*kf)[kKP], const TileRegs& r, int kind) {
   const int tid = threadIdx.x;
   if (tid < kTile) {
     sh.pos[tid] = r.pos;
@@ -219,7 +225,7 @@ __device__ __forceinline__ void store_tile(PrefillShared& sh, const TileRegs& r,
   const int j = tid >> 2, qt = tid & 3;
   if (kind != kFar) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sh.kf[j][32 * qt + 8 * i]) = r.kf[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&kf[j][32 * qt + 8 * i]) = r.kf[i];
   }
   if (kind != kLines) {
 #pragma unroll
@@ -260,14 +266,17 @@ __device__ __forceinline__ float sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Online softmax of one column block's 16 logits per lane (keys 16 kb + 4 g
-// + r), then its P^T operands for the two 32-key steps.
-__device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&z)[4][4], uint4 (&pb)[2]) {
+// Online softmax of one column block's 16 values per lane (keys 16 kb + 4 g
+// + r), whose logits in log2 units are scale * y (scale > 0, one per lane:
+// the maximum is taken over y and each exponent is one fma), then its P^T
+// operands for the two 32-key steps.
+__device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&y)[4][4], float scale,
+                                              uint4 (&pb)[2]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
-    mx = fmaxf(mx, fmaxf(fmaxf(z[kb][0], z[kb][1]), fmaxf(z[kb][2], z[kb][3])));
-  mx = max4(mx);
+    mx = fmaxf(mx, fmaxf(fmaxf(y[kb][0], y[kb][1]), fmaxf(y[kb][2], y[kb][3])));
+  mx = max4(mx) * scale;
   const float m_new = fmaxf(ws.m[cb], mx);
   const float mu = m_new == -INFINITY ? 0.0f : m_new;
   const float alpha = __builtin_amdgcn_exp2f(ws.m[cb] - mu);
@@ -276,20 +285,23 @@ __device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&z)[
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[kb][r] = __builtin_amdgcn_exp2f(z[kb][r] - mu);
-      ps += z[kb][r];
+      y[kb][r] = __builtin_amdgcn_exp2f(fmaf(y[kb][r], scale, -mu));
+      ps += y[kb][r];
     }
   ws.l[cb] = ws.l[cb] * alpha + ps;
   ws.m[cb] = m_new;
+  // rescale only when some query of the wave got a larger maximum
+  if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) ws.o[cb][db] *= alpha;
+    for (int db = 0; db < 8; ++db) ws.o[cb][db] *= alpha;
+  }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     half8_t h;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      h[r] = static_cast<_Float16>(z[2 * kk][r]);
-      h[4 + r] = static_cast<_Float16>(z[2 * kk + 1][r]);
+      h[r] = static_cast<_Float16>(y[2 * kk][r]);
+      h[4 + r] = static_cast<_Float16>(y[2 * kk + 1][r]);
     }
     pb[kk] = __builtin_bit_cast(uint4, h);
   }
@@ -297,7 +309,7 @@ __device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&z)[
 
 // O^T += V^T P^T; the V^T operand of dims 16 db + lane % 16 holds the same
 // key order as the P^T operand (keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g + r)
-__device__ __forceinline__ void pv_tile(WaveState& ws, const PrefillShared& sh, const uint4 (&pb)[2][2],
+__device__ __forceinline__ void pv_tile(WaveState& ws, const TileBuf& sh, const uint4 (&pb)[2][2],
                                         int lane) {
   const int g = lane >> 4;
 #pragma unroll
@@ -314,7 +326,7 @@ __device__ __forceinline__ void pv_tile(WaveState& ws, const PrefillShared& sh, 
 }
 
 // INT8 S^T of the tile for both column blocks: rows = keys 16 kb + lane % 16
-__device__ __forceinline__ void s_int8(float4_t (&si)[2][4], const WaveState& ws, const PrefillShared& sh,
+__device__ __forceinline__ void s_int8(float4_t (&si)[2][4], const WaveState& ws, const TileBuf& sh,
                                        int lane) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -331,11 +343,11 @@ __device__ __forceinline__ void s_int8(float4_t (&si)[2][4], const WaveState& ws
 }
 
 // FP16 S^T of the tile for both column blocks
-__device__ __forceinline__ void s_fp16(float4_t (&sf)[2][4], const half8_t (&qf)[2][4], const PrefillShared& sh,
-                                       int lane) {
+__device__ __forceinline__ void s_fp16(float4_t (&sf)[2][4], const half8_t (&qf)[2][4],
+                                       const uint16_t (*kf)[kKP], int lane) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const uint16_t* row = sh.kf[16 * kb + (lane & 15)] + 8 * (lane >> 4);
+    const uint16_t* row = kf[16 * kb + (lane & 15)] + 8 * (lane >> 4);
     half8_t ar[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) ar[kk] = as_h8(*reinterpret_cast<const uint4*>(row + 32 * kk));
@@ -350,7 +362,7 @@ __device__ __forceinline__ void s_fp16(float4_t (&sf)[2][4], const half8_t (&qf)
 }
 
 // A far tile: INT8 logits, vertical lines masked (bias), no causal mask.
-__device__ __forceinline__ void far_tile(WaveState& ws, const PrefillShared& sh, int lane) {
+__device__ __forceinline__ void far_tile(WaveState& ws, const TileBuf& sh, int lane) {
   const int g = lane >> 4;
   float4_t si[2][4];
   s_int8(si, ws, sh, lane);
@@ -364,21 +376,22 @@ __device__ __forceinline__ void far_tile(WaveState& ws, const PrefillShared& sh,
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * kb + 4 * g + r;
         const float acc = static_cast<float>(__builtin_bit_cast(int4_t, si[cb][kb])[r]);
-        z[kb][r] = fmaf(acc, ws.qs2[cb] * sh.sk[j], sh.bias[j]);
+        z[kb][r] = fmaf(acc, sh.sk[j], sh.bias[j]);      // logit / qs2
       }
-    softmax_block(ws, cb, z, pb[cb]);
+    softmax_block(ws, cb, z, ws.qs2[cb], pb[cb]);
   }
   pv_tile(ws, sh, pb, lane);
 }
 
 // A near-diagonal tile (INT8 and FP16 logits chosen per element, causal) or
 // a tile of gathered vertical lines (FP16, key <= query - W).
-__device__ __forceinline__ void mixed_tile(WaveState& ws, const half8_t (&qf)[2][4], const PrefillShared& sh,
-                                           const PrefillArgs& a, int kind, int pos0, int lane) {
+__device__ __forceinline__ void mixed_tile(WaveState& ws, const half8_t (&qf)[2][4], const TileBuf& sh,
+                                           const uint16_t (*kf)[kKP], const PrefillArgs& a, int kind,
+                                           int pos0, int lane) {
   const int g = lane >> 4;
   float4_t si[2][4], sf[2][4];
   if (kind == kNear) s_int8(si, ws, sh, lane);
-  s_fp16(sf, qf, sh, lane);
+  s_fp16(sf, qf, kf, lane);
   uint4 pb[2][2];
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
@@ -401,7 +414,7 @@ __device__ __forceinline__ void mixed_tile(WaveState& ws, const half8_t (&qf)[2]
         }
         z[kb][r] = zz;
       }
-    softmax_block(ws, cb, z, pb[cb]);
+    softmax_block(ws, cb, z, 1.0f, pb[cb]);
   }
   pv_tile(ws, sh, pb, lane);
 }
@@ -430,7 +443,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
 #pragma unroll
     for (int c = 0; c < 2; ++c)
       ws.q8[cb][c] = ok ? *reinterpret_cast<const uint4*>(row + 64 * c) : make_uint4(0, 0, 0, 0);
-    ws.qs2[cb] = ok ? a.sq[bh * a.L + p] * a.c2 : 0.0f;
+    // kept positive: an all-zero query row has all-zero codes, so its INT8
+    // logits stay 0 = 0 * anything finite, and -inf stays -inf
+    ws.qs2[cb] = fmaxf(ok ? a.sq[bh * a.L + p] * a.c2 : 0.0f, 1e-30f);
     ws.m[cb] = -INFINITY;
     ws.l[cb] = 0.0f;
 #pragma unroll
@@ -441,13 +456,19 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
   // the next tile's loads are in flight while this one is computed
   const int n_tiles = pmax / kTile + 1;
   const int n_far = min(n_tiles, max(0, (m0 - a.W + 1) / kTile));
+  // (buffer t % 2 is read while buffer (t + 1) % 2 is filled: it was last
+  // read in the previous iteration, before that iteration's barrier)
   TileRegs tr;
-  if (n_far > 0) load_tile(tr, a, u, kFar, 0, kTile, nullptr);
+  if (n_far > 0) {
+    load_tile(tr, a, u, kFar, 0, kTile, nullptr);
+    store_tile(sh.tb[0], sh.kf, tr, kFar);
+  }
+  __syncthreads();
   for (int t = 0; t < n_far; ++t) {
-    store_tile(sh, tr, kFar);
-    __syncthreads();
-    if (t + 1 < n_far) load_tile(tr, a, u, kFar, (t + 1) * kTile, kTile, nullptr);
-    far_tile(ws, sh, lane);
+    const bool more = t + 1 < n_far;
+    if (more) load_tile(tr, a, u, kFar, (t + 1) * kTile, kTile, nullptr);
+    far_tile(ws, sh.tb[t & 1], lane);
+    if (more) store_tile(sh.tb[(t + 1) & 1], sh.kf, tr, kFar);
     __syncthreads();
   }
 
@@ -464,9 +485,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
   for (int t = n_far; t < n_tiles; ++t) {
     const int base = t * kTile;
     load_tile(tr, a, u, kNear, base, min(kTile, a.L - base), nullptr);
-    store_tile(sh, tr, kNear);
+    store_tile(sh.tb[0], sh.kf, tr, kNear);
     __syncthreads();
-    if (base <= pos0 + kQW - 1) mixed_tile(ws, qf, sh, a, kNear, pos0, lane);
+    if (base <= pos0 + kQW - 1) mixed_tile(ws, qf, sh.tb[0], sh.kf, a, kNear, pos0, lane);
     __syncthreads();
   }
   if (a.vl_list) {
@@ -476,9 +497,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
       const int first = list[base];
       if (first > pmax - a.W) break;      // ascending: nothing further is W before a query
       load_tile(tr, a, u, kLines, base, min(kTile, cnt - base), list);
-      store_tile(sh, tr, kLines);
+      store_tile(sh.tb[0], sh.kf, tr, kLines);
       __syncthreads();
-      if (first <= pos0 + kQW - 1 - a.W) mixed_tile(ws, qf, sh, a, kLines, pos0, lane);
+      if (first <= pos0 + kQW - 1 - a.W) mixed_tile(ws, qf, sh.tb[0], sh.kf, a, kLines, pos0, lane);
       __syncthreads();
     }
   }
