@@ -57,6 +57,8 @@ def parse():
                    help="skip the whole-model capacity run (36 layers at the largest 32K batch)")
     p.add_argument("--capacity-only", action="store_true",
                    help="print only the capacity run's JSON object")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="print only the prefill timing's JSON object")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill attention timing")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the decode batch sweep and the streaming-read ceiling")
@@ -128,6 +130,9 @@ def main():
 
     if args.capacity_only:
         print(json.dumps({"capacity": capacity_run(H, torch)}))
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_timing(H, torch)}))
         return
 
     over = {}
