@@ -58,6 +58,8 @@ lib.hq_append_merge_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(h
                                        ctypes.c_int32, _p, _p, _p, _p]
 lib.hq_decode_attn_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), _p,
                                       ctypes.c_int32, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.hq_decode_step.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32, _p, _p,
+                               _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 lib.hq_quant_int8.argtypes = [_p, ctypes.c_int64, _p, _p, _p]
 lib.hq_prefill_attn.argtypes = [ctypes.POINTER(hq_dims), _p, _p, _p, ctypes.c_int32, _p, _p, _p, _p,
                                 ctypes.c_size_t, _p]
@@ -68,7 +70,7 @@ lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
-           "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn"):
+           "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -263,6 +265,35 @@ def hq_decode_attn_ragged(dims, cache: HybridCache, L_seq, L_max, q, out, ws, ls
                                    _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
                                    ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_attn_ragged")
+
+
+def hq_decode_step(dims, cache: HybridCache, t, k_new, v_new, q, out, ws, lse=None, evict_is_vl=None,
+                   stream=None):
+    """hq_append_merge(t) + hq_decode_attn(t) in one launch (nothing may be staged)."""
+    cs = cache.struct()
+    st = lib.hq_decode_step(ctypes.byref(dims), ctypes.byref(cs), t, _ptr(k_new, torch.float16, "k_new"),
+                            _ptr(v_new, torch.float16, "v_new"), _ptr(evict_is_vl, torch.uint8, "evict_is_vl"),
+                            _ptr(q, torch.float16, "q"), _ptr(out, torch.float16, "out"),
+                            _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "hq_decode_step")
+
+
+def bind_step(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):
+    """Returns f(t, k_ptr, v_ptr, q_ptr=None): hq_decode_step on fixed buffers."""
+    cs = cache.struct()
+    d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
+    qp = _ptr(q, torch.float16, "q")
+    op, lp = _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse")
+    wp, wb, sp = _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)
+    fn = lib.hq_decode_step
+
+    def call(t, k_ptr, v_ptr, q_ptr=None):
+        st = fn(d_ref, c_ref, t, k_ptr, v_ptr, None, q_ptr or qp, op, lp, wp, wb, sp)
+        if st:
+            raise HQError(st, "hq_decode_step")
+    call.keep = (dims, cs, q, out, ws, lse)
+    return call
 
 
 def hq_quant_int8(x, codes, scales, stream=None):

@@ -70,9 +70,63 @@ struct DecodeArgs {
   int32_t L_max;
   int32_t nsplit;                   // workgroups per unit
   float c2;                         // log2(e) / sqrt(d)
+  // decode step with its staging merge (hq_decode_step): the new token's
+  // rows take the place of the staging slot, and the unit's last workgroup
+  // moves them into the ring afterwards; null for a plain decode
+  const uint16_t* k_new;            // [B][Hkv][d]
+  const uint16_t* v_new;
+  const uint8_t* evict_is_vl;       // [B][Hkv] or null
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
+
+// The staging merge of a decode step at position t, run by one wave of the
+// unit's last workgroup once every workgroup of the unit has finished its
+// scan (so nothing reads the ring any more): the token leaving the window
+// (position t - W; with no window the new token itself) is quantised into
+// the next K4V4 slot, or copied to the vertical-line region when flagged,
+// and the new token takes its ring slot t mod W.  Lanes 0-15 carry the K
+// row, 16-31 the V row, 16 bytes each; a quantisation group is a lane quad.
+template <int kKB, int kVB>
+__device__ __forceinline__ void step_merge(const DecodeArgs& a, int64_t u, int t, int lane) {
+  const bool mover = lane < 32;
+  const int kv = (lane >> 4) & 1, part = lane & 15;
+  const int W = a.W;
+  const int ev = t - W;
+  uint16_t* win = W > 0 ? (kv ? a.c.vwin : a.c.kwin) + (u * W + t % W) * kD + 8 * part : nullptr;
+  const uint4 fresh = mover ? ld16((kv ? a.v_new : a.k_new) + u * kD + 8 * part) : make_uint4(0, 0, 0, 0);
+  const uint4 old = (mover && win && ev >= 0) ? ld16(win) : make_uint4(0, 0, 0, 0);
+  const int nq = a.c.n_q[u];
+  const int nvl = a.c.n_vl[u];
+  if (ev >= 0) {
+    const uint4 evv = W > 0 ? old : fresh;
+    const bool to_vl = a.evict_is_vl && a.evict_is_vl[u] != 0 && nvl < a.cap_vl;
+    if (to_vl) {
+      if (mover) st16((kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + nvl) * kD + 8 * part, evv);
+      if (lane == 0) {
+        a.c.vl_pos[u * a.cap_vl + nvl] = ev;
+        a.c.n_vl[u] = nvl + 1;
+      }
+    } else if (nq < a.cap_q) {
+      const int bits = kv ? kVB : kKB;
+      uint32_t meta;
+      const uint64_t codes = quant_quad8(evv, bits, &meta);
+      if (mover) {
+        const int64_t slot = u * a.cap_q + nq;
+        store_codes8((kv ? a.c.vq : a.c.kq) + slot * (kD * bits / 8) + bits * part, codes, bits);
+        if ((part & 3) == 0)
+          reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta)[slot * kMetaWords + (part >> 2)] = meta;
+      }
+      if (lane == 0) {
+        a.c.q_pos[u * a.cap_q + nq] = ev;
+        a.c.n_q[u] = nq + 1;
+      }
+    }
+  }
+  // the leaving token was read (above) before its slot is overwritten
+  __builtin_amdgcn_s_waitcnt(0);
+  if (win && mover) st16(win, fresh);
+}
 
 // Valid window slots of sequence b: min(W, L) at its own position L in a
 // ragged batch (clamped to [0, L_max]), else the batch's common count.
@@ -818,7 +872,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     {
       const int nvl = min(a.c.n_vl[u], a.cap_vl);
-      const int nst = min(a.c.n_stg[u], a.cap_stg);
+      const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
       const int nwin = unit_n_win(a, b);
       const int nf = nvl + nwin + nst;
       const int nblk_f = (nf + kBlk - 1) / kBlk;
@@ -829,8 +883,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         f.vvl = a.c.vvl + u * a.cap_vl * kD;
         f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
         f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-        f.kstg = a.c.kstg + u * a.cap_stg * kD;
-        f.vstg = a.c.vstg + u * a.cap_stg * kD;
+        f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
+        f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
         f.nvl = nvl;
         f.nwin = nwin;
         f.nf = nf;
@@ -931,7 +985,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
     {
       const int nvl = min(a.c.n_vl[u], a.cap_vl);
-      const int nst = min(a.c.n_stg[u], a.cap_stg);
+      const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
       const int nwin = unit_n_win(a, b);
       const int nf = nvl + nwin + nst;
       const int nblk_f = (nf + kBlk - 1) / kBlk;
@@ -946,8 +1000,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         f.vvl = a.c.vvl + u * a.cap_vl * kD;
         f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
         f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-        f.kstg = a.c.kstg + u * a.cap_stg * kD;
-        f.vstg = a.c.vstg + u * a.cap_stg * kD;
+        f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
+        f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
         f.nvl = nvl;
         f.nwin = nwin;
         f.nf = nf;
@@ -1102,6 +1156,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
+  if (a.k_new && wave == 0) step_merge<kKB, kVB>(a, u, a.L_max, lane);
   if (tid == 0) a.counters[u] = 0;
 }
 
@@ -1109,8 +1164,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const DecodePlan& plan,
                          const uint16_t* q, uint16_t* out, float* lse, void* ws, hipStream_t s,
-                         const int32_t* L_seq) {
+                         const int32_t* L_seq, const uint16_t* k_new, const uint16_t* v_new,
+                         const uint8_t* evict_is_vl) {
   DecodeArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.evict_is_vl = evict_is_vl;
   a.L_seq = L_seq;
   a.L_max = L;
   a.c = c;

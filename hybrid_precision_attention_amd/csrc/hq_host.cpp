@@ -124,7 +124,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 5; }
+int hq_abi_version(void) { return 6; }
 
 const char* hq_status_string(int status) {
   switch (status) {
@@ -283,6 +283,27 @@ int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int3
   if (!aligned16(ws)) return HQ_ERR_ALIGN;
   const DecodePlan plan = plan_decode(*dims, L_max);
   if (launch_decode(*dims, *cache, L_max, plan, q, out, lse_or_null, ws, stream, L_seq) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_decode_step(const hq_dims* dims, const hq_cache* cache, int32_t t, const uint16_t* k_new,
+                   const uint16_t* v_new, const uint8_t* evict_is_vl_or_null, const uint16_t* q,
+                   uint16_t* out, float* lse_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t < 0 || !k_new || !v_new || !q || !out) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out)) return HQ_ERR_ALIGN;
+  if (evict_is_vl_or_null && !aligned16(evict_is_vl_or_null)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  // after the step the K4V4 region may hold every position up to t - W
+  if (static_cast<int64_t>(dims->cap_q) < static_cast<int64_t>(t) + 1 - dims->W) return HQ_ERR_CAPACITY;
+  if (!ws || ws_bytes < decode_ws_bytes(*dims, t)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  const DecodePlan plan = plan_decode(*dims, t);
+  if (launch_decode(*dims, *cache, t, plan, q, out, lse_or_null, ws, stream, nullptr, k_new, v_new,
+                    evict_is_vl_or_null) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }

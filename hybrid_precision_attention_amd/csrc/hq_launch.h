@@ -34,7 +34,9 @@ hipError_t launch_append_merge(const hq_dims& d, const hq_cache& c, int32_t t,
 
 hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L,
                          const DecodePlan& plan, const uint16_t* q, uint16_t* out,
-                         float* lse, void* ws, hipStream_t s, const int32_t* L_seq = nullptr);
+                         float* lse, void* ws, hipStream_t s, const int32_t* L_seq = nullptr,
+                         const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
+                         const uint8_t* evict_is_vl = nullptr);
 
 hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb,
                          const uint16_t* k, int32_t L, const float* lse_in,

@@ -273,6 +273,32 @@ int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int3
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hq_decode_step -- one decode step in one launch: hq_append_merge of the
+ * token at position t followed by hq_decode_attn at t, with the same result
+ * (agihunt digest on HyQuant, decode paragraph: new tokens are staged, then
+ * merged into the hybrid layout; the attention scan dequantises in place).
+ *
+ *   t            position of the new token (the query's position)
+ *   k_new, v_new [B][Hkv][d] fp16 rows of the new token
+ *   evict_is_vl_or_null [B][Hkv] u8: the token leaving the window becomes a
+ *                vertical line (as in hq_append_merge)
+ *   q, out, lse_or_null, ws, ws_bytes  as in hq_decode_attn
+ * The query attends to the cache's K4V4 slots, vertical lines and window
+ * (positions max(0, t-W) .. t-1) and to the new token itself.  Afterwards
+ * the token at t - W (with W = 0: the new token) has left the window (into
+ * the next K4V4 slot, or the vertical-line region when flagged) and the new
+ * token sits in the ring at slot t mod W, so that nothing is staged.
+ * Precondition: nothing is staged (n_stg = 0, as after hq_quant_pack or a
+ * previous hq_decode_step); the window holds positions max(0, t-W) .. t-1.
+ * Mixing with hq_append_merge / hq_decode_attn is allowed in that state: a
+ * plain hq_append_merge at t then stages t and moves nothing.
+ * Errors: as hq_decode_attn; HQ_ERR_CAPACITY when cap_q < t + 1 - W.
+ */
+int hq_decode_step(const hq_dims* dims, const hq_cache* cache, int32_t t, const uint16_t* k_new,
+                   const uint16_t* v_new, const uint8_t* evict_is_vl_or_null, const uint16_t* q,
+                   uint16_t* out, float* lse_or_null, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * hq_quant_int8 -- symmetric INT8 of 128-element fp16 rows, the low-bit
  * operand of the prefill's QK product (agihunt digest on HyQuant, method
  * paragraph, prefill sentences; HyQuant README, Overview item 2, and the ops

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
             "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
-            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn",
+            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step",
             "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
@@ -33,7 +33,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 5
+    assert H.lib.hq_abi_version() == 6
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -166,6 +166,25 @@ def test_scored_merge_validation():
     assert f(*args(ld=99)) == -1                         # the leaving position may be t - 1
     assert f(*args(k=P + 2)) == -3
     assert f(ctypes.byref(_dims(cap_stg=0)), ctypes.byref(c), 100, P, P, P, 100, P, None) == -4
+
+
+def test_step_validation():
+    d = _dims()
+    c = _fake_cache()
+    need = H.hq_workspace_bytes(d, H.HQ_OP_DECODE, 32768)
+    f = H.lib.hq_decode_step
+    args = lambda t=1000, k=P, q=P, ev=None, lse=None, ws=P, wsb=need, dd=d: (
+        ctypes.byref(dd), ctypes.byref(c), t, k, P, ev, q, P, lse, ws, wsb, None)
+    assert f(*args(t=-1)) == -1
+    assert f(*args(k=None)) == -1
+    assert f(*args(q=None)) == -1
+    assert f(*args(k=P + 2)) == -3
+    assert f(*args(ev=P + 1)) == -3
+    assert f(*args(lse=P + 4)) == -3
+    assert f(*args(ws=None)) == -5
+    assert f(*args(wsb=need - 1)) == -5
+    assert f(*args(t=32640 + 128, dd=_dims(cap_q=32640))) == -4       # the K4V4 region would overflow
+    assert f(ctypes.byref(d), None, 10, P, P, None, P, P, None, P, need, None) == -1
 
 
 def test_prefill_validation():
