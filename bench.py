@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the hybrid K4V4/FP16 decode-attention path on one MI355X.
 
-A timed *step* is one streaming decode step of the whole hot path:
-hq_append_merge (stage the new token, merge the previous one, quantise the
-token leaving the window) and hq_decode_attn (split-K fused scan + in-kernel
-log-sum-exp merge); every 64th step also runs the vertical-line refresh
-hq_select_vertical over 64 buffered queries (the pages' refresh cadence), so
-its cost is amortised into the step.  hq_quant_pack, which builds the cache
+A timed *step* is one streaming decode step of the whole hot path, one
+hq_decode_step launch: the staging merge of the new token (the token leaving
+the window quantised or promoted, the new one into the ring) and the decode
+attention (split-K fused scan + in-kernel log-sum-exp merge).  Every 64th
+step also runs the vertical-line refresh hq_select_vertical over 64 buffered
+queries (the pages' refresh cadence), so its cost is amortised into the
+step.  The same steps as two launches (hq_append_merge, then hq_decode_attn)
+are timed too (``step_us_unfused``).  hq_quant_pack, which builds the cache
 once after the prefill, is timed on its own and reported beside the step.
 
 The cache footprint of one small-batch layer fits in the 256 MB Infinity
@@ -170,7 +172,9 @@ def main():
     per_unit_fp16 = 512 * (n_vl + min(W, L) + 1)
     footprint = U * (160 * (n_nw - n_vl) + per_unit_fp16)
     R = args.replicas or max(1, math.ceil((1 << 30) / max(footprint, 1)))
-    L_max = L + total_steps + 64 + 8
+    # positions a replica may advance: warm-up, the timed steps, the same
+    # number unfused, the per-row merges and the refresh timing
+    L_max = L + total_steps + args.steps + 64 + 16
     base = H.HybridCache.allocate(B, Hq, Hkv, W, wl.rho, L_max)
     H.hq_quant_pack(base.dims, K, V, L, vl_flag, base)
     torch.cuda.synchronize()
@@ -195,18 +199,25 @@ def main():
     vp = [v_new[j].data_ptr() for j in range(pool)]
     qp = [q_new[j].data_ptr() for j in range(pool)]
 
-    def make_step(stream):
-        """Step function launching on ``stream`` (pointer arguments marshalled once)."""
+    def make_step(stream, fused=True):
+        """Step function launching on ``stream`` (pointer arguments marshalled
+        once): hq_decode_step, or (fused=False) hq_append_merge then
+        hq_decode_attn, which attend the same tokens."""
         dec = [H.bind_decode(dims, caches[r], q_new[0], out, ws[r], lse=lse, stream=stream)
                for r in range(R)]
         mrg = [H.bind_merge(dims, caches[r], stream=stream) for r in range(R)]
+        stp = [H.bind_step(dims, caches[r], q_new[0], out, ws[r], lse=lse, stream=stream)
+               for r in range(R)]
 
         def step(i):
             r = i % R
             t = pos[r]
             j = i % pool
-            mrg[r](t, kp[j], vp[j])
-            dec[r](t, qp[j])
+            if fused:
+                stp[r](t, kp[j], vp[j], qp[j])
+            else:
+                mrg[r](t, kp[j], vp[j])
+                dec[r](t, qp[j])
             pos[r] = t + 1
             if i % REFRESH == REFRESH - 1:
                 H.hq_select_vertical(dims_sel, qbuf, K_rep[(i // REFRESH) % R_sel], L, score,
@@ -252,6 +263,20 @@ def main():
     t_host = time.perf_counter() - t_host
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
+
+    # the same number of steps with the merge and the decode as two launches
+    def timed_steps_unfused(stream):
+        st, _ = make_step(stream, fused=False)
+        for k in range(args.steps):
+            st(args.warmup + args.steps + k)
+    g_unf = capture(timed_steps_unfused)
+    torch.cuda.synchronize()
+    start.record()
+    g_unf.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_unfused = start.elapsed_time(stop) / args.steps
+    del g_unf
 
     # Average decode launch duration: the same decode launches back to back
     # (rotating replicas, current positions), replayed from a graph between
@@ -318,7 +343,9 @@ def main():
     # ---- algorithmic bytes ------------------------------------------------
     n_q_mid = (n_nw - n_vl) + (args.warmup + args.steps // 2) // R
     dec_bytes = U * (160 * n_q_mid + 512 * (n_vl + min(W, L) + 1)) + B * Hq * d * 2 * 2
-    merge_bytes = U * (512 * 5 + 160)      # read staged/evictee/new, write ring/stage, K4 slot
+    # the merge reads the leaving token and writes its K4V4 slot and the new
+    # token's ring slot (the new token's read is in the decode's bytes)
+    merge_bytes = U * (512 + 160 + 512)
     sel_bytes = 2 * U * L * d * 2 + B * Hq * wl.nb * d * 2 * 2 + U * n_nw * 4 * 2 + U * L
     step_bytes = dec_bytes + merge_bytes + sel_bytes / REFRESH
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -364,11 +391,18 @@ def main():
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "step_us": round(ms_step * 1e3, 2), "timed_host_s": round(t_host, 4),
-        "timing": "K steps captured as one HIP graph, replayed once between HIP events",
+        "step_us_unfused": round(ms_step_unfused * 1e3, 2),
+        "timing": "K steps (hq_decode_step, the refresh every 64th) captured as one HIP graph, replayed once between HIP events",
         "rows_us": {"decode": round(dec_avg_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
                     "select": round(sel_ms * 1e3, 2), "pack": round(pack_ms * 1e3, 2)},
+        # the selection's share of the amortised step: hq_select_vertical (rows
+        # a1-a3, two passes over the dense keys) as the step runs it, and the
+        # decode-time refresh over the hybrid cache in its place
         "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step, 4),
-                         "amortized": round(sel_ms / (sel_ms + REFRESH * (ms_step - sel_ms / REFRESH)), 4)},
+                         "amortized": round(sel_ms / (sel_ms + REFRESH * (ms_step - sel_ms / REFRESH)), 4),
+                         "amortized_decode_time_refresh": round(
+                             refresh["us"] * 1e-3 / (refresh["us"] * 1e-3 + REFRESH * (ms_step - sel_ms / REFRESH)),
+                             4)},
         "select_util": sel_util,
         "decode_time_refresh": refresh,
         "b_sweep": sweep,
