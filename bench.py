@@ -603,9 +603,10 @@ def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n
     allocated (only the attention path runs).  Each layer's cache is built by
     hq_select_vertical + hq_quant_pack one sequence at a time, from n_var
     independent bf16-rounded N(0,1) prefixes.  A token step is
-    hq_append_merge + hq_decode_attn in every layer for the whole batch; K
-    steps are captured in one graph and replayed once between HIP events, and
-    a graph of one step's decodes gives the decode share."""
+    hq_decode_step (the staging merge and the decode in one launch) in every
+    layer for the whole batch; K steps are captured in one graph and replayed
+    once between HIP events, and a graph of one step's plain decodes gives
+    the decode share."""
     from hybrid_precision_attention_amd.model_cache import QWEN3_8B as shape, ModelCache, plan_capacity
     d, Hq, Hkv = shape.d, shape.Hq, shape.Hkv
     torch.cuda.empty_cache()
@@ -655,8 +656,8 @@ def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n
 
     def binds(stream):
         dec = [H.bind_decode(c.dims, c, q[l], out, ws, stream=stream) for l, c in enumerate(mc.layers)]
-        mrg = [H.bind_merge(c.dims, c, stream=stream) for c in mc.layers]
-        return dec, mrg
+        stp = [H.bind_step(c.dims, c, q[l], out, ws, stream=stream) for l, c in enumerate(mc.layers)]
+        return dec, stp
 
     dec, _ = binds(torch.cuda.current_stream())
     for f in dec:                   # warm-up: one decode per layer over the packed prefix
@@ -671,11 +672,10 @@ def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n
         return gr
 
     def token_steps(stream):
-        dec_s, mrg_s = binds(stream)
+        _, stp_s = binds(stream)
         for s in range(steps):
             for l in range(shape.layers):
-                mrg_s[l](L + s, k_new[l].data_ptr(), v_new[l].data_ptr())
-                dec_s[l](L + s)
+                stp_s[l](L + s, k_new[l].data_ptr(), v_new[l].data_ptr())
 
     def decode_step(stream):
         dec_s, _ = binds(stream)
@@ -708,7 +708,7 @@ def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n
                 "decode_bytes": dec_bytes,
                 "decode_GBs": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
                 "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_GBS, 4),
-                "timing": "K token steps (merge + decode in every layer) as one graph, replayed once"})
+                "timing": "K token steps (hq_decode_step in every layer) as one graph, replayed once"})
     del g_steps, g_dec, mc, ws, k_new, v_new, q, out
     torch.cuda.empty_cache()
     return res
