@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (active) {
       const int g = item >> 5, c = item & 31;
       const float* base = recs + static_cast<int64_t>(g) * kPart;
-      constexpr int kChunk = 8;
+      constexpr int kChunk = 16;
       for (int s0 = sub; s0 < nsplit; s0 += kChunk * S) {
         float2 ml[kChunk], o01[kChunk], o23[kChunk];
 #pragma unroll
