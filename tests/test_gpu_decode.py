@@ -101,3 +101,59 @@ def test_decode_streaming_steps():
             torch.cuda.synchronize()
             ref, ref_lse = oracle_decode_on(cache, pos, x["q_dec"][t])
             check_decode(out.cpu().numpy(), lse.cpu().numpy(), ref, ref_lse, tag=f"step {t}")
+
+
+def test_step_full_size_llama_layer():
+    """hq_decode_step in the benchmark's launch configuration (B=1, 32/8
+    heads, L=32768): two steps equal, bit for bit, hq_append_merge +
+    hq_decode_attn on a copy of the cache, which the oracle checks."""
+    wl = workload("llama31_8b")
+    T = 2
+    x, c1 = _setup(wl, T=T)
+    c2 = c1.clone()
+    ws1 = H.workspace(c1.dims, H.HQ_OP_DECODE, wl.L + T)
+    ws2 = H.workspace(c2.dims, H.HQ_OP_DECODE, wl.L + T)
+    o1 = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device="cuda")
+    o2 = torch.empty_like(o1)
+    l1 = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
+    l2 = torch.empty_like(l1)
+    for s in range(T):
+        t = wl.L + s
+        k, v, q = dev(x["k_dec"][s]), dev(x["v_dec"][s]), dev(x["q_dec"][s])
+        H.hq_decode_step(c1.dims, c1, t, k, v, q, o1, ws1, lse=l1)
+        H.hq_append_merge(c2.dims, c2, t, k, v)
+        H.hq_decode_attn(c2.dims, c2, t, q, o2, ws2, lse=l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"step {s}"
+        assert torch.equal(l1, l2), f"step {s}"
+        ref, ref_lse = oracle_decode_on(c2, t, x["q_dec"][s])
+        check_decode(o2.cpu().numpy(), l2.cpu().numpy(), ref, ref_lse, tag=f"step {s}")
+
+
+def test_decode_full_size_qwen3_8b_batch32_sampled():
+    """The batch sweep's largest launch: Qwen3-8B-shaped layer, B=32,
+    L=32768 (256 units, the split plan of that size).  Four seeded sequences
+    are tiled over the batch (units are independent); the oracle checks
+    sampled units, one from each tile group and head."""
+    wl = workload("qwen3_8b")
+    assert wl.B == 32 and wl.L == 32768
+    xs = batch(wl, steps=1, seqs=[0, 1, 2, 3])
+    _, _, f4 = O.select_vertical(xs["K"], xs["qbuf"], wl.L, wl.W, wl.rho)
+    rep = wl.B // 4
+    x = {"K": np.concatenate([xs["K"]] * rep), "V": np.concatenate([xs["V"]] * rep),
+         "qbuf": np.concatenate([xs["qbuf"]] * rep)}
+    flags = np.concatenate([f4] * rep)
+    cache = gpu_pack(x, wl.L, wl.W, wl.rho, flags, L_max=wl.L + 1)
+    del x
+    k_new = np.concatenate([xs["k_dec"][0]] * rep)
+    v_new = np.concatenate([xs["v_dec"][0]] * rep)
+    q = np.concatenate([xs["q_dec"][0]] * rep)
+    H.hq_append_merge(cache.dims, cache, wl.L, dev(k_new), dev(v_new))
+    out, lse = gpu_decode(cache, wl.L, q)
+    units = [(0, 0), (5, 3), (18, 6), (31, 7)]
+    ref, ref_lse = oracle_decode_on(cache, wl.L, q, units=units)
+    G = wl.G
+    # the output bound applies to the checked output as a whole (the sampled
+    # units together), as it applies to a whole call's output elsewhere
+    pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
+    check_decode(pick(out), pick(lse), pick(ref), pick(ref_lse), tag="sampled units")
