@@ -60,6 +60,8 @@ lib.hq_decode_attn_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq
                                       ctypes.c_int32, _p, _p, _p, _p, ctypes.c_size_t, _p]
 lib.hq_decode_step.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32, _p, _p,
                                _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.hq_decode_step_ragged.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), _p, ctypes.c_int32,
+                                      _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
 lib.hq_quant_int8.argtypes = [_p, ctypes.c_int64, _p, _p, _p]
 lib.hq_prefill_attn.argtypes = [ctypes.POINTER(hq_dims), _p, _p, _p, ctypes.c_int32, _p, _p, _p, _p,
                                 ctypes.c_size_t, _p]
@@ -70,7 +72,8 @@ lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
-           "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step"):
+           "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step",
+           "hq_decode_step_ragged"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -277,6 +280,18 @@ def hq_decode_step(dims, cache: HybridCache, t, k_new, v_new, q, out, ws, lse=No
                             _ptr(lse, torch.float32, "lse"), _ptr(ws, None, "ws"),
                             ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_step")
+
+
+def hq_decode_step_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new, q, out, ws, lse=None,
+                          evict_is_vl=None, stream=None):
+    """t_seq: [B] int32 device tensor of per-sequence positions (<= t_max)."""
+    cs = cache.struct()
+    st = lib.hq_decode_step_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(t_seq, torch.int32, "t_seq"), t_max,
+                                   _ptr(k_new, torch.float16, "k_new"), _ptr(v_new, torch.float16, "v_new"),
+                                   _ptr(evict_is_vl, torch.uint8, "evict_is_vl"), _ptr(q, torch.float16, "q"),
+                                   _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
+                                   _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "hq_decode_step_ragged")
 
 
 def bind_step(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):

@@ -1156,7 +1156,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
-  if (a.k_new && wave == 0) step_merge<kKB, kVB>(a, u, a.L_max, lane);
+  if (a.k_new && wave == 0) {
+    // the new token's position: its sequence's own in a ragged batch
+    const int t = a.L_seq ? min(max(a.L_seq[b], 0), a.L_max) : a.L_max;
+    step_merge<kKB, kVB>(a, u, t, lane);
+  }
   if (tid == 0) a.counters[u] = 0;
 }
 

@@ -124,7 +124,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 6; }
+int hq_abi_version(void) { return 7; }
 
 const char* hq_status_string(int status) {
   switch (status) {
@@ -303,6 +303,28 @@ int hq_decode_step(const hq_dims* dims, const hq_cache* cache, int32_t t, const 
   if (!aligned16(ws)) return HQ_ERR_ALIGN;
   const DecodePlan plan = plan_decode(*dims, t);
   if (launch_decode(*dims, *cache, t, plan, q, out, lse_or_null, ws, stream, nullptr, k_new, v_new,
+                    evict_is_vl_or_null) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_decode_step_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* t_seq,
+                          int32_t t_max, const uint16_t* k_new, const uint16_t* v_new,
+                          const uint8_t* evict_is_vl_or_null, const uint16_t* q, uint16_t* out,
+                          float* lse_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (t_max < 0 || !t_seq || !k_new || !v_new || !q || !out) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(t_seq) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(out))
+    return HQ_ERR_ALIGN;
+  if (evict_is_vl_or_null && !aligned16(evict_is_vl_or_null)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  if (static_cast<int64_t>(dims->cap_q) < static_cast<int64_t>(t_max) + 1 - dims->W) return HQ_ERR_CAPACITY;
+  if (!ws || ws_bytes < decode_ws_bytes(*dims, t_max)) return HQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return HQ_ERR_ALIGN;
+  const DecodePlan plan = plan_decode(*dims, t_max);
+  if (launch_decode(*dims, *cache, t_max, plan, q, out, lse_or_null, ws, stream, t_seq, k_new, v_new,
                     evict_is_vl_or_null) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;

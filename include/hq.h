@@ -299,6 +299,17 @@ int hq_decode_step(const hq_dims* dims, const hq_cache* cache, int32_t t, const 
                    uint16_t* out, float* lse_or_null, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * hq_decode_step_ragged -- hq_decode_step with each sequence at its own
+ * position: t_seq [B] int32 device array (clamped to [0, t_max]), t_max a
+ * host bound on every entry (capacity check, split plan, workspace as for
+ * hq_decode_attn at t_max).  Same passages, arguments and errors otherwise.
+ */
+int hq_decode_step_ragged(const hq_dims* dims, const hq_cache* cache, const int32_t* t_seq,
+                          int32_t t_max, const uint16_t* k_new, const uint16_t* v_new,
+                          const uint8_t* evict_is_vl_or_null, const uint16_t* q, uint16_t* out,
+                          float* lse_or_null, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * hq_quant_int8 -- symmetric INT8 of 128-element fp16 rows, the low-bit
  * operand of the prefill's QK product (agihunt digest on HyQuant, method
  * paragraph, prefill sentences; HyQuant README, Overview item 2, and the ops

@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     names = _declared()
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
             "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
-            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step",
+            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step", "hq_decode_step_ragged",
             "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
@@ -33,7 +33,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 6
+    assert H.lib.hq_abi_version() == 7
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -185,6 +185,15 @@ def test_step_validation():
     assert f(*args(wsb=need - 1)) == -5
     assert f(*args(t=32640 + 128, dd=_dims(cap_q=32640))) == -4       # the K4V4 region would overflow
     assert f(ctypes.byref(d), None, 10, P, P, None, P, P, None, P, need, None) == -1
+    g = H.lib.hq_decode_step_ragged
+    rargs = lambda ts=P, tmax=1000, k=P, wsb=need, dd=d: (
+        ctypes.byref(dd), ctypes.byref(c), ts, tmax, k, P, None, P, P, None, P, wsb, None)
+    assert g(*rargs(ts=None)) == -1
+    assert g(*rargs(tmax=-1)) == -1
+    assert g(*rargs(ts=P + 4)) == -3
+    assert g(*rargs(k=P + 2)) == -3
+    assert g(*rargs(wsb=need - 1)) == -5
+    assert g(*rargs(tmax=32640 + 128, dd=_dims(cap_q=32640))) == -4
 
 
 def test_prefill_validation():

@@ -96,3 +96,51 @@ def test_ragged_equals_plain_for_equal_lengths():
     for k in c1.t:
         if c1.t[k] is not None:
             assert torch.equal(c1.t[k], c2.t[k]), k
+
+
+@pytest.mark.parametrize("name,over,lengths", [
+    ("tiny", {"B": 3, "L": 1500}, [1500, 700, 1100]),
+    ("tiny", {"B": 4, "L": 1200}, [1200, 60, 1, 300]),
+    ("qwen3_32b", {"B": 2, "L": 1500}, [1500, 1000]),
+])
+def test_ragged_step(name, over, lengths):
+    """hq_decode_step_ragged: every sequence merges and attends at its own
+    position in one launch; outputs against the oracle's merge + decode per
+    sequence, then one plain ragged merge on both sides and the caches
+    compared bit for bit."""
+    wl = workload(name, **over)
+    print(f"case {name} {over} {lengths} (step)", flush=True)
+    T = 4
+    x = batch(wl, steps=T + 1)
+    cache, refs = _build(wl, x, lengths, T + 1)
+    B, Hkv, G = wl.B, wl.Hkv, wl.G
+    L_max = max(lengths)
+    ws = H.workspace(cache.dims, H.HQ_OP_DECODE, L_max + T + 1)
+    out = torch.empty((B, wl.Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((B, wl.Hq), dtype=torch.float32, device="cuda")
+    for s in range(T + 1):
+        t = np.array([Lb + s for Lb in lengths], np.int32)
+        if s < T:
+            H.hq_decode_step_ragged(cache.dims, cache, dev(t), int(t.max()), dev(x["k_dec"][s]),
+                                    dev(x["v_dec"][s]), dev(x["q_dec"][s]), out, ws, lse=lse)
+        else:
+            H.hq_append_merge_ragged(cache.dims, cache, dev(t), int(t.max()), dev(x["k_dec"][s]),
+                                     dev(x["v_dec"][s]))
+        for b in range(B):
+            for g in range(Hkv):
+                O.append_merge_unit(refs[b][g], int(t[b]), x["k_dec"][s, b, g], x["v_dec"][s, b, g])
+        if s == T:
+            break
+        torch.cuda.synchronize()
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+        ref = np.zeros((B, wl.Hq, 128))
+        ref_l = np.zeros((B, wl.Hq))
+        for b in range(B):
+            for g in range(Hkv):
+                ref[b, g * G:(g + 1) * G], ref_l[b, g * G:(g + 1) * G] = O.decode_fused(
+                    refs[b][g], x["q_dec"][s][b, g * G:(g + 1) * G], int(t[b]))
+        check_decode(o, l, ref, ref_l, tag=f"step {s}")
+    torch.cuda.synchronize()
+    for b in range(B):
+        for g in range(Hkv):
+            assert_unit_equal(unit_from_gpu(cache, b, g), refs[b][g], lengths[b] + T, wl.W, tag=f"b{b} g{g}")
