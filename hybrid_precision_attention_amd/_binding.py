@@ -25,6 +25,7 @@ HQ_OK = 0
 HQ_OP_SELECT = 1
 HQ_OP_DECODE = 2
 HQ_OP_PREFILL = 3
+PAGE = 32           # K4V4 slots per block of a paged cache
 D = 128
 
 
@@ -38,7 +39,7 @@ class hq_dims(ctypes.Structure):
 class hq_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "kq", "vq", "kq_meta", "vq_meta", "q_pos", "kvl", "vvl", "vl_pos",
-        "kwin", "vwin", "kstg", "vstg", "n_q", "n_vl", "n_stg")]
+        "kwin", "vwin", "kstg", "vstg", "n_q", "n_vl", "n_stg", "k4_pages")]
 
 
 _p = ctypes.c_void_p
@@ -152,8 +153,76 @@ class HybridCache:
             "n_q": torch.zeros((B, Hkv), dtype=i32, device=dev),
             "n_vl": torch.zeros((B, Hkv), dtype=i32, device=dev),
             "n_stg": torch.zeros((B, Hkv), dtype=i32, device=dev),
+            "k4_pages": None,
         }
         return HybridCache(dims, t)
+
+    @staticmethod
+    def allocate_paged(B, Hq, Hkv, W, rho, L_max, extra_vl=0, cap_stg=1, device="cuda", k_bits=4, v_bits=4,
+                       seq_L_max=None, shuffle_seed=None):
+        """Paged K4V4 slots: a pool of 32-slot blocks shared by all units and
+        a page table per unit.  Sequence b's units get blocks only for the
+        slots their own maximum length seq_L_max[b] (default L_max) can
+        reach; the other table entries point at one spare block at the end
+        of the pool, so that a stray write stays in bounds.  With
+        shuffle_seed the blocks are handed out in a seeded random order (the
+        layout is then far from contiguous; results are unchanged)."""
+        n_nw = max(0, L_max - W)
+        npb = max(1, -(-n_nw // PAGE))
+        cap_q = npb * PAGE
+        cap_vl = max(1, n_vertical(rho, n_nw) + extra_vl)
+        dims = make_dims(B, Hq, Hkv, W, rho, cap_q, cap_vl, max(1, cap_stg), k_bits=k_bits, v_bits=v_bits)
+        lens = list(seq_L_max) if seq_L_max is not None else [L_max] * B
+        need = [-(-max(0, Lb - W) // PAGE) for Lb in lens]
+        total = sum(need) * Hkv
+        order = list(range(total))
+        if shuffle_seed is not None:
+            import random
+            random.Random(shuffle_seed).shuffle(order)
+        spare = total                                  # the overflow block
+        pages = torch.full((B, Hkv, npb), spare, dtype=torch.int32)
+        k = 0
+        for b in range(B):
+            for g in range(Hkv):
+                for i in range(need[b]):
+                    pages[b, g, i] = order[k]
+                    k += 1
+        P = total + 1
+        dev = torch.device(device)
+        u8, f16, i32 = torch.uint8, torch.float16, torch.int32
+        t = {
+            "kq": torch.zeros((P * PAGE, D * k_bits // 8), dtype=u8, device=dev),
+            "vq": torch.zeros((P * PAGE, D * v_bits // 8), dtype=u8, device=dev),
+            "kq_meta": torch.zeros((P * PAGE, D // 32, 2), dtype=f16, device=dev),
+            "vq_meta": torch.zeros((P * PAGE, D // 32, 2), dtype=f16, device=dev),
+            "q_pos": torch.zeros((P * PAGE,), dtype=i32, device=dev),
+            "kvl": torch.zeros((B, Hkv, cap_vl, D), dtype=f16, device=dev),
+            "vvl": torch.zeros((B, Hkv, cap_vl, D), dtype=f16, device=dev),
+            "vl_pos": torch.zeros((B, Hkv, cap_vl), dtype=i32, device=dev),
+            "kwin": torch.zeros((B, Hkv, W, D), dtype=f16, device=dev) if W else None,
+            "vwin": torch.zeros((B, Hkv, W, D), dtype=f16, device=dev) if W else None,
+            "kstg": torch.zeros((B, Hkv, dims.cap_stg, D), dtype=f16, device=dev),
+            "vstg": torch.zeros((B, Hkv, dims.cap_stg, D), dtype=f16, device=dev),
+            "n_q": torch.zeros((B, Hkv), dtype=i32, device=dev),
+            "n_vl": torch.zeros((B, Hkv), dtype=i32, device=dev),
+            "n_stg": torch.zeros((B, Hkv), dtype=i32, device=dev),
+            "k4_pages": pages.to(dev),
+        }
+        return HybridCache(dims, t)
+
+    @property
+    def paged(self) -> bool:
+        return self.t.get("k4_pages") is not None
+
+    def k4_unit(self, b: int, g: int):
+        """The K4V4 slots of unit (b, g) in slot order (through the page
+        table when paged): kq, vq, kq_meta, vq_meta, q_pos."""
+        names = ("kq", "vq", "kq_meta", "vq_meta", "q_pos")
+        if not self.paged:
+            return tuple(self.t[n][b, g] for n in names)
+        pages = self.t["k4_pages"][b, g].long()
+        rows = (pages[:, None] * PAGE + torch.arange(PAGE, device=pages.device)[None, :]).reshape(-1)
+        return tuple(self.t[n][rows] for n in names)
 
     def struct(self) -> hq_cache:
         """The ``hq_cache`` of these buffers (built once: tensors never move)."""
@@ -169,7 +238,9 @@ class HybridCache:
         building the caches of a ragged batch one sequence at a time)."""
         d = hq_dims.from_buffer_copy(self.dims)
         d.B = 1
-        return HybridCache(d, {k: (v[b:b + 1] if v is not None else None) for k, v in self.t.items()})
+        pools = {"kq", "vq", "kq_meta", "vq_meta", "q_pos"} if self.paged else set()
+        return HybridCache(d, {k: (v if k in pools else v[b:b + 1]) if v is not None else None
+                               for k, v in self.t.items()})
 
     def nbytes(self) -> int:
         return sum(v.numel() * v.element_size() for v in self.t.values() if v is not None)

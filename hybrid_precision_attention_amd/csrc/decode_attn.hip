@@ -111,14 +111,14 @@ __device__ __forceinline__ void step_merge(const DecodeArgs& a, int64_t u, int t
       const int bits = kv ? kVB : kKB;
       uint32_t meta;
       const uint64_t codes = quant_quad8(evv, bits, &meta);
+      const int64_t slot = k4_slot(a.c.k4_pages, a.cap_q, u, nq);
       if (mover) {
-        const int64_t slot = u * a.cap_q + nq;
         store_codes8((kv ? a.c.vq : a.c.kq) + slot * (kD * bits / 8) + bits * part, codes, bits);
         if ((part & 3) == 0)
           reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta)[slot * kMetaWords + (part >> 2)] = meta;
       }
       if (lane == 0) {
-        a.c.q_pos[u * a.cap_q + nq] = ev;
+        a.c.q_pos[slot] = ev;
         a.c.n_q[u] = nq + 1;
       }
     }
@@ -750,7 +750,7 @@ __device__ __forceinline__ void st4_agent(float* p, float4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
 }
 
-template <bool kG4, int kKB, int kVB>
+template <bool kG4, int kKB, int kVB, bool kPaged>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // K4V4 takes the grouped-code paths; other widths dequantise each block
   // into an LDS tile and use the FP16-block code
@@ -837,6 +837,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
       const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
       const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+      // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
+      // block when the slots are paged (offsets then relative to the block,
+      // the tail clamp inside it)
+      auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
+                          const uint32_t*& vmb, int& tb, int& nqb) {
+        if constexpr (kPaged) {
+          const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
+          kb = a.c.kq + fs * (16 * kKB);
+          vb = a.c.vq + fs * (16 * kVB);
+          kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
+          vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
+          tb = 0;
+          nqb = nq - bi * kBlk;
+        } else {
+          kb = kq;
+          vb = vq;
+          kmb = kmeta;
+          vmb = vmeta;
+          tb = bi * kBlk;
+          nqb = nq;
+        }
+      };
+      auto ld_k4 = [&](K4Raw& r, int bi) {
+        const uint8_t *kb, *vb;
+        const uint32_t *kmb, *vmb;
+        int tb, nqb;
+        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+        load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
+      };
+      auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
+        const uint8_t *kb, *vb;
+        const uint32_t *kmb, *vmb;
+        int tb, nqb;
+        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+        load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
+      };
       const int last = nblk_q - 1;
       int blk = gw;
       if constexpr (kK4V4) {
@@ -844,27 +880,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const Masks km = make_masks();
         K4Raw ra, rb;
         K4Mid x;
-        load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+        ld_k4(ra, blk);
         for (; blk < nblk_q; blk += 2 * nwaves) {
-          load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+          ld_k4(rb, min(blk + nwaves, last));
           k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
           k4_phase_b(st, x, km, c2);
           if (blk + nwaves >= nblk_q) break;
-          load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+          ld_k4(ra, min(blk + 2 * nwaves, last));
           k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + nwaves) * kBlk, nq, lane, n, j);
           k4_phase_b(st, x, km, c2);
         }
       } else {
         DqTile& tl = s_lds.stage[wave];
         GenRaw<kKB, kVB> ra, rb;
-        load_gen(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane);
+        ld_gen(ra, blk);
         for (; blk < nblk_q; blk += 2 * nwaves) {
           uint4 kr[8], vr[8];
-          load_gen(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane);
+          ld_gen(rb, min(blk + nwaves, last));
           gen_operands(kr, vr, ra, tl, lane, n, j);
           f16_compute_g(st, qf, kr, vr, nq - blk * kBlk, j, c2);
           if (blk + nwaves >= nblk_q) break;
-          load_gen(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane);
+          ld_gen(ra, min(blk + 2 * nwaves, last));
           gen_operands(kr, vr, rb, tl, lane, n, j);
           f16_compute_g(st, qf, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
         }
@@ -941,6 +977,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
       const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
       const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+      // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
+      // block when the slots are paged (offsets then relative to the block,
+      // the tail clamp inside it)
+      auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
+                          const uint32_t*& vmb, int& tb, int& nqb) {
+        if constexpr (kPaged) {
+          const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
+          kb = a.c.kq + fs * (16 * kKB);
+          vb = a.c.vq + fs * (16 * kVB);
+          kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
+          vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
+          tb = 0;
+          nqb = nq - bi * kBlk;
+        } else {
+          kb = kq;
+          vb = vq;
+          kmb = kmeta;
+          vmb = vmeta;
+          tb = bi * kBlk;
+          nqb = nq;
+        }
+      };
+      auto ld_k4 = [&](K4Raw& r, int bi) {
+        const uint8_t *kb, *vb;
+        const uint32_t *kmb, *vmb;
+        int tb, nqb;
+        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+        load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
+      };
+      auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
+        const uint8_t *kb, *vb;
+        const uint32_t *kmb, *vmb;
+        int tb, nqb;
+        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+        load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
+      };
       // one block of prefetch in two alternating buffers (no register copies);
       // the loads are unconditional (past the end they re-read the last block)
       // so that the wait before a compute only covers its own loads
@@ -956,12 +1028,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         K4Stage& sg = s_lds.stage[wave];
         const Masks km = make_masks();
         K4Raw ra, rb;
-        load_k4(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane, n, j);
+        ld_k4(ra, blk);
         for (; blk < nblk_q; blk += 2 * nwaves) {
-          load_k4(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane, n, j);
+          ld_k4(rb, min(blk + nwaves, last));
           compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
           if (blk + nwaves >= nblk_q) break;
-          load_k4(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane, n, j);
+          ld_k4(ra, min(blk + 2 * nwaves, last));
           compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
         }
       } else {
@@ -970,14 +1042,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
         DqTile& tl = s_lds.stage[wave];
         GenRaw<kKB, kVB> ra, rb;
-        load_gen(ra, kq, kmeta, vq, vmeta, blk * kBlk, nq, lane);
+        ld_gen(ra, blk);
         for (; blk < nblk_q; blk += 2 * nwaves) {
           uint4 kr[8], vr[8];
-          load_gen(rb, kq, kmeta, vq, vmeta, min(blk + nwaves, last) * kBlk, nq, lane);
+          ld_gen(rb, min(blk + nwaves, last));
           gen_operands(kr, vr, ra, tl, lane, n, j);
           f16_compute(st, qn, kr, vr, nq - blk * kBlk, j, c2);
           if (blk + nwaves >= nblk_q) break;
-          load_gen(ra, kq, kmeta, vq, vmeta, min(blk + 2 * nwaves, last) * kBlk, nq, lane);
+          ld_gen(ra, min(blk + 2 * nwaves, last));
           gen_operands(kr, vr, rb, tl, lane, n, j);
           f16_compute(st, qn, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
         }
@@ -1195,9 +1267,15 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   (void)L;
   dim3 grid(plan.nsplit, d.B * d.Hkv);
   const int kb = kv_bits(d.k_bits), vb = kv_bits(d.v_bits);
+  // paged K4V4 slots are a template parameter: the contiguous instances
+  // keep their block loads free of the page-table branch
   auto launch = [&](auto g4, auto kbc, auto vbc) {
-    hipLaunchKernelGGL((decode_kernel<decltype(g4)::value, decltype(kbc)::value, decltype(vbc)::value>),
-                       grid, dim3(kThreads), 0, s, a);
+    if (c.k4_pages)
+      hipLaunchKernelGGL((decode_kernel<decltype(g4)::value, decltype(kbc)::value, decltype(vbc)::value, true>),
+                         grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<decltype(g4)::value, decltype(kbc)::value, decltype(vbc)::value, false>),
+                         grid, dim3(kThreads), 0, s, a);
   };
   auto by_v = [&](auto g4, auto kbc) {
     if (vb == 2) launch(g4, kbc, std::integral_constant<int, 2>{});

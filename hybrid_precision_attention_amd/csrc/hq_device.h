@@ -152,6 +152,15 @@ __device__ __forceinline__ void store_codes8(uint8_t* dst, uint64_t codes, int b
   else *reinterpret_cast<uint32_t*>(dst) = static_cast<uint32_t>(codes);
 }
 
+// Flat slot index of K4V4 slot s of unit u: u * cap_q + s, or through the
+// unit's page table (32-slot blocks of a shared pool) when the cache is paged.
+constexpr int kPageSlots = 32;
+__device__ __forceinline__ int64_t k4_slot(const int32_t* pages, int32_t cap_q, int64_t u, int s) {
+  if (!pages) return u * cap_q + s;
+  return static_cast<int64_t>(pages[u * (cap_q / kPageSlots) + s / kPageSlots]) * kPageSlots +
+         (s & (kPageSlots - 1));
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

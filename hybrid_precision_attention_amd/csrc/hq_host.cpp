@@ -55,9 +55,11 @@ int check_cache(const hq_dims& d, const hq_cache* c) {
   const void* rows[] = {c->kq, c->vq, c->kq_meta, c->vq_meta, c->kvl, c->vvl, c->kstg, c->vstg};
   for (const void* p : rows)
     if (!aligned16(p)) return HQ_ERR_ALIGN;
-  const void* words[] = {c->q_pos, c->vl_pos, c->n_q, c->n_vl, c->n_stg};
+  const void* words[] = {c->q_pos, c->vl_pos, c->n_q, c->n_vl, c->n_stg, c->k4_pages};
   for (const void* p : words)
     if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return HQ_ERR_ALIGN;
+  // paged K4V4 slots come in whole 32-slot blocks
+  if (c->k4_pages && d.cap_q % 32 != 0) return HQ_ERR_ARG;
   if (d.W > 0 && (!aligned16(c->kwin) || !aligned16(c->vwin))) return HQ_ERR_ALIGN;
   return HQ_OK;
 }
@@ -124,7 +126,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 7; }
+int hq_abi_version(void) { return 8; }
 
 const char* hq_status_string(int status) {
   switch (status) {

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
     } else {
       kind = 1;
       slot = p - vl_before;
-      a.c.q_pos[u * a.cap_q + slot] = p;
+      a.c.q_pos[k4_slot(a.c.k4_pages, a.cap_q, u, slot)] = p;
     }
   }
   s_kind[tid] = kind;
@@ -114,9 +114,10 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
     }
     if (knd == 1) {
       const int bits = kv ? a.v_bits : a.k_bits;
-      uint8_t* dst = (kv ? a.c.vq : a.c.kq) + (u * a.cap_q + sl) * (kD * bits / 8) + g * (4 * bits);
+      const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, sl);
+      uint8_t* dst = (kv ? a.c.vq : a.c.kq) + fs * (kD * bits / 8) + g * (4 * bits);
       uint32_t* md = reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta);
-      quant_store_group_bits(bits, x, dst, &md[(u * a.cap_q + sl) * kMetaWords + g]);
+      quant_store_group_bits(bits, x, dst, &md[fs * kMetaWords + g]);
     } else {
       uint16_t* dst;
       if (knd == 2) dst = (kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + sl) * kD + g * kGroup;
@@ -192,14 +193,14 @@ __global__ __launch_bounds__(64) void append_merge_kernel(MergeArgs a) {
         const int bits = kv ? a.v_bits : a.k_bits;
         uint32_t meta;
         const uint64_t codes = quant_quad8(evv, bits, &meta);
+        const int64_t slot = k4_slot(a.c.k4_pages, a.cap_q, u, nq);
         if (mover) {
-          const int64_t slot = u * a.cap_q + nq;
           store_codes8((kv ? a.c.vq : a.c.kq) + slot * (kD * bits / 8) + bits * part, codes, bits);
           if ((part & 3) == 0)
             reinterpret_cast<uint32_t*>(kv ? a.c.vq_meta : a.c.kq_meta)[slot * kMetaWords + (part >> 2)] = meta;
         }
         if (lane == 0) {
-          a.c.q_pos[u * a.cap_q + nq] = ev;
+          a.c.q_pos[slot] = ev;
           a.c.n_q[u] = nq + 1;
         }
       }

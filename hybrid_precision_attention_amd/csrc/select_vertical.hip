@@ -605,9 +605,12 @@ __device__ __forceinline__ void load_group_codes(uint32_t w[kKB], const uint8_t*
 
 template <int kKB>
 __device__ __forceinline__ void load_k4raw(KRaw<kKB>& r, const SelArgs& a, int64_t u, int k0, int n, int j) {
+  // k0 is a multiple of 64: entries x = 0, 1 share one 32-slot block, x = 2, 3 the next
+  const int64_t s01 = k4_slot(a.c.k4_pages, a.cap_q, u, k0 + n);
+  const int64_t s23 = k4_slot(a.c.k4_pages, a.cap_q, u, k0 + 32 + n);
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int64_t sl = u * a.cap_q + k0 + 16 * x + n;
+    const int64_t sl = (x < 2 ? s01 : s23) + 16 * (x & 1);
     load_group_codes<kKB>(r.codes[x], a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
     r.meta[x] = reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j];
     r.pos[x] = a.c.q_pos[sl];
@@ -671,7 +674,7 @@ __device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelAr
   for (int x = 0; x < 4; ++x) {
     const int ki = k0 + 16 * x + n;
     if (ki < h.nq) {
-      const int64_t sl = u * a.cap_q + ki;
+      const int64_t sl = k4_slot(a.c.k4_pages, a.cap_q, u, ki);
       uint32_t w[kKB];
       load_group_codes<kKB>(w, a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
       dequant_group<kKB>(kr[x], w, reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j]);

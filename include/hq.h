@@ -94,7 +94,18 @@ typedef struct {
  *   n_q, n_vl,    [B][Hkv]                 device counters: tokens held in the
  *   n_stg                                  K4V4, vertical-line and staging
  *                                          regions of each unit
- * kwin/vwin may be NULL when W == 0. */
+ *   k4_pages      [B][Hkv][cap_q/32] or NULL: paged K4V4 slots (below)
+ * kwin/vwin may be NULL when W == 0.
+ *
+ * Paged K4V4 slots: with k4_pages set, kq, vq, kq_meta, vq_meta and q_pos are
+ * pools of 32-slot blocks shared by all units ([P*32][...] with the same
+ * per-slot rows), and slot s of unit u lives in pool block
+ * k4_pages[u][s / 32], row s mod 32.  cap_q must then be a multiple of 32.
+ * The caller allocates the pool and assigns the blocks (each block to at
+ * most one (unit, index) pair, every index below P); a sequence's units
+ * need blocks only for the slots their positions can reach, so a ragged
+ * batch does not reserve every sequence's K4V4 region for the longest
+ * one.  Every entry point reads and writes the slots through the table. */
 typedef struct {
   uint8_t *kq, *vq;
   uint16_t *kq_meta, *vq_meta;
@@ -104,6 +115,7 @@ typedef struct {
   uint16_t *kwin, *vwin;
   uint16_t *kstg, *vstg;
   int32_t *n_q, *n_vl, *n_stg;
+  int32_t *k4_pages;
 } hq_cache;
 
 /* Operation ids for hq_workspace_bytes. */

@@ -32,7 +32,10 @@ def gpu_pack(x, L, W, rho, flags, L_max=None, extra_vl=0, k_bits=4, v_bits=4):
 
 def unit_from_gpu(cache, b, g):
     """One unit of the GPU cache as an oracle cache dict (valid rows only)."""
-    t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()}
+    pools = ("kq", "vq", "kq_meta", "vq_meta", "q_pos")
+    t = {k: (v[b, g].cpu().numpy() if v is not None else None) for k, v in cache.t.items()
+         if k not in pools and k != "k4_pages"}
+    t.update({k: v.cpu().numpy() for k, v in zip(pools, cache.k4_unit(b, g))})
     n_q, n_vl, n_stg = int(t["n_q"]), int(t["n_vl"]), int(t["n_stg"])
     W = cache.dims.W
     c = O.empty_unit_cache(128, W, cache.dims.k_bits, cache.dims.v_bits)

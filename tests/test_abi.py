@@ -33,7 +33,7 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 7
+    assert H.lib.hq_abi_version() == 8
 
 
 def _fake_cache(W=128, base=1 << 20):
@@ -42,6 +42,7 @@ def _fake_cache(W=128, base=1 << 20):
     c = B.hq_cache()
     for i, (n, _) in enumerate(B.hq_cache._fields_):
         setattr(c, n, base + 4096 * i)
+    c.k4_pages = None
     if W == 0:
         c.kwin = None
         c.vwin = None
@@ -89,6 +90,14 @@ def test_pack_validation():
     c.q_pos = (1 << 20) + 2                             # positions need 4 bytes
     assert _pack(d, cache=c) == -3
     assert _pack(_dims(W=128), cache=_fake_cache(W=0)) == -1   # W > 0 needs a ring
+
+
+def test_paged_cache_validation():
+    c = _fake_cache()
+    c.k4_pages = (1 << 20) + 4096 * 40
+    assert _pack(_dims(cap_q=32640 - 16), cache=c) == -1         # paged slots come in 32-slot blocks
+    c.k4_pages = (1 << 20) + 4096 * 40 + 2
+    assert _pack(_dims(cap_q=32640), cache=c) == -3              # the table needs 4-byte alignment
 
 
 def test_merge_validation():
