@@ -131,7 +131,8 @@ def main():
     from hq_inputs import workload, batch
 
     if args.capacity_only:
-        print(json.dumps({"capacity": capacity_run(H, torch)}))
+        print(json.dumps({"capacity": capacity_run(H, torch),
+                          "capacity_ragged_paged": capacity_ragged_run(H, torch)}))
         return
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_timing(H, torch)}))
@@ -377,6 +378,7 @@ def main():
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
     prefill = None if args.no_prefill else prefill_timing(H, torch)
     capacity = None if args.no_capacity else capacity_run(H, torch)
+    capacity_ragged = None if args.no_capacity else capacity_ragged_run(H, torch)
 
     rec = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -410,6 +412,7 @@ def main():
         "read_ceiling": ceiling,
         "prefill": prefill,
         "capacity": capacity,
+        "capacity_ragged_paged": capacity_ragged,
         "replicas": R, "input_gen_s": round(gen_s, 1),
     }
     if ceiling:
@@ -710,6 +713,109 @@ def capacity_run(H, torch, steps=4, L=32768, W=128, rho=0.05, reserve=8 << 30, n
                 "decode_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_GBS, 4),
                 "timing": "K token steps (hq_decode_step in every layer) as one graph, replayed once"})
     del g_steps, g_dec, mc, ws, k_new, v_new, q, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def capacity_ragged_run(H, torch, steps=4, L_cap=32768, W=128, rho=0.05, reserve=8 << 30, seed=31):
+    """The capacity run's model (Qwen3-8B-shaped attention, 36 layers) with
+    paged K4V4 slots and a ragged batch: sequence lengths drawn (seeded) from
+    {4096, 8192, ..., 32768}, sequences added while their paged caches fit
+    the same HBM budget as the uniform run (each owns K4V4 blocks only for
+    its own length).  Caches built by select + pack per sequence; a token
+    step is hq_decode_step_ragged in every layer, K steps from one graph."""
+    from hybrid_precision_attention_amd.model_cache import (QWEN3_8B as shape, paged_layer_bytes_per_sequence,
+                                                            plan_capacity)
+    d, Hq, Hkv = shape.d, shape.Hq, shape.Hkv
+    torch.cuda.empty_cache()
+    free, total = torch.cuda.mem_get_info()
+    budget = min(total - shape.weight_bytes - reserve, free - (6 << 30))
+    L_alloc = L_cap + steps + 1
+    choices = list(range(4096, L_cap + 1, 4096))
+    rng = np.random.default_rng(seed)
+    lens, used = [], 0
+    while True:
+        Lb = int(rng.choice(choices))
+        need = shape.layers * paged_layer_bytes_per_sequence(shape, Lb + steps + 1, L_alloc, W, rho,
+                                                             extra_vl=steps + 1)
+        if used + need + shape.layers * (1 << 20) > budget:
+            break
+        lens.append(Lb)
+        used += need
+    B = len(lens)
+    uniform = plan_capacity(shape, L_alloc, W, rho, total, reserve_bytes=reserve)["max_batch_hybrid"]
+    res = {"model": f"{shape.name} attention, {shape.layers} layers, paged K4V4 slots",
+           "lengths": "uniform over {4096, 8192, ..., 32768} (seeded)", "W": W, "rho": rho,
+           "batch": B, "mean_L": round(float(np.mean(lens)), 1) if lens else 0,
+           "uniform_32k_batch_same_budget": uniform}
+    if B < 1:
+        res["skipped"] = "no room for one sequence"
+        return res
+    t0 = time.time()
+    g = torch.Generator(device="cuda").manual_seed(78)
+    dims1 = H.make_dims(1, Hq, Hkv, W, rho)
+    K = torch.randn((1, Hkv, L_cap, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    V = torch.randn((1, Hkv, L_cap, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    qb = torch.randn((1, Hq, 64, d), generator=g, device="cuda").half()
+    n_vl = H.n_vertical(rho, L_cap - W)
+    score = torch.zeros((1, Hkv, L_cap), device="cuda")
+    idx = torch.zeros((1, Hkv, n_vl), dtype=torch.int32, device="cuda")
+    flag = torch.zeros((1, Hkv, L_cap), dtype=torch.uint8, device="cuda")
+    H.hq_select_vertical(dims1, qb, K, L_cap, score, idx, flag, H.workspace(dims1, H.HQ_OP_SELECT, L_cap))
+    pre = {}                              # dense prefixes, one contiguous copy per length
+    for Lb in sorted(set(lens)):
+        f = flag[:, :, :Lb].clone()
+        f[:, :, max(0, Lb - W):] = 0
+        pre[Lb] = (K[:, :, :Lb].contiguous(), V[:, :, :Lb].contiguous(), f)
+    del K, V, score, idx, flag
+    seq_max = [Lb + steps + 1 for Lb in lens]
+    layers = []
+    for l in range(shape.layers):
+        c = H.HybridCache.allocate_paged(B, Hq, Hkv, W, rho, L_alloc, extra_vl=steps + 1, seq_L_max=seq_max)
+        for b, Lb in enumerate(lens):
+            v = c.view(b)
+            Kb, Vb, fb = pre[Lb]
+            H.hq_quant_pack(v.dims, Kb, Vb, Lb, fb, v)
+        layers.append(c)
+    torch.cuda.synchronize()
+    del pre
+    build_s = time.time() - t0
+    cache_bytes = sum(c.nbytes() for c in layers)
+    k_new = [torch.randn((B, Hkv, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    v_new = [torch.randn((B, Hkv, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    q = [torch.randn((B, Hq, d), generator=g, device="cuda").half() for _ in range(shape.layers)]
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device="cuda")
+    ws = H.workspace(layers[0].dims, H.HQ_OP_DECODE, L_alloc)
+    t_dev = [torch.tensor([Lb + s_ for Lb in lens], dtype=torch.int32, device="cuda") for s_ in range(steps)]
+    t_max = [max(lens) + s_ for s_ in range(steps)]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        st = torch.cuda.current_stream()
+        for s_ in range(steps):
+            for l, c in enumerate(layers):
+                H.hq_decode_step_ragged(c.dims, c, t_dev[s_], t_max[s_], k_new[l], v_new[l], q[l], out, ws,
+                                        stream=st)
+    graph_upload(gr, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_ms = e0.elapsed_time(e1) / steps
+    # algorithmic decode bytes of a step: each unit's K4V4 and FP16 tokens at its own length
+    dec_bytes = 0
+    for Lb in lens:
+        n_nw = max(0, Lb + steps // 2 - W)
+        nv = H.n_vertical(rho, max(0, Lb - W))
+        dec_bytes += Hkv * (160 * (n_nw - nv) + 512 * (nv + min(W, Lb) + 1))
+    dec_bytes = shape.layers * (dec_bytes + B * Hq * d * 4)
+    res.update({"cache_bytes": cache_bytes, "build_s": round(build_s, 1), "steps": steps,
+                "token_step_ms": round(step_ms, 3),
+                "attn_tokens_per_s": round(B / (step_ms * 1e-3), 1),
+                "step_bytes": dec_bytes, "step_GBs": round(dec_bytes / (step_ms * 1e-3) / 1e9, 1),
+                "timing": "K token steps (hq_decode_step_ragged in every layer) as one graph, replayed once"})
+    del gr, layers, ws, k_new, v_new, q, out
     torch.cuda.empty_cache()
     return res
 

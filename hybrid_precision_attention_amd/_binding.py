@@ -172,21 +172,18 @@ class HybridCache:
         cap_q = npb * PAGE
         cap_vl = max(1, n_vertical(rho, n_nw) + extra_vl)
         dims = make_dims(B, Hq, Hkv, W, rho, cap_q, cap_vl, max(1, cap_stg), k_bits=k_bits, v_bits=v_bits)
+        import numpy as np
         lens = list(seq_L_max) if seq_L_max is not None else [L_max] * B
-        need = [-(-max(0, Lb - W) // PAGE) for Lb in lens]
-        total = sum(need) * Hkv
-        order = list(range(total))
+        need = np.array([min(npb, -(-max(0, Lb - W) // PAGE)) for Lb in lens], dtype=np.int64)
+        unit_need = np.repeat(need, Hkv)                 # blocks of each unit, in unit order
+        total = int(unit_need.sum())
+        order = np.arange(total, dtype=np.int32)
         if shuffle_seed is not None:
-            import random
-            random.Random(shuffle_seed).shuffle(order)
+            np.random.default_rng(shuffle_seed).shuffle(order)
         spare = total                                  # the overflow block
-        pages = torch.full((B, Hkv, npb), spare, dtype=torch.int32)
-        k = 0
-        for b in range(B):
-            for g in range(Hkv):
-                for i in range(need[b]):
-                    pages[b, g, i] = order[k]
-                    k += 1
+        table = np.full((B * Hkv, npb), spare, dtype=np.int32)
+        table[np.arange(npb)[None, :] < unit_need[:, None]] = order     # row by row: each unit's blocks
+        pages = torch.from_numpy(table.reshape(B, Hkv, npb))
         P = total + 1
         dev = torch.device(device)
         u8, f16, i32 = torch.uint8, torch.float16, torch.int32

@@ -63,6 +63,26 @@ def cache_bytes_per_sequence(shape: ModelShape, L_max: int, W: int, rho: float, 
                for l in range(shape.layers))
 
 
+def paged_layer_bytes_per_sequence(shape: ModelShape, L_seq: int, L_cap: int, W: int, rho: float,
+                                   k_bits: int = 4, v_bits: int = 4, extra_vl: int = 0, cap_stg: int = 1) -> int:
+    """Bytes one sequence of up to L_seq tokens takes in one layer of a
+    paged cache whose longest sequence may reach L_cap
+    (``HybridCache.allocate_paged``): K4V4 blocks of 32 slots only for its
+    own non-window positions, plus its page table; the vertical-line region,
+    window ring, staging slots and counters as in a contiguous cache of
+    L_cap tokens."""
+    d = shape.d
+    n_nw_cap = max(0, L_cap - W)
+    npb = max(1, -(-n_nw_cap // 32))
+    blocks = -(-max(0, L_seq - W) // 32)
+    cap_vl = max(1, n_vertical(rho, n_nw_cap) + extra_vl)
+    q_tok = d * k_bits // 8 + d * v_bits // 8 + 2 * (d // GROUP) * 2 * 2 + 4
+    f_tok = 2 * d * 2
+    per_unit = (blocks * 32 * q_tok + npb * 4 + cap_vl * (f_tok + 4) + W * f_tok
+                + max(1, cap_stg) * f_tok + 3 * 4)
+    return shape.Hkv * per_unit
+
+
 def fp16_cache_bytes_per_sequence(shape: ModelShape, L: int) -> int:
     """A plain fp16 K/V cache of L tokens over all layers."""
     return shape.layers * shape.Hkv * L * shape.d * 2 * 2

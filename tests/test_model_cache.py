@@ -66,3 +66,21 @@ def test_ragged_validation():
     g = H.lib.hq_append_merge_ragged
     assert g(ctypes.byref(d), ctypes.byref(c), None, 100, P, P, None, None) == -1
     assert g(ctypes.byref(d), ctypes.byref(c), P, 40000, P, P, None, None) == -4   # cap_q < t_max - W
+
+
+def test_paged_bytes_match_a_paged_allocation():
+    """The paged byte model equals what HybridCache.allocate_paged allocates
+    (on the CPU): per-sequence blocks, the shared spare block aside."""
+    import hybrid_precision_attention_amd as H
+    from hybrid_precision_attention_amd.model_cache import paged_layer_bytes_per_sequence, ModelShape
+    shape = ModelShape("toy", 1, 8, 2, 128, 0)
+    lens = [1500, 300, 60]
+    L_cap = 1600
+    c = H.HybridCache.allocate_paged(3, 8, 2, 128, 0.05, L_cap, extra_vl=3, seq_L_max=lens, device="cpu")
+    spare = 32 * (64 + 64 + 16 + 16 + 4)            # one spare block of the pool (K4V4 rows and positions)
+    want = sum(paged_layer_bytes_per_sequence(shape, Lb, L_cap, 128, 0.05, extra_vl=3) for Lb in lens)
+    assert c.nbytes() - spare == want
+    # a short sequence pays for its own K4V4 blocks only (the window and the
+    # line region are sized by the cap for every sequence)
+    assert paged_layer_bytes_per_sequence(shape, 300, L_cap, 128, 0.05) < \
+        paged_layer_bytes_per_sequence(shape, 1500, L_cap, 128, 0.05) / 2
