@@ -55,7 +55,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
-constexpr int kMaxSplit = 128;      // partial records per unit
 
 struct DecodeArgs {
   hq_cache c;

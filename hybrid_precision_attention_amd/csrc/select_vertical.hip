@@ -1296,7 +1296,6 @@ hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, con
   a.wg_keys = kChunk * kSWaves * a.C;
   a.nwg1 = (L + a.wg_keys - 1) / a.wg_keys;
   const size_t stats_bytes = units * a.nwg1 * a.R * sizeof(float2);
-  const size_t part_bytes = a.nrg > 1 ? static_cast<size_t>(a.nrg) * units * a.n_nw * sizeof(float) : 0;
   char* w = reinterpret_cast<char*>(ws);
   a.stats = reinterpret_cast<float2*>(w);
   a.colpart = reinterpret_cast<float*>(w + round256(stats_bytes));
