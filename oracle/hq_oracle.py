@@ -118,6 +118,27 @@ def column_mass_unit(K: np.ndarray, qgrp: np.ndarray, L: int, W: int) -> np.ndar
     return dc
 
 
+def column_mass_given_lse_unit(K: np.ndarray, qgrp: np.ndarray, lse: np.ndarray, L: int,
+                               W: int) -> np.ndarray:
+    """The column-mass delta with each buffered row normalised by a given
+    natural-log LSE (lse [G][nb]) instead of its own: exp(tau q.k_i - lse)
+    summed over the heads and rows, causal, non-window columns [n_nw].  With
+    the rows' own LSE this is column_mass_unit; a caller may supply LSE rows
+    it already has (the prefill's)."""
+    G, nb, d = qgrp.shape
+    n_nw, _ = partition(L, W)
+    pos = buffered_positions(L, nb)
+    tau = softmax_scale(d)
+    Kd = K[:L].astype(np.float64)
+    keys = np.arange(L)
+    dc = np.zeros(n_nw, dtype=np.float64)
+    for h in range(G):
+        z = tau * (qgrp[h].astype(np.float64) @ Kd.T)
+        a = np.where(keys[None, :] <= pos[:, None], np.exp(z - lse[h][:, None]), 0.0)
+        dc += a[:, :n_nw].sum(axis=0)
+    return dc
+
+
 def row_lse_unit(K: np.ndarray, qgrp: np.ndarray, L: int) -> np.ndarray:
     """Natural-log LSE of each buffered query's causal row: [G][nb]."""
     G, nb, d = qgrp.shape

@@ -135,3 +135,27 @@ def test_planted_lines_dominate_when_strong():
     _, idx, _ = O.select_vertical(x["K"], x["qbuf"], wl.L, wl.W, wl.rho)
     for g in range(wl.Hkv):
         assert set(x["plant"][0].tolist()) <= set(idx[0][g].tolist())
+
+
+def test_column_mass_given_lse():
+    """With the rows' own LSE it is column_mass_unit; against a pure-Python
+    brute force with an arbitrary LSE."""
+    import math
+    rng = np.random.default_rng(21)
+    G, nb, d, L, W = 2, 5, 16, 30, 4
+    K = rng.standard_normal((L, d)).astype(np.float16)
+    qg = rng.standard_normal((G, nb, d)).astype(np.float16)
+    own = O.row_lse_unit(K, qg, L)
+    assert np.abs(O.column_mass_given_lse_unit(K, qg, own, L, W) - O.column_mass_unit(K, qg, L, W)).max() < 1e-12
+    lse = rng.uniform(1.0, 3.0, (G, nb))
+    got = O.column_mass_given_lse_unit(K, qg, lse, L, W)
+    tau = 1.0 / math.sqrt(d)
+    for i in range(L - W):
+        want = 0.0
+        for h in range(G):
+            for jq in range(nb):
+                p = L - nb + jq
+                if i <= p:
+                    z = tau * math.fsum(float(a) * float(b) for a, b in zip(qg[h, jq], K[i]))
+                    want += math.exp(z - lse[h, jq])
+        assert abs(got[i] - want) <= 1e-12 * max(1.0, want)
