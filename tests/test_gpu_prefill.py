@@ -131,3 +131,40 @@ def test_prefill_full_size_sampled_rows():
                                      flag[0, g], wl.W)
         check_decode(o[0, g * G:(g + 1) * G][:, pos], l[0, g * G:(g + 1) * G][:, pos], ro, rl,
                      tag=f"kv head {g}")
+
+
+def test_prefill_lse_feeds_the_selection():
+    """The prefill's LSE rows of the last 64 positions, given to
+    hq_select_vertical as its lse (the first pass skipped) with the prefill's
+    tail queries as the buffered ones: scores against the oracle's column
+    mass with that LSE (relative 2e-5), flags and indices exactly the
+    top-n_vl of the GPU's own scores, and the set equal to the oracle's
+    outside the 1e-5 tie band."""
+    wl, x, Q = _inputs("tiny", L=1024)
+    flag = _flags(wl, x)
+    o, lse = _run(wl, Q, x, flag)
+    L, W, G, nb = wl.L, wl.W, wl.G, 64
+    qbuf = np.ascontiguousarray(Q[:, :, L - nb:])
+    lse_rows = np.ascontiguousarray(lse[:, :, L - nb:]).astype(np.float32)
+    dims = H.make_dims(wl.B, wl.Hq, wl.Hkv, W, wl.rho)
+    n_nw = L - W
+    n_vl = O.n_vertical(wl.rho, n_nw)
+    score = torch.zeros((wl.B, wl.Hkv, L), dtype=torch.float32, device="cuda")
+    idx = torch.full((wl.B, wl.Hkv, n_vl), -1, dtype=torch.int32, device="cuda")
+    fl = torch.zeros((wl.B, wl.Hkv, L), dtype=torch.uint8, device="cuda")
+    H.hq_select_vertical(dims, dev(qbuf), dev(x["K"]), L, score, idx, fl,
+                         H.workspace(dims, H.HQ_OP_SELECT, L), lse=dev(lse_rows))
+    torch.cuda.synchronize()
+    sg, ig, fg = score.cpu().numpy(), idx.cpu().numpy(), fl.cpu().numpy()
+    for b in range(wl.B):
+        for g in range(wl.Hkv):
+            so = O.column_mass_given_lse_unit(x["K"][b, g], qbuf[b, g * G:(g + 1) * G],
+                                              lse_rows[b, g * G:(g + 1) * G].astype(np.float64), L, W)
+            err = np.abs(sg[b, g, :n_nw] - so) / np.maximum(so, 1e-30)
+            assert err.max() <= 2e-5, f"b{b} g{g} score rel err {err.max():.2e}"
+            mine = np.sort(np.lexsort((np.arange(n_nw), -sg[b, g, :n_nw].astype(np.float64)))[:n_vl])
+            assert np.array_equal(np.nonzero(fg[b, g])[0], mine) and np.array_equal(ig[b, g], mine)
+            theirs = O.top_rho(so, n_vl)
+            cut = np.sort(so)[::-1][n_vl - 1]
+            bad = [p for p in np.setxor1d(mine, theirs) if abs(so[p] - cut) > 1e-5 * cut]
+            assert not bad, f"b{b} g{g}: {len(bad)} set differences outside the tie band"
