@@ -43,6 +43,20 @@ __device__ __forceinline__ uint16_t d2h_rne_nonneg(double x) {
   return static_cast<uint16_t>(((e + 15) << 10) + static_cast<int>(r) - 1024);
 }
 
+// The code of one element, x in [m, M], by the exact rule.  A float32
+// quotient (x - m) / s decides it unless the quotient lies within 5e-4 of a
+// half-integer: x - m, 1/s and their product are each rounded once, so its
+// relative error is below 2^-21 and its absolute error below 1e-4 for every
+// quotient up to 2^b, where the clamp does not already decide.  Near a
+// half-integer the fp64 division (exact decision) is taken instead.
+__device__ __forceinline__ uint32_t exact_code(float x, float mf, float rf, double m, double s, float qmax) {
+  const float q = (x - mf) * rf;
+  float c = rintf(q);
+  if (q <= qmax + 1.0f && fabsf(q - floorf(q) - 0.5f) <= 5e-4f)
+    c = static_cast<float>(rint((static_cast<double>(x) - m) / s));
+  return static_cast<uint32_t>(fminf(fmaxf(c, 0.0f), qmax));
+}
+
 // Quantise one group of 32 fp16 values held as 16 dwords (two per dword,
 // element 2i in the low half) to b-bit codes.  Returns the 4 b code bytes in
 // codes[kBits] (element e at bits b e .. of the little-endian group) and
@@ -68,15 +82,15 @@ __device__ __forceinline__ void quant_group32(const uint32_t in[16], uint32_t co
 #pragma unroll
   for (int w = 0; w < kBits; ++w) codes[w] = 0;
   if (s_bits == 0) return;
+  const float rf = 1.0f / h2f(s_bits);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const double x = static_cast<double>(h2f(static_cast<uint16_t>(in[i] >> (16 * h))));
-      double c = rint((x - m) / s);
-      c = c < 0.0 ? 0.0 : (c > static_cast<double>(kQmax) ? static_cast<double>(kQmax) : c);
+      const float x = h2f(static_cast<uint16_t>(in[i] >> (16 * h)));
+      const uint32_t c = exact_code(x, mn, rf, m, s, static_cast<float>(kQmax));
       const int e = 2 * i + h;                 // element index in the group
-      codes[(kBits * e) >> 5] |= static_cast<uint32_t>(c) << ((kBits * e) & 31);
+      codes[(kBits * e) >> 5] |= c << ((kBits * e) & 31);
     }
   }
 }
@@ -134,11 +148,11 @@ __device__ __forceinline__ uint64_t quant_quad8(const uint4 v, int bits, uint32_
           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, m_h)) << 16);
   uint64_t codes = 0;
   if (s_bits == 0) return codes;
+  const float rf = 1.0f / h2f(s_bits);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const double x = static_cast<double>(h2f(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1)))));
-    double c = rint((x - m) / s);
-    c = c < 0.0 ? 0.0 : (c > qmax ? qmax : c);
+    const float x = h2f(static_cast<uint16_t>(w[j >> 1] >> (16 * (j & 1))));
+    const uint32_t c = exact_code(x, mn, rf, m, s, static_cast<float>(qmax));
     codes |= static_cast<uint64_t>(c) << (bits * j);
   }
   return codes;

@@ -136,3 +136,43 @@ def test_merge_streaming_bit_exact(name, over, T, ev_every):
                     gc = unit_from_gpu(cache, b, g)
                     assert int(cache.t["n_stg"][b, g]) == 1
                     assert_unit_equal(gc, ref[b][g], pos, wl.W, tag=f"t{t} b{b} g{g}")
+
+
+def _tie_rows(n_tok, bits, seed):
+    """fp16 token rows whose groups put many values exactly on, or just
+    beside, half-integer quotients (x - min) / scale: the float32 estimate of
+    the quantiser must hand those to the exact decision."""
+    rng = np.random.default_rng(seed)
+    qmax = 2 ** bits - 1
+    X = np.zeros((n_tok, 128), np.float64)
+    scales = [2.0 ** -8, 1.0, 4.0, 2.0 ** -12]
+    mins = [0.0, -0.75, 0.5]
+    for t in range(n_tok):
+        for g in range(4):
+            s = scales[(t + g) % len(scales)]
+            m = mins[(3 * t + g) % len(mins)] * s
+            k = rng.integers(0, qmax, 32).astype(np.float64)
+            off = rng.choice([0.5, 0.5, 0.5, 0.0, 0.5 + 2.0 ** -7, 0.5 - 2.0 ** -7], 32)
+            v = m + (k + off) * s
+            v[0], v[1] = m, m + qmax * s
+            X[t, 32 * g:32 * g + 32] = v
+    return X.astype(np.float16)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_pack_and_merge_tie_rich_groups(bits):
+    """Pack (W = 0: every token quantised) and streamed merges of tie-rich
+    tokens, K and V at the same width: codes, scales and minimums bit-exact
+    against the oracle."""
+    L, T = 300, 40
+    K = _tie_rows(L + T, bits, 1)
+    V = _tie_rows(L + T, bits, 2)
+    x = {"K": K[None, None], "V": V[None, None], "qbuf": np.zeros((1, 1, 1, 128), np.float16)}
+    flags = np.zeros((1, 1, L + T), np.uint8)
+    cache = gpu_pack(x, L, 0, 0.0, flags, L_max=L + T + 1, k_bits=bits, v_bits=bits)
+    ref = O.quant_pack_unit(K[:L], V[:L], L, 0, flags[0, 0, :L], bits, bits)
+    for t in range(L, L + T):
+        H.hq_append_merge(cache.dims, cache, t, dev(K[None, None, t]), dev(V[None, None, t]))
+        O.append_merge_unit(ref, t, K[t], V[t])
+    torch.cuda.synchronize()
+    assert_unit_equal(unit_from_gpu(cache, 0, 0), ref, L + T - 1, 0, tag=f"{bits}-bit")
