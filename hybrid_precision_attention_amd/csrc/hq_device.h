@@ -4,12 +4,13 @@
 // b-bit codes (b = 4 for K4V4; 2 and 8 for the other strict low-bit caches):
 // min m, max M, scale s = fp16_rne((M - m) / (2^b - 1)), code =
 // clamp(rne((x - m)/s), 0, 2^b - 1), all codes 0 when s == 0; 8/b codes per
-// byte, the lower element in the lower bits.  The decision is taken in fp64:
+// byte, the lower element in the lower bits.  The scale is decided in fp64,
+// and so is every code whose float32 estimate is close to a half-integer:
 // x - m and M - m are exact there (fp16 differences need at most 41
 // significant bits), and the single correctly-rounded fp64 division cannot
 // move a quotient across a half-integer boundary or an fp16 rounding
 // midpoint (the divisors are at most 255), so the codes equal the
-// exact-arithmetic definition.
+// exact-arithmetic definition (exact_code below).
 #pragma once
 
 #include <hip/hip_runtime.h>
