@@ -37,10 +37,10 @@ int check_dims(const hq_dims* d) {
   for (const int32_t b : {d->k_bits, d->v_bits})
     if (b != 0 && b != 2 && b != 4 && b != 8) return HQ_ERR_UNSUPPORTED;
   if (d->Hq / d->Hkv > kMaxGroup) return HQ_ERR_UNSUPPORTED;
-  // keep every flat index comfortably inside int64 and every per-unit row
-  // count inside int32
+  // several launches put the (sequence, KV head) units on a grid dimension
+  // limited to 65535
   const int64_t units = static_cast<int64_t>(d->B) * d->Hkv;
-  if (units > (1 << 24)) return HQ_ERR_ARG;
+  if (units > 65535) return HQ_ERR_ARG;
   return HQ_OK;
 }
 
@@ -350,6 +350,14 @@ int hq_prefill_attn(const hq_dims* dims, const uint16_t* q, const uint16_t* k, c
   if (!q || !k || !v || !out) return HQ_ERR_ARG;
   // positions, and rows of one unit, stay inside int32 in the kernels
   if (static_cast<int64_t>(L) * 128 > (int64_t{1} << 31) - 1) return HQ_ERR_ARG;
+  {
+    // the query blocks (32, 64 or 128 positions by the GQA group) are a grid
+    // dimension limited to 65535
+    const int G = dims->Hq / dims->Hkv;
+    const int gw = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+    const int64_t pos_wg = 32 * (4 / gw);
+    if ((static_cast<int64_t>(L) + pos_wg - 1) / pos_wg > 65535) return HQ_ERR_UNSUPPORTED;
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return HQ_ERR_ALIGN;
   if (vl_flag_or_null && !aligned16(vl_flag_or_null)) return HQ_ERR_ALIGN;
   if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;

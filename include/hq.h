@@ -39,6 +39,7 @@
  *     before anything is launched; on an error nothing is launched and no
  *     output is touched.  A launch failure returns HQ_ERR_HIP.
  *   - head_dim d must be 128 (HQ_ERR_UNSUPPORTED otherwise); Hq % Hkv == 0;
+ *     B * Hkv <= 65535 (HQ_ERR_ARG otherwise);
  *     query head h uses KV head h / (Hq / Hkv).  A "unit" is one
  *     (sequence b, KV head) pair; units are independent.
  *   - The softmax scale is 1/sqrt(d); logsumexp outputs are natural-log.
@@ -355,7 +356,9 @@ int hq_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales,
  * query's own window, itself included), else tau (q8 . k8) s_q s_k with the
  * hq_quant_int8 codes and scales of the two rows; tau = 1/sqrt(d).  P V uses
  * the FP16 values of every key.  dims->rho, cap_* and the bit widths are not
- * used.  L = 0 does nothing.  Errors: HQ_ERR_ARG, HQ_ERR_UNSUPPORTED (d),
+ * used.  L = 0 does nothing; L is at most 65535 blocks of 32 (G a multiple
+ * of 4), 64 (G even) or 128 positions (HQ_ERR_UNSUPPORTED beyond).
+ * Errors: HQ_ERR_ARG, HQ_ERR_UNSUPPORTED (d, L),
  * HQ_ERR_ALIGN, HQ_ERR_WORKSPACE, HQ_ERR_HIP.
  */
 int hq_prefill_attn(const hq_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,

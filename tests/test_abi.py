@@ -71,6 +71,7 @@ def test_dims_validation():
     assert _pack(_dims(rho=float("nan"))) == -1
     assert _pack(_dims(d=64)) == -2                    # unsupported head_dim
     assert _pack(_dims(Hq=64, Hkv=2)) == -2            # G = 32 > 16
+    assert _pack(_dims(B=8192, Hq=8, Hkv=8)) == -1     # 65536 units: more than a grid dimension holds
     assert H.lib.hq_quant_pack(None, P, P, 10, P, ctypes.byref(_fake_cache()), None) == -1
 
 
@@ -223,6 +224,7 @@ def test_prefill_validation():
     assert f(*args(wsb=need - 1)) == -5
     assert f(ctypes.byref(_dims(d=64)), P, P, P, L, None, P, None, P, need, None) == -2
     assert H.hq_workspace_bytes(d, H.HQ_OP_PREFILL, 8192) > need
+    assert f(*args(L=65535 * 32 + 1)) == -2             # more query blocks than a grid dimension holds
     g = H.lib.hq_quant_int8
     assert g(P, -1, P, P, None) == -1
     assert g(None, 4, P, P, None) == -1
