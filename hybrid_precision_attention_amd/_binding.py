@@ -109,6 +109,53 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor") -> Optional[int]:
     return t.data_ptr() or None
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str) -> None:
+    """The C ABI takes plain pointers and cannot see sizes: raise before the
+    call unless t (when given) holds the n elements the call reads or writes."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the call reads or writes {n}")
+
+
+def _rows4(t: torch.Tensor, B: int, H: int, name: str) -> int:
+    """Rows per head of a [B][H][rows][128] tensor (shape checked)."""
+    if t.dim() != 4 or tuple(t.shape[:2]) != (B, H) or t.shape[3] != D:
+        raise ValueError(f"{name} must be [{B}][{H}][rows][{D}], got {list(t.shape)}")
+    return int(t.shape[2])
+
+
+def _bits(b: int) -> int:
+    return 4 if b == 0 else b
+
+
+def _same_cache(dims: hq_dims, cache: "HybridCache") -> None:
+    """The dims of a cache call must describe the buffers the cache holds."""
+    c = cache.dims
+    for f in ("B", "Hkv", "d", "W", "cap_q", "cap_vl", "cap_stg"):
+        if getattr(dims, f) != getattr(c, f):
+            raise ValueError(f"dims.{f} = {getattr(dims, f)} differs from the cache's {getattr(c, f)}")
+    for f in ("k_bits", "v_bits"):
+        if _bits(getattr(dims, f)) != _bits(getattr(c, f)):
+            raise ValueError(f"dims.{f} = {getattr(dims, f)} differs from the cache's {getattr(c, f)}")
+
+
+def _check_token(dims, cache, k_new, v_new, evict_is_vl) -> None:
+    """A new token's K and V rows [B][Hkv][128] and its eviction flags [B][Hkv]."""
+    _same_cache(dims, cache)
+    U = dims.B * dims.Hkv
+    _need(k_new, U * D, "k_new")
+    _need(v_new, U * D, "v_new")
+    _need(evict_is_vl, U, "evict_is_vl")
+
+
+def _check_query(dims, cache, q, out, lse) -> None:
+    """Decode queries and outputs [B][Hq][128], LSE [B][Hq]."""
+    _same_cache(dims, cache)
+    R = dims.B * dims.Hq
+    _need(q, R * D, "q")
+    _need(out, R * D, "out")
+    _need(lse, R, "lse")
+
+
 def _stream(stream) -> int:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
@@ -260,7 +307,15 @@ def workspace(dims: hq_dims, op: int, L_max: int, device="cuda") -> torch.Tensor
 
 
 def hq_select_vertical(dims, qbuf, k, L, score, vl_idx, vl_flag, ws, lse=None, stream=None):
-    nb = qbuf.shape[2]
+    """qbuf [B][Hq][nb][128] fp16, k [B][Hkv][L][128] fp16, lse [B][Hq][nb]
+    fp32 or None; score and vl_flag [B][Hkv][L], vl_idx [B][Hkv][n_vl]."""
+    nb = _rows4(qbuf, dims.B, dims.Hq, "qbuf")
+    U = dims.B * dims.Hkv
+    _need(k, U * L * D, "k")
+    _need(lse, dims.B * dims.Hq * nb, "lse")
+    _need(score, U * L, "score")
+    _need(vl_idx, U * n_vertical(dims.rho, max(0, L - dims.W)), "vl_idx")
+    _need(vl_flag, U * L, "vl_flag")
     st = lib.hq_select_vertical(ctypes.byref(dims), _ptr(qbuf, torch.float16, "qbuf"), nb,
                                 _ptr(k, torch.float16, "k"), L, _ptr(lse, torch.float32, "lse"),
                                 _ptr(score, torch.float32, "score"),
@@ -271,6 +326,11 @@ def hq_select_vertical(dims, qbuf, k, L, score, vl_idx, vl_flag, ws, lse=None, s
 
 
 def hq_quant_pack(dims, k, v, L, vl_flag, cache: HybridCache, stream=None):
+    _same_cache(dims, cache)
+    U = dims.B * dims.Hkv
+    _need(k, U * L * D, "k")
+    _need(v, U * L * D, "v")
+    _need(vl_flag, U * L, "vl_flag")
     cs = cache.struct()
     st = lib.hq_quant_pack(ctypes.byref(dims), _ptr(k, torch.float16, "k"),
                            _ptr(v, torch.float16, "v"), L, _ptr(vl_flag, torch.uint8, "vl_flag"),
@@ -279,6 +339,7 @@ def hq_quant_pack(dims, k, v, L, vl_flag, cache: HybridCache, stream=None):
 
 
 def hq_append_merge(dims, cache: HybridCache, t, k_new, v_new, evict_is_vl=None, stream=None):
+    _check_token(dims, cache, k_new, v_new, evict_is_vl)
     cs = cache.struct()
     st = lib.hq_append_merge(ctypes.byref(dims), ctypes.byref(cs), t,
                              _ptr(k_new, torch.float16, "k_new"), _ptr(v_new, torch.float16, "v_new"),
@@ -287,6 +348,7 @@ def hq_append_merge(dims, cache: HybridCache, t, k_new, v_new, evict_is_vl=None,
 
 
 def hq_decode_attn(dims, cache: HybridCache, L, q, out, ws, lse=None, stream=None):
+    _check_query(dims, cache, q, out, lse)
     cs = cache.struct()
     st = lib.hq_decode_attn(ctypes.byref(dims), ctypes.byref(cs), L, _ptr(q, torch.float16, "q"),
                             _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
@@ -297,6 +359,14 @@ def hq_decode_attn(dims, cache: HybridCache, L, q, out, ws, lse=None, stream=Non
 def hq_refresh_hybrid(dims, cache: HybridCache, t, qbuf, lse, score, vl_idx, vl_flag, cut,
                       stream=None):
     """score [B][Hkv][score_ld] (score_ld = its last dimension)."""
+    _same_cache(dims, cache)
+    nb = _rows4(qbuf, dims.B, dims.Hq, "qbuf")
+    U, ld = dims.B * dims.Hkv, score.shape[-1]
+    _need(lse, dims.B * dims.Hq * nb, "lse")
+    _need(score, U * ld, "score")
+    _need(vl_idx, U * n_vertical(dims.rho, max(0, t - dims.W)), "vl_idx")
+    _need(vl_flag, U * ld, "vl_flag")
+    _need(cut, U, "cut")
     cs = cache.struct()
     st = lib.hq_refresh_hybrid(ctypes.byref(dims), ctypes.byref(cs), t,
                                _ptr(qbuf, torch.float16, "qbuf"), qbuf.shape[2],
@@ -308,6 +378,9 @@ def hq_refresh_hybrid(dims, cache: HybridCache, t, qbuf, lse, score, vl_idx, vl_
 
 
 def hq_append_merge_scored(dims, cache: HybridCache, t, k_new, v_new, score, cut, stream=None):
+    _check_token(dims, cache, k_new, v_new, None)
+    _need(score, dims.B * dims.Hkv * score.shape[-1], "score")
+    _need(cut, dims.B * dims.Hkv, "cut")
     cs = cache.struct()
     st = lib.hq_append_merge_scored(ctypes.byref(dims), ctypes.byref(cs), t,
                                     _ptr(k_new, torch.float16, "k_new"),
@@ -320,6 +393,8 @@ def hq_append_merge_scored(dims, cache: HybridCache, t, k_new, v_new, score, cut
 def hq_append_merge_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new, evict_is_vl=None,
                            stream=None):
     """t_seq: [B] int32 device tensor of per-sequence positions (<= t_max)."""
+    _check_token(dims, cache, k_new, v_new, evict_is_vl)
+    _need(t_seq, dims.B, "t_seq")
     cs = cache.struct()
     st = lib.hq_append_merge_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(t_seq, torch.int32, "t_seq"),
                                     t_max, _ptr(k_new, torch.float16, "k_new"),
@@ -330,6 +405,8 @@ def hq_append_merge_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new,
 
 def hq_decode_attn_ragged(dims, cache: HybridCache, L_seq, L_max, q, out, ws, lse=None, stream=None):
     """L_seq: [B] int32 device tensor of per-sequence query positions (<= L_max)."""
+    _check_query(dims, cache, q, out, lse)
+    _need(L_seq, dims.B, "L_seq")
     cs = cache.struct()
     st = lib.hq_decode_attn_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(L_seq, torch.int32, "L_seq"),
                                    L_max, _ptr(q, torch.float16, "q"), _ptr(out, torch.float16, "out"),
@@ -341,6 +418,8 @@ def hq_decode_attn_ragged(dims, cache: HybridCache, L_seq, L_max, q, out, ws, ls
 def hq_decode_step(dims, cache: HybridCache, t, k_new, v_new, q, out, ws, lse=None, evict_is_vl=None,
                    stream=None):
     """hq_append_merge(t) + hq_decode_attn(t) in one launch (nothing may be staged)."""
+    _check_token(dims, cache, k_new, v_new, evict_is_vl)
+    _check_query(dims, cache, q, out, lse)
     cs = cache.struct()
     st = lib.hq_decode_step(ctypes.byref(dims), ctypes.byref(cs), t, _ptr(k_new, torch.float16, "k_new"),
                             _ptr(v_new, torch.float16, "v_new"), _ptr(evict_is_vl, torch.uint8, "evict_is_vl"),
@@ -353,6 +432,9 @@ def hq_decode_step(dims, cache: HybridCache, t, k_new, v_new, q, out, ws, lse=No
 def hq_decode_step_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new, q, out, ws, lse=None,
                           evict_is_vl=None, stream=None):
     """t_seq: [B] int32 device tensor of per-sequence positions (<= t_max)."""
+    _check_token(dims, cache, k_new, v_new, evict_is_vl)
+    _check_query(dims, cache, q, out, lse)
+    _need(t_seq, dims.B, "t_seq")
     cs = cache.struct()
     st = lib.hq_decode_step_ragged(ctypes.byref(dims), ctypes.byref(cs), _ptr(t_seq, torch.int32, "t_seq"), t_max,
                                    _ptr(k_new, torch.float16, "k_new"), _ptr(v_new, torch.float16, "v_new"),
@@ -363,7 +445,10 @@ def hq_decode_step_ragged(dims, cache: HybridCache, t_seq, t_max, k_new, v_new, 
 
 
 def bind_step(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):
-    """Returns f(t, k_ptr, v_ptr, q_ptr=None): hq_decode_step on fixed buffers."""
+    """Returns f(t, k_ptr, v_ptr, q_ptr=None): hq_decode_step on fixed buffers.
+    The bound tensors are checked here; the raw addresses passed per call are
+    not (each must hold a [B][Hkv][128] or [B][Hq][128] fp16 row set)."""
+    _check_query(dims, cache, q, out, lse)
     cs = cache.struct()
     d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
     qp = _ptr(q, torch.float16, "q")
@@ -393,6 +478,13 @@ def hq_prefill_attn(dims, q, k, v, L, vl_flag, out, ws, lse=None, stream=None):
     """q [B][Hq][L][128], k, v [B][Hkv][L][128] fp16; vl_flag [B][Hkv][L] uint8
     or None; out like q; lse [B][Hq][L] fp32 or None; ws from
     workspace(dims, HQ_OP_PREFILL, L)."""
+    U, R = dims.B * dims.Hkv, dims.B * dims.Hq
+    _need(q, R * L * D, "q")
+    _need(out, R * L * D, "out")
+    _need(lse, R * L, "lse")
+    _need(k, U * L * D, "k")
+    _need(v, U * L * D, "v")
+    _need(vl_flag, U * L, "vl_flag")
     st = lib.hq_prefill_attn(ctypes.byref(dims), _ptr(q, torch.float16, "q"), _ptr(k, torch.float16, "k"),
                              _ptr(v, torch.float16, "v"), L, _ptr(vl_flag, torch.uint8, "vl_flag"),
                              _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
@@ -406,7 +498,9 @@ def hq_prefill_attn(dims, q, k, v, L, vl_flag, out, ws, lse=None, stream=None):
 # --------------------------------------------------------------------------
 def bind_decode(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):
     """Returns f(L, q_ptr=None): hq_decode_attn on fixed buffers; q_ptr
-    optionally points at another query tensor of the same shape."""
+    optionally points at another query tensor of the same shape (not
+    checked)."""
+    _check_query(dims, cache, q, out, lse)
     cs = cache.struct()
     d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
     qp = _ptr(q, torch.float16, "q")
@@ -424,7 +518,8 @@ def bind_decode(dims, cache: HybridCache, q, out, ws, lse=None, stream=None):
 
 def bind_merge(dims, cache: HybridCache, evict_is_vl=None, stream=None):
     """Returns f(t, k_ptr, v_ptr): hq_append_merge of the token at t whose
-    [B][Hkv][d] fp16 rows start at the given device addresses."""
+    [B][Hkv][d] fp16 rows start at the given device addresses (not checked)."""
+    _check_token(dims, cache, None, None, evict_is_vl)
     cs = cache.struct()
     d_ref, c_ref = ctypes.byref(dims), ctypes.byref(cs)
     ep, sp = _ptr(evict_is_vl, torch.uint8, "evict_is_vl"), _stream(stream)
