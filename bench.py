@@ -15,6 +15,14 @@ The cache footprint of one small-batch layer fits in the 256 MB Infinity
 Cache, so the step rotates over R independent cache replicas (R * footprint
 >= 1 GiB) to measure HBM rather than cache bandwidth.
 
+Beside the step, with the sweeps on (default): the batch sweep of the
+Qwen3-8B-shaped layer (B = 1, 4, 16, 32), the other code widths, a context
+sweep of the Llama-shaped layer (L = 1K .. 32K), a grid of the
+GLM-4-9B-shaped GQA-16 layer (B = 8, L = 1K .. 32K, rho = 1, 5, 10 %, with
+the selection, its one-pass form and the decode-time refresh timed at 32K),
+a Qwen3-32B-shaped layer streaming 128 tokens at B = 32, the read ceiling,
+the prefill attention and the capacity runs.
+
 Prints one JSON line.  ``value`` is the effective HBM bandwidth of the step:
 algorithmic bytes (what the method must move: 160 B per K4V4 token and 512 B
 per FP16 token per KV head, q in, out, merge and amortised refresh traffic)
@@ -370,10 +378,13 @@ def main():
     if not (args.no_sweep and args.no_prefill and args.no_capacity):
         del caches, ws, K_rep, base, spare
         torch.cuda.empty_cache()
-    sweep, ceiling, widths = None, None, None
+    sweep, ceiling, widths, contexts, gqa16, streaming = None, None, None, None, None, None
     if not args.no_sweep:
         sweep = decode_sweep(H, torch, workload)
         widths = width_sweep(H, torch, workload)
+        contexts = context_sweep(H, torch, workload)
+        gqa16 = gqa16_grid(H, torch, workload)
+        streaming = streaming_run(H, torch, workload)
         ceiling = read_ceiling(torch, 4 << 30)
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
     prefill = None if args.no_prefill else prefill_timing(H, torch)
@@ -409,6 +420,9 @@ def main():
         "decode_time_refresh": refresh,
         "b_sweep": sweep,
         "kv_width_sweep": widths,
+        "context_sweep": contexts,
+        "gqa16_grid": gqa16,
+        "streaming_qwen3_32b": streaming,
         "read_ceiling": ceiling,
         "prefill": prefill,
         "capacity": capacity,
@@ -471,9 +485,33 @@ def refresh_timing(H, torch, wl, dims, caches, pos, qbuf, capture):
             "per_step_us": round(us / REFRESH, 3)}
 
 
-def graph_decode_us(H, torch, dims, caches, wss, L, q, out, n):
-    """Average duration of n back-to-back hq_decode_attn launches over the
-    rotating caches, replayed from a captured graph between HIP events."""
+def capture_graph(torch, body):
+    """body(stream) captured into a HIP graph (through torch) and uploaded."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body(torch.cuda.current_stream())
+    graph_upload(g, torch)
+    return g
+
+
+def replay_stats(g, torch, n, reps=5):
+    """Per-launch µs of a graph of n launches (already replayed once): the
+    median and p90 over `reps` replays, each between HIP events."""
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / n)
+    ts.sort()
+    return ts[len(ts) // 2], ts[min(len(ts) - 1, math.ceil(0.9 * len(ts)) - 1)]
+
+
+def graph_decode_us(H, torch, dims, caches, wss, L, q, out, n, reps=5):
+    """(median, p90) of the average duration of n back-to-back hq_decode_attn
+    launches over the rotating caches, replayed from a captured graph."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         st = torch.cuda.current_stream()
@@ -483,12 +521,7 @@ def graph_decode_us(H, torch, dims, caches, wss, L, q, out, n):
     graph_upload(g, torch)
     g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / n * 1e3
+    return replay_stats(g, torch, n, reps)
 
 
 def decode_sweep(H, torch, workload, Bs=(1, 4, 16, 32)):
@@ -506,10 +539,132 @@ def width_sweep(H, torch, workload, points=((1, 8, 8), (1, 4, 2), (1, 2, 4), (32
     return [decode_point(H, torch, workload, B, kb, vb) for B, kb, vb in points]
 
 
-def decode_point(H, torch, workload, B, kb=4, vb=4):
+def context_sweep(H, torch, workload, Ls=(1024, 2048, 4096, 8192, 16384, 32768)):
+    """Decode of the Llama-3.1-8B-shaped layer (B = 1) at the prefix lengths
+    of the pages' latency table, for comparison with its shape only."""
+    return [decode_point(H, torch, workload, 1, name="llama31_8b", L=L) for L in Ls]
+
+
+def gqa16_grid(H, torch, workload, Ls=(1024, 4096, 16384, 32768), rhos=(0.01, 0.05, 0.10)):
+    """GLM-4-9B-shaped layer (32 query heads on 2 KV heads, B = 8): decode
+    µs and GB/s over prefix length and rho; at L = 32K the selection is timed
+    too (its two passes are MFMA-heavy at 16 query heads per KV head)."""
+    return [decode_point(H, torch, workload, 8, name="glm4_9b", select=(L == max(Ls)), L=L, rho=r)
+            for L in Ls for r in rhos]
+
+
+def streaming_run(H, torch, workload, steps=128):
+    """A Qwen3-32B-shaped layer (B = 32, 64/8 heads) streaming 128 tokens
+    from a 32K prefix: per-step µs of the merge and the decode on their own,
+    of the two as separate launches, and of hq_decode_step, each from a graph
+    of the 128 steps replayed once on a fresh copy of the cache (one launch
+    moves 1.5 GB, past the Infinity Cache)."""
+    wl = workload("qwen3_32b")
+    B, Hq, Hkv, L, W, rho, d = wl.B, wl.Hq, wl.Hkv, wl.L, wl.W, wl.rho, 128
+    U = B * Hkv
+    g = torch.Generator(device="cuda").manual_seed(32)
+    K = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    V = torch.randn((B, Hkv, L, d), generator=g, device="cuda").to(torch.bfloat16).half()
+    qb = torch.randn((B, Hq, 64, d), generator=g, device="cuda").half()
+    dims_s = H.make_dims(B, Hq, Hkv, W, rho)
+    n_nw = L - W
+    n_vl = H.n_vertical(rho, n_nw)
+    score = torch.zeros((B, Hkv, L), device="cuda")
+    idx = torch.zeros((B, Hkv, n_vl), dtype=torch.int32, device="cuda")
+    flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device="cuda")
+    H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, H.workspace(dims_s, H.HQ_OP_SELECT, L))
+    base = H.HybridCache.allocate(B, Hq, Hkv, W, rho, L + steps + 2)
+    H.hq_quant_pack(base.dims, K, V, L, flag, base)
+    del K, V, qb, score, idx, flag
+    kn = torch.randn((steps, B, Hkv, d), generator=g, device="cuda").half()
+    vn = torch.randn((steps, B, Hkv, d), generator=g, device="cuda").half()
+    qn = torch.randn((steps, B, Hq, d), generator=g, device="cuda").half()
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device="cuda")
+    dims = base.dims
+    ws = H.workspace(dims, H.HQ_OP_DECODE, L + steps + 2)
+    kp = [kn[i].data_ptr() for i in range(steps)]
+    vp = [vn[i].data_ptr() for i in range(steps)]
+    qp = [qn[i].data_ptr() for i in range(steps)]
+    # warm every kernel once on a throwaway copy
+    w = base.clone()
+    H.hq_decode_step(dims, w, L, kn[0], vn[0], qn[0], out, ws)
+    H.hq_append_merge(dims, w, L + 1, kn[1], vn[1])
+    H.hq_decode_attn(dims, w, L + 1, qn[1], out, ws)
+    torch.cuda.synchronize()
+    del w
+
+    def once(body):
+        c = base.clone()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            body(c, torch.cuda.current_stream())
+        graph_upload(gr, torch)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        del gr
+        return us, c
+
+    def fused(c, st):
+        f = H.bind_step(dims, c, qn[0], out, ws, stream=st)
+        for i in range(steps):
+            f(L + i, kp[i], vp[i], qp[i])
+
+    def unfused(c, st):
+        m = H.bind_merge(dims, c, stream=st)
+        dq = H.bind_decode(dims, c, qn[0], out, ws, stream=st)
+        for i in range(steps):
+            m(L + i, kp[i], vp[i])
+            dq(L + i, qp[i])
+
+    def merges(c, st):
+        m = H.bind_merge(dims, c, stream=st)
+        for i in range(steps):
+            m(L + i, kp[i], vp[i])
+
+    step_us, _ = once(fused)
+    unfused_us, _ = once(unfused)
+    merge_us, cm = once(merges)
+
+    def decodes(c, st):
+        dq = H.bind_decode(dims, cm, qn[0], out, ws, stream=st)
+        for i in range(steps):
+            dq(L + steps - 1, qp[i])
+    decode_us, _ = once(decodes)
+    # algorithmic bytes at the middle of the run: the decode reads the K4V4
+    # tokens, the FP16 lines, window and staged token, q in and out; the merge
+    # reads the leaving token and writes its K4V4 slot and the ring slot
+    n_q_mid = (n_nw - n_vl) + steps // 2
+    dec_bytes = U * (160 * n_q_mid + 512 * (n_vl + W + 1)) + B * Hq * d * 4
+    merge_bytes = U * (512 + 160 + 512)
+    res = {"workload": "Qwen3-32B-shaped layer, B=32, 64/8 heads, 128 steps from L=32768", "W": W,
+           "rho": rho, "steps": steps, "step_us": round(step_us, 2), "unfused_us": round(unfused_us, 2),
+           "decode_us": round(decode_us, 2), "merge_us": round(merge_us, 2),
+           "step_GBs": round((dec_bytes + merge_bytes) / (step_us * 1e-6) / 1e9, 1),
+           "decode_GBs": round(dec_bytes / (decode_us * 1e-6) / 1e9, 1),
+           "decode_frac": round(dec_bytes / (decode_us * 1e-6) / 1e9 / PEAK_GBS, 4),
+           "bytes_per_step": dec_bytes + merge_bytes,
+           "timing": "each variant: the 128 steps as one graph, replayed once on a fresh copy of the cache"}
+    del base, cm, kn, vn, qn, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_point(H, torch, workload, B, kb=4, vb=4, name="qwen3_8b", select=False, **over):
+    """Decode launches of one workload shape (the named layer at batch B,
+    with overrides such as L and rho): cache built on the device from
+    bf16-rounded N(0,1) keys and values by select + pack + one merge, then
+    rotated over replicas of at least 1 GiB in all; µs (median and p90 over
+    graph replays) and GB/s of the algorithmic bytes.  With select=True the
+    selection over the same prefix is timed too, with its share of the step
+    at one refresh per 64 decodes."""
     d = 128
     if True:
-        wl = workload("qwen3_8b", B=B)
+        wl = workload(name, B=B, **over)
         Hq, Hkv, L, W, rho = wl.Hq, wl.Hkv, wl.L, wl.W, wl.rho
         U = B * Hkv
         g = torch.Generator(device="cuda").manual_seed(1000 + B)
@@ -522,25 +677,60 @@ def decode_point(H, torch, workload, B, kb=4, vb=4):
         score = torch.zeros((B, Hkv, L), device="cuda")
         idx = torch.zeros((B, Hkv, n_vl), dtype=torch.int32, device="cuda")
         flag = torch.zeros((B, Hkv, L), dtype=torch.uint8, device="cuda")
-        H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, H.workspace(dims_s, H.HQ_OP_SELECT, L))
+        ws_s = H.workspace(dims_s, H.HQ_OP_SELECT, L)
+        H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, ws_s)
+        sel_us = sel1_us = None
+        if select:
+            # both passes, and the column-mass pass alone with the rows' LSE
+            # handed over as the producing attention would (a constant here:
+            # timing only)
+            lse_c = torch.full((B, Hq, 64), 8.0, dtype=torch.float32, device="cuda")
+
+            def sel_graph(lse_in):
+                torch.cuda.synchronize()
+                gs = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gs):
+                    st = torch.cuda.current_stream()
+                    for _ in range(8):
+                        H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, ws_s, lse=lse_in, stream=st)
+                graph_upload(gs, torch)
+                gs.replay()
+                torch.cuda.synchronize()
+                return replay_stats(gs, torch, 8, 3)[0]
+            sel_us = sel_graph(None)
+            sel1_us = sel_graph(lse_c)
+            H.hq_select_vertical(dims_s, qb, K, L, score, idx, flag, ws_s)
+            qb_keep = qb
         base = H.HybridCache.allocate(B, Hq, Hkv, W, rho, L + 8, k_bits=kb, v_bits=vb)
         H.hq_quant_pack(base.dims, K, V, L, flag, base)
         H.hq_append_merge(base.dims, base, L, K[:, :, 0].contiguous(), V[:, :, 0].contiguous())
         del K, V, qb, score, idx, flag
         q_tok = 16 * (kb + vb) + 32
         footprint = U * (q_tok * (n_nw - n_vl) + 512 * (n_vl + W + 1))
-        R = max(1, math.ceil((1 << 30) / footprint))
+        R = min(256, max(1, math.ceil((1 << 30) / footprint)))
         caches = [base] + [base.clone() for _ in range(R - 1)]
         wss = [H.workspace(base.dims, H.HQ_OP_DECODE, L + 8) for _ in range(R)]
         q = torch.randn((B, Hq, d), generator=g, device="cuda").half()
         out = torch.empty_like(q)
-        us = graph_decode_us(H, torch, base.dims, caches, wss, L + 1, q, out, max(2 * R, 32))
+        us, p90 = graph_decode_us(H, torch, base.dims, caches, wss, L + 1, q, out, max(2 * R, 32))
+        ref_us = None
+        if select:
+            ref_us = refresh_timing(H, torch, wl, base.dims, caches, [L + 1] * R, qb_keep,
+                                    lambda body: capture_graph(torch, body))["us"]
+            del qb_keep
         nbytes = U * (q_tok * (n_nw - n_vl) + 512 * (n_vl + W + 1)) + B * Hq * d * 4
         gbs = nbytes / (us * 1e-6) / 1e9
-        res = {"B": B, "decode_us": round(us, 2), "GBs": round(gbs, 1),
+        res = {"B": B, "decode_us": round(us, 2), "p90_us": round(p90, 2), "GBs": round(gbs, 1),
                "frac": round(gbs / PEAK_GBS, 4), "bytes": nbytes, "replicas": R}
+        if name != "qwen3_8b" or over:
+            res.update({"L": L, "rho": rho})
         if (kb, vb) != (4, 4):
             res["kv_bits"] = f"K{kb}V{vb}"
+        if sel_us is not None:
+            share = lambda x: round(x / (x + REFRESH * us), 4)
+            res.update({"select_us": round(sel_us, 2), "select_share_amortized": share(sel_us),
+                        "select_given_lse_us": round(sel1_us, 2), "select_given_lse_share": share(sel1_us),
+                        "decode_time_refresh_us": round(ref_us, 2), "decode_time_refresh_share": share(ref_us)})
         del caches, wss, base
         torch.cuda.empty_cache()
     return res
