@@ -157,3 +157,33 @@ def test_decode_full_size_qwen3_8b_batch32_sampled():
     # units together), as it applies to a whole call's output elsewhere
     pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
     check_decode(pick(out), pick(lse), pick(ref), pick(ref_lse), tag="sampled units")
+
+
+@pytest.mark.parametrize("name,seqs,units", [
+    # Qwen3-32B-shaped, B=32, 64/8 heads (G = 8, the general path): four
+    # seeded sequences tiled over the batch, one sampled unit per tile group
+    ("qwen3_32b", [0, 1, 2, 3], [(0, 0), (9, 2), (22, 5), (31, 7)]),
+    # GLM-4-9B-shaped, B=8, 32/2 heads (G = 16): every sequence its own seed
+    ("glm4_9b", list(range(8)), [(0, 0), (3, 1), (6, 0), (7, 1)]),
+])
+def test_decode_full_size_sampled(name, seqs, units):
+    """The streaming and GQA-16 runs' decode at full size (L=32768, the
+    split plan of that launch), checked by the oracle on sampled units."""
+    wl = workload(name, rho=0.05)
+    assert wl.L == 32768
+    xs = batch(wl, steps=1, seqs=seqs)
+    _, _, f = O.select_vertical(xs["K"], xs["qbuf"], wl.L, wl.W, wl.rho)
+    rep = wl.B // len(seqs)
+    x = {"K": np.concatenate([xs["K"]] * rep), "V": np.concatenate([xs["V"]] * rep),
+         "qbuf": np.concatenate([xs["qbuf"]] * rep)}
+    cache = gpu_pack(x, wl.L, wl.W, wl.rho, np.concatenate([f] * rep), L_max=wl.L + 1)
+    del x
+    k_new = np.concatenate([xs["k_dec"][0]] * rep)
+    v_new = np.concatenate([xs["v_dec"][0]] * rep)
+    q = np.concatenate([xs["q_dec"][0]] * rep)
+    H.hq_append_merge(cache.dims, cache, wl.L, dev(k_new), dev(v_new))
+    out, lse = gpu_decode(cache, wl.L, q)
+    ref, ref_lse = oracle_decode_on(cache, wl.L, q, units=units)
+    G = wl.G
+    pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
+    check_decode(pick(out), pick(lse), pick(ref), pick(ref_lse), tag=f"{name} sampled units")

@@ -103,6 +103,19 @@ def test_select_full_size_llama_layer():
     check(wl, x, score_g, idx_g, flag_g, n_vl, score_o)
 
 
+def test_select_full_size_gqa16_layer():
+    """The GQA-16 grid's selection as timed: GLM-4-9B-shaped layer (32 query
+    heads on 2 KV heads), B=8, L=32768, rho=5 %: 1024 rows per unit in four
+    row groups, whose column-mass parts top-k folds in."""
+    wl = workload("glm4_9b", rho=0.05)
+    assert (wl.B, wl.L, wl.G) == (8, 32768, 16)
+    x = batch(wl, steps=1)
+    score_o, _, _ = O.select_vertical(x["K"], x["qbuf"], wl.L, wl.W, wl.rho)
+    score_g, idx_g, flag_g, n_vl = gpu_select(x, wl)
+    assert n_vl == 1632
+    check(wl, x, score_g, idx_g, flag_g, n_vl, score_o)
+
+
 def test_select_with_supplied_lse_and_running_score():
     wl = workload("qwen3_8b", B=2, L=2500)
     x = batch(wl, steps=1)
