@@ -28,6 +28,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "hq_device.h"
 #include "hq_launch.h"
@@ -903,6 +904,22 @@ __device__ __forceinline__ void block_excl_scan(int x, int& excl, int& total, To
   __syncthreads();
 }
 
+// Lane kLane of v takes the wave-uniform value x (v_writelane_b32 with an
+// immediate lane select).  x is usually a ballot just written by a VALU
+// compare; the wait states before the lane write let that SGPR write land
+// (the compiler does not insert them for an asm statement).
+template <int kLane>
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t x) {
+  asm volatile("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "n"(kLane));
+  return v;
+}
+
+// f(std::integral_constant<int, k>) for k = 0, 1, ..., in order.
+template <typename F, int... K>
+__device__ __forceinline__ void for_each_k(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+
 // One histogram pass: keys in [lo, hi] counted into 256 bins of 2^shift keys
 // in one LDS histogram (the lanes that share the first in-range lane's bin
 // add with one atomic, since same-address LDS atomics serialise).  Keys past
@@ -996,6 +1013,7 @@ __device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
 // Before the radix passes, a 1/16 sample brackets the cut-off; one exact count
 // checks the bracket (else the full range is used), so the passes then see
 // a few hundred keys instead of all of them.
+template <bool kCut>
 __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   __shared__ TopShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1171,33 +1189,59 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   // segment 0 takes its keys from registers, later ones re-read them (the
   // first call is separate so that the register keys die with it)
   auto emit = [&](int seg, bool from_regs) {
+    uint32_t* gt32 = reinterpret_cast<uint32_t*>(sh.gt);
+    uint32_t* eq32 = reinterpret_cast<uint32_t*>(sh.eq);
     if (k_want > 0) {
-#pragma unroll
-      for (int k = 0; k < kKeysPerThread; ++k) {
-        const int i = seg + tid + k * kTopThreads;
-        const uint32_t key = from_regs ? keys[k] : order_key(sc[min(i, n - 1)]);
-        const bool valid = i < n;
-        const bool g = valid && key > thresh, e = valid && key == thresh;
-        if (g) tmin = min(tmin, key);
-        const uint64_t bg = __ballot(g), be = __ballot(e);
-        if (lane == 0) {
-          // positions seg + 1024 k + 64 wave .. + 63 are 64-bit word 16 k + wave
-          sh.gt[16 * k + wave] = bg;
-          sh.eq[16 * k + wave] = be;
-        }
+      // The ballot of row k (positions seg + 1024 k + 64 wave .. + 63, 64-bit
+      // word 16 k + wave) goes into lanes 2k and 2k + 1 of one register, which
+      // the wave then stores with one LDS write per lane.  When every
+      // threshold-equal key is taken, or none is, one comparison per key
+      // decides (key >= thresh, or key >= thresh + 1: finite scores never
+      // reach the top key); otherwise the above and equal bitmaps are both
+      // kept for the ranking of ties below.
+      // v_writelane writes its lane whatever the exec mask, so the two forms
+      // sit behind a branch on a wave-uniform (scalar) value: only the taken
+      // side runs.
+      const bool eq_all_u = __builtin_amdgcn_readfirstlane(eq_all ? 1 : 0) != 0;
+      const uint32_t tcmp = thresh + (take_eq > 0 ? 0u : 1u);
+      uint32_t wa = 0, wb = 0;
+      if (eq_all_u) {
+        for_each_k([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          const int i = seg + tid + k * kTopThreads;
+          const uint32_t key = from_regs ? keys[k] : order_key(sc[min(i, n - 1)]);
+          const bool t = i < n && key >= tcmp;
+          if (kCut && t) tmin = min(tmin, key);
+          const uint64_t b = __ballot(t);
+          wa = write_lane<2 * k>(wa, static_cast<uint32_t>(b));
+          wa = write_lane<2 * k + 1>(wa, static_cast<uint32_t>(b >> 32));
+        }, std::make_integer_sequence<int, kKeysPerThread>{});
+      } else {
+        for_each_k([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          const int i = seg + tid + k * kTopThreads;
+          const uint32_t key = from_regs ? keys[k] : order_key(sc[min(i, n - 1)]);
+          const bool valid = i < n;
+          const bool g = valid && key > thresh, e = valid && key == thresh;
+          if (kCut && g) tmin = min(tmin, key);
+          const uint64_t bg = __ballot(g), be = __ballot(e);
+          wa = write_lane<2 * k>(wa, static_cast<uint32_t>(bg));
+          wa = write_lane<2 * k + 1>(wa, static_cast<uint32_t>(bg >> 32));
+          wb = write_lane<2 * k>(wb, static_cast<uint32_t>(be));
+          wb = write_lane<2 * k + 1>(wb, static_cast<uint32_t>(be >> 32));
+        }, std::make_integer_sequence<int, kKeysPerThread>{});
       }
+      const int w32 = 2 * (16 * (lane >> 1) + wave) + (lane & 1);
+      gt32[w32] = wa;
+      if (!eq_all_u) eq32[w32] = wb;
     } else if (tid < kSegWords / 2) {
       sh.gt[tid] = 0;
-      sh.eq[tid] = 0;
     }
     __syncthreads();
-    const uint32_t* gt32 = reinterpret_cast<const uint32_t*>(sh.gt);
-    uint32_t* eq32 = reinterpret_cast<uint32_t*>(sh.eq);
-    const uint32_t e = eq32[tid];
+    // with eq_all the gt bitmap already holds every taken position
     uint32_t take = gt32[tid];
-    if (eq_all) {
-      if (take_eq > 0) take |= e;        // all of them (a whole-bin cut takes none)
-    } else {
+    if (!eq_all) {
+      const uint32_t e = eq32[tid];
       // ties at the cut-off: the first take_eq equal keys in position order
       int ex_e, tot_e;
       block_excl_scan(__popc(e), ex_e, tot_e, sh);
@@ -1209,8 +1253,8 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
         --want;
       }
       eq_seen += tot_e;
+      if (kCut && (take & e)) tmin = min(tmin, thresh);
     }
-    if (take & e) tmin = min(tmin, thresh);
     // this thread's taken positions, ascending, after those of the threads before it
     int ex_t, tot_t;
     block_excl_scan(__popc(take), ex_t, tot_t, sh);
@@ -1242,7 +1286,7 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   };
   emit(0, true);
   for (int seg = kSeg; seg < a.L; seg += kSeg) emit(seg, false);
-  if (a.cut) {
+  if constexpr (kCut) {
     // the n_vl-th largest score: the smallest taken key (+inf when none)
     tmin = wave_min(tmin);
     if (lane == 0) sh.red[0][wave] = static_cast<int>(tmin);
@@ -1316,7 +1360,7 @@ hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb, con
     const unsigned nwg2 = static_cast<unsigned>((a.n_nw + a.wg_keys - 1) / a.wg_keys);
     hipLaunchKernelGGL(col_mass_kernel, dim3(nwg2, U, nrg), dim3(kSThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
+  hipLaunchKernelGGL(topk_kernel<false>, dim3(U), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1360,7 +1404,8 @@ hipError_t launch_refresh(const hq_dims& d, const hq_cache& c, int32_t t, const 
   else if (kb == 8) hipLaunchKernelGGL(refresh_mass_kernel<8>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
   else hipLaunchKernelGGL(refresh_mass_kernel<4>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
   a.nrg = 1;                       // the scores are complete: nothing to fold
-  hipLaunchKernelGGL(topk_kernel, dim3(U), dim3(kTopThreads), 0, s, a);
+  if (cut) hipLaunchKernelGGL(topk_kernel<true>, dim3(U), dim3(kTopThreads), 0, s, a);
+  else hipLaunchKernelGGL(topk_kernel<false>, dim3(U), dim3(kTopThreads), 0, s, a);
   return hipGetLastError();
 }
 
