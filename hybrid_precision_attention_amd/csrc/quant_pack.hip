@@ -27,6 +27,12 @@ struct PackArgs {
   int32_t k_bits, v_bits;           // code widths of the quantised region
 };
 
+// Number of nonzero bytes of w: bit 7 of each byte ends up set iff the byte
+// is nonzero (its low seven bits carry into bit 7, or bit 7 was set).
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  return __popc((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u);
+}
+
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -50,10 +56,19 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
   const int p1 = min(L, p0 + kChunk);
   const uint8_t* flag = a.flag + u * L;
 
-  // flagged non-window positions before this chunk
+  // flagged non-window positions before this chunk: sixteen flags a load over
+  // the 16-byte-aligned body of the row, single bytes for its head and tail
   int cnt = 0;
   const int lim = min(p0, n_nw);
-  for (int i = tid; i < lim; i += kPackThreads) cnt += flag[i] != 0;
+  const int head = min(lim, static_cast<int>((16u - (reinterpret_cast<uintptr_t>(flag) & 15u)) & 15u));
+  if (tid < head) cnt += flag[tid] != 0;
+  const uint4* body = reinterpret_cast<const uint4*>(flag + head);
+  const int nbody = (lim - head) >> 4;
+  for (int i = tid; i < nbody; i += kPackThreads) {
+    const uint4 w = body[i];
+    cnt += nonzero_bytes(w.x) + nonzero_bytes(w.y) + nonzero_bytes(w.z) + nonzero_bytes(w.w);
+  }
+  for (int i = head + 16 * nbody + tid; i < lim; i += kPackThreads) cnt += flag[i] != 0;
   cnt = wave_sum(cnt);
   if (lane == 0) s_wave[wave] = cnt;
   __syncthreads();
@@ -100,18 +115,26 @@ __global__ __launch_bounds__(kPackThreads) void quant_pack_kernel(PackArgs a) {
 
   const int sub = tid & 7;            // {K,V} x group
   const int kv = sub >> 2, g = sub & 3;
-  for (int t0 = 0; t0 < kChunk; t0 += kPackThreads / 8) {
-    const int tl = t0 + (tid >> 3);
-    const int pp = p0 + tl;
-    if (pp >= p1) break;
-    const int knd = s_kind[tl], sl = s_slot[tl];
-    const uint16_t* src = (kv ? a.v : a.k) + (u * L + pp) * kD + g * kGroup;
-    uint32_t x[16];
+  const int ntok = p1 - p0;
+  constexpr int kStride = kPackThreads / 8;   // tokens per pass
+  // the group of token t of the chunk (64 bytes), as 16 words
+  auto load = [&](int t, uint32_t (&x)[16]) {
+    const uint16_t* src = (kv ? a.v : a.k) + (u * L + p0 + t) * kD + g * kGroup;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 w4 = ld16(src + 8 * i);
       x[4 * i + 0] = w4.x; x[4 * i + 1] = w4.y; x[4 * i + 2] = w4.z; x[4 * i + 3] = w4.w;
     }
+  };
+  uint32_t xn[16];
+  if ((tid >> 3) < ntok) load(tid >> 3, xn);
+  for (int tl = tid >> 3; tl < ntok; tl += kStride) {
+    // this pass's group, and the next pass's in flight while it is stored
+    uint32_t x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = xn[i];
+    if (tl + kStride < ntok) load(tl + kStride, xn);
+    const int knd = s_kind[tl], sl = s_slot[tl];
     if (knd == 1) {
       const int bits = kv ? a.v_bits : a.k_bits;
       const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, sl);
