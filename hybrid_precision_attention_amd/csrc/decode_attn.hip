@@ -86,20 +86,40 @@ __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast
 // the next K4V4 slot, or copied to the vertical-line region when flagged,
 // and the new token takes its ring slot t mod W.  Lanes 0-15 carry the K
 // row, 16-31 the V row, 16 bytes each; a quantisation group is a lane quad.
+// step_load issues every load of the merge, so that they are in flight
+// while the workgroup folds the records; step_store finishes it.
+struct StepIn {
+  uint4 fresh, old;
+  int nq, nvl;
+  bool flagged;
+};
+
+__device__ __forceinline__ StepIn step_load(const DecodeArgs& a, int64_t u, int t, int lane) {
+  const bool mover = lane < 32;
+  const int kv = (lane >> 4) & 1, part = lane & 15;
+  const int W = a.W;
+  const int ev = t - W;
+  const uint16_t* win = W > 0 ? (kv ? a.c.vwin : a.c.kwin) + (u * W + t % W) * kD + 8 * part : nullptr;
+  StepIn in;
+  in.fresh = mover ? ld16((kv ? a.v_new : a.k_new) + u * kD + 8 * part) : make_uint4(0, 0, 0, 0);
+  in.old = (mover && win && ev >= 0) ? ld16(win) : make_uint4(0, 0, 0, 0);
+  in.nq = a.c.n_q[u];
+  in.nvl = a.c.n_vl[u];
+  in.flagged = a.evict_is_vl && a.evict_is_vl[u] != 0;
+  return in;
+}
+
 template <int kKB, int kVB>
-__device__ __forceinline__ void step_merge(const DecodeArgs& a, int64_t u, int t, int lane) {
+__device__ __forceinline__ void step_store(const DecodeArgs& a, int64_t u, int t, int lane, const StepIn& in) {
   const bool mover = lane < 32;
   const int kv = (lane >> 4) & 1, part = lane & 15;
   const int W = a.W;
   const int ev = t - W;
   uint16_t* win = W > 0 ? (kv ? a.c.vwin : a.c.kwin) + (u * W + t % W) * kD + 8 * part : nullptr;
-  const uint4 fresh = mover ? ld16((kv ? a.v_new : a.k_new) + u * kD + 8 * part) : make_uint4(0, 0, 0, 0);
-  const uint4 old = (mover && win && ev >= 0) ? ld16(win) : make_uint4(0, 0, 0, 0);
-  const int nq = a.c.n_q[u];
-  const int nvl = a.c.n_vl[u];
+  const int nq = in.nq, nvl = in.nvl;
   if (ev >= 0) {
-    const uint4 evv = W > 0 ? old : fresh;
-    const bool to_vl = a.evict_is_vl && a.evict_is_vl[u] != 0 && nvl < a.cap_vl;
+    const uint4 evv = W > 0 ? in.old : in.fresh;
+    const bool to_vl = in.flagged && nvl < a.cap_vl;
     if (to_vl) {
       if (mover) st16((kv ? a.c.vvl : a.c.kvl) + (u * a.cap_vl + nvl) * kD + 8 * part, evv);
       if (lane == 0) {
@@ -122,9 +142,13 @@ __device__ __forceinline__ void step_merge(const DecodeArgs& a, int64_t u, int t
       }
     }
   }
-  // the leaving token was read (above) before its slot is overwritten
-  __builtin_amdgcn_s_waitcnt(0);
-  if (win && mover) st16(win, fresh);
+  // the leaving token's read (in step_load) completes before its slot is
+  // overwritten: the empty statement consumes the loaded value, so the
+  // compiler waits for that load (and not for the younger stores)
+  if (win && mover) {
+    asm volatile("" : : "v"(in.old.x), "v"(in.old.w));
+    st16(win, in.fresh);
+  }
 }
 
 // Valid window slots of sequence b: min(W, L) at its own position L in a
@@ -1156,6 +1180,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (!s_last) return;
+  // the step's merge (its loads in flight during the fold), by the last wave
+  const bool merger = a.k_new && wave == kWaves - 1;
+  const int t_step = a.L_seq ? min(max(a.L_seq[b], 0), a.L_max) : a.L_max;
+  StepIn step_in{};
+  if (merger) step_in = step_load(a, u, t_step, lane);
 
   // The last workgroup merges the unit's records.  Thread (sub, head g, dims
   // 4c..4c+3) folds records sub, sub + S, ... with all of a chunk's loads in
@@ -1227,11 +1256,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
-  if (a.k_new && wave == 0) {
-    // the new token's position: its sequence's own in a ragged batch
-    const int t = a.L_seq ? min(max(a.L_seq[b], 0), a.L_max) : a.L_max;
-    step_merge<kKB, kVB>(a, u, t, lane);
-  }
+  if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
   if (tid == 0) a.counters[u] = 0;
 }
 
