@@ -30,7 +30,7 @@ def _flags(wl, x):
 
 
 def _evict(wl, s, mode):
-    if mode != "promote":
+    if not mode or not mode.startswith("promote"):
         return None
     e = np.zeros((wl.B, wl.Hkv), np.uint8)
     e.flat[s % 2::2] = 1                   # every other unit promotes, alternating by step
@@ -45,6 +45,7 @@ CASES = [
     ("tiny", {"L": 60}, 4, 4, None),                       # the window is not full yet
     ("tiny", {"L": 800}, 4, 4, "promote"),                 # leaving tokens promoted to lines
     ("llama31_8b", {"L": 4096}, 4, 4, "promote"),          # 8 KV heads
+    ("tiny", {"L": 800}, 4, 4, "promote-full"),            # no room for lines: promoted tokens stay K4V4
 ]
 
 
@@ -55,12 +56,22 @@ def test_step_parity(name, over, kb, vb, mode):
     x = batch(wl, steps=T + 1)
     L, W = wl.L, wl.W
     flags = _flags(wl, x)
-    cache = gpu_pack(x, L, W, wl.rho, flags, L_max=L + T + 2, extra_vl=T + 2, k_bits=kb, v_bits=vb)
+    extra = T + 2
+    if mode == "promote-full":
+        # one free line slot per unit: the first promotion fits, later ones
+        # are turned away (negative extra: fewer slots than rho would give)
+        extra = int(flags.sum(axis=2).max()) + 1 - O.n_vertical(wl.rho, L + T + 2 - W)
+    cache = gpu_pack(x, L, W, wl.rho, flags, L_max=L + T + 2, extra_vl=extra, k_bits=kb, v_bits=vb)
     refs = O.quant_pack(x["K"][:, :, :L], x["V"][:, :, :L], L, W, flags, kb, vb)
     ws = H.workspace(cache.dims, H.HQ_OP_DECODE, L + T + 1)
     out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device="cuda")
     lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
     prev = None                                   # the promotion flags of the previous step
+    # a flagged token becomes a line only while the unit's line region has
+    # room (the library's capacity rule; the oracle's cache has no capacity)
+    room = np.array([[cache.dims.cap_vl - refs[b][g]["vl_pos"].size for g in range(wl.Hkv)]
+                     for b in range(wl.B)])
+    refused = 0
     for s in range(T):
         t = L + s
         ev = _evict(wl, s, mode)
@@ -72,6 +83,11 @@ def test_step_parity(name, over, kb, vb, mode):
         O.append_merge(refs, t, x["k_dec"][s], x["v_dec"][s], prev)
         ref_o, ref_l = O.decode(refs, x["q_dec"][s], t)
         check_decode(out.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, tag=f"step {s}")
+        if ev is not None and L + s - W >= 0:
+            kept = ev & (room > 0)
+            refused += int(ev.sum() - kept.sum())
+            room -= kept
+            ev = kept
         prev = ev
     # one plain merge on both sides: the caches then hold the same staged token
     t = L + T
@@ -81,6 +97,8 @@ def test_step_parity(name, over, kb, vb, mode):
     for b in range(wl.B):
         for g in range(wl.Hkv):
             assert_unit_equal(unit_from_gpu(cache, b, g), refs[b][g], t, W, tag=f"b{b} g{g}")
+    if mode == "promote-full":
+        assert refused > 0                        # the full region did turn promotions away
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {"L": 1500}), ("qwen3_32b", {"L": 900, "B": 2}),
