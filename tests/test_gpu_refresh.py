@@ -298,3 +298,41 @@ def test_running_refresh_decode_loop():
     t = wl.L + T - 1
     for g in range(Hkv):
         assert_unit_equal(unit_from_gpu(cache, 0, g), ref[0][g], t, wl.W, tag=f"g{g}")
+
+
+def test_refresh_cut_with_split_ties():
+    """Running scores so large that the refresh's mass vanishes in their fp32
+    rounding: most positions share one value, the cut-off falls inside that
+    block and only its lowest positions are taken.  The refresh's top-k (the
+    instance that also returns the cut-off) must pick exactly the top n_vl of
+    its own scores, ties to the lower position, and return that value."""
+    wl = workload("tiny", L=700)
+    x = batch(wl, steps=2)
+    cache, ref, t = _build(wl, x, 2)
+    B, Hkv, G, nb = wl.B, wl.Hkv, wl.G, 64
+    ld = t + 1
+    qb = np.ascontiguousarray(x["qbuf"][:, :, -nb:])
+    lse = np.zeros((B, wl.Hq, nb))
+    for b in range(B):
+        for g in range(Hkv):
+            lse[b, g * G:(g + 1) * G] = _exact_lse(ref[b][g], t, qb[b, g * G:(g + 1) * G])
+    n_nw = t - wl.W
+    n_vl = O.n_vertical(wl.rho, n_nw)
+    score_in = np.full((B, Hkv, ld), 1.0e9, np.float32)
+    score_in[:, :, 5:5 + n_vl // 3] = 4.0e9                  # a third of the set clearly above
+    score = dev(score_in)
+    idx = torch.full((B, Hkv, n_vl), -1, dtype=torch.int32, device="cuda")
+    flag = torch.full((B, Hkv, ld), 7, dtype=torch.uint8, device="cuda")
+    cut = torch.full((B, Hkv), -1.0, dtype=torch.float32, device="cuda")
+    H.hq_refresh_hybrid(cache.dims, cache, t, dev(qb), dev(lse.astype(np.float32)), score, idx, flag, cut)
+    torch.cuda.synchronize()
+    sg, ig, fg, cg = score.cpu().numpy(), idx.cpu().numpy(), flag.cpu().numpy(), cut.cpu().numpy()
+    for b in range(B):
+        for g in range(Hkv):
+            s = sg[b, g, :n_nw]
+            want_cut = np.sort(s)[::-1][n_vl - 1]
+            assert (s == want_cut).sum() > n_vl - (s > want_cut).sum(), "the cut must split a tie"
+            mine = _own_topk(s, n_vl)
+            assert np.array_equal(np.nonzero(fg[b, g])[0], mine), f"b{b} g{g} flags"
+            assert np.array_equal(ig[b, g], mine), f"b{b} g{g} indices"
+            assert cg[b, g] == want_cut, f"b{b} g{g} cut"
