@@ -1010,38 +1010,48 @@ def capacity_ragged_run(H, torch, steps=4, L_cap=32768, W=128, rho=0.05, reserve
     return res
 
 
-def read_ceiling(torch, nbytes=1 << 30):
-    """A plain streaming read of 1 GiB (libhq_probe.so: 16-byte loads, eight
-    in flight per thread, every word consumed) on the same device: the
-    achievable-bandwidth reference beside the nominal peak.  The best of a
-    few grid sizes is reported."""
+def _probe_lib():
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "hybrid_precision_attention_amd", "libhq_probe.so"))
-    lib.hq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                         ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    for f in (lib.hq_probe_stream_read, lib.hq_probe_stream_read_nt):
+        f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
+                      ctypes.c_void_p]
+    return {"ordinary": lib.hq_probe_stream_read, "nt": lib.hq_probe_stream_read_nt}
+
+
+def read_ceiling(torch, nbytes=1 << 30):
+    """A plain streaming read of nbytes (libhq_probe.so: 16-byte loads, eight
+    in flight per thread, every word consumed) on the same device: the
+    achievable-bandwidth reference beside the nominal peak.  Both load
+    policies (ordinary, and the non-temporal one the decode uses) at a few
+    grid sizes; the best is reported, with each policy's best beside it."""
+    fns = _probe_lib()
     x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
-    best = None
-    for grid in (2048, 4096, 8192, 16384, 32768):
-        def run():
-            if lib.hq_probe_stream_read(x.data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, grid, s):
-                raise RuntimeError("stream probe launch failed")
-        for _ in range(2):
-            run()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = 10
-        e0.record()
-        for _ in range(n):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        gbs = nbytes / (e0.elapsed_time(e1) / n * 1e-3) / 1e9
-        if best is None or gbs > best[0]:
-            best = (gbs, grid)
+    best, per = None, {}
+    for pol, fn in fns.items():
+        for grid in (2048, 4096, 8192, 16384, 32768):
+            def run():
+                if fn(x.data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, grid, s):
+                    raise RuntimeError("stream probe launch failed")
+            for _ in range(2):
+                run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 10
+            e0.record()
+            for _ in range(n):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes / (e0.elapsed_time(e1) / n * 1e-3) / 1e9
+            per[pol] = max(per.get(pol, 0.0), round(gbs, 1))
+            if best is None or gbs > best[0]:
+                best = (gbs, grid, pol)
     del x
-    return {"read_gbs": round(best[0], 1), "bytes": nbytes, "grid": best[1],
+    return {"read_gbs": round(best[0], 1), "bytes": nbytes, "grid": best[1], "policy": best[2],
+            "read_gbs_by_policy": per,
             "kernel": "stream_read_kernel (libhq_probe.so): 16-byte loads, 256-thread workgroups"}
 
 
@@ -1049,41 +1059,38 @@ def read_ceiling_footprint(torch, footprint):
     """The same streaming read at the decode's footprint: back-to-back
     launches over R = ceil(1 GiB / footprint) buffers (so each launch reads
     from HBM, not the Infinity Cache), replayed from a HIP graph; the best of
-    a few grid sizes.  What one launch of that size can reach, latency
-    included."""
-    import ctypes
-    lib = ctypes.CDLL(os.path.join(ROOT, "hybrid_precision_attention_amd", "libhq_probe.so"))
-    lib.hq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                         ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+    both load policies and a few grid sizes.  What one launch of that size
+    can reach, latency included."""
+    fns = _probe_lib()
     nbytes = (footprint + 255) // 256 * 256
     R = max(2, math.ceil((1 << 30) / nbytes))
     bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(R)]
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     best = None
-    for grid in (256, 512, 1024, 2048, 4096):
-        n = 2 * R
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s = torch.cuda.current_stream().cuda_stream
-            for i in range(n):
-                if lib.hq_probe_stream_read(bufs[i % R].data_ptr(), nbytes, sink.data_ptr(),
-                                            0x9E3779B9, grid, s):
-                    raise RuntimeError("stream probe launch failed")
-        graph_upload(g, torch)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
-        if best is None or us < best[0]:
-            best = (us, grid)
-        del g
+    for pol, fn in fns.items():
+        for grid in (256, 512, 1024, 2048, 4096):
+            n = 2 * R
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s = torch.cuda.current_stream().cuda_stream
+                for i in range(n):
+                    if fn(bufs[i % R].data_ptr(), nbytes, sink.data_ptr(), 0x9E3779B9, grid, s):
+                        raise RuntimeError("stream probe launch failed")
+            graph_upload(g, torch)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            if best is None or us < best[0]:
+                best = (us, grid, pol)
+            del g
     del bufs
     return {"read_gbs": round(nbytes / (best[0] * 1e-6) / 1e9, 1), "us": round(best[0], 2),
-            "bytes": nbytes, "grid": best[1], "buffers": R,
+            "bytes": nbytes, "grid": best[1], "policy": best[2], "buffers": R,
             "kernel": "stream_read_kernel (libhq_probe.so), launches of the decode's byte count"}
 
 

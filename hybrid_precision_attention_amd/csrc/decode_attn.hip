@@ -7,11 +7,11 @@
 // decode paragraph; HyQuant README, Overview item 3: online softmax over
 // quantised blocks).
 //
-// Work decomposition.  Grid = (splits, units).  A unit's work list is its
-// K4V4 slots in 32-token blocks followed by its FP16 sequence (vertical lines,
-// window slots, staging) in 32-token blocks; the unit's nsplit * 4 waves take
-// the items round-robin, so every wave gets the same number of blocks to
-// within one whatever the mix.  Workgroups are four waves, so that two fit
+// Work decomposition.  Grid = (splits, units).  A unit's work is its K4V4
+// slots in 32-token blocks and its FP16 sequence (vertical lines, window
+// slots, staging) in 32-token blocks; of the unit's nsplit * 4 waves, each
+// takes a contiguous range of K4V4 blocks and every (nsplit * 4)-th FP16
+// block, sized so that every wave streams about the same bytes (wave_work).  Workgroups are four waves, so that two fit
 // on a CU at the register count of the scan and one's merge and ramp-up
 // overlap the other's streaming.  Each workgroup merges its four waves'
 // (max, sum, output) states through LDS into one partial record; the last
@@ -55,6 +55,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
+constexpr int kRecF4 = kPart / 4;   // 16-byte words per record
+constexpr int kFoldRecs = 128;      // records the final merge stages in LDS at a time (66 KB)
+constexpr int kFoldPer = (kFoldRecs * kRecF4 + kThreads - 1) / kThreads;  // 16-byte loads per thread
+constexpr int kFoldItems = 2;       // outputs (head, 4 dims) per thread: G * 32 <= 2 * kThreads
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
+constexpr int kSc1 = 16;            // cache-policy bit sc1 of a buffer load: device-scope coherent
 
 struct DecodeArgs {
   hq_cache c;
@@ -69,6 +75,7 @@ struct DecodeArgs {
   int32_t L_max;
   int32_t nsplit;                   // workgroups per unit
   float c2;                         // log2(e) / sqrt(d)
+  float slack;                      // 8 / c2: how far a block's max may pass the running reference
   // decode step with its staging merge (hq_decode_step): the new token's
   // rows take the place of the staging slot, and the unit's last workgroup
   // moves them into the ring afterwards; null for a plain decode
@@ -202,6 +209,24 @@ __device__ __forceinline__ float4_t mfma(half8_t a, half8_t b, float4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// The running reference m of an online softmax moves only when a block's
+// maximum exceeds it by `slack` (raw-score units, 8 / c2: a factor of 2^8 in
+// probability), so every p = 2^((s - m) c2) stays at most 256, which the
+// fp16 P operand and the fp32 sums hold with the same relative precision as
+// p <= 1, and the rescale of the accumulators runs a few times per scan
+// rather than at every new maximum.  The first block of a scan only sets m
+// (the accumulators are still zero).  Any reference gives the same result:
+// the partial records carry it, and the merges rescale by it.
+template <typename Scale>
+__device__ __forceinline__ void rescale_on_growth(float& m, float bm, float slack, float c2, Scale&& scale) {
+  const bool grow = bm > m + slack;
+  if (__any(grow)) {
+    const float m_new = grow ? bm : m;
+    if (__any(grow && m != -INFINITY)) scale(grow ? __builtin_amdgcn_exp2f((m - m_new) * c2) : 1.0f);
+    m = m_new;
+  }
+}
+
 // Online-softmax state of one wave: lane (head n, j).
 struct SoftState {
   float m;                          // running max of raw scores q.k (same for all j)
@@ -212,7 +237,7 @@ struct SoftState {
 // Fold one 32-token block of raw scores s[8] (tokens 4j+r and 16+4j+r, -inf
 // when masked) into the state; returns the B operand P^T for the PV MFMAs.
 // The accumulator is rescaled only when some head's running max grew.
-__device__ __forceinline__ half8_t softmax_block(SoftState& st, const float s[8], float c2) {
+__device__ __forceinline__ half8_t softmax_block(SoftState& st, const float s[8], float c2, float slack) {
   float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                    fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
   {  // max over the four j-lanes of the head (lanes l^16, l^32)
@@ -221,16 +246,12 @@ __device__ __forceinline__ half8_t softmax_block(SoftState& st, const float s[8]
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     bm = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
   }
-  const float m_new = fmaxf(st.m, bm);
-  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  if (__any(m_new > st.m)) {
-    const float alpha = __builtin_amdgcn_exp2f((st.m - m_use) * c2);
+  rescale_on_growth(st.m, bm, slack, c2, [&](float alpha) {
     st.l *= alpha;
 #pragma unroll
     for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
-  }
-  st.m = m_new;
-  const float nmc = -m_use * c2;
+  });
+  const float nmc = -(st.m == -INFINITY ? 0.0f : st.m) * c2;
   float p[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, nmc));
@@ -281,12 +302,12 @@ __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint3
   const uint32_t ova = static_cast<uint32_t>(min(tb + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
   const uint32_t ovb = static_cast<uint32_t>(min(tb + 16 + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
   const uint32_t om = static_cast<uint32_t>(min(tb + (lane >> 1), last)) * (kMetaWords * 4) + 8 * (lane & 1);
-  r.ka = ld16(kq + oka);
-  r.kb = ld16(kq + okb);
-  r.va = ld16(vq + ova);
-  r.vb = ld16(vq + ovb);
-  r.kmw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kmeta) + om);
-  r.vmw = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vmeta) + om);
+  r.ka = ld16_stream(kq + oka);
+  r.kb = ld16_stream(kq + okb);
+  r.va = ld16_stream(vq + ova);
+  r.vb = ld16_stream(vq + ovb);
+  r.kmw = ld8_stream(reinterpret_cast<const uint8_t*>(kmeta) + om);
+  r.vmw = ld8_stream(reinterpret_cast<const uint8_t*>(vmeta) + om);
 }
 
 __device__ __forceinline__ void qk_tile(float4_t& acc, uint4 codes, uint32_t meta,
@@ -302,7 +323,7 @@ __device__ __forceinline__ void qk_tile(float4_t& acc, uint4 codes, uint32_t met
 
 __device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stage& sg,
                                            const half8_t qb[4], const Masks& k, int tb, int nq,
-                                           int lane, int n, int j, float c2) {
+                                           int lane, int n, int j, float c2, float slack) {
   // stage, then read back the transposed operands
   wave_sync();
   *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
@@ -331,7 +352,7 @@ __device__ __forceinline__ void compute_k4(SoftState& st, const K4Raw& r, K4Stag
       if (tb + 16 + 4 * j + e >= nq) s[4 + e] = -INFINITY;
     }
   }
-  const half8_t pb = softmax_block(st, s, c2);
+  const half8_t pb = softmax_block(st, s, c2, slack);
 
   // V^T operands: token pairs (2p, 2p+1) interleaved so one and_or gives a
   // biased fp16 pair for both tokens
@@ -382,8 +403,8 @@ __device__ __forceinline__ void load_f16_k(uint4 kr[8], const F16Rows& f, int tb
   const uint16_t* rb = f16_row(f.kvl, f.kwin, f.kstg, tbb, f.nvl, f.nwin) + 32 * j;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    kr[kk] = ld16(ra + 8 * kk);
-    kr[4 + kk] = ld16(rb + 8 * kk);
+    kr[kk] = ld16_stream(ra + 8 * kk);
+    kr[4 + kk] = ld16_stream(rb + 8 * kk);
   }
 }
 
@@ -391,7 +412,7 @@ __device__ __forceinline__ void load_f16_k(uint4 kr[8], const F16Rows& f, int tb
 // 32j + 31 of tokens t and 16 + t; vr: dims 8n .. 8n + 7 of the lane's eight
 // tokens), tokens from `valid` on masked.
 __device__ __forceinline__ void f16_compute(SoftState& st, const half8_t qn[4], const uint4 kr[8],
-                                            const uint4 vr[8], int valid, int j, float c2) {
+                                            const uint4 vr[8], int valid, int j, float c2, float slack) {
   float4_t sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -406,7 +427,7 @@ __device__ __forceinline__ void f16_compute(SoftState& st, const half8_t qn[4], 
       if (16 + 4 * j + e >= valid) s[4 + e] = -INFINITY;
     }
   }
-  const half8_t pb = softmax_block(st, s, c2);
+  const half8_t pb = softmax_block(st, s, c2, slack);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
@@ -421,15 +442,14 @@ __device__ __forceinline__ void f16_compute(SoftState& st, const half8_t qn[4], 
   }
 }
 
-__device__ __forceinline__ void process_f16(SoftState& st, const half8_t qn[4], const F16Rows& f,
-                                            const uint4 kr[8], int tb, int n, int j, float c2) {
-  uint4 vr[8];
+// V rows of one FP16 block: lane (n, j) loads dims 8n .. 8n + 7 of its
+// eight tokens (those its PV k-slice contracts).
+__device__ __forceinline__ void load_f16_v(uint4 vr[8], const F16Rows& f, int tb, int n, int j) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int t = min(k4_token(tb, j, e), f.nf - 1);
-    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * n);
+    vr[e] = ld16_stream(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * n);
   }
-  f16_compute(st, qn, kr, vr, f.nf - tb, j, c2);
 }
 
 // ---------------------------------------------------------------------------
@@ -456,7 +476,27 @@ struct GState {
   float4_t o[8];                    // o[i][rr]: dims 32j + 8rr + i of head h, used where g == j
   float4_t corr;                    // 1024 * sum_t P'[t] (every row alike)
   float4_t mt;                      // sum_t m_v[t][j] P[h][t] (every row alike)
+  float4_t acc[8];                  // unbiased output of the blocks folded so far (flush_g)
 };
+
+// The biased accumulators hold about 1024 sum P' while the output is a
+// small fraction of that, so their fp32 rounding error, relative to the
+// output, grows with the number of blocks accumulated.  Every kFlushBlocks
+// K4V4 blocks they are folded into the unbiased acc, O = (o - corr) (1 or
+// 1/16) + mt, and restarted from zero: the error then stays at what a scan
+// of that many blocks has, however long the wave's range is.
+constexpr int kFlushBlocks = 8;
+__device__ __forceinline__ void flush_g(GState& st) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float f = (i & 1) ? 0.0625f : 1.0f;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) st.acc[i][rr] += fmaf(st.o[i][rr] - st.corr[rr], f, st.mt[rr]);
+    st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  }
+  st.corr = (float4_t){0.f, 0.f, 0.f, 0.f};
+  st.mt = (float4_t){0.f, 0.f, 0.f, 0.f};
+}
 
 // sum over the lane quad (the four group columns of a head); every lane of
 // the quad ends with the same bits
@@ -473,7 +513,7 @@ __device__ __forceinline__ half8_t k_biased(uint32_t w, const Masks& k) {
 
 // Online softmax of one block of raw scores s[8] into the grouped state;
 // p[8] gets the block's probabilities.
-__device__ __forceinline__ void softmax_g(GState& st, const float s[8], float c2, float p[8]) {
+__device__ __forceinline__ void softmax_g(GState& st, const float s[8], float c2, float slack, float p[8]) {
   float bm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
                    fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
   {  // max over the four j-lanes of the column (lanes l^16, l^32)
@@ -482,18 +522,17 @@ __device__ __forceinline__ void softmax_g(GState& st, const float s[8], float c2
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     bm = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
   }
-  const float m_new = fmaxf(st.m, bm);
-  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-  if (__any(m_new > st.m)) {
-    const float alpha = __builtin_amdgcn_exp2f((st.m - m_use) * c2);
+  rescale_on_growth(st.m, bm, slack, c2, [&](float alpha) {
     st.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[i] *= alpha;
+    for (int i = 0; i < 8; ++i) {
+      st.o[i] *= alpha;
+      st.acc[i] *= alpha;
+    }
     st.corr *= alpha;
     st.mt *= alpha;
-  }
-  st.m = m_new;
-  const float nmc = -m_use * c2;
+  });
+  const float nmc = -(st.m == -INFINITY ? 0.0f : st.m) * c2;
 #pragma unroll
   for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], c2, nmc));
   st.l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
@@ -566,9 +605,9 @@ __device__ __forceinline__ void k4_phase_a(K4Mid& x, const K4Raw& r, K4Stage& sg
   }
 }
 
-__device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Masks& k, float c2) {
+__device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Masks& k, float c2, float slack) {
   float pr[8];
-  softmax_g(st, x.s, c2, pr);
+  softmax_g(st, x.s, c2, slack, pr);
   // B operands: P' = s_v P for the codes, P for the min term
   half8_t p16;
 #pragma unroll
@@ -609,7 +648,7 @@ __device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Mas
 // scale), P for even and 16 P for odd output dims, so that the FP16 and
 // K4V4 contributions share one accumulator under O = (o - corr) (1 or 1/16) + mt.
 __device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], const uint4 kr[8],
-                                              const uint4 vr[8], int valid, int j, float c2) {
+                                              const uint4 vr[8], int valid, int j, float c2, float slack) {
   float4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -627,7 +666,7 @@ __device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], c
     }
   }
   float pr[8];
-  softmax_g(st, s, c2, pr);
+  softmax_g(st, s, c2, slack, pr);
   half8_t p1, p16x;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -648,16 +687,7 @@ __device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], c
   }
 }
 
-__device__ __forceinline__ void process_f16_g(GState& st, const half8_t qf[4], const F16Rows& f,
-                                              const uint4 kr[8], int tb, int c, int j, float c2) {
-  uint4 vr[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = min(k4_token(tb, j, e), f.nf - 1);
-    vr[e] = ld16(f16_row(f.vvl, f.vwin, f.vstg, t, f.nvl, f.nwin) + 8 * c);
-  }
-  f16_compute_g(st, qf, kr, vr, f.nf - tb, j, c2);
-}
+
 
 
 // ---------------------------------------------------------------------------
@@ -690,11 +720,11 @@ __device__ __forceinline__ void load_gen(GenRaw<kKB, kVB>& r, const uint8_t* kq,
   const uint8_t* kp = kq + t * (16 * kKB) + h * (8 * kKB);
   const uint8_t* vp = vq + t * (16 * kVB) + h * (8 * kVB);
 #pragma unroll
-  for (int i = 0; i < kKB / 2; ++i) r.k[i] = ld16(kp + 16 * i);
+  for (int i = 0; i < kKB / 2; ++i) r.k[i] = ld16_stream(kp + 16 * i);
 #pragma unroll
-  for (int i = 0; i < kVB / 2; ++i) r.v[i] = ld16(vp + 16 * i);
-  r.km = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kmeta) + t * 16 + h * 8);
-  r.vm = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vmeta) + t * 16 + h * 8);
+  for (int i = 0; i < kVB / 2; ++i) r.v[i] = ld16_stream(vp + 16 * i);
+  r.km = ld8_stream(reinterpret_cast<const uint8_t*>(kmeta) + t * 16 + h * 8);
+  r.vm = ld8_stream(reinterpret_cast<const uint8_t*>(vmeta) + t * 16 + h * 8);
 }
 
 // 64 b-bit codes (element e at bits b e .. of the little-endian words w) of
@@ -742,6 +772,34 @@ __device__ __forceinline__ void gen_operands(uint4 kr[8], uint4 vr[8], const Gen
   for (int e = 0; e < 8; ++e) vr[e] = ld16(&tl.v[k4_token(0, j, e)][8 * n]);
 }
 
+// The blocks one wave of a unit scans: K4V4 blocks [k0, k1) (a contiguous
+// range) and FP16 blocks f0, f0 + nwaves, ... below nblk_f.  An FP16 block
+// moves wF = 512 / (bytes of a quantised token) times the bytes of a K4V4
+// block (3.2 at K4V4), so the FP16 blocks go round-robin from wave 0 and the
+// K4V4 blocks fill up to a common level: every wave gets about the same
+// bytes whatever the mix.  Every wave evaluates the same float expressions
+// for its own and its neighbour's boundary, so the ranges tile [0, nblk_q).
+struct WaveWork {
+  int k0, k1, f0;
+};
+
+__device__ __forceinline__ WaveWork wave_work(int gw, int nwaves, int nblk_q, int nblk_f, float wF) {
+  const int full = nblk_f / nwaves, rem = nblk_f % nwaves;   // waves < rem hold full + 1 FP16 blocks
+  const float cA = static_cast<float>(full + 1) * wF, cB = static_cast<float>(full) * wF;
+  float level = (static_cast<float>(nblk_q) + rem * cA + (nwaves - rem) * cB) / nwaves;
+  if (level < cA) level = cB + static_cast<float>(nblk_q) / (nwaves - rem);  // waves < rem take no K4V4 block
+  const float kA = fmaxf(0.0f, level - cA), kB = fmaxf(0.0f, level - cB);
+  auto start = [&](int w) {
+    const float p = static_cast<float>(min(w, rem)) * kA + static_cast<float>(max(0, w - rem)) * kB;
+    return min(nblk_q, static_cast<int>(p + 0.5f));
+  };
+  WaveWork r;
+  r.k0 = start(gw);
+  r.k1 = gw == nwaves - 1 ? nblk_q : start(gw + 1);
+  r.f0 = gw;
+  return r;
+}
+
 // LDS image of the waves' states for up to eight heads at a time:
 // o[w][g][dim], plus each wave's running max and denominator per head.
 constexpr int kImgHeads = 8;
@@ -757,16 +815,10 @@ struct FinPart {
   float4_t o;
 };
 
-// Partial records cross XCDs.  They are written and read with device-scope
-// relaxed atomics (write-through / coherent-read of the XCD-local L2), and the
-// writer waits for its stores before counting its arrival, so no fence has to
-// write back or invalidate a whole L2.
-// 8-byte device-scope load of two adjacent record floats
-__device__ __forceinline__ float2 ld2_agent(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(float2, v);
-}
+// Partial records cross XCDs.  They are written with device-scope (sc1)
+// write-through stores and read with sc1 loads that miss the XCD-local L2,
+// and the writer waits for its stores before counting its arrival, so no
+// fence has to write back or invalidate a whole L2.
 // 16-byte store with the device-scope write-through policy (sc1), so a
 // record leaves in whole lines
 __device__ __forceinline__ void st4_agent(float* p, float4_t v) {
@@ -778,6 +830,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // K4V4 takes the grouped-code paths; other widths dequantise each block
   // into an LDS tile and use the FP16-block code
   constexpr bool kK4V4 = kKB == 4 && kVB == 4;
+  // bytes of an FP16 block over those of a quantised block (3.2 at K4V4)
+  constexpr float kF16Weight = 512.0f / (16 * (kKB + kVB) + 32);
   using Stage = std::conditional_t<kK4V4, K4Stage, DqTile>;
   // the per-wave staging areas of the scan, the image of the waves' states
   // and the partials of the final merge share LDS (barriers separate them)
@@ -785,6 +839,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     Stage stage[kWaves];                           // 14 KB (K4V4), 68 KB (tiles)
     WgImage img;                                   // 16.5 KB
     FinPart fin[kThreads];                         // 8 KB
+    float4_t fold[kFoldPer * kThreads];            // 68 KB: a chunk of records in the final merge
   } s_lds;
   __shared__ int s_last;
 
@@ -799,6 +854,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int64_t b = u / a.Hkv;
   const int h0 = static_cast<int>(u % a.Hkv) * G;
   const float c2 = a.c2;
+  const float slack = a.slack;
 
   // Every lane ends its scan with one head's state: `valid` lanes hold
   // dims 32j + 8r + i (r < 4, i < 8) of head `head` in ofin[i][r]; m_h is the
@@ -847,7 +903,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     st.m = -INFINITY;
     st.l = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) {
+      st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      st.acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    }
     st.corr = (float4_t){0.f, 0.f, 0.f, 0.f};
     st.mt = (float4_t){0.f, 0.f, 0.f, 0.f};
 
@@ -855,121 +914,145 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int gw = split * kWaves + wave;
     const int nq = min(a.c.n_q[u], a.cap_q);
     const int nblk_q = (nq + kBlk - 1) / kBlk;
-    if (gw < nblk_q) {
-      const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
-      const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
-      const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
-      const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
-      // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
-      // block when the slots are paged (offsets then relative to the block,
-      // the tail clamp inside it)
-      auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
-                          const uint32_t*& vmb, int& tb, int& nqb) {
-        if constexpr (kPaged) {
-          const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
-          kb = a.c.kq + fs * (16 * kKB);
-          vb = a.c.vq + fs * (16 * kVB);
-          kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
-          vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
-          tb = 0;
-          nqb = nq - bi * kBlk;
-        } else {
-          kb = kq;
-          vb = vq;
-          kmb = kmeta;
-          vmb = vmeta;
-          tb = bi * kBlk;
-          nqb = nq;
-        }
-      };
-      auto ld_k4 = [&](K4Raw& r, int bi) {
-        const uint8_t *kb, *vb;
-        const uint32_t *kmb, *vmb;
-        int tb, nqb;
-        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
-        load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
-      };
-      auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
-        const uint8_t *kb, *vb;
-        const uint32_t *kmb, *vmb;
-        int tb, nqb;
-        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
-        load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
-      };
-      const int last = nblk_q - 1;
-      int blk = gw;
-      if constexpr (kK4V4) {
-        K4Stage& sg = s_lds.stage[wave];
-        const Masks km = make_masks();
-        K4Raw ra, rb;
-        K4Mid x;
-        ld_k4(ra, blk);
-        for (; blk < nblk_q; blk += 2 * nwaves) {
-          ld_k4(rb, min(blk + nwaves, last));
-          k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
-          k4_phase_b(st, x, km, c2);
-          if (blk + nwaves >= nblk_q) break;
-          ld_k4(ra, min(blk + 2 * nwaves, last));
-          k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + nwaves) * kBlk, nq, lane, n, j);
-          k4_phase_b(st, x, km, c2);
-        }
+    const int nvl = min(a.c.n_vl[u], a.cap_vl);
+    const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
+    const int nwin = unit_n_win(a, b);
+    const int nf = nvl + nwin + nst;
+    const int nblk_f = (nf + kBlk - 1) / kBlk;
+    const WaveWork ww = wave_work(gw, nwaves, nblk_q, nblk_f, kF16Weight);
+    const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
+    const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
+    const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
+    const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+    // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
+    // block when the slots are paged (offsets then relative to the block,
+    // the tail clamp inside it)
+    auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
+                        const uint32_t*& vmb, int& tb, int& nqb) {
+      if constexpr (kPaged) {
+        const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
+        kb = a.c.kq + fs * (16 * kKB);
+        vb = a.c.vq + fs * (16 * kVB);
+        kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
+        vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
+        tb = 0;
+        nqb = nq - bi * kBlk;
       } else {
-        DqTile& tl = s_lds.stage[wave];
-        GenRaw<kKB, kVB> ra, rb;
-        ld_gen(ra, blk);
-        for (; blk < nblk_q; blk += 2 * nwaves) {
-          uint4 kr[8], vr[8];
-          ld_gen(rb, min(blk + nwaves, last));
-          gen_operands(kr, vr, ra, tl, lane, n, j);
-          f16_compute_g(st, qf, kr, vr, nq - blk * kBlk, j, c2);
-          if (blk + nwaves >= nblk_q) break;
-          ld_gen(ra, min(blk + 2 * nwaves, last));
-          gen_operands(kr, vr, rb, tl, lane, n, j);
-          f16_compute_g(st, qf, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
-        }
+        kb = kq;
+        vb = vq;
+        kmb = kmeta;
+        vmb = vmeta;
+        tb = bi * kBlk;
+        nqb = nq;
       }
+    };
+    auto ld_k4 = [&](K4Raw& r, int bi) {
+      const uint8_t *kb, *vb;
+      const uint32_t *kmb, *vmb;
+      int tb, nqb;
+      blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+      load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
+    };
+    auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
+      const uint8_t *kb, *vb;
+      const uint32_t *kmb, *vmb;
+      int tb, nqb;
+      blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+      load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
+    };
+    F16Rows f;
+    f.kvl = a.c.kvl + u * a.cap_vl * kD;
+    f.vvl = a.c.vvl + u * a.cap_vl * kD;
+    f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+    f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+    f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
+    f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
+    f.nvl = nvl;
+    f.nwin = nwin;
+    f.nf = nf;
+    // A wave's FP16 blocks come first: the K and V rows of the first one
+    // and the wave's first quantised block are in flight together before
+    // any compute, so no load latency is left exposed between the two
+    // parts.  Later FP16 blocks have their K rows loaded one block ahead.
+    const bool has_f = ww.f0 < nblk_f, has_k = ww.k0 < ww.k1;
+    uint4 kcur[8], vcur[8];
+    if (has_f) {
+      load_f16_k(kcur, f, ww.f0 * kBlk, n, j);
+      load_f16_v(vcur, f, ww.f0 * kBlk, n, j);
     }
-    {
-      const int nvl = min(a.c.n_vl[u], a.cap_vl);
-      const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
-      const int nwin = unit_n_win(a, b);
-      const int nf = nvl + nwin + nst;
-      const int nblk_f = (nf + kBlk - 1) / kBlk;
-      const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
-      if (first < nblk_f) {
-        F16Rows f;
-        f.kvl = a.c.kvl + u * a.cap_vl * kD;
-        f.vvl = a.c.vvl + u * a.cap_vl * kD;
-        f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
-        f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-        f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
-        f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
-        f.nvl = nvl;
-        f.nwin = nwin;
-        f.nf = nf;
-        int blk = first;
-        uint4 kcur[8];
-        load_f16_k(kcur, f, blk * kBlk, n, j);
-        for (; blk < nblk_f; blk += nwaves) {
+    // one block of prefetch in two alternating buffers (no register copies);
+    // the loads are unconditional (past the end they re-read the wave's last
+    // block) so that the wait before a compute only covers its own loads
+    const int last = ww.k1 - 1;
+    if constexpr (kK4V4) {
+      K4Stage& sg = s_lds.stage[wave];
+      const Masks km = make_masks();
+      K4Raw ra, rb;
+      K4Mid x;
+      if (has_k) ld_k4(ra, ww.k0);
+      if (has_f) {
+        int blk = ww.f0;
+        for (; blk + nwaves < nblk_f; blk += nwaves) {
           uint4 knxt[8];
-          load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
-          process_f16_g(st, qf, f, kcur, blk * kBlk, n, j, c2);
+          load_f16_k(knxt, f, (blk + nwaves) * kBlk, n, j);
+          f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
 #pragma unroll
           for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+          load_f16_v(vcur, f, (blk + nwaves) * kBlk, n, j);
+        }
+        f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+      }
+      if (has_k) {
+        int blk = ww.k0;
+        for (; blk < ww.k1; blk += 2) {
+          ld_k4(rb, min(blk + 1, last));
+          k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
+          k4_phase_b(st, x, km, c2, slack);
+          if (blk + 1 >= ww.k1) break;
+          ld_k4(ra, min(blk + 2, last));
+          k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + 1) * kBlk, nq, lane, n, j);
+          k4_phase_b(st, x, km, c2, slack);
+          if ((blk + 2 - ww.k0) % kFlushBlocks == 0) flush_g(st);
+        }
+      }
+    } else {
+      DqTile& tl = s_lds.stage[wave];
+      GenRaw<kKB, kVB> ra, rb;
+      if (has_k) ld_gen(ra, ww.k0);
+      if (has_f) {
+        int blk = ww.f0;
+        for (; blk + nwaves < nblk_f; blk += nwaves) {
+          uint4 knxt[8];
+          load_f16_k(knxt, f, (blk + nwaves) * kBlk, n, j);
+          f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+          load_f16_v(vcur, f, (blk + nwaves) * kBlk, n, j);
+        }
+        f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+      }
+      if (has_k) {
+        int blk = ww.k0;
+        for (; blk < ww.k1; blk += 2) {
+          uint4 kr[8], vr[8];
+          ld_gen(rb, min(blk + 1, last));
+          gen_operands(kr, vr, ra, tl, lane, n, j);
+          f16_compute_g(st, qf, kr, vr, nq - blk * kBlk, j, c2, slack);
+          if (blk + 1 >= ww.k1) break;
+          ld_gen(ra, min(blk + 2, last));
+          gen_operands(kr, vr, rb, tl, lane, n, j);
+          f16_compute_g(st, qf, kr, vr, nq - (blk + 1) * kBlk, j, c2, slack);
         }
       }
     }
-    // the head's state, unbiased: O = (o - corr) (1 or 1/16) + mt
+    // the head's state, unbiased: acc + (o - corr) (1 or 1/16) + mt
     head = h;
     valid = active;
     m_h = st.m;
     l_h = st.l;
+    flush_g(st);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float f = (i & 1) ? 0.0625f : 1.0f;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) ofin[i][rr] = fmaf(st.o[i][rr] - st.corr[rr], f, st.mt[rr]);
-    }
+    for (int i = 0; i < 8; ++i) ofin[i] = st.acc[i];
   } else {
     // this lane's slice of the query: head h0 + n, dims 32j..32j+31
     uint4 qraw[4];
@@ -988,127 +1071,134 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   #pragma unroll
     for (int i = 0; i < 8; ++i) st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    // The unit's work list: its K4V4 blocks, then its FP16 blocks (vertical
-    // lines, window, staging), 32 tokens each.  Wave w of workgroup `split`
-    // (global wave gw of the unit's nsplit * 8) takes items gw, gw + nwaves, ...
+    // The unit's work: its K4V4 blocks, then its FP16 blocks (vertical
+    // lines, window, staging), 32 tokens each; wave w of workgroup `split` is
+    // wave gw of the unit's nsplit * 4 and scans the blocks wave_work gives it.
     const int nwaves = nsplit * kWaves;
     const int gw = split * kWaves + wave;
     const int nq = min(a.c.n_q[u], a.cap_q);
     const int nblk_q = (nq + kBlk - 1) / kBlk;
-    if (gw < nblk_q) {
-      const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
-      const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
-      const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
-      const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
-      // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
-      // block when the slots are paged (offsets then relative to the block,
-      // the tail clamp inside it)
-      auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
-                          const uint32_t*& vmb, int& tb, int& nqb) {
-        if constexpr (kPaged) {
-          const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
-          kb = a.c.kq + fs * (16 * kKB);
-          vb = a.c.vq + fs * (16 * kVB);
-          kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
-          vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
-          tb = 0;
-          nqb = nq - bi * kBlk;
-        } else {
-          kb = kq;
-          vb = vq;
-          kmb = kmeta;
-          vmb = vmeta;
-          tb = bi * kBlk;
-          nqb = nq;
-        }
-      };
-      auto ld_k4 = [&](K4Raw& r, int bi) {
-        const uint8_t *kb, *vb;
-        const uint32_t *kmb, *vmb;
-        int tb, nqb;
-        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
-        load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
-      };
-      auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
-        const uint8_t *kb, *vb;
-        const uint32_t *kmb, *vmb;
-        int tb, nqb;
-        blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
-        load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
-      };
-      // one block of prefetch in two alternating buffers (no register copies);
-      // the loads are unconditional (past the end they re-read the last block)
-      // so that the wait before a compute only covers its own loads
-      const int last = nblk_q - 1;
-      int blk = gw;
-      if constexpr (kK4V4) {
-        half8_t qb[4];
-  #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const half8_t nat = as_half8(qraw[kk]);
-          qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
-        }
-        K4Stage& sg = s_lds.stage[wave];
-        const Masks km = make_masks();
-        K4Raw ra, rb;
-        ld_k4(ra, blk);
-        for (; blk < nblk_q; blk += 2 * nwaves) {
-          ld_k4(rb, min(blk + nwaves, last));
-          compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2);
-          if (blk + nwaves >= nblk_q) break;
-          ld_k4(ra, min(blk + 2 * nwaves, last));
-          compute_k4(st, rb, sg, qb, km, (blk + nwaves) * kBlk, nq, lane, n, j, c2);
-        }
+    const int nvl = min(a.c.n_vl[u], a.cap_vl);
+    const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
+    const int nwin = unit_n_win(a, b);
+    const int nf = nvl + nwin + nst;
+    const int nblk_f = (nf + kBlk - 1) / kBlk;
+    const WaveWork ww = wave_work(gw, nwaves, nblk_q, nblk_f, kF16Weight);
+    const uint8_t* kq = a.c.kq + u * a.cap_q * (16 * kKB);
+    const uint8_t* vq = a.c.vq + u * a.cap_q * (16 * kVB);
+    const uint32_t* kmeta = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + u * a.cap_q * kMetaWords;
+    const uint32_t* vmeta = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + u * a.cap_q * kMetaWords;
+    // block bi of the unit's K4V4 slots: at the unit's base, or at its pool
+    // block when the slots are paged (offsets then relative to the block,
+    // the tail clamp inside it)
+    auto blk_ptrs = [&](int bi, const uint8_t*& kb, const uint32_t*& kmb, const uint8_t*& vb,
+                        const uint32_t*& vmb, int& tb, int& nqb) {
+      if constexpr (kPaged) {
+        const int64_t fs = k4_slot(a.c.k4_pages, a.cap_q, u, bi * kBlk);
+        kb = a.c.kq + fs * (16 * kKB);
+        vb = a.c.vq + fs * (16 * kVB);
+        kmb = reinterpret_cast<const uint32_t*>(a.c.kq_meta) + fs * kMetaWords;
+        vmb = reinterpret_cast<const uint32_t*>(a.c.vq_meta) + fs * kMetaWords;
+        tb = 0;
+        nqb = nq - bi * kBlk;
       } else {
-        half8_t qn[4];
-  #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
-        DqTile& tl = s_lds.stage[wave];
-        GenRaw<kKB, kVB> ra, rb;
-        ld_gen(ra, blk);
-        for (; blk < nblk_q; blk += 2 * nwaves) {
-          uint4 kr[8], vr[8];
-          ld_gen(rb, min(blk + nwaves, last));
-          gen_operands(kr, vr, ra, tl, lane, n, j);
-          f16_compute(st, qn, kr, vr, nq - blk * kBlk, j, c2);
-          if (blk + nwaves >= nblk_q) break;
-          ld_gen(ra, min(blk + 2 * nwaves, last));
-          gen_operands(kr, vr, rb, tl, lane, n, j);
-          f16_compute(st, qn, kr, vr, nq - (blk + nwaves) * kBlk, j, c2);
+        kb = kq;
+        vb = vq;
+        kmb = kmeta;
+        vmb = vmeta;
+        tb = bi * kBlk;
+        nqb = nq;
+      }
+    };
+    auto ld_k4 = [&](K4Raw& r, int bi) {
+      const uint8_t *kb, *vb;
+      const uint32_t *kmb, *vmb;
+      int tb, nqb;
+      blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+      load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
+    };
+    auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
+      const uint8_t *kb, *vb;
+      const uint32_t *kmb, *vmb;
+      int tb, nqb;
+      blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
+      load_gen(r, kb, kmb, vb, vmb, tb, nqb, lane);
+    };
+    F16Rows f;
+    f.kvl = a.c.kvl + u * a.cap_vl * kD;
+    f.vvl = a.c.vvl + u * a.cap_vl * kD;
+    f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
+    f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
+    f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
+    f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
+    f.nvl = nvl;
+    f.nwin = nwin;
+    f.nf = nf;
+    // A wave's FP16 blocks come first: the K and V rows of the first one
+    // and the wave's first quantised block are in flight together before
+    // any compute, so no load latency is left exposed between the two
+    // parts.  Later FP16 blocks have their K rows loaded one block ahead.
+    const bool has_f = ww.f0 < nblk_f, has_k = ww.k0 < ww.k1;
+    uint4 kcur[8], vcur[8];
+    if (has_f) {
+      load_f16_k(kcur, f, ww.f0 * kBlk, n, j);
+      load_f16_v(vcur, f, ww.f0 * kBlk, n, j);
+    }
+    const int last = ww.k1 - 1;
+    half8_t qn[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
+    auto f16_part = [&]() {
+      if (!has_f) return;
+      int blk = ww.f0;
+      for (; blk + nwaves < nblk_f; blk += nwaves) {
+        uint4 knxt[8];
+        load_f16_k(knxt, f, (blk + nwaves) * kBlk, n, j);
+        f16_compute(st, qn, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+        load_f16_v(vcur, f, (blk + nwaves) * kBlk, n, j);
+      }
+      f16_compute(st, qn, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+    };
+    if constexpr (kK4V4) {
+      half8_t qb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const half8_t nat = as_half8(qraw[kk]);
+        qb[kk] = __builtin_shufflevector(nat, nat, 0, 4, 1, 5, 2, 6, 3, 7);
+      }
+      K4Stage& sg = s_lds.stage[wave];
+      const Masks km = make_masks();
+      K4Raw ra, rb;
+      if (has_k) ld_k4(ra, ww.k0);
+      f16_part();
+      if (has_k) {
+        int blk = ww.k0;
+        for (; blk < ww.k1; blk += 2) {
+          ld_k4(rb, min(blk + 1, last));
+          compute_k4(st, ra, sg, qb, km, blk * kBlk, nq, lane, n, j, c2, slack);
+          if (blk + 1 >= ww.k1) break;
+          ld_k4(ra, min(blk + 2, last));
+          compute_k4(st, rb, sg, qb, km, (blk + 1) * kBlk, nq, lane, n, j, c2, slack);
         }
       }
-    }
-    {
-      const int nvl = min(a.c.n_vl[u], a.cap_vl);
-      const int nst = a.k_new ? 1 : min(a.c.n_stg[u], a.cap_stg);
-      const int nwin = unit_n_win(a, b);
-      const int nf = nvl + nwin + nst;
-      const int nblk_f = (nf + kBlk - 1) / kBlk;
-      // this wave's first item past the K4 blocks
-      const int first = gw + max(0, (nblk_q - gw + nwaves - 1) / nwaves) * nwaves - nblk_q;
-      if (first < nblk_f) {
-        half8_t qn[4];
-  #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qn[kk] = as_half8(qraw[kk]);
-        F16Rows f;
-        f.kvl = a.c.kvl + u * a.cap_vl * kD;
-        f.vvl = a.c.vvl + u * a.cap_vl * kD;
-        f.kwin = a.W > 0 ? a.c.kwin + u * a.W * kD : nullptr;
-        f.vwin = a.W > 0 ? a.c.vwin + u * a.W * kD : nullptr;
-        f.kstg = a.k_new ? a.k_new + u * kD : a.c.kstg + u * a.cap_stg * kD;
-        f.vstg = a.k_new ? a.v_new + u * kD : a.c.vstg + u * a.cap_stg * kD;
-        f.nvl = nvl;
-        f.nwin = nwin;
-        f.nf = nf;
-        int blk = first;
-        uint4 kcur[8];
-        load_f16_k(kcur, f, blk * kBlk, n, j);
-        for (; blk < nblk_f; blk += nwaves) {
-          uint4 knxt[8];
-          load_f16_k(knxt, f, min(blk + nwaves, nblk_f - 1) * kBlk, n, j);
-          process_f16(st, qn, f, kcur, blk * kBlk, n, j, c2);
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
+    } else {
+      DqTile& tl = s_lds.stage[wave];
+      GenRaw<kKB, kVB> ra, rb;
+      if (has_k) ld_gen(ra, ww.k0);
+      f16_part();
+      if (has_k) {
+        int blk = ww.k0;
+        for (; blk < ww.k1; blk += 2) {
+          uint4 kr[8], vr[8];
+          ld_gen(rb, min(blk + 1, last));
+          gen_operands(kr, vr, ra, tl, lane, n, j);
+          f16_compute(st, qn, kr, vr, nq - blk * kBlk, j, c2, slack);
+          if (blk + 1 >= ww.k1) break;
+          ld_gen(ra, min(blk + 2, last));
+          gen_operands(kr, vr, rb, tl, lane, n, j);
+          f16_compute(st, qn, kr, vr, nq - (blk + 1) * kBlk, j, c2, slack);
         }
       }
     }
@@ -1174,7 +1264,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(a.counters + u, 1, __ATOMIC_RELAXED,
+    const int old = __hip_atomic_fetch_add(a.counters + u * kCounterStride, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     s_last = (old == nsplit - 1);
   }
@@ -1186,61 +1276,100 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   StepIn step_in{};
   if (merger) step_in = step_load(a, u, t_step, lane);
 
-  // The last workgroup merges the unit's records.  Thread (sub, head g, dims
-  // 4c..4c+3) folds records sub, sub + S, ... with all of a chunk's loads in
-  // flight at once; the S partials of an output are then combined in LDS.
+  // The last workgroup merges the unit's nsplit * G records, kFoldRecs at a
+  // time: every thread issues its share of a chunk's 16-byte device-scope
+  // loads at once (whole records, consecutive lanes on consecutive 16 bytes;
+  // the next chunk's loads are in flight while a chunk is folded), the chunk
+  // goes to LDS, and thread (sub, head g, dims 4c..4c+3) folds the records of
+  // its output with split index = sub (mod S), 16 at a time with all their
+  // LDS reads in flight.  The S partials of an output are combined in LDS at
+  // the end.
+  const int nrec = nsplit * G;
   const int items = G * (kD / 4);
   const int S = max(1, kThreads / items);
-  for (int it0 = 0; it0 < items; it0 += kThreads) {
-    const int item = it0 + tid % items;
-    const int sub = tid / items;
-    const bool active = sub < S && item < items;
-    FinPart part = {-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-    if (active) {
+  const int sub = tid / items;                     // < S when items <= kThreads
+  const int n_items = (items + kThreads - 1) / kThreads;   // outputs per thread (1 or 2)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      recs, static_cast<short>(0), nrec * kPart * 4, kRsrcWord3);
+  FinPart part[kFoldItems];
+#pragma unroll
+  for (int q = 0; q < kFoldItems; ++q) part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+  float4_t ld[kFoldPer];
+  auto load_chunk = [&](int r0) {
+    const int nf4 = min(kFoldRecs, nrec - r0) * kRecF4;
+#pragma unroll
+    for (int k = 0; k < kFoldPer; ++k)
+      ld[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                  rs, (r0 * kRecF4 + min(tid + k * kThreads, nf4 - 1)) * 16, 0, kSc1));
+  };
+  load_chunk(0);
+  for (int r0 = 0; r0 < nrec; r0 += kFoldRecs) {
+    const int r1 = min(nrec, r0 + kFoldRecs);
+    const int nf4 = (r1 - r0) * kRecF4;
+    if (r0 > 0) __syncthreads();                   // the previous chunk is folded
+#pragma unroll
+    for (int k = 0; k < kFoldPer; ++k) s_lds.fold[tid + k * kThreads] = ld[k];   // past nf4: unused copies
+    __syncthreads();
+    if (r1 < nrec) load_chunk(r1);
+#pragma unroll
+    for (int q = 0; q < kFoldItems; ++q) {
+      if (q >= n_items) break;
+      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+      if (item >= items || sub >= S) continue;
       const int g = item >> 5, c = item & 31;
-      const float* base = recs + static_cast<int64_t>(g) * kPart;
-      constexpr int kChunk = 16;
-      for (int s0 = sub; s0 < nsplit; s0 += kChunk * S) {
-        float2 ml[kChunk], o01[kChunk], o23[kChunk];
+      // this output's records in the chunk: split s = s0, s0 + S, ... with
+      // r0 <= s G + g < r1, at LDS records i0, i0 + step, ...
+      int s0 = r0 > g ? (r0 - g + G - 1) / G : 0;
+      s0 += ((sub - s0 % S) % S + S) % S;
+      const int i0 = s0 * G + g - r0, step = S * G;
+      const int cnt = i0 < r1 - r0 ? (r1 - r0 - 1 - i0) / step + 1 : 0;
+      const float* lds = reinterpret_cast<const float*>(s_lds.fold);
+      for (int k0 = 0; k0 < cnt; k0 += 8) {
+        float m8[8], l8[8];
+        float4_t o8[8];
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const int sidx = min(s0 + k * S, nsplit - 1);   // clamped; weight 0 below
-          const float* rec = base + static_cast<int64_t>(sidx) * G * kPart;
-          ml[k] = ld2_agent(rec);
-          o01[k] = ld2_agent(rec + 4 + 4 * c);
-          o23[k] = ld2_agent(rec + 6 + 4 * c);
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t at = static_cast<uint32_t>(i0 + min(k0 + k, cnt - 1) * step) * kPart;
+          const float2 ml = *reinterpret_cast<const float2*>(lds + at);
+          m8[k] = k0 + k < cnt ? ml.x : -INFINITY;
+          l8[k] = ml.y;
+          o8[k] = *reinterpret_cast<const float4_t*>(lds + at + 4 + 4 * c);
         }
-        float mx = part.m;
+        const float mx = fmaxf(fmaxf(fmaxf(part[q].m, fmaxf(m8[0], m8[1])), fmaxf(m8[2], m8[3])),
+                               fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        const float mu = mx == -INFINITY ? 0.0f : mx;
+        const float fa = __builtin_amdgcn_exp2f((part[q].m - mu) * c2);
+        part[q].l *= fa;
+        part[q].o *= fa;
 #pragma unroll
-        for (int k = 0; k < kChunk; ++k)
-          if (s0 + k * S < nsplit) mx = fmaxf(mx, ml[k].x);
-        if (mx == -INFINITY) continue;
-        const float fa = __builtin_amdgcn_exp2f((part.m - mx) * c2);
-        part.l *= fa;
-        part.o *= fa;
-#pragma unroll
-        for (int k = 0; k < kChunk; ++k) {
-          const float f = (s0 + k * S < nsplit) ? __builtin_amdgcn_exp2f((ml[k].x - mx) * c2) : 0.0f;
-          part.l = fmaf(f, ml[k].y, part.l);
-          part.o += f * (float4_t){o01[k].x, o01[k].y, o23[k].x, o23[k].y};
+        for (int k = 0; k < 8; ++k) {
+          const float f = __builtin_amdgcn_exp2f((m8[k] - mu) * c2);
+          part[q].l = fmaf(f, l8[k], part[q].l);
+          part[q].o += f * o8[k];
         }
-        part.m = mx;
+        part[q].m = mx;
       }
     }
-    if (it0 > 0) __syncthreads();                  // previous round's partials read
-    s_lds.fin[tid] = part;
+  }
+#pragma unroll
+  for (int q = 0; q < kFoldItems; ++q) {
+    if (q >= n_items) break;                       // uniform: every thread has the same n_items
+    const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+    const bool active = item < items && sub < S;
+    __syncthreads();                               // the fold area / previous round's partials are free
+    s_lds.fin[tid] = part[q];
     __syncthreads();
     if (active && sub == 0) {
       float mx = -INFINITY;
-      for (int q = 0; q < S; ++q) mx = fmaxf(mx, s_lds.fin[tid + q * items].m);
+      for (int w = 0; w < S; ++w) mx = fmaxf(mx, s_lds.fin[tid + w * items].m);
       float lt = 0.0f;
       float4_t acc = {0.f, 0.f, 0.f, 0.f};
       if (mx != -INFINITY) {
-        for (int q = 0; q < S; ++q) {
-          const FinPart& pq = s_lds.fin[tid + q * items];
-          const float f = __builtin_amdgcn_exp2f((pq.m - mx) * c2);
-          lt = fmaf(f, pq.l, lt);
-          acc += f * pq.o;
+        for (int w = 0; w < S; ++w) {
+          const FinPart& pw = s_lds.fin[tid + w * items];
+          const float f = __builtin_amdgcn_exp2f((pw.m - mx) * c2);
+          lt = fmaf(f, pw.l, lt);
+          acc += f * pw.o;
         }
       }
       const int g = item >> 5, c = item & 31;
@@ -1257,7 +1386,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
   }
   if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
-  if (tid == 0) a.counters[u] = 0;
+  if (tid == 0) a.counters[u * kCounterStride] = 0;
 }
 
 }  // namespace
@@ -1276,7 +1405,7 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.q = q;
   a.out = out;
   a.lse = lse;
-  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.counters = reinterpret_cast<int32_t*>(ws);   // counter of unit u at word u * kCounterStride
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_counter_bytes(d));
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
@@ -1288,6 +1417,7 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.n_win = plan.n_win;
   a.nsplit = plan.nsplit;
   a.c2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d.d)));
+  a.slack = 8.0f / a.c2;
   (void)L;
   dim3 grid(plan.nsplit, d.B * d.Hkv);
   const int kb = kv_bits(d.k_bits), vb = kv_bits(d.v_bits);

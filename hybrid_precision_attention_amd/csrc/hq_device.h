@@ -179,6 +179,21 @@ __device__ __forceinline__ int64_t k4_slot(const int32_t* pages, int32_t cap_q, 
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+
+// Loads of data a launch reads once (the cache regions the decode scan
+// streams): the non-temporal policy (nt) keeps them from displacing L2 and
+// Infinity Cache contents they would never be read from again.  The decode's
+// HBM rate at B = 32, L = 32K went from 5.6 to 6.5 TB/s with them.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8_stream(const void* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void st16(void* p, uint4 v) {
   *reinterpret_cast<uint4*>(p) = v;
 }

@@ -21,7 +21,8 @@ constexpr int kMaxGroup = 16;      // query heads per KV head handled by one MFM
 constexpr int kCUs = 256;          // MI355X compute units
 constexpr int kDecodeWaves = 4;    // waves per decode workgroup (two workgroups per CU)
 constexpr int kBlk = 32;           // tokens per decode block
-constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most
+constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most (short prefixes)
+constexpr int kMaxPerCU = 2;       // decode workgroups per CU the byte plan aims at, at most
 constexpr int kMaxSplit = 128;     // decode workgroups per unit, at most (LDS of the final merge)
 constexpr int kPartFloats = 132;   // m, l, 2 pad, o[128]
 constexpr double kWgBytes = 384.0 * 1024;  // bytes one decode workgroup streams at small batch
@@ -74,8 +75,12 @@ int32_t n_vertical(double rho, int32_t n_nw) {
 }
 
 // Splits per unit for the decode: workgroups carry about equal bytes (160 per
-// K4V4 token, 16 (k_bits + v_bits) + 32 at other widths, 512 per FP16 token).  Small problems get one workgroup per CU;
-// large ones up to eight per CU so that uneven finishing times average out.
+// K4V4 token, 16 (k_bits + v_bits) + 32 at other widths, 512 per FP16 token).
+// Small problems get one workgroup per CU; large ones two, so that the
+// launch is one round of long workgroups (two resident per CU at the scan's
+// register count): each workgroup's start-up loads and its merge then come
+// once per CU slot, not once per 384 KB (B = 32 at L = 32K: 268 us against
+// 283 us with up to eight workgroups per CU).
 static int64_t max_splits(int64_t units) {
   return std::min<int64_t>(kMaxSplit, cdiv(kMaxWG, units) + 3);
 }
@@ -94,7 +99,7 @@ DecodePlan plan_decode(const hq_dims& d, int32_t L) {
   const double q_tok = 16.0 * (kv_bits(d.k_bits) + kv_bits(d.v_bits)) + 32.0;
   const double per_unit = q_tok * static_cast<double>(n_q) + 512.0 * static_cast<double>(n_f);
   const double total = static_cast<double>(units) * per_unit;
-  const double per_cu = std::min(8.0, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
+  const double per_cu = std::min<double>(kMaxPerCU, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
   const double wg_bytes = std::max(total / (kCUs * per_cu), 1.0);
   const int64_t items = cdiv(n_q, kBlk) + cdiv(n_f, kBlk);
   int64_t ns = std::max<int64_t>(1, std::llround(per_unit / wg_bytes));
@@ -108,7 +113,7 @@ DecodePlan plan_decode(const hq_dims& d, int32_t L) {
 
 size_t decode_counter_bytes(const hq_dims& d) {
   const size_t units = static_cast<size_t>(d.B) * d.Hkv;
-  return (units * 4 + 255) / 256 * 256;
+  return (units * 4 * kCounterStride + 255) / 256 * 256;
 }
 
 size_t decode_ws_bytes(const hq_dims& d, int32_t /*L_max*/) {

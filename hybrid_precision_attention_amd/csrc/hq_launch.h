@@ -17,6 +17,11 @@ struct DecodePlan {
   int n_win;          // valid window slots: min(W, L)
 };
 
+// Decode arrival counters: one int32 per unit, each on its own 128-byte line
+// (the atomics of a unit's workgroups then do not queue behind those of the
+// other units on one line).
+constexpr int kCounterStride = 32;
+
 DecodePlan plan_decode(const hq_dims& d, int32_t L);
 size_t decode_ws_bytes(const hq_dims& d, int32_t L_max);
 size_t decode_counter_bytes(const hq_dims& d);

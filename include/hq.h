@@ -200,9 +200,9 @@ int hq_append_merge(const hq_dims* dims, const hq_cache* cache, int32_t t,
  * lse = -inf.
  *
  * ws: at least hq_workspace_bytes(dims, HQ_OP_DECODE, L) bytes.  Its first
- * 4*B*Hkv bytes are arrival counters that must be zero before the first call
- * that uses this workspace (allocate it zero-filled); every completed call
- * leaves them zero again.
+ * 128*B*Hkv bytes hold the arrival counters (one int32 per unit, 128 bytes
+ * apart), which must be zero before the first call that uses this workspace
+ * (allocate it zero-filled); every completed call leaves them zero again.
  * Requires L >= 0.
  */
 int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L,

@@ -1,7 +1,7 @@
 /*
  * hq_probe.h -- measurement helper beside libhq.so (not part of the method).
  *
- * libhq_probe.so holds one plain streaming-read kernel, the achievable-HBM
+ * libhq_probe.so holds a plain streaming-read kernel, the achievable-HBM
  * reference that the benchmark reports next to the nominal 8 TB/s peak.
  */
 #ifndef HQ_PROBE_H
@@ -25,6 +25,11 @@ extern "C" {
  */
 int hq_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
                          int grid, hipStream_t stream);
+
+/* The same read with non-temporal loads (the policy of the decode scan's
+ * cache loads). */
+int hq_probe_stream_read_nt(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
+                            int grid, hipStream_t stream);
 
 #ifdef __cplusplus
 }
