@@ -4,12 +4,15 @@
 A timed *step* is one streaming decode step of the whole hot path, one
 hq_decode_step launch: the staging merge of the new token (the token leaving
 the window quantised or promoted, the new one into the ring) and the decode
-attention (split-K fused scan + in-kernel log-sum-exp merge).  Every 64th
-step also runs the vertical-line refresh hq_select_vertical over 64 buffered
-queries (the pages' refresh cadence), so its cost is amortised into the
-step.  The same steps as two launches (hq_append_merge, then hq_decode_attn)
-are timed too (``step_us_unfused``).  hq_quant_pack, which builds the cache
-once after the prefill, is timed on its own and reported beside the step.
+attention (split-K fused scan + in-kernel log-sum-exp merge).  The first step
+of every 64-step period of the timed window also runs the vertical-line
+refresh hq_select_vertical over 64 buffered queries (the pages' refresh
+cadence), so K timed steps hold ceil(K / 64) refreshes.  The same steps
+without the refresh (``step_us_decode_only``) and as two launches
+(hq_append_merge, then hq_decode_attn; ``step_us_unfused``) are timed too,
+and ``step_us_amortized_64`` is the decode-only step plus 1/64 of the
+measured refresh.  hq_quant_pack, which builds the cache once after the
+prefill, is timed on its own and reported beside the step.
 
 The cache footprint of one small-batch layer fits in the 256 MB Infinity
 Cache, so the step rotates over R independent cache replicas (R * footprint
@@ -23,10 +26,12 @@ the selection, its one-pass form and the decode-time refresh timed at 32K),
 a Qwen3-32B-shaped layer streaming 128 tokens at B = 32, the read ceiling,
 the prefill attention and the capacity runs.
 
-Prints one JSON line.  ``value`` is the effective HBM bandwidth of the step:
-algorithmic bytes (what the method must move: 160 B per K4V4 token and 512 B
-per FP16 token per KV head, q in, out, merge and amortised refresh traffic)
-divided by the measured step time.
+Prints one JSON line.  ``value`` is the effective HBM bandwidth of the timed
+window: the algorithmic bytes of the launches it ran (what the method must
+move: 160 B per K4V4 token and 512 B per FP16 token per KV head, q in, out,
+merge traffic, and both selection passes over the dense keys for each
+refresh) divided by the window's measured time, so value * ms_per_step * K
+equals those bytes.
 """
 from __future__ import annotations
 
@@ -183,7 +188,7 @@ def main():
     R = args.replicas or max(1, math.ceil((1 << 30) / max(footprint, 1)))
     # positions a replica may advance: warm-up, the timed steps, the same
     # number unfused, the per-row merges and the refresh timing
-    L_max = L + total_steps + args.steps + 64 + 16
+    L_max = L + total_steps + 3 * args.steps + 64 + 16
     base = H.HybridCache.allocate(B, Hq, Hkv, W, wl.rho, L_max)
     H.hq_quant_pack(base.dims, K, V, L, vl_flag, base)
     torch.cuda.synchronize()
@@ -218,7 +223,7 @@ def main():
         stp = [H.bind_step(dims, caches[r], q_new[0], out, ws[r], lse=lse, stream=stream)
                for r in range(R)]
 
-        def step(i):
+        def step(i, refresh=False):
             r = i % R
             t = pos[r]
             j = i % pool
@@ -228,7 +233,7 @@ def main():
                 mrg[r](t, kp[j], vp[j])
                 dec[r](t, qp[j])
             pos[r] = t + 1
-            if i % REFRESH == REFRESH - 1:
+            if refresh:
                 H.hq_select_vertical(dims_sel, qbuf, K_rep[(i // REFRESH) % R_sel], L, score,
                                      vl_idx, vl_flag, ws_sel, stream=stream)
         return step, dec
@@ -244,7 +249,7 @@ def main():
 
     eager_step, _ = make_step(torch.cuda.current_stream())
     for i in range(args.warmup):
-        eager_step(i)
+        eager_step(i, refresh=(i % REFRESH == 0))
     torch.cuda.synchronize()
 
     # The K timed steps are captured once into a HIP graph (through torch) and
@@ -256,10 +261,15 @@ def main():
         graph_upload(g, torch)
         return g
 
+    # The refresh runs at the first step of every 64-step period of the timed
+    # window (the pages' cadence), so K timed steps hold ceil(K / 64)
+    # refreshes and `value` counts exactly the bytes those launches move.
+    n_refresh = sum(1 for k in range(args.steps) if k % REFRESH == 0)
+
     def timed_steps(stream):
         st, _ = make_step(stream)
         for k in range(args.steps):
-            st(args.warmup + k)
+            st(args.warmup + k, refresh=(k % REFRESH == 0))
     g_steps = capture(timed_steps)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -273,19 +283,22 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
 
-    # the same number of steps with the merge and the decode as two launches
-    def timed_steps_unfused(stream):
-        st, _ = make_step(stream, fused=False)
-        for k in range(args.steps):
-            st(args.warmup + args.steps + k)
-    g_unf = capture(timed_steps_unfused)
-    torch.cuda.synchronize()
-    start.record()
-    g_unf.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step_unfused = start.elapsed_time(stop) / args.steps
-    del g_unf
+    # the same number of decode steps without the refresh: one launch each,
+    # and the merge and the decode as two launches
+    def plain_steps(fused):
+        def body(stream):
+            st, _ = make_step(stream, fused=fused)
+            for k in range(args.steps):
+                st(args.warmup + (2 if fused else 3) * args.steps + k)
+        g = capture(body)
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+    ms_step_plain = plain_steps(True)
+    ms_step_unfused = plain_steps(False)
 
     # Average decode launch duration: the same decode launches back to back
     # (rotating replicas, current positions), replayed from a graph between
@@ -356,8 +369,9 @@ def main():
     # token's ring slot (the new token's read is in the decode's bytes)
     merge_bytes = U * (512 + 160 + 512)
     sel_bytes = 2 * U * L * d * 2 + B * Hq * wl.nb * d * 2 * 2 + U * n_nw * 4 * 2 + U * L
-    step_bytes = dec_bytes + merge_bytes + sel_bytes / REFRESH
-    value = step_bytes / (ms_step * 1e-3) / 1e9
+    # what the timed graph executed: K steps and n_refresh refreshes
+    timed_bytes = args.steps * (dec_bytes + merge_bytes) + n_refresh * sel_bytes
+    value = timed_bytes / (total_ms * 1e-3) / 1e9
     achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
     traffic = load_traffic(wl.name, B)
 
@@ -404,18 +418,23 @@ def main():
                      "bytes_per_launch": dec_bytes, "avg_launch_us": round(dec_avg_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "step_us": round(ms_step * 1e3, 2), "timed_host_s": round(t_host, 4),
+        "timed_bytes": timed_bytes, "refreshes_timed": n_refresh,
+        "step_us_decode_only": round(ms_step_plain * 1e3, 2),
         "step_us_unfused": round(ms_step_unfused * 1e3, 2),
-        "timing": "K steps (hq_decode_step, the refresh every 64th) captured as one HIP graph, replayed once between HIP events",
+        # the step at the pages' cadence, one refresh per 64 decode steps
+        "step_us_amortized_64": round((ms_step_plain + sel_ms / REFRESH) * 1e3, 2),
+        "timing": (f"{args.steps} steps (one hq_decode_step each; hq_select_vertical at the first step of "
+                   f"every 64-step period: {n_refresh} in the window) captured as one HIP graph, replayed once "
+                   f"between HIP events; value = the bytes of those launches / the graph's time"),
         "rows_us": {"decode": round(dec_avg_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
                     "select": round(sel_ms * 1e3, 2), "pack": round(pack_ms * 1e3, 2)},
         # the selection's share of the amortised step: hq_select_vertical (rows
         # a1-a3, two passes over the dense keys) as the step runs it, and the
         # decode-time refresh over the hybrid cache in its place
-        "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step, 4),
-                         "amortized": round(sel_ms / (sel_ms + REFRESH * (ms_step - sel_ms / REFRESH)), 4),
+        "select_share": {"per_refresh_vs_step": round(sel_ms / ms_step_plain, 4),
+                         "amortized": round(sel_ms / (sel_ms + REFRESH * ms_step_plain), 4),
                          "amortized_decode_time_refresh": round(
-                             refresh["us"] * 1e-3 / (refresh["us"] * 1e-3 + REFRESH * (ms_step - sel_ms / REFRESH)),
-                             4)},
+                             refresh["us"] * 1e-3 / (refresh["us"] * 1e-3 + REFRESH * ms_step_plain), 4)},
         "select_util": sel_util,
         "decode_time_refresh": refresh,
         "b_sweep": sweep,

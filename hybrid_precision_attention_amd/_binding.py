@@ -71,6 +71,8 @@ lib.hq_workspace_bytes.restype = ctypes.c_size_t
 lib.hq_status_string.argtypes = [ctypes.c_int]
 lib.hq_status_string.restype = ctypes.c_char_p
 lib.hq_abi_version.restype = ctypes.c_int
+lib.hq_n_vertical.argtypes = [ctypes.c_double, ctypes.c_int32]
+lib.hq_n_vertical.restype = ctypes.c_int32
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step",
@@ -89,8 +91,9 @@ def hq_status_string(status: int) -> str:
 
 
 def n_vertical(rho: float, n_nw: int) -> int:
-    """floor(rho * n_nw + 1e-6): the vertical-line count the library uses."""
-    return int(math.floor(rho * n_nw + 1e-6)) if n_nw > 0 else 0
+    """The vertical-line count the library uses for n_nw candidates
+    (hq_n_vertical: floor(rho * n_nw + 1e-6))."""
+    return int(lib.hq_n_vertical(float(rho), int(n_nw)))
 
 
 def make_dims(B, Hq, Hkv, W, rho, cap_q=0, cap_vl=0, cap_stg=1, d=D, k_bits=4, v_bits=4) -> hq_dims:

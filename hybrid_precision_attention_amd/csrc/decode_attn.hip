@@ -1271,7 +1271,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   // the step's merge (its loads in flight during the fold), by the last wave
-  const bool merger = a.k_new && wave == kWaves - 1;
+  // A decode step needs nothing staged (the new token takes the staging
+  // slot's place in the scan); a unit that has a staged token is refused:
+  // its outputs and LSE are NaN and its cache is left as it was.
+  const bool refused = a.k_new && a.c.n_stg[u] != 0;
+  const bool merger = a.k_new && !refused && wave == kWaves - 1;
   const int t_step = a.L_seq ? min(max(a.L_seq[b], 0), a.L_max) : a.L_max;
   StepIn step_in{};
   if (merger) step_in = step_load(a, u, t_step, lane);
@@ -1380,9 +1384,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
              ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[1] * inv)) << 16);
       pk.y = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[2] * inv)) |
              ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[3] * inv)) << 16);
+      if (refused) pk = make_uint2(0x7E007E00u, 0x7E007E00u);          // fp16 quiet NaNs
       *reinterpret_cast<uint2*>(dst) = pk;
       if (c == 0 && a.lse)
-        a.lse[b * a.Hq + h0 + g] = lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+        a.lse[b * a.Hq + h0 + g] = refused ? __builtin_nanf("")
+                                   : lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
   if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);

@@ -70,7 +70,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 int32_t n_vertical(double rho, int32_t n_nw) {
-  if (n_nw <= 0) return 0;
+  if (n_nw <= 0 || !(rho >= 0.0 && rho <= 1.0)) return 0;
   return static_cast<int32_t>(floor(rho * static_cast<double>(n_nw) + 1e-6));
 }
 
@@ -131,7 +131,9 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 8; }
+int hq_abi_version(void) { return 9; }
+
+int32_t hq_n_vertical(double rho, int32_t n_nw) { return n_vertical(rho, n_nw); }
 
 const char* hq_status_string(int status) {
   switch (status) {

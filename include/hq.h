@@ -220,7 +220,8 @@ int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L,
  * hq_append_merge leave it: the K4V4 and vertical-line regions hold the
  * positions below t - W, the window ring positions max(0, t - W) .. t - 1,
  * and the staging region the token at t (at most one staged token is read).
- * A K4V4 key enters as the fp16 rounding of code * scale + min.  Buffered
+ * A K4V4 key is code * scale + min; the kernel rounds each element of it to
+ * fp16 for the matrix cores (relative error at most 2^-11).  Buffered
  * query j of each query head (position p_j = t - nb + 1 + j) adds, for every
  * cached key at a position i <= p_j, exp(q.k_i / sqrt(d) - lse_j) to
  * score_inout[b][kvh][i], summed over the unit's heads and queries; lse_j is
@@ -304,7 +305,10 @@ int hq_decode_attn_ragged(const hq_dims* dims, const hq_cache* cache, const int3
  * Precondition: nothing is staged (n_stg = 0, as after hq_quant_pack or a
  * previous hq_decode_step); the window holds positions max(0, t-W) .. t-1.
  * Mixing with hq_append_merge / hq_decode_attn is allowed in that state: a
- * plain hq_append_merge at t then stages t and moves nothing.
+ * plain hq_append_merge at t then stages t and moves nothing.  The staging
+ * count lives on the device, so the precondition is checked there: a unit
+ * with a staged token is refused, its out rows and lse entries are set to
+ * NaN and its cache is left unchanged (the other units step normally).
  * Errors: as hq_decode_attn; HQ_ERR_CAPACITY when cap_q < t + 1 - W.
  */
 int hq_decode_step(const hq_dims* dims, const hq_cache* cache, int32_t t, const uint16_t* k_new,
@@ -364,6 +368,13 @@ int hq_quant_int8(const uint16_t* x, int64_t rows, int8_t* codes, float* scales,
 int hq_prefill_attn(const hq_dims* dims, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     int32_t L, const uint8_t* vl_flag_or_null, uint16_t* out, float* lse_or_null,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Size of the vertical-line set of n_nw candidate (non-window) positions:
+ * floor(rho * n_nw + 1e-6), 0 when n_nw <= 0 (agihunt digest, method
+ * paragraph: the top-rho of the non-window prefix; the 1e-6 absorbs the
+ * binary representation of rho, e.g. 0.29 * 100).  The count every entry
+ * point uses; rho outside [0, 1] or NaN gives 0. */
+int32_t hq_n_vertical(double rho, int32_t n_nw);
 
 /* Workspace bytes an operation needs for any prefix length up to L_max;
  * 0 for an invalid request. */

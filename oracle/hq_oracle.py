@@ -468,15 +468,13 @@ def decode(caches, q, L, fused=True):
 # non-window prefix; a token leaving the window becomes a vertical line when
 # its running score reaches the cut-off.
 # --------------------------------------------------------------------------
-def hybrid_keys_fp16(cache: Dict, t: int):
+def hybrid_keys(cache: Dict, t: int):
     """Positions and keys [n][d] (fp64) of every key cached at decode
-    position t: K4V4 slots as fp16(code * scale + min), then the FP16
-    vertical lines, window and staged token."""
+    position t: the K4V4 slots as their exact dequantisation code * scale +
+    min (the key the cache holds, as decode attention takes it), then the
+    FP16 vertical lines, window and staged token."""
     regs = hybrid_regions(cache, t)
-    k4 = regs[0]
-    pos = [k4[1]] + [r[1] for r in regs[1:]]
-    keys = [k4[2].astype(np.float16).astype(np.float64)] + [r[2] for r in regs[1:]]
-    return np.concatenate(pos), np.concatenate(keys)
+    return np.concatenate([r[1] for r in regs]), np.concatenate([r[2] for r in regs])
 
 
 def refresh_hybrid_unit(cache: Dict, t: int, qgrp: np.ndarray, lse: np.ndarray,
@@ -491,7 +489,7 @@ def refresh_hybrid_unit(cache: Dict, t: int, qgrp: np.ndarray, lse: np.ndarray,
     G, nb, d = qgrp.shape
     W = cache["W"]
     tau = softmax_scale(d)
-    pos, keys = hybrid_keys_fp16(cache, t)
+    pos, keys = hybrid_keys(cache, t)
     rows_pos = t - nb + 1 + np.arange(nb)
     for h in range(G):
         z = tau * (qgrp[h].astype(np.float64) @ keys.T)            # [nb][n]

@@ -1,5 +1,7 @@
 """Helpers shared by the GPU parity tests: run the HIP path through the C ABI
 and bring its cache back in the oracle's per-unit form."""
+import math
+
 import numpy as np
 import torch
 
@@ -106,3 +108,35 @@ def oracle_decode_on(cache, L, q, units=None):
             out[b, g * G:(g + 1) * G], lse[b, g * G:(g + 1) * G] = O.decode_fused(
                 c, q[b, g * G:(g + 1) * G], L)
     return out, lse
+
+
+# Bound of a refresh's GPU score against the oracle's (the decode-time refresh
+# feeds the matrix cores each dequantised K4V4 key element rounded to fp16).
+SCORE_RTOL = 2e-5          # fp32 MFMA + exp2 of exact fp16 keys against fp64
+U16 = 2.0 ** -11           # fp16 unit roundoff
+SUB16 = 2.0 ** -25         # half the spacing of fp16 subnormals
+
+
+def score_bounds(c, t, q, lse, lse_tol=0.0):
+    """Per cached position i, a bound on |GPU - oracle| of one refresh's
+    increment: sum over rows r (head, buffered query) of p_ri (exp(b_ri) - 1),
+    where p_ri = exp(tau q_r.k_i - lse_r) on the oracle's exact keys (causal),
+    b_ri = tau sum_e |q_re| (u |k_ie| + 2^-25) for a K4V4 key (the fp16
+    rounding of its dequantised elements) and 0 for an FP16 key, plus lse_tol
+    when the GPU's row normalisers differ from the oracle's by up to that.
+    Returns (positions, bounds)."""
+    G, nb, d = q.shape
+    pos, keys = O.hybrid_keys(c, t)
+    k4 = np.zeros(len(pos), bool)
+    k4[:c["q_pos"].shape[0]] = True                     # K4V4 slots come first
+    rows = t - nb + 1 + np.arange(nb)
+    tau = 1.0 / math.sqrt(d)
+    kabs = np.where(k4[:, None], U16 * np.abs(keys) + SUB16, 0.0)
+    out = np.zeros(len(pos))
+    for h in range(G):
+        qh = q[h].astype(np.float64)
+        z = tau * (qh @ keys.T)
+        p = np.exp(z - lse[h][:, None]) * (pos[None, :] <= rows[:, None])
+        beta = tau * (np.abs(qh) @ kabs.T) + lse_tol
+        out += (p * np.expm1(beta)).sum(axis=0)
+    return pos, out

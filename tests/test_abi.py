@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
             "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
             "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step", "hq_decode_step_ragged",
-            "hq_workspace_bytes", "hq_status_string", "hq_abi_version"} <= set(names)
+            "hq_workspace_bytes", "hq_status_string", "hq_abi_version", "hq_n_vertical"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
 
@@ -33,7 +33,23 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 8
+    assert H.lib.hq_abi_version() == 9
+
+
+def test_n_vertical_is_the_oracles_count():
+    """The library's top-rho count (the one every entry point sizes its set
+    with) equals the oracle's floor(rho * n + 1e-6) over a grid of rho and
+    candidate counts, incl. the tiny workload's 44 of 896 and 0.29 * 100 = 29
+    (binary rho); out-of-range rho and empty candidate sets give 0."""
+    from oracle import hq_oracle as O
+    assert H.n_vertical(0.05, 896) == 44
+    assert H.n_vertical(0.29, 100) == 29
+    for rho in (0.0, 0.01, 0.05, 0.1, 0.29, 0.3, 1 / 3, 0.5, 0.999999, 1.0):
+        for n in (0, 1, 7, 100, 896, 1000, 32640, 65535, 1 << 24):
+            assert H.n_vertical(rho, n) == O.n_vertical(rho, n), (rho, n)
+    assert H.n_vertical(0.05, -3) == 0
+    assert H.n_vertical(-0.1, 100) == 0 and H.n_vertical(1.5, 100) == 0
+    assert H.n_vertical(float("nan"), 100) == 0
 
 
 def _fake_cache(W=128, base=1 << 20):

@@ -127,3 +127,37 @@ def test_step_equals_merge_then_decode(name, over):
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), f"step {s}"
         assert torch.equal(l1, l2), f"step {s}"
+
+
+def test_step_refuses_units_with_a_staged_token():
+    """hq_decode_step needs nothing staged.  With a token staged in sequence 0
+    only (a plain hq_append_merge on its B = 1 view), the step refuses
+    sequence 0's units (NaN out and lse, their cache bytes unchanged) and
+    steps sequence 1 exactly as it does on a cache where nothing is staged."""
+    wl = workload("tiny", B=2, L=600)
+    x = batch(wl, steps=2)
+    L, W = wl.L, wl.W
+    flags = _flags(wl, x)
+    c = gpu_pack(x, L, W, wl.rho, flags, L_max=L + 4, extra_vl=2)
+    ref = c.clone()
+    v0 = c.view(0)
+    H.hq_append_merge(v0.dims, v0, L, dev(x["k_dec"][0][:1]), dev(x["v_dec"][0][:1]))
+    torch.cuda.synchronize()
+    before = {k: v[0].clone() for k, v in c.t.items() if v is not None and k != "k4_pages"}
+    k, v, q = dev(x["k_dec"][1]), dev(x["v_dec"][1]), dev(x["q_dec"][1])
+    outs = []
+    for cc in (c, ref):
+        o = torch.zeros((wl.B, wl.Hq, 128), dtype=torch.float16, device="cuda")
+        ls = torch.zeros((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
+        H.hq_decode_step(cc.dims, cc, L, k, v, q, o, H.workspace(cc.dims, H.HQ_OP_DECODE, L + 4), lse=ls)
+        outs.append((o, ls))
+    torch.cuda.synchronize()
+    (o, ls), (o_ref, ls_ref) = outs
+    assert torch.isnan(o[0]).all() and torch.isnan(ls[0]).all()
+    for key, val in before.items():
+        assert torch.equal(c.t[key][0].view(torch.uint8), val.view(torch.uint8)), key
+    assert torch.equal(o[1].view(torch.int16), o_ref[1].view(torch.int16))
+    assert torch.equal(ls[1], ls_ref[1])
+    for key, val in c.t.items():
+        if val is not None and key != "k4_pages":
+            assert torch.equal(val[1].view(torch.uint8), ref.t[key][1].view(torch.uint8)), key

@@ -126,6 +126,28 @@ def test_signed_zero_is_stored_as_plus_zero():
     assert m.view(np.uint16)[1, 1] == 0 and s.view(np.uint16)[1, 1] != 0
 
 
+def test_min_of_both_zeros_is_plus_zero_in_either_order():
+    """-0 and +0 compare equal, so which one a min reduction returns depends
+    on the order of the comparisons; the stored minimum of a group holding
+    both is +0 (bits 0x0000) whichever comes first, and the codes and the
+    scale do not depend on the order either."""
+    rng = np.random.default_rng(7)
+    tail = np.abs(rng.standard_normal(30)).astype(np.float16) + np.float16(0.5)
+    a = np.concatenate([[np.float16(-0.0), np.float16(0.0)], tail]).astype(np.float16)
+    b = np.concatenate([[np.float16(0.0), np.float16(-0.0)], tail]).astype(np.float16)
+    c = np.concatenate([tail[:15], [np.float16(-0.0)], tail[15:], [np.float16(0.0)]]).astype(np.float16)
+    X = np.zeros((3, 128), np.float16)
+    X[0, :32], X[1, :32], X[2, :32] = a, b, c
+    X[:, 32:] = np.float16(1.0)
+    codes, s, m = O.quantize_groups(X)
+    assert m.view(np.uint16)[:, 0].tolist() == [0, 0, 0]
+    assert s[0, 0] == s[1, 0] == s[2, 0] and s[0, 0] > 0
+    # the zeros take code 0 in every order; the shared tail the same codes
+    assert codes[0, 0] == codes[0, 1] == codes[1, 0] == codes[1, 1] == 0
+    assert np.array_equal(codes[0, 2:32], codes[1, 2:32])
+    assert codes[2, 15] == codes[2, 31] == 0
+
+
 def test_nibble_order_golden():
     with open(os.path.join(GOLD, "nibble_order.json")) as f:
         g = json.load(f)

@@ -5,8 +5,12 @@
 * With each row's normaliser computed from the same keys, every buffered row
   adds exactly 1 over the cached positions (mass conservation), whatever the
   quantised part holds.
-* A K4V4 key enters as the fp16 rounding of code * scale + min, checked
-  against a hand dequantisation of one token.
+* The refresh of a cache with K4V4 slots, pack-time and promoted vertical
+  lines, a window and a staged token equals the dense column mass (pinned
+  by brute force in the selection tests) of the key matrix indexed by
+  position, each position's key rebuilt here from its own slot: a K4V4
+  slot's nibbles (low first) times its scale plus its min, exactly.  A
+  key paired with the wrong position changes that position's score.
 * The cut-off is the n_vl-th largest running score of the non-window prefix
   (brute-force sort), +inf when n_vl = 0; the set is the exact top-n_vl.
 * The scored merge promotes exactly when score >= cut, and is otherwise the
@@ -71,7 +75,7 @@ def test_refresh_mass_conservation(W, rho):
         O.append_merge_unit(c, t, K[t], V[t])
     t = L + 2
     q = rng.standard_normal((G, nb, d)).astype(np.float16)
-    pos, keys = O.hybrid_keys_fp16(c, t)
+    pos, keys = O.hybrid_keys(c, t)
     assert sorted(pos.tolist()) == list(range(t + 1))
     rows_pos = t - nb + 1 + np.arange(nb)
     lse = np.stack([_exact_lse(keys, pos, q[h], rows_pos, d) for h in range(G)])
@@ -84,25 +88,63 @@ def test_refresh_mass_conservation(W, rho):
     assert np.allclose(s2, 2 * score, rtol=1e-14)
 
 
-def test_k4_key_is_fp16_of_code_scale_min():
-    L, W, d = 80, 8, 128
-    K, V, _ = _prefix(L, seed=5)
-    c = O.quant_pack_unit(K[:L], V[:L], L, W, np.zeros(L, np.uint8))
-    O.append_merge_unit(c, L, K[L], V[L])
-    pos, keys = O.hybrid_keys_fp16(c, L)
-    slot = 7
-    codes = np.zeros(d, np.int64)
-    row = c["kq"][slot]
-    for b in range(d // 2):                      # low nibble first
-        codes[2 * b] = row[b] & 0xF
-        codes[2 * b + 1] = row[b] >> 4
-    want = np.zeros(d)
-    for g in range(d // 32):
-        s, m = (float(x) for x in c["kq_meta"][slot, g])
-        for e in range(32):
-            want[32 * g + e] = float(np.float16(codes[32 * g + e] * s + m))
-    i = int(np.nonzero(pos == c["q_pos"][slot])[0][0])
-    assert np.array_equal(keys[i], want)
+def _keys_by_position(c, t, d=128):
+    """Dense key matrix [t + 1][d] of the cache at decode position t, every
+    position's key taken from its own slot (written out here, independently
+    of the oracle's region lists): K4V4 slots dequantised from their bytes,
+    vertical lines, window ring slots p mod W, the staged token."""
+    K = np.full((t + 1, d), np.nan)
+    seen = np.zeros(t + 1, np.int64)
+    for s_ in range(c["kq"].shape[0]):
+        row, p = c["kq"][s_], int(c["q_pos"][s_])
+        for g in range(d // 32):
+            scale, mn = (float(x) for x in c["kq_meta"][s_, g])
+            for e in range(32):
+                byte = int(row[(32 * g + e) // 2])
+                code = byte & 0xF if e % 2 == 0 else byte >> 4
+                K[p, 32 * g + e] = code * scale + mn
+        seen[p] += 1
+    for i in range(c["kvl"].shape[0]):
+        p = int(c["vl_pos"][i])
+        K[p] = c["kvl"][i].astype(np.float64)
+        seen[p] += 1
+    W = c["W"]
+    for p in range(max(0, t - W), t):
+        K[p] = c["kwin"][p % W].astype(np.float64)
+        seen[p] += 1
+    K[t] = c["kstg"][0].astype(np.float64)
+    seen[t] += 1
+    assert np.all(seen == 1)
+    return K
+
+
+@pytest.mark.parametrize("W", [16, 0])
+def test_refresh_equals_dense_column_mass_of_the_cache_keys(W):
+    L, G, nb, d, rho = 160, 2, 10, 128, 0.1
+    K, V, rng = _prefix(L, seed=13)
+    K = np.concatenate([K, rng.standard_normal((24, d)).astype(np.float16)])
+    V = np.concatenate([V, rng.standard_normal((24, d)).astype(np.float16)])
+    n_nw = L - W
+    flag = np.zeros(L, np.uint8)
+    flag[rng.choice(n_nw, size=n_nw // 10, replace=False)] = 1
+    c = O.quant_pack_unit(K[:L], V[:L], L, W, flag)
+    # stream tokens, promoting some of the ones that leave the window
+    for t in range(L, L + 20):
+        O.append_merge_unit(c, t, K[t], V[t], evict_is_vl=(t % 3 == 0))
+    t = L + 19
+    assert c["kvl"].shape[0] > n_nw // 10            # promoted lines joined the pack-time ones
+    q = rng.standard_normal((G, nb, d)).astype(np.float16)
+    lse = rng.uniform(2.0, 6.0, (G, nb))              # any normalisers: nothing cancels
+    score = np.zeros(t + 1)
+    O.refresh_hybrid_unit(c, t, q, lse, rho, score)
+    want = O.column_mass_given_lse_unit(_keys_by_position(c, t, d), q, lse, t + 1, 0)
+    assert np.allclose(score, want, rtol=1e-12, atol=0.0)
+    # the pairing matters: a key moved to another position changes the result
+    Kx = _keys_by_position(c, t, d)
+    p0, p1 = int(c["q_pos"][3]), int(c["q_pos"][40])
+    Kx[[p0, p1]] = Kx[[p1, p0]]
+    bad = O.column_mass_given_lse_unit(Kx, q, lse, t + 1, 0)
+    assert not np.allclose(score, bad, rtol=1e-9, atol=0.0)
 
 
 def test_cut_off_and_set():
