@@ -51,6 +51,8 @@ lib.hq_append_merge.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache
                                 _p, _p, _p, _p]
 lib.hq_decode_attn.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32,
                                _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.hq_decode_attn_noalloc.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32,
+                                       _p, _p, _p, _p]
 lib.hq_refresh_hybrid.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache), ctypes.c_int32,
                                   _p, ctypes.c_int32, _p, _p, ctypes.c_int32, _p, _p, _p, _p]
 lib.hq_append_merge_scored.argtypes = [ctypes.POINTER(hq_dims), ctypes.POINTER(hq_cache),
@@ -76,7 +78,7 @@ lib.hq_n_vertical.restype = ctypes.c_int32
 for _f in ("hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
            "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
            "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step",
-           "hq_decode_step_ragged"):
+           "hq_decode_step_ragged", "hq_decode_attn_noalloc"):
     getattr(lib, _f).restype = ctypes.c_int
 
 
@@ -357,6 +359,18 @@ def hq_decode_attn(dims, cache: HybridCache, L, q, out, ws, lse=None, stream=Non
                             _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
                             _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "hq_decode_attn")
+
+
+def hq_decode_attn_noalloc(dims, cache: HybridCache, L, q, out, lse=None, stream=None):
+    """hq_decode_attn without a workspace: the library's static per-GPU
+    scratch holds the arrival counters and partial records (calls that
+    overlap on one GPU race)."""
+    _check_query(dims, cache, q, out, lse)
+    cs = cache.struct()
+    st = lib.hq_decode_attn_noalloc(ctypes.byref(dims), ctypes.byref(cs), L, _ptr(q, torch.float16, "q"),
+                                    _ptr(out, torch.float16, "out"), _ptr(lse, torch.float32, "lse"),
+                                    _stream(stream))
+    _check(st, "hq_decode_attn_noalloc")
 
 
 def hq_refresh_hybrid(dims, cache: HybridCache, t, qbuf, lse, score, vl_idx, vl_flag, cut,

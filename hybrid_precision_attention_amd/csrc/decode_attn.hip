@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "hq_device.h"
@@ -54,7 +55,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
-constexpr int kPart = 132;          // floats per partial record: m, l, pad, pad, o[128]
+constexpr int kPart = kPartFloatsPerRecord;   // floats per partial record: m, l, pad, pad, o[128]
 constexpr int kRecF4 = kPart / 4;   // 16-byte words per record
 constexpr int kFoldRecs = 128;      // records the final merge stages in LDS at a time (66 KB)
 constexpr int kFoldPer = (kFoldRecs * kRecF4 + kThreads - 1) / kThreads;  // 16-byte loads per thread
@@ -1397,10 +1398,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch of hq_decode_attn_noalloc (for callers that cannot
+// allocate): the arrival counters and partial records a decode workspace
+// carries otherwise.  One copy per GPU, held until the process ends; every
+// call on a GPU shares it.  In host code the array's name is only a stand-in:
+// its device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* p, size_t n16) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+       i += static_cast<size_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace
+
+hipError_t decode_scratch(void** ptr, hipStream_t s) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the arrival counters start at zero (a fill kernel, not a memset, so
+    // that a captured first call records no memset node); every completed
+    // call leaves the counters it used at zero again
+    hipLaunchKernelGGL(zero16_kernel, dim3(64), dim3(256), 0, s, static_cast<uint4*>(p),
+                       kScratchCounterBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const DecodePlan& plan,
                          const uint16_t* q, uint16_t* out, float* lse, void* ws, hipStream_t s,
                          const int32_t* L_seq, const uint16_t* k_new, const uint16_t* v_new,
                          const uint8_t* evict_is_vl) {
+  return launch_decode_at(d, c, L, plan, q, out, lse, reinterpret_cast<int32_t*>(ws),
+                          reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_counter_bytes(d)),
+                          s, L_seq, k_new, v_new, evict_is_vl);
+}
+
+hipError_t launch_decode_at(const hq_dims& d, const hq_cache& c, int32_t L, const DecodePlan& plan,
+                            const uint16_t* q, uint16_t* out, float* lse, int32_t* counters,
+                            float* part, hipStream_t s, const int32_t* L_seq,
+                            const uint16_t* k_new, const uint16_t* v_new, const uint8_t* evict_is_vl) {
   DecodeArgs a;
   a.k_new = k_new;
   a.v_new = v_new;
@@ -1411,8 +1469,8 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L, const D
   a.q = q;
   a.out = out;
   a.lse = lse;
-  a.counters = reinterpret_cast<int32_t*>(ws);   // counter of unit u at word u * kCounterStride
-  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + decode_counter_bytes(d));
+  a.counters = counters;   // counter of unit u at word u * kCounterStride
+  a.part = part;
   a.Hq = d.Hq;
   a.Hkv = d.Hkv;
   a.G = d.Hq / d.Hkv;

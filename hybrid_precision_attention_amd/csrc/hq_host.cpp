@@ -24,7 +24,7 @@ constexpr int kBlk = 32;           // tokens per decode block
 constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most (short prefixes)
 constexpr int kMaxPerCU = 2;       // decode workgroups per CU the byte plan aims at, at most
 constexpr int kMaxSplit = 128;     // decode workgroups per unit, at most (LDS of the final merge)
-constexpr int kPartFloats = 132;   // m, l, 2 pad, o[128]
+constexpr int kPartFloats = kPartFloatsPerRecord;
 constexpr double kWgBytes = 384.0 * 1024;  // bytes one decode workgroup streams at small batch
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -131,7 +131,7 @@ using namespace hq;
 
 extern "C" {
 
-int hq_abi_version(void) { return 9; }
+int hq_abi_version(void) { return 10; }
 
 int32_t hq_n_vertical(double rho, int32_t n_nw) { return n_vertical(rho, n_nw); }
 
@@ -144,6 +144,7 @@ const char* hq_status_string(int status) {
     case HQ_ERR_CAPACITY: return "cache region capacity too small";
     case HQ_ERR_WORKSPACE: return "workspace missing or too small";
     case HQ_ERR_HIP: return "HIP launch or runtime error";
+    case HQ_ERR_SCRATCH: return "request exceeds the static decode scratch (hq_decode_attn_noalloc)";
     default: return "unknown status";
   }
 }
@@ -198,6 +199,30 @@ int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L, const 
   if (!aligned16(ws)) return HQ_ERR_ALIGN;
   const DecodePlan plan = plan_decode(*dims, L);
   if (launch_decode(*dims, *cache, L, plan, q, out, lse_or_null, ws, stream) != hipSuccess)
+    return HQ_ERR_HIP;
+  return HQ_OK;
+}
+
+int hq_decode_attn_noalloc(const hq_dims* dims, const hq_cache* cache, int32_t L, const uint16_t* q,
+                           uint16_t* out, float* lse_or_null, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (L < 0 || !q || !out) return HQ_ERR_ARG;
+  if ((st = check_cache(*dims, cache))) return st;
+  if (!aligned16(q) || !aligned16(out)) return HQ_ERR_ALIGN;
+  if (lse_or_null && !aligned16(lse_or_null)) return HQ_ERR_ALIGN;
+  // the request must fit the static scratch: its counter area and the
+  // records of this call's split plan
+  const DecodePlan plan = plan_decode(*dims, L);
+  const int64_t units = static_cast<int64_t>(dims->B) * dims->Hkv;
+  const int64_t G = dims->Hq / dims->Hkv;
+  const int64_t rec_bytes = units * plan.nsplit * G * kPartFloats * static_cast<int64_t>(sizeof(float));
+  if (units > kScratchUnits || rec_bytes > static_cast<int64_t>(kScratchRecordBytes)) return HQ_ERR_SCRATCH;
+  void* base = nullptr;
+  if (decode_scratch(&base, stream) != hipSuccess) return HQ_ERR_HIP;
+  if (launch_decode_at(*dims, *cache, L, plan, q, out, lse_or_null, static_cast<int32_t*>(base),
+                       reinterpret_cast<float*>(static_cast<char*>(base) + kScratchCounterBytes),
+                       stream) != hipSuccess)
     return HQ_ERR_HIP;
   return HQ_OK;
 }

@@ -43,6 +43,29 @@ hipError_t launch_decode(const hq_dims& d, const hq_cache& c, int32_t L,
                          const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
                          const uint8_t* evict_is_vl = nullptr);
 
+// The decode with its arrival counters (one per unit, kCounterStride words
+// apart, zero before the call, zero again after it) and partial records at
+// the given device addresses.
+hipError_t launch_decode_at(const hq_dims& d, const hq_cache& c, int32_t L, const DecodePlan& plan,
+                            const uint16_t* q, uint16_t* out, float* lse, int32_t* counters,
+                            float* part, hipStream_t s, const int32_t* L_seq = nullptr,
+                            const uint16_t* k_new = nullptr, const uint16_t* v_new = nullptr,
+                            const uint8_t* evict_is_vl = nullptr);
+
+// Static scratch of hq_decode_attn_noalloc: one copy per GPU of
+// kDecodeScratchBytes, the arrival counters of up to kScratchUnits units in
+// its first kScratchCounterBytes and the partial records after them.
+constexpr size_t kDecodeScratchBytes = size_t{8} << 20;
+constexpr int kScratchUnits = 4096;
+constexpr size_t kScratchCounterBytes = size_t{kScratchUnits} * 4 * kCounterStride;
+constexpr size_t kScratchRecordBytes = kDecodeScratchBytes - kScratchCounterBytes;
+constexpr int kPartFloatsPerRecord = 132;     // m, l, 2 pad, o[128]
+
+// Device address of the current GPU's scratch: looked up once per device
+// (with that device current) and its counter area cleared then, by a fill
+// kernel on `s`; later calls return the kept address.
+hipError_t decode_scratch(void** ptr, hipStream_t s);
+
 hipError_t launch_select(const hq_dims& d, const uint16_t* qbuf, int32_t nb,
                          const uint16_t* k, int32_t L, const float* lse_in,
                          float* score, int32_t* vl_idx, uint8_t* vl_flag, void* ws,

@@ -64,6 +64,7 @@ extern "C" {
 #define HQ_ERR_CAPACITY    -4   /* a cache region too small for the request */
 #define HQ_ERR_WORKSPACE   -5   /* workspace missing or smaller than required */
 #define HQ_ERR_HIP         -6   /* a HIP launch or runtime call failed */
+#define HQ_ERR_SCRATCH     -7   /* request larger than hq_decode_attn_noalloc's static scratch */
 
 /* Problem shape: batch, query/KV heads, head_dim, window W, vertical-line
  * ratio rho in [0, 1], the capacities (tokens per unit) of the quantised,
@@ -208,6 +209,29 @@ int hq_append_merge(const hq_dims* dims, const hq_cache* cache, int32_t t,
 int hq_decode_attn(const hq_dims* dims, const hq_cache* cache, int32_t L,
                    const uint16_t* q, uint16_t* out, float* lse_or_null,
                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * hq_decode_attn_noalloc -- hq_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): no workspace argument; the arrival counters and
+ * partial records live in a static device array of the library, 8 MiB per
+ * GPU, held until the process ends.  Arguments, result and the other errors
+ * as hq_decode_attn.
+ *   - Limit: at most 4096 units (B * Hkv), and the records of the call's
+ *     split plan (units * splits * Hq/Hkv * 528 bytes) within the
+ *     7.5 MiB after the counters; larger requests return HQ_ERR_SCRATCH
+ *     before anything is launched.  (The Qwen3-32B-shaped layer at B = 32
+ *     and L = 32K needs 2.2 MB.)
+ *   - The first call on a GPU looks the array up (hipGetSymbolAddress, with
+ *     that GPU current) and clears its counters with a fill kernel on
+ *     `stream`; every completed call leaves them zero again.
+ *   - Every call on one GPU uses the same array: calls that overlap on one
+ *     GPU (concurrent streams, host threads) race and must not be issued.
+ * Calls no hipMalloc, hipFree or other allocating routine.
+ */
+int hq_decode_attn_noalloc(const hq_dims* dims, const hq_cache* cache, int32_t L,
+                           const uint16_t* q, uint16_t* out, float* lse_or_null,
+                           hipStream_t stream);
 
 /*
  * hq_refresh_hybrid -- decode-time refresh of the running vertical-line

@@ -24,16 +24,16 @@ def test_every_declared_symbol_is_exported():
     assert {"hq_select_vertical", "hq_quant_pack", "hq_append_merge", "hq_decode_attn",
             "hq_refresh_hybrid", "hq_append_merge_scored", "hq_append_merge_ragged",
             "hq_decode_attn_ragged", "hq_quant_int8", "hq_prefill_attn", "hq_decode_step", "hq_decode_step_ragged",
-            "hq_workspace_bytes", "hq_status_string", "hq_abi_version", "hq_n_vertical"} <= set(names)
+            "hq_workspace_bytes", "hq_status_string", "hq_abi_version", "hq_n_vertical", "hq_decode_attn_noalloc"} <= set(names)
     for n in names:
         assert hasattr(H.lib, n), n
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert H.hq_status_string(s) != "unknown status"
     assert H.hq_status_string(7) == "unknown status"
-    assert H.lib.hq_abi_version() == 9
+    assert H.lib.hq_abi_version() == 10
 
 
 def test_n_vertical_is_the_oracles_count():
@@ -256,3 +256,21 @@ def test_workspace_bytes():
     small = H.hq_workspace_bytes(d, H.HQ_OP_SELECT, 1024)
     big = H.hq_workspace_bytes(d, H.HQ_OP_SELECT, 32768)
     assert 0 < small <= big
+
+
+def test_noalloc_decode_rejects_requests_beyond_its_scratch():
+    """hq_decode_attn_noalloc checks on the host, before any HIP call, that
+    the request fits its static scratch: at most 4096 units, and the records
+    of the call's split plan within the area after the counters."""
+    q, out = P, P + (1 << 22)
+    for kw, L in ((dict(B=8190, Hkv=8, Hq=64), 4096),               # 65520 units
+                  (dict(B=512, Hkv=8, Hq=128, cap_q=32768), 32768)):  # 4096 units, 16 heads each
+        d = _dims(**kw)
+        st = H.lib.hq_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(_fake_cache()), L, q, out, None, None)
+        assert st == -7, (kw, st)
+    # argument errors come first, as in hq_decode_attn
+    d = _dims()
+    assert H.lib.hq_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(_fake_cache()), -1, q, out, None, None) == -1
+    assert H.lib.hq_decode_attn_noalloc(ctypes.byref(d), ctypes.byref(_fake_cache()), 10, q + 8, out, None,
+                                        None) == -3
+
