@@ -9,7 +9,7 @@ import hybrid_precision_attention_amd as H
 from hq_inputs import workload, batch
 from oracle import hq_oracle as O
 
-from gpu_util import check_decode, dev, gpu_decode, gpu_pack, oracle_decode_on
+from gpu_util import assert_unit_equal, check_decode, dev, gpu_decode, gpu_pack, oracle_decode_on, unit_from_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -159,17 +159,21 @@ def test_decode_full_size_qwen3_8b_batch32_sampled():
     check_decode(pick(out), pick(lse), pick(ref), pick(ref_lse), tag="sampled units")
 
 
-@pytest.mark.parametrize("name,seqs,units", [
+@pytest.mark.parametrize("name,seqs,units,rho", [
     # Qwen3-32B-shaped, B=32, 64/8 heads (G = 8, the general path): four
     # seeded sequences tiled over the batch, one sampled unit per tile group
-    ("qwen3_32b", [0, 1, 2, 3], [(0, 0), (9, 2), (22, 5), (31, 7)]),
-    # GLM-4-9B-shaped, B=8, 32/2 heads (G = 16): every sequence its own seed
-    ("glm4_9b", list(range(8)), [(0, 0), (3, 1), (6, 0), (7, 1)]),
+    ("qwen3_32b", [0, 1, 2, 3], [(0, 0), (9, 2), (22, 5), (31, 7)], 0.05),
+    # GLM-4-9B-shaped, B=8, 32/2 heads (G = 16): every sequence its own seed,
+    # at the grid's three line ratios
+    ("glm4_9b", list(range(8)), [(0, 0), (3, 1), (6, 0), (7, 1)], 0.05),
+    ("glm4_9b", list(range(8)), [(1, 0), (2, 1), (5, 1), (7, 0)], 0.01),
+    ("glm4_9b", list(range(8)), [(0, 1), (4, 0), (6, 1), (7, 1)], 0.10),
 ])
-def test_decode_full_size_sampled(name, seqs, units):
+def test_decode_full_size_sampled(name, seqs, units, rho):
     """The streaming and GQA-16 runs' decode at full size (L=32768, the
     split plan of that launch), checked by the oracle on sampled units."""
-    wl = workload(name, rho=0.05)
+    wl = workload(name, rho=rho)
+    print(f"case {name} rho={rho}", flush=True)
     assert wl.L == 32768
     xs = batch(wl, steps=1, seqs=seqs)
     _, _, f = O.select_vertical(xs["K"], xs["qbuf"], wl.L, wl.W, wl.rho)
@@ -187,3 +191,51 @@ def test_decode_full_size_sampled(name, seqs, units):
     G = wl.G
     pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
     check_decode(pick(out), pick(lse), pick(ref), pick(ref_lse), tag=f"{name} sampled units")
+
+
+def test_streaming_full_size_qwen3_32b_sampled():
+    """The benchmark's streaming run at full size: Qwen3-32B-shaped layer,
+    B=32, 64/8 heads, L0=32768, W=128, rho=5%, 128 hq_decode_step calls.
+    Four seeded sequences (prefix and decode tokens) are tiled over the batch
+    (units are independent); the oracle packs and streams the sampled units on
+    its own.  Outputs at steps 0, 1, 63 and 127 within the decode tolerance;
+    after one more plain merge on both sides, the sampled units' caches are
+    bit-exact."""
+    wl = workload("qwen3_32b")
+    assert wl.B == 32 and wl.L == 32768 and wl.Hq == 64 and wl.Hkv == 8
+    T, L, W, G = 128, wl.L, wl.W, wl.G
+    print("case qwen3_32b streaming, full size", flush=True)
+    xs = batch(wl, steps=T + 1, seqs=[0, 1, 2, 3])
+    _, _, f4 = O.select_vertical(xs["K"], xs["qbuf"], L, W, wl.rho)
+    rep = wl.B // 4
+    tile = lambda a: np.ascontiguousarray(np.concatenate([a] * rep))
+    x = {"K": tile(xs["K"]), "V": tile(xs["V"]), "qbuf": tile(xs["qbuf"])}
+    cache = gpu_pack(x, L, W, wl.rho, tile(f4), L_max=L + T + 1)
+    del x
+    units = [(0, 0), (9, 2), (22, 5), (31, 7)]
+    refs = {(b, g): O.quant_pack_unit(xs["K"][b % 4, g], xs["V"][b % 4, g], L, W, f4[b % 4, g])
+            for b, g in units}
+    ws = H.workspace(cache.dims, H.HQ_OP_DECODE, L + T)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
+    for s in range(T):
+        t = L + s
+        q = tile(xs["q_dec"][s])
+        H.hq_decode_step(cache.dims, cache, t, dev(tile(xs["k_dec"][s])), dev(tile(xs["v_dec"][s])), dev(q),
+                         out, ws, lse=lse)
+        for b, g in units:
+            O.append_merge_unit(refs[(b, g)], t, xs["k_dec"][s, b % 4, g], xs["v_dec"][s, b % 4, g])
+        if s in (0, 1, 63, 127):
+            torch.cuda.synchronize()
+            o, lg = out.cpu().numpy(), lse.cpu().numpy()
+            ro, rl = zip(*(O.decode_fused(refs[(b, g)], q[b, g * G:(g + 1) * G], t) for b, g in units))
+            pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
+            check_decode(pick(o), pick(lg), np.stack(ro), np.stack(rl), tag=f"step {s}")
+    t = L + T
+    H.hq_append_merge(cache.dims, cache, t, dev(tile(xs["k_dec"][T])), dev(tile(xs["v_dec"][T])))
+    for b, g in units:
+        O.append_merge_unit(refs[(b, g)], t, xs["k_dec"][T, b % 4, g], xs["v_dec"][T, b % 4, g])
+    torch.cuda.synchronize()
+    for b, g in units:
+        assert_unit_equal(unit_from_gpu(cache, b, g), refs[(b, g)], t, W, tag=f"b{b} g{g}")
+
