@@ -56,9 +56,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;
 constexpr int kPart = kPartFloatsPerRecord;   // floats per partial record: m, l, pad, pad, o[128]
-constexpr int kRecF4 = kPart / 4;   // 16-byte words per record
-constexpr int kFoldRecs = 128;      // records the final merge stages in LDS at a time (66 KB)
-constexpr int kFoldPer = (kFoldRecs * kRecF4 + kThreads - 1) / kThreads;  // 16-byte loads per thread
 constexpr int kFoldItems = 2;       // outputs (head, 4 dims) per thread: G * 32 <= 2 * kThreads
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 for raw 32-bit loads (gfx9 family)
 constexpr int kSc1 = 16;            // cache-policy bit sc1 of a buffer load: device-scope coherent
@@ -840,7 +837,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     Stage stage[kWaves];                           // 14 KB (K4V4), 68 KB (tiles)
     WgImage img;                                   // 16.5 KB
     FinPart fin[kThreads];                         // 8 KB
-    float4_t fold[kFoldPer * kThreads];            // 68 KB: a chunk of records in the final merge
   } s_lds;
   __shared__ int s_last;
 
@@ -1281,79 +1277,56 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   StepIn step_in{};
   if (merger) step_in = step_load(a, u, t_step, lane);
 
-  // The last workgroup merges the unit's nsplit * G records, kFoldRecs at a
-  // time: every thread issues its share of a chunk's 16-byte device-scope
-  // loads at once (whole records, consecutive lanes on consecutive 16 bytes;
-  // the next chunk's loads are in flight while a chunk is folded), the chunk
-  // goes to LDS, and thread (sub, head g, dims 4c..4c+3) folds the records of
-  // its output with split index = sub (mod S), 16 at a time with all their
-  // LDS reads in flight.  The S partials of an output are combined in LDS at
-  // the end.
+  // The last workgroup merges the unit's nsplit * G records: thread (sub,
+  // head g, dims 4c..4c+3) folds the records of its output with split index
+  // sub, sub + S, ..., 16 at a time with all their loads in flight (device-
+  // scope buffer loads: 8 bytes of (max, sum) and 16 of the output per
+  // record).  The S partials of an output are then combined in LDS.  (Staging
+  // whole records through LDS first, with fewer and wider loads, measured
+  // slower: 17.5 against 16.8 us for the B = 1 launch.)
   const int nrec = nsplit * G;
   const int items = G * (kD / 4);
   const int S = max(1, kThreads / items);
-  const int sub = tid / items;                     // < S when items <= kThreads
-  const int n_items = (items + kThreads - 1) / kThreads;   // outputs per thread (1 or 2)
+  const int sub = tid / items;
+  const int n_items = (items + kThreads - 1) / kThreads;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       recs, static_cast<short>(0), nrec * kPart * 4, kRsrcWord3);
   FinPart part[kFoldItems];
 #pragma unroll
-  for (int q = 0; q < kFoldItems; ++q) part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-  float4_t ld[kFoldPer];
-  auto load_chunk = [&](int r0) {
-    const int nf4 = min(kFoldRecs, nrec - r0) * kRecF4;
+  for (int q = 0; q < kFoldItems; ++q) {
+    part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+    if (q >= n_items) break;
+    const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+    if (item >= items || sub >= S) continue;
+    const int g = item >> 5, c = item & 31;
+    for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
+      float2 ml[16];
+      float4_t o4[16];
 #pragma unroll
-    for (int k = 0; k < kFoldPer; ++k)
-      ld[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                  rs, (r0 * kRecF4 + min(tid + k * kThreads, nf4 - 1)) * 16, 0, kSc1));
-  };
-  load_chunk(0);
-  for (int r0 = 0; r0 < nrec; r0 += kFoldRecs) {
-    const int r1 = min(nrec, r0 + kFoldRecs);
-    const int nf4 = (r1 - r0) * kRecF4;
-    if (r0 > 0) __syncthreads();                   // the previous chunk is folded
-#pragma unroll
-    for (int k = 0; k < kFoldPer; ++k) s_lds.fold[tid + k * kThreads] = ld[k];   // past nf4: unused copies
-    __syncthreads();
-    if (r1 < nrec) load_chunk(r1);
-#pragma unroll
-    for (int q = 0; q < kFoldItems; ++q) {
-      if (q >= n_items) break;
-      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-      if (item >= items || sub >= S) continue;
-      const int g = item >> 5, c = item & 31;
-      // this output's records in the chunk: split s = s0, s0 + S, ... with
-      // r0 <= s G + g < r1, at LDS records i0, i0 + step, ...
-      int s0 = r0 > g ? (r0 - g + G - 1) / G : 0;
-      s0 += ((sub - s0 % S) % S + S) % S;
-      const int i0 = s0 * G + g - r0, step = S * G;
-      const int cnt = i0 < r1 - r0 ? (r1 - r0 - 1 - i0) / step + 1 : 0;
-      const float* lds = reinterpret_cast<const float*>(s_lds.fold);
-      for (int k0 = 0; k0 < cnt; k0 += 8) {
-        float m8[8], l8[8];
-        float4_t o8[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t at = static_cast<uint32_t>(i0 + min(k0 + k, cnt - 1) * step) * kPart;
-          const float2 ml = *reinterpret_cast<const float2*>(lds + at);
-          m8[k] = k0 + k < cnt ? ml.x : -INFINITY;
-          l8[k] = ml.y;
-          o8[k] = *reinterpret_cast<const float4_t*>(lds + at + 4 + 4 * c);
-        }
-        const float mx = fmaxf(fmaxf(fmaxf(part[q].m, fmaxf(m8[0], m8[1])), fmaxf(m8[2], m8[3])),
-                               fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-        const float mu = mx == -INFINITY ? 0.0f : mx;
-        const float fa = __builtin_amdgcn_exp2f((part[q].m - mu) * c2);
-        part[q].l *= fa;
-        part[q].o *= fa;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float f = __builtin_amdgcn_exp2f((m8[k] - mu) * c2);
-          part[q].l = fmaf(f, l8[k], part[q].l);
-          part[q].o += f * o8[k];
-        }
-        part[q].m = mx;
+      for (int k = 0; k < 16; ++k) {
+        const int sp = min(s0 + k * S, nsplit - 1);
+        const int at = (sp * G + g) * kPart * 4;
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, at, 0, kSc1);
+        ml[k] = make_float2(__uint_as_float(v2[0]), __uint_as_float(v2[1]));
+        o4[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at + 16 + 16 * c, 0, kSc1));
       }
+      float m16[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m16[k] = s0 + k * S < nsplit ? ml[k].x : -INFINITY;
+      float mx = part[q].m;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mx = fmaxf(mx, m16[k]);
+      const float mu = mx == -INFINITY ? 0.0f : mx;
+      const float fa = __builtin_amdgcn_exp2f((part[q].m - mu) * c2);
+      part[q].l *= fa;
+      part[q].o *= fa;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float f = __builtin_amdgcn_exp2f((m16[k] - mu) * c2);
+        part[q].l = fmaf(f, ml[k].y, part[q].l);
+        part[q].o += f * o4[k];
+      }
+      part[q].m = mx;
     }
   }
 #pragma unroll
