@@ -553,9 +553,11 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
 // Decode-time refresh over the hybrid cache.  The unit's keys are its cache
 // as stored at decode position t, in list order: the K4V4 slots, the
 // vertical lines, the window positions t - nwin .. t - 1 (ring slot pos mod
-// W) and the staged token (position t).  A K4V4 key enters the scores as the
-// fp16 rounding of code * scale + min, the value the attention scan computes
-// with.  Row r = g * nb + jq is the buffered query at position
+// W) and the staged token (position t).  A K4V4 key's elements enter the
+// matrix cores as fp16 roundings of code * scale + min (the fp16 operand
+// type of v_mfma_f32_16x16x32_f16): each within 2^-11 relative (or half an
+// fp16 subnormal step) of the cache's key, an error the scores' tolerance
+// allows for.  Row r = g * nb + jq is the buffered query at position
 // t - nb + 1 + jq; every cached key at a position up to the row's own gets
 // exp(tau q.k - lse) added to the running score at that position.
 // ---------------------------------------------------------------------------
@@ -920,10 +922,24 @@ __device__ __forceinline__ void for_each_k(F&& f, std::integer_sequence<int, K..
   (f(std::integral_constant<int, K>{}), ...);
 }
 
+// Add the wave's in-range lanes to an LDS histogram: the lanes that share
+// the first in-range lane's bin add with one atomic (same-address LDS
+// atomics serialise, and the bins crowd around the bulk of the scores); the
+// others add one each (a loop over every distinct bin measured slower: the
+// keys of a wave spread over many bins).
+__device__ __forceinline__ void wave_hist_add(int* hist, uint32_t bin, bool in, int lane) {
+  const uint64_t act = __ballot(in);
+  if (act) {
+    const int leader = __builtin_ctzll(act);
+    const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+    const uint64_t same = __ballot(in && bin == lbin);
+    if (lane == leader) atomicAdd(&hist[lbin], __popcll(same));
+    else if (in && bin != lbin) atomicAdd(&hist[bin], 1);
+  }
+}
+
 // One histogram pass: keys in [lo, hi] counted into 256 bins of 2^shift keys
-// in one LDS histogram (the lanes that share the first in-range lane's bin
-// add with one atomic, since same-address LDS atomics serialise).  Keys past
-// the first segment are re-read.
+// in one LDS histogram.  Keys past the first segment are re-read.
 __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], const float* sc, int n,
                                           uint32_t lo, uint32_t hi, int shift, bool sample,
                                           TopShared& sh) {
@@ -932,15 +948,7 @@ __device__ __forceinline__ void hist_pass(const uint32_t keys[kKeysPerThread], c
   __syncthreads();
   auto add = [&](uint32_t key, bool valid) {
     const bool in = valid && key >= lo && key <= hi;
-    const uint32_t bin = (key - lo) >> shift;
-    const uint64_t act = __ballot(in);
-    if (act) {
-      const int leader = __builtin_ctzll(act);
-      const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
-      const uint64_t same = __ballot(in && bin == lbin);
-      if (lane == leader) atomicAdd(&sh.hist[lbin], __popcll(same));
-      else if (in && bin != lbin) atomicAdd(&sh.hist[bin], 1);
-    }
+    wave_hist_add(sh.hist, (key - lo) >> shift, in, lane);
   };
 #pragma unroll
   for (int k = 0; k < kKeysPerThread; ++k) {
@@ -962,15 +970,7 @@ __device__ __forceinline__ void hist_list(int cnt, uint32_t lo, uint32_t hi, int
     const int i = i0 + tid;
     const uint32_t key = sh.list[max(min(i, cnt - 1), 0)];
     const bool in = i < cnt && key >= lo && key <= hi;
-    const uint32_t bin = (key - lo) >> shift;
-    const uint64_t act = __ballot(in);
-    if (act) {
-      const int leader = __builtin_ctzll(act);
-      const uint32_t lbin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
-      const uint64_t same = __ballot(in && bin == lbin);
-      if (lane == leader) atomicAdd(&sh.hist[lbin], __popcll(same));
-      else if (in && bin != lbin) atomicAdd(&sh.hist[bin], 1);
-    }
+    wave_hist_add(sh.hist, (key - lo) >> shift, in, lane);
   }
   __syncthreads();
 }
@@ -1023,24 +1023,52 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   int32_t* idx = a.vl_idx + u * a.n_vl;
   const int n = a.n_nw, k_want = a.n_vl;
 
-  // several row groups: fold their column-mass parts into the running score
-  // (each position stays with the thread that reads it below)
-  if (a.nrg > 1) {
-    for (int i = tid; i < n; i += kTopThreads) {
-      float v = sc[i];
-      for (int g = 0; g < a.nrg; ++g) v += a.colpart[(static_cast<int64_t>(g) * a.U + u) * a.n_nw + i];
-      sc[i] = v;
+  // The keys of the first segment (positions tid + 1024 k) into registers.
+  // With several row groups their column-mass parts are folded into the
+  // running score first (it is an output: the sums are written back), eight
+  // positions at a time with every load of the eight in flight together;
+  // positions past the first segment are folded in memory, by the thread
+  // that reads them again below.  Loads use clamped indices, so they are
+  // unconditional; only positions below n are written.
+  uint32_t keys[kKeysPerThread];
+  const bool fold = a.nrg > 1;
+  if (n > 0) {
+#pragma unroll
+    for (int k0 = 0; k0 < kKeysPerThread; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = sc[min(tid + (k0 + e) * kTopThreads, n - 1)];
+      if (fold) {
+        for (int g = 0; g < a.nrg; ++g) {
+          const float* cp = a.colpart + (static_cast<int64_t>(g) * a.U + u) * a.n_nw;
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = cp[min(tid + (k0 + e) * kTopThreads, n - 1)];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] += p[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = tid + (k0 + e) * kTopThreads;
+          if (i < n) sc[i] = v[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) keys[k0 + e] = order_key(v[e]);
+    }
+    if (fold) {
+      for (int i = kSeg + tid; i < n; i += kTopThreads) {
+        float v = sc[i];
+        for (int g = 0; g < a.nrg; ++g) v += a.colpart[(static_cast<int64_t>(g) * a.U + u) * a.n_nw + i];
+        sc[i] = v;
+      }
     }
   }
 
-  uint32_t keys[kKeysPerThread];
   uint32_t thresh = 0;                 // keys > thresh are taken
   int take_eq = 0;                     // and this many keys == thresh, lowest positions first
   bool eq_all = true;                  // known: every key == thresh is taken, or none is
   if (k_want > 0) {
-    // unconditional loads (clamped index) so that all 32 are in flight at once
-#pragma unroll
-    for (int k = 0; k < kKeysPerThread; ++k) keys[k] = order_key(sc[min(tid + k * kTopThreads, n - 1)]);
     uint32_t lo = 0, hi = 0;
     int kk = k_want;                   // rank of the target inside [lo, hi]
     int list_n = -1;                   // >= 0: the keys in [lo, hi] are in sh.list
@@ -1191,6 +1219,16 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
   auto emit = [&](int seg, bool from_regs) {
     uint32_t* gt32 = reinterpret_cast<uint32_t*>(sh.gt);
     uint32_t* eq32 = reinterpret_cast<uint32_t*>(sh.eq);
+    if (seg >= n) {
+      // past the last candidate (window positions): nothing is taken
+      const int end = min(seg + kSeg, a.L);
+      if (flags4 && end == seg + kSeg) {
+        for (int q = tid; q < kSeg / 4; q += kTopThreads) reinterpret_cast<uint32_t*>(flag + seg)[q] = 0u;
+      } else {
+        for (int i = seg + tid; i < end; i += kTopThreads) flag[i] = 0;
+      }
+      return;
+    }
     if (k_want > 0) {
       // The ballot of row k (positions seg + 1024 k + 64 wave .. + 63, 64-bit
       // word 16 k + wave) goes into lanes 2k and 2k + 1 of one register, which
