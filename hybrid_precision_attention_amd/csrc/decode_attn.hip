@@ -289,6 +289,7 @@ __device__ __forceinline__ int k4_token(int tb, int j, int e) {
 
 // Rows past the unit's last token are clamped to it, so every address stays
 // inside the unit and masked tokens still dequantise to finite values.
+template <int kVB = 4, int kKB = 4>
 __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint32_t* kmeta,
                                         const uint8_t* vq, const uint32_t* vmeta, int tb,
                                         int nq, int lane, int n, int j) {
@@ -300,10 +301,26 @@ __device__ __forceinline__ void load_k4(K4Raw& r, const uint8_t* kq, const uint3
   const uint32_t ova = static_cast<uint32_t>(min(tb + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
   const uint32_t ovb = static_cast<uint32_t>(min(tb + 16 + (lane >> 2), last)) * kRowBytes + 16 * (lane & 3);
   const uint32_t om = static_cast<uint32_t>(min(tb + (lane >> 1), last)) * (kMetaWords * 4) + 8 * (lane & 1);
-  r.ka = ld16_stream(kq + oka);
-  r.kb = ld16_stream(kq + okb);
-  r.va = ld16_stream(vq + ova);
-  r.vb = ld16_stream(vq + ovb);
+  if constexpr (kKB == 4) {
+    r.ka = ld16_stream(kq + oka);
+    r.kb = ld16_stream(kq + okb);
+  } else {
+    // 2-bit K rows are 32 bytes, a group 8 of them (in ka.x, ka.y)
+    const int last2 = nq - 1;
+    const uint2 a = ld8_stream(kq + static_cast<uint32_t>(min(tb + n, last2)) * row_bytes<2>() + 8 * j);
+    const uint2 b = ld8_stream(kq + static_cast<uint32_t>(min(tb + 16 + n, last2)) * row_bytes<2>() + 8 * j);
+    r.ka = make_uint4(a.x, a.y, 0u, 0u);
+    r.kb = make_uint4(b.x, b.y, 0u, 0u);
+  }
+  if constexpr (kVB == 4) {
+    r.va = ld16_stream(vq + ova);
+    r.vb = ld16_stream(vq + ovb);
+  } else {
+    // 2-bit V rows are 32 bytes: lane l loads half (l & 1) of token l / 2,
+    // so one load a lane covers the block (vb is unused)
+    const uint32_t ov = static_cast<uint32_t>(min(tb + (lane >> 1), last)) * row_bytes<2>() + 16 * (lane & 1);
+    r.va = ld16_stream(vq + ov);
+  }
   r.kmw = ld8_stream(reinterpret_cast<const uint8_t*>(kmeta) + om);
   r.vmw = ld8_stream(reinterpret_cast<const uint8_t*>(vmeta) + om);
 }
@@ -472,7 +489,7 @@ struct GState {
   float m;                          // running max of raw scores of head h (same in the quad, all j)
   float l;                          // this lane's share of the running denominator
   float4_t o[8];                    // o[i][rr]: dims 32j + 8rr + i of head h, used where g == j
-  float4_t corr;                    // 1024 * sum_t P'[t] (every row alike)
+  float4_t corr;                    // bias * sum_t P'[t] (every row alike; bias 1024, or 4 for 2-bit V)
   float4_t mt;                      // sum_t m_v[t][j] P[h][t] (every row alike)
   float4_t acc[8];                  // unbiased output of the blocks folded so far (flush_g)
 };
@@ -482,12 +499,14 @@ struct GState {
 // output, grows with the number of blocks accumulated.  Every kFlushBlocks
 // K4V4 blocks they are folded into the unbiased acc, O = (o - corr) (1 or
 // 1/16) + mt, and restarted from zero: the error then stays at what a scan
-// of that many blocks has, however long the wave's range is.
+// of that many blocks has, however long the wave's range is.  (With 2-bit
+// V codes every dim's operand is 4 + code: the factor is 1, kOdd16 off.)
 constexpr int kFlushBlocks = 8;
+template <bool kOdd16 = true>
 __device__ __forceinline__ void flush_g(GState& st) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float f = (i & 1) ? 0.0625f : 1.0f;
+    const float f = (kOdd16 && (i & 1)) ? 0.0625f : 1.0f;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) st.acc[i][rr] += fmaf(st.o[i][rr] - st.corr[rr], f, st.mt[rr]);
     st.o[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
@@ -507,6 +526,15 @@ __device__ __forceinline__ float quad_sum(float x) {
 __device__ __forceinline__ half8_t k_biased(uint32_t w, const Masks& k) {
   const uint32_t w8 = w >> 8;
   return pack4((w & k.lo) | k.magic, (w & k.hi) | k.magic, (w8 & k.lo) | k.magic, (w8 & k.hi) | k.magic);
+}
+
+// 2-bit keys: the eight codes of one 16-bit chunk (code i at bits 2i),
+// its low byte in bits 0-7 and its high byte in bits 16-23 of x, as biased
+// fp16 pairs (i, 4 + i) in the order {0,4,1,5,2,6,3,7} of k_biased: a code
+// goes into mantissa bits 8-9 under the exponent of 4 (exactly 4 + code),
+// so the bias is 4 and no query entry needs the 1/16 of a high nibble.
+__device__ __forceinline__ half8_t k_biased2(uint32_t x, uint32_t m2, uint32_t mg) {
+  return pack4(((x << 8) & m2) | mg, ((x << 6) & m2) | mg, ((x << 4) & m2) | mg, ((x << 2) & m2) | mg);
 }
 
 // Online softmax of one block of raw scores s[8] into the grouped state;
@@ -549,13 +577,21 @@ struct K4Mid {
   uint4 mha, mhb;                   // V {scale, min} of the tokens, group c >> 2
 };
 
+// kVB = 2: 2-bit V codes, a 32-byte row per token (word w holds dims
+// 16 w .. 16 w + 15).  Lane column c still owns output dims 8c .. 8c + 7:
+// bits 16 (c & 1) .. + 15 of word c / 2, which phase B selects.
+template <int kVB = 4, int kKB = 4>
 __device__ __forceinline__ void k4_phase_a(K4Mid& x, const K4Raw& r, K4Stage& sg,
                                            const half8_t qg[4], float rc, float qsc,
                                            const Masks& k, int tb, int nq, int lane, int c, int j) {
   const int g = c & 3;
   wave_sync();
-  *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
-  *reinterpret_cast<uint4*>(&sg.v[16 + (lane >> 2)][4 * (lane & 3)]) = r.vb;
+  if constexpr (kVB == 4) {
+    *reinterpret_cast<uint4*>(&sg.v[lane >> 2][4 * (lane & 3)]) = r.va;
+    *reinterpret_cast<uint4*>(&sg.v[16 + (lane >> 2)][4 * (lane & 3)]) = r.vb;
+  } else {
+    *reinterpret_cast<uint4*>(&sg.v[lane >> 1][4 * (lane & 1)]) = r.va;
+  }
   {  // this lane loaded token lane/2, groups 2 (lane & 1) and 2 (lane & 1) + 1
     const int tm = lane >> 1, g0 = 2 * (lane & 1);
     sg.km[32 * g0 + tm] = r.kmw.x;
@@ -573,16 +609,30 @@ __device__ __forceinline__ void k4_phase_a(K4Mid& x, const K4Raw& r, K4Stage& sg
   x.mha = *reinterpret_cast<const uint4*>(&sg.vm[32 * (c >> 2) + 4 * j]);
   x.mhb = *reinterpret_cast<const uint4*>(&sg.vm[32 * (c >> 2) + 16 + 4 * j]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x.vc[e] = sg.v[k4_token(0, j, e)][c];
+  for (int e = 0; e < 8; ++e) x.vc[e] = sg.v[k4_token(0, j, e)][kVB == 4 ? c : (c >> 1)];
 
   // accumulators start at -R, so they end at D - R
   float4_t da = {-rc, -rc, -rc, -rc}, db = {-rc, -rc, -rc, -rc};
-  const uint32_t wa[4] = {r.ka.x, r.ka.y, r.ka.z, r.ka.w};
-  const uint32_t wb[4] = {r.kb.x, r.kb.y, r.kb.z, r.kb.w};
+  if constexpr (kKB == 4) {
+    const uint32_t wa[4] = {r.ka.x, r.ka.y, r.ka.z, r.ka.w};
+    const uint32_t wb[4] = {r.kb.x, r.kb.y, r.kb.z, r.kb.w};
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    da = mfma(k_biased(wa[kk], k), qg[kk], da);
-    db = mfma(k_biased(wb[kk], k), qg[kk], db);
+    for (int kk = 0; kk < 4; ++kk) {
+      da = mfma(k_biased(wa[kk], k), qg[kk], da);
+      db = mfma(k_biased(wb[kk], k), qg[kk], db);
+    }
+  } else {
+    uint32_t m2, mg;
+    asm volatile("v_mov_b32 %0, 0x03000300" : "=v"(m2));
+    asm volatile("v_mov_b32 %0, 0x44004400" : "=v"(mg));
+    // chunk kk: the low or high 16 bits of word kk / 2, bytes split into halves
+    const uint32_t wa[2] = {r.ka.x, r.ka.y}, wb[2] = {r.kb.x, r.kb.y};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t sel = (kk & 1) ? 0x0C030C02u : 0x0C010C00u;
+      da = mfma(k_biased2(__builtin_amdgcn_perm(0u, wa[kk >> 1], sel), m2, mg), qg[kk], da);
+      db = mfma(k_biased2(__builtin_amdgcn_perm(0u, wb[kk >> 1], sel), m2, mg), qg[kk], db);
+    }
   }
   const uint32_t ka4[4] = {kma.x, kma.y, kma.z, kma.w};
   const uint32_t kb4[4] = {kmb.x, kmb.y, kmb.z, kmb.w};
@@ -603,7 +653,9 @@ __device__ __forceinline__ void k4_phase_a(K4Mid& x, const K4Raw& r, K4Stage& sg
   }
 }
 
-__device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Masks& k, float c2, float slack) {
+template <int kVB = 4>
+__device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Masks& k, float c2, float slack,
+                                           int c = 0) {
   float pr[8];
   softmax_g(st, x.s, c2, slack, pr);
   // B operands: P' = s_v P for the codes, P for the min term
@@ -621,30 +673,59 @@ __device__ __forceinline__ void k4_phase_b(GState& st, const K4Mid& x, const Mas
                            __builtin_amdgcn_perm(x.mhb.y, x.mhb.x, 0x07060302u),
                            __builtin_amdgcn_perm(x.mhb.w, x.mhb.z, 0x07060302u));
   // V^T operands: biased codes, token pairs interleaved as in the generic path
-  uint32_t xl[4], xh[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    xl[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x05040100u);
-    xh[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x07060302u);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t v[4];
+  if constexpr (kVB == 4) {
+    uint32_t xl[4], xh[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t w = (i < 4) ? xl[q] : xh[q];
-      if (i & 2) w >>= 8;
-      v[q] = (w & ((i & 1) ? k.hi : k.lo)) | k.magic;
+      xl[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x05040100u);
+      xh[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], 0x07060302u);
     }
-    st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pp, st.o[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w = (i < 4) ? xl[q] : xh[q];
+        if (i & 2) w >>= 8;
+        v[q] = (w & ((i & 1) ? k.hi : k.lo)) | k.magic;
+      }
+      st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pp, st.o[i]);
+    }
+    st.corr = mfma(pack4(k.magic, k.magic, k.magic, k.magic), pp, st.corr);
+  } else {
+    // 2-bit codes: the lane's 16-bit half of each token's word (eight codes,
+    // dim 8c + i at bits 2i), two tokens a register.  A code goes into
+    // mantissa bits 8-9 under the exponent of 4 (0x4400 | c << 8 is exactly
+    // 4 + c), so the bias is 4, not 1024: with codes of at most 3, a bias of
+    // 1024 would leave the biased sums' fp32 rounding several hundred times
+    // the size of the output's
+    uint32_t m2, mg;
+    asm volatile("v_mov_b32 %0, 0x03000300" : "=v"(m2));
+    asm volatile("v_mov_b32 %0, 0x44004400" : "=v"(mg));
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t xv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = __builtin_amdgcn_perm(x.vc[2 * q + 1], x.vc[2 * q], sel);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = (i < 4) ? (xv[q] << (8 - 2 * i)) : (xv[q] >> (2 * i - 8));
+        v[q] = (w & m2) | mg;
+      }
+      st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), pp, st.o[i]);
+    }
+    st.corr = mfma(pack4(mg, mg, mg, mg), pp, st.corr);
   }
-  st.corr = mfma(pack4(k.magic, k.magic, k.magic, k.magic), pp, st.corr);
   st.mt = mfma(am, p16, st.mt);
 }
 
 // One FP16 block in the grouped layout: the same columns (no bias, no
 // scale), P for even and 16 P for odd output dims, so that the FP16 and
-// K4V4 contributions share one accumulator under O = (o - corr) (1 or 1/16) + mt.
+// K4V4 contributions share one accumulator under O = (o - corr) (1 or 1/16) + mt
+// (with kOdd16 off, P for every dim: the 2-bit V convention).
+template <bool kOdd16 = true>
 __device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], const uint4 kr[8],
                                               const uint4 vr[8], int valid, int j, float c2, float slack) {
   float4_t da = {0.f, 0.f, 0.f, 0.f}, db = {0.f, 0.f, 0.f, 0.f};
@@ -681,7 +762,7 @@ __device__ __forceinline__ void f16_compute_g(GState& st, const half8_t qf[4], c
       const uint32_t a1[4] = {vr[2 * q + 1].x, vr[2 * q + 1].y, vr[2 * q + 1].z, vr[2 * q + 1].w};
       v[q] = __builtin_amdgcn_perm(a1[i >> 1], a0[i >> 1], sel);
     }
-    st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), (i & 1) ? p16x : p1, st.o[i]);
+    st.o[i] = mfma(pack4(v[0], v[1], v[2], v[3]), (kOdd16 && (i & 1)) ? p16x : p1, st.o[i]);
   }
 }
 
@@ -712,17 +793,21 @@ template <int kKB, int kVB>
 __device__ __forceinline__ void load_gen(GenRaw<kKB, kVB>& r, const uint8_t* kq, const uint32_t* kmeta,
                                          const uint8_t* vq, const uint32_t* vmeta, int tb, int nq,
                                          int lane) {
-  // rows past the unit's last token re-read it (masked below)
+  // rows past the unit's last token re-read it (masked below).  Ordinary
+  // loads: each instruction takes 16 bytes a lane at a stride of 8 kKB
+  // bytes, so the next instructions read the rest of the same lines, which
+  // the non-temporal policy would not keep (K8V8 at B = 32: 669 us with it,
+  // 452 us without)
   const uint32_t t = static_cast<uint32_t>(min(tb + (lane >> 1), nq - 1));
   const uint32_t h = lane & 1;
   const uint8_t* kp = kq + t * (16 * kKB) + h * (8 * kKB);
   const uint8_t* vp = vq + t * (16 * kVB) + h * (8 * kVB);
 #pragma unroll
-  for (int i = 0; i < kKB / 2; ++i) r.k[i] = ld16_stream(kp + 16 * i);
+  for (int i = 0; i < kKB / 2; ++i) r.k[i] = ld16(kp + 16 * i);
 #pragma unroll
-  for (int i = 0; i < kVB / 2; ++i) r.v[i] = ld16_stream(vp + 16 * i);
-  r.km = ld8_stream(reinterpret_cast<const uint8_t*>(kmeta) + t * 16 + h * 8);
-  r.vm = ld8_stream(reinterpret_cast<const uint8_t*>(vmeta) + t * 16 + h * 8);
+  for (int i = 0; i < kVB / 2; ++i) r.v[i] = ld16(vp + 16 * i);
+  r.km = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(kmeta) + t * 16 + h * 8);
+  r.vm = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(vmeta) + t * 16 + h * 8);
 }
 
 // 64 b-bit codes (element e at bits b e .. of the little-endian words w) of
@@ -828,13 +913,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   // K4V4 takes the grouped-code paths; other widths dequantise each block
   // into an LDS tile and use the FP16-block code
   constexpr bool kK4V4 = kKB == 4 && kVB == 4;
+  // With G <= 4 the 2-bit widths (K4V2, K2V4, K2V2) take the grouped-code
+  // path too: 2-bit codes are unpacked in registers as 4 + code (2-bit V:
+  // every dim's operand, so the odd dims carry no 1/16 factor, kOdd16 off;
+  // 2-bit K: no 1/16 query entries, R = 4 sum q)
+  constexpr bool kGC = kG4 && (kKB == 2 || kKB == 4) && (kVB == 2 || kVB == 4);
+  constexpr bool kK4G = kK4V4 || kGC;
+  constexpr int kVC = kVB == 2 ? 2 : 4;
+  constexpr int kKC = kKB == 2 ? 2 : 4;
+  constexpr bool kOdd16 = !(kGC && kVB == 2);
   // bytes of an FP16 block over those of a quantised block (3.2 at K4V4)
   constexpr float kF16Weight = 512.0f / (16 * (kKB + kVB) + 32);
-  using Stage = std::conditional_t<kK4V4, K4Stage, DqTile>;
+  using Stage = std::conditional_t<kK4G, K4Stage, DqTile>;
   // the per-wave staging areas of the scan, the image of the waves' states
   // and the partials of the final merge share LDS (barriers separate them)
   __shared__ union {
-    Stage stage[kWaves];                           // 14 KB (K4V4), 68 KB (tiles)
+    Stage stage[kWaves];                           // 14 KB (K4 codes), 68 KB (tiles)
     WgImage img;                                   // 16.5 KB
     FinPart fin[kThreads];                         // 8 KB
   } s_lds;
@@ -874,11 +968,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         // K4V4 B operand: the unpack order {0,4,1,5,2,6,3,7}, high-nibble
         // entries (odd dims) scaled by 1/16
         const half8_t sh = __builtin_shufflevector(qf[kk], qf[kk], 0, 4, 1, 5, 2, 6, 3, 7);
-        const _Float16 k16 = static_cast<_Float16>(0.0625f);
+        const _Float16 k16 = static_cast<_Float16>(kKC == 4 ? 0.0625f : 1.0f);
         qg[kk] = (half8_t){sh[0], sh[1], sh[2] * k16, sh[3] * k16, sh[4], sh[5], sh[6] * k16, sh[7] * k16};
       }
     }
-    // R = 1024 * (sum of column c's operand entries) and qs = sum of group g
+    // R = bias * (sum of column c's operand entries: bias 1024, or 4 for
+    // 2-bit keys) and qs = sum of group g
     // of head h (every j needs them, so each lane reads the group itself)
     float rc = 0.0f, qsc = 0.0f;
     if (h < G) {
@@ -890,10 +985,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) {
           const float x = static_cast<float>(v[e]);
           qsc += x;
-          rc += (e & 1) ? static_cast<float>(v[e] * static_cast<_Float16>(0.0625f)) : x;
+          rc += (kKC == 4 && (e & 1)) ? static_cast<float>(v[e] * static_cast<_Float16>(0.0625f)) : x;
         }
       }
-      rc *= 1024.0f;
+      rc *= kKC == 4 ? 1024.0f : 4.0f;
     }
 
     GState st;
@@ -948,7 +1043,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       const uint32_t *kmb, *vmb;
       int tb, nqb;
       blk_ptrs(bi, kb, kmb, vb, vmb, tb, nqb);
-      load_k4(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
+      load_k4<kVC, kKC>(r, kb, kmb, vb, vmb, tb, nqb, lane, n, j);
     };
     auto ld_gen = [&](GenRaw<kKB, kVB>& r, int bi) {
       const uint8_t *kb, *vb;
@@ -981,7 +1076,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // the loads are unconditional (past the end they re-read the wave's last
     // block) so that the wait before a compute only covers its own loads
     const int last = ww.k1 - 1;
-    if constexpr (kK4V4) {
+    if constexpr (kK4G) {
       K4Stage& sg = s_lds.stage[wave];
       const Masks km = make_masks();
       K4Raw ra, rb;
@@ -992,24 +1087,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (; blk + nwaves < nblk_f; blk += nwaves) {
           uint4 knxt[8];
           load_f16_k(knxt, f, (blk + nwaves) * kBlk, n, j);
-          f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+          f16_compute_g<kOdd16>(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
 #pragma unroll
           for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
           load_f16_v(vcur, f, (blk + nwaves) * kBlk, n, j);
         }
-        f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+        f16_compute_g<kOdd16>(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
       }
       if (has_k) {
         int blk = ww.k0;
         for (; blk < ww.k1; blk += 2) {
           ld_k4(rb, min(blk + 1, last));
-          k4_phase_a(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
-          k4_phase_b(st, x, km, c2, slack);
+          k4_phase_a<kVC, kKC>(x, ra, sg, qg, rc, qsc, km, blk * kBlk, nq, lane, n, j);
+          k4_phase_b<kVC>(st, x, km, c2, slack, n);
           if (blk + 1 >= ww.k1) break;
           ld_k4(ra, min(blk + 2, last));
-          k4_phase_a(x, rb, sg, qg, rc, qsc, km, (blk + 1) * kBlk, nq, lane, n, j);
-          k4_phase_b(st, x, km, c2, slack);
-          if ((blk + 2 - ww.k0) % kFlushBlocks == 0) flush_g(st);
+          k4_phase_a<kVC, kKC>(x, rb, sg, qg, rc, qsc, km, (blk + 1) * kBlk, nq, lane, n, j);
+          k4_phase_b<kVC>(st, x, km, c2, slack, n);
+          if ((blk + 2 - ww.k0) % kFlushBlocks == 0) flush_g<kOdd16>(st);
         }
       }
     } else {
@@ -1021,12 +1116,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (; blk + nwaves < nblk_f; blk += nwaves) {
           uint4 knxt[8];
           load_f16_k(knxt, f, (blk + nwaves) * kBlk, n, j);
-          f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+          f16_compute_g<kOdd16>(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
 #pragma unroll
           for (int e = 0; e < 8; ++e) kcur[e] = knxt[e];
           load_f16_v(vcur, f, (blk + nwaves) * kBlk, n, j);
         }
-        f16_compute_g(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
+        f16_compute_g<kOdd16>(st, qf, kcur, vcur, nf - blk * kBlk, j, c2, slack);
       }
       if (has_k) {
         int blk = ww.k0;
@@ -1034,11 +1129,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
           uint4 kr[8], vr[8];
           ld_gen(rb, min(blk + 1, last));
           gen_operands(kr, vr, ra, tl, lane, n, j);
-          f16_compute_g(st, qf, kr, vr, nq - blk * kBlk, j, c2, slack);
+          f16_compute_g<kOdd16>(st, qf, kr, vr, nq - blk * kBlk, j, c2, slack);
           if (blk + 1 >= ww.k1) break;
           ld_gen(ra, min(blk + 2, last));
           gen_operands(kr, vr, rb, tl, lane, n, j);
-          f16_compute_g(st, qf, kr, vr, nq - (blk + 1) * kBlk, j, c2, slack);
+          f16_compute_g<kOdd16>(st, qf, kr, vr, nq - (blk + 1) * kBlk, j, c2, slack);
         }
       }
     }
@@ -1047,7 +1142,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     valid = active;
     m_h = st.m;
     l_h = st.l;
-    flush_g(st);
+    flush_g<kOdd16>(st);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ofin[i] = st.acc[i];
   } else {

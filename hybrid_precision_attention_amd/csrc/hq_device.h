@@ -183,7 +183,9 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 // Loads of data a launch reads once (the cache regions the decode scan
 // streams): the non-temporal policy (nt) keeps them from displacing L2 and
 // Infinity Cache contents they would never be read from again.  The decode's
-// HBM rate at B = 32, L = 32K went from 5.6 to 6.5 TB/s with them.
+// HBM rate at B = 32, L = 32K went from 5.6 to 6.5 TB/s with them.  Only for
+// loads whose lanes cover whole lines in one instruction: a line the next
+// instructions still read is not kept under this policy.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld16_stream(const void* p) {

@@ -41,6 +41,9 @@ CASES = [
     ("tiny", {"L": 1500}, 4, 4, None),                     # G = 4: the grouped-column path
     ("qwen3_32b", {"L": 700, "B": 2}, 4, 4, None),         # G = 8: the general path
     ("tiny", {"L": 900}, 8, 4, None),                      # another width (LDS-tile path)
+    ("tiny", {"L": 1100}, 4, 2, None),                     # K4V2 at G = 4: grouped path, 2-bit V codes
+    ("tiny", {"L": 1000}, 2, 4, None),                     # K2V4 at G = 4: grouped path, 2-bit K codes
+    ("tiny", {"L": 700}, 2, 2, "promote"),                 # K2V2, with promotions
     ("tiny", {"L": 300, "W": 0}, 4, 4, None),              # no window: the new token itself leaves
     ("tiny", {"L": 60}, 4, 4, None),                       # the window is not full yet
     ("tiny", {"L": 800}, 4, 4, "promote"),                 # leaving tokens promoted to lines

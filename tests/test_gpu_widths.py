@@ -62,7 +62,7 @@ DECODE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 2), (2, 4)], ids=["K8V8", "K4V2", "K2V4"])
+@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 2), (2, 4), (2, 2)], ids=["K8V8", "K4V2", "K2V4", "K2V2"])
 @pytest.mark.parametrize("name,over", DECODE_CASES, ids=[f"{n}-{o}" for n, o in DECODE_CASES])
 def test_decode_parity(name, over, kb, vb):
     wl = workload(name, **over)
@@ -77,7 +77,7 @@ def test_decode_parity(name, over, kb, vb):
     check_decode(out, lse, ref, ref_lse, tag=f"{name} {over} K{kb}V{vb}")
 
 
-@pytest.mark.parametrize("kb,vb", [(8, 8), (2, 4)], ids=["K8V8", "K2V4"])
+@pytest.mark.parametrize("kb,vb", [(8, 8), (4, 2), (2, 4)], ids=["K8V8", "K4V2", "K2V4"])
 def test_decode_full_size_llama_layer(kb, vb):
     """Llama-3.1-8B-shaped layer at a 32K prefix: every unit."""
     wl = workload("llama31_8b")
