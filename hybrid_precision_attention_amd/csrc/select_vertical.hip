@@ -43,6 +43,7 @@ constexpr int kChunk = 64;            // keys a wave holds in registers at a tim
 constexpr int kRG = 256;              // rows per row group (queries staged in LDS)
 constexpr int kRB = kRG / 16;         // 16-row blocks per row group
 constexpr int kTopThreads = 1024;
+constexpr int kSelCUs = 256;          // MI355X compute units
 
 struct SelArgs {
   const uint16_t* qbuf;
@@ -63,6 +64,8 @@ struct SelArgs {
   // decode-time refresh only: the hybrid cache at decode position t
   hq_cache c;
   int32_t t, cap_q, cap_vl, cap_stg;
+  int32_t nwgr;                     // refresh workgroups per unit (its chunks split evenly)
+  int32_t xcd_group;                // 1: a unit's workgroups are placed on one XCD
 };
 
 __device__ __forceinline__ half8_t as_half8(uint4 v) { return __builtin_bit_cast(half8_t, v); }
@@ -159,32 +162,39 @@ __device__ __forceinline__ void load_keys(uint4 kr[4][4], const uint16_t* kunit,
   }
 }
 
-// Rows [256 rg, 256 rg + 256) of the unit's buffered queries in LDS, in the
+// Rows [R rg, R rg + R) of the unit's buffered queries in LDS (R = 16 kNRB
+// rows a group: 256 in the dense passes, 256 or 512 in the refresh), in the
 // B-operand order of the MFMA: q[rb][kk][16 j + n] = dims 32j + 8kk .. +7 of
 // row 16 rb + n.  Rows past the last one repeat it (their results are
 // discarded).  Every lane of a wave then reads 16 consecutive bytes.
-using QStage = uint4[kRB][4][64];
+template <int kNRB>
+using QStageT = uint4[kNRB][4][64];
+using QStage = QStageT<kRB>;
 
-constexpr int kStageIters = kRG * 16 / kSThreads;   // 16-byte pieces per thread
+constexpr int kStageIters = kRG * 16 / kSThreads;   // 16-byte pieces per thread (256 rows)
 
-// In two halves, so that other loads can be in flight between them: all of
-// the thread's loads are issued before any is stored.
+// The staging is split into loads and stores, so that other loads can be in
+// flight with it: all of the thread's loads are issued before any is stored.
+// Part `part` of a group of 16 kNRB rows covers its rows
+// [256 part, 256 part + 256).
+template <int kNRB = kRB>
 __device__ __forceinline__ void stage_load(uint4 v[kStageIters], const SelArgs& a, int64_t b, int h0,
-                                           int rg) {
+                                           int rg, int part = 0) {
 #pragma unroll
   for (int i = 0; i < kStageIters; ++i) {
     const int idx = threadIdx.x + i * kSThreads;
-    const int rr = idx >> 4, ch = idx & 15;
-    const int r = min(rg * kRG + rr, a.R - 1);
+    const int rr = kRG * part + (idx >> 4), ch = idx & 15;
+    const int r = min(rg * 16 * kNRB + rr, a.R - 1);
     const int g = r / a.nb, jq = r - g * a.nb;
     v[i] = ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
   }
 }
-__device__ __forceinline__ void stage_store(QStage& sq, const uint4 v[kStageIters]) {
+template <int kNRB = kRB>
+__device__ __forceinline__ void stage_store(QStageT<kNRB>& sq, const uint4 v[kStageIters], int part = 0) {
 #pragma unroll
   for (int i = 0; i < kStageIters; ++i) {
     const int idx = threadIdx.x + i * kSThreads;
-    const int rr = idx >> 4, ch = idx & 15;
+    const int rr = kRG * part + (idx >> 4), ch = idx & 15;
     sq[rr >> 4][ch & 3][16 * (ch >> 2) + (rr & 15)] = v[i];
   }
 }
@@ -194,25 +204,32 @@ __device__ __forceinline__ void stage_rows(QStage& sq, const SelArgs& a, int64_t
   stage_store(sq, v);
 }
 
-__device__ __forceinline__ void load_q(half8_t qb[4], const QStage& sq, int rb, int lane) {
+template <int kNRB = kRB>
+__device__ __forceinline__ void load_q(half8_t qb[4], const QStageT<kNRB>& sq, int rb, int lane) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qb[kk] = as_half8(sq[rb][kk][lane]);
 }
+// k-steps k0, k0 + 1 of row block rb
+template <int kNRB = kRB>
+__device__ __forceinline__ void load_q2(half8_t qb[2], const QStageT<kNRB>& sq, int rb, int k0, int lane) {
+  qb[0] = as_half8(sq[rb][k0][lane]);
+  qb[1] = as_half8(sq[rb][k0 + 1][lane]);
+}
 
+// S of the first kNX blocks of 16 keys (four independent accumulation
+// chains when kNX = 4, interleaved)
+template <int kNX = 4>
 __device__ __forceinline__ void mfma_scores(float4_t s[4], const uint4 kr[4][4], const half8_t qb[4]) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) s[x] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  // four independent accumulation chains, interleaved
+  for (int x = 0; x < kNX; ++x) s[x] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int x = 0; x < 4; ++x) s[x] = mfma(as_half8(kr[x][kk]), qb[kk], s[x]);
+    for (int x = 0; x < kNX; ++x) s[x] = mfma(as_half8(kr[x][kk]), qb[kk], s[x]);
 }
 
-// The row statistics keep their LDS operands ahead of use: the query operands
-// of row block rb + 2 and the running state of rb + 1 are read while row block
-// rb is computed.  (The column-mass loops keep theirs one block ahead: two
-// would not fit their registers.)
+// Every pass keeps its LDS operands ahead of use: the query operands of row
+// block rb + 2 are read while row block rb is computed.
 
 // Streaming workgroup (x, unit, row group): keys [x * wg_keys, ...), wave w
 // taking 64-key chunks w, w + 8, ... with the next chunk's keys in flight
@@ -357,24 +374,31 @@ __global__ __launch_bounds__(kSThreads) void row_stats_kernel(SelArgs a) {
 }
 
 // Pass 2 over one chunk: acc[4x + e] += sum over the lane's rows of
-// exp2(c2 s - lse log2 e) for key k0 + 16x + 4j + e.
+// exp2(c2 s - lse log2 e) for key k0 + 16x + 4j + e.  The query operands and
+// -lse of row block rb + 2 are read from LDS while row block rb is computed,
+// so the MFMAs of rb + 1 never wait for an LDS round trip.
 template <bool kMasked>
 __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][4], const QStage& sq,
                                                const float* s_nl, const SelArgs& a, int rg, int k0,
                                                int lane, int n, int j) {
   float4_t sc[4];
-  half8_t qb[4];
-  load_q(qb, sq, 0, lane);
-  mfma_scores(sc, kr, qb);
-  float nl_c = s_nl[n];
+  half8_t q0[4], q01[2], q23[2], n01[2];
+  load_q(q0, sq, 0, lane);
+  mfma_scores(sc, kr, q0);
+  load_q2(q01, sq, 1, 0, lane);
+  float nl_c = s_nl[n], nl_1 = s_nl[16 + n];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     float4_t sn[4];
-    float nl_n = 0.0f;
+    float nl_2 = 0.0f;
+    if (rb + 1 < kRB) load_q2(q23, sq, rb + 1, 2, lane);
+    if (rb + 2 < kRB) {
+      load_q2(n01, sq, rb + 2, 0, lane);
+      nl_2 = s_nl[(rb + 2) * 16 + n];
+    }
     if (rb + 1 < kRB) {
-      load_q(qb, sq, rb + 1, lane);
-      nl_n = s_nl[(rb + 1) * 16 + n];
-      mfma_scores(sn, kr, qb);
+      const half8_t q1[4] = {q01[0], q01[1], q23[0], q23[1]};
+      mfma_scores(sn, kr, q1);
     }
     if (!kMasked) {
 #pragma unroll
@@ -383,7 +407,10 @@ __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][
         for (int e = 0; e < 4; ++e)
           acc[4 * x + e] += __builtin_amdgcn_exp2f(fmaf(sc[x][e], a.c2, nl_c));
       if (rb + 1 < kRB) {
-        // the next row block's 16 MFMAs interleaved with this block's 48 VALU
+        // the LDS reads of rb + 2 first, then the next row block's 16 MFMAs
+        // interleaved with this block's 48 VALU
+        if (rb + 2 < kRB) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -405,8 +432,14 @@ __device__ __forceinline__ void chunk_col_mass(float acc[16], const uint4 kr[4][
     if (rb + 1 < kRB) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) sc[x] = sn[x];
-      nl_c = nl_n;
+      q01[0] = n01[0];
+      q01[1] = n01[1];
+      nl_c = nl_1;
+      nl_1 = nl_2;
     }
+    // one scheduling region a row block: the reads issued for rb + 2 are
+    // not sunk to their use
+    if (!kMasked) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -555,12 +588,27 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
 // vertical lines, the window positions t - nwin .. t - 1 (ring slot pos mod
 // W) and the staged token (position t).  A K4V4 key's elements enter the
 // matrix cores as fp16 roundings of code * scale + min (the fp16 operand
-// type of v_mfma_f32_16x16x32_f16): each within 2^-11 relative (or half an
-// fp16 subnormal step) of the cache's key, an error the scores' tolerance
-// allows for.  Row r = g * nb + jq is the buffered query at position
-// t - nb + 1 + jq; every cached key at a position up to the row's own gets
-// exp(tau q.k - lse) added to the running score at that position.
+// type of the MFMA): each within 2^-11 relative (or half an fp16 subnormal
+// step) of the cache's key, an error the scores' tolerance allows for.  Row
+// r = g * nb + jq is the buffered query at position t - nb + 1 + jq; every
+// cached key at a position up to the row's own gets exp(tau q.k - lse)
+// added to the running score at that position.
+//
+// The products are v_mfma_f32_32x32x16_f16 tiles, S = K Q^T with 32 keys
+// (A) by 32 rows (B), which on gfx950 deliver twice the rate of the
+// 16x16x32 form.  A wave holds a chunk of 64 entries as two key tiles; lane
+// (kl, h) = (lane % 32, lane / 32) holds dims 64 h + 8 ks .. + 7 of entry
+// 32 kt + kl for k-steps ks = 0..7 (the contraction runs over the dims in
+// that order on both operands, so a lane's dims are one contiguous half of
+// the row: two groups of 32).  Output register r of tile (kt, row tile)
+// holds entry 32 kt + 8 (r / 4) + 4 h + r % 4 against row lane % 32.
 // ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16_t mfma32(half8_t a, half8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 struct HybridList {
   int nq, nvl, nwin, nst, n;
 };
@@ -577,46 +625,66 @@ __device__ __forceinline__ HybridList hybrid_list(const SelArgs& a, int64_t u) {
 
 constexpr int kNoPos = 0x7FFFFFFF;   // list entries past the last key
 
-// K4V4 entries k0 + 16x + n (all of them below nq) for lane (n, j): the
-// group-j codes, {scale, min} and position of each.
-// (kKB-bit key codes: group j of a token is 4 kKB bytes at byte 4 kKB j of
-// its 16 kKB-byte row.)
+// Query rows in LDS in the B-operand order of the 32x32x16 tiles:
+// q[rt][ks][lane] = dims 64 (lane / 32) + 8 ks .. + 7 of row 32 rt + lane % 32.
+template <int kNRT>
+using QStage32 = uint4[kNRT][8][64];
+using QTile32 = uint4[8][64];                // one row tile
+
+// Rows [rows rg + 256 part, ... + 256) of the group into their row tiles
+template <int kNRT>
+__device__ __forceinline__ void stage32_load(uint4 v[kStageIters], const SelArgs& a, int64_t b, int h0,
+                                             int rg, int part) {
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) {
+    const int idx = threadIdx.x + i * kSThreads;
+    const int rr = kRG * part + (idx >> 4), ch = idx & 15;
+    const int r = min(rg * 32 * kNRT + rr, a.R - 1);
+    const int g = r / a.nb, jq = r - g * a.nb;
+    v[i] = ld16(a.qbuf + ((b * a.Hq + h0 + g) * a.nb + jq) * kD + 8 * ch);
+  }
+}
+template <int kNRT>
+__device__ __forceinline__ void stage32_store(QStage32<kNRT>& sq, const uint4 v[kStageIters], int part) {
+#pragma unroll
+  for (int i = 0; i < kStageIters; ++i) {
+    const int idx = threadIdx.x + i * kSThreads;
+    const int rr = kRG * part + (idx >> 4), ch = idx & 15;
+    sq[rr >> 5][ch & 7][32 * (ch >> 3) + (rr & 31)] = v[i];
+  }
+}
+
+// K4V4 entries k0 + 32 kt + kl (all below nq) for lane (kl, h): the codes of
+// dims 64 h .. 64 h + 63 (2 kKB words), the {scale, min} words of groups
+// 2h and 2h + 1, and the position, of both key tiles.
 template <int kKB>
-struct KRaw {
-  uint32_t codes[4][kKB];
-  uint32_t meta[4];
-  int pos[4];
+struct KRaw32 {
+  uint32_t codes[2][2 * kKB];
+  uint2 meta[2];
+  int pos[2];
 };
 
 template <int kKB>
-__device__ __forceinline__ void load_group_codes(uint32_t w[kKB], const uint8_t* p) {
-  if constexpr (kKB == 2) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-  } else {
+__device__ __forceinline__ void load_codes_half(uint32_t w[2 * kKB], const uint8_t* p) {
 #pragma unroll
-    for (int i = 0; i < kKB; i += 4) {
-      const uint4 v = ld16(p + 4 * i);
-      w[i] = v.x;
-      w[i + 1] = v.y;
-      w[i + 2] = v.z;
-      w[i + 3] = v.w;
-    }
+  for (int i = 0; i < 2 * kKB; i += 4) {
+    const uint4 v = ld16(p + 4 * i);
+    w[i] = v.x;
+    w[i + 1] = v.y;
+    w[i + 2] = v.z;
+    w[i + 3] = v.w;
   }
 }
 
 template <int kKB>
-__device__ __forceinline__ void load_k4raw(KRaw<kKB>& r, const SelArgs& a, int64_t u, int k0, int n, int j) {
-  // k0 is a multiple of 64: entries x = 0, 1 share one 32-slot block, x = 2, 3 the next
-  const int64_t s01 = k4_slot(a.c.k4_pages, a.cap_q, u, k0 + n);
-  const int64_t s23 = k4_slot(a.c.k4_pages, a.cap_q, u, k0 + 32 + n);
+__device__ __forceinline__ void load_k4raw32(KRaw32<kKB>& r, const SelArgs& a, int64_t u, int k0, int kl, int h) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int64_t sl = (x < 2 ? s01 : s23) + 16 * (x & 1);
-    load_group_codes<kKB>(r.codes[x], a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
-    r.meta[x] = reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j];
-    r.pos[x] = a.c.q_pos[sl];
+  for (int kt = 0; kt < 2; ++kt) {
+    const int64_t sl = k4_slot(a.c.k4_pages, a.cap_q, u, k0 + 32 * kt + kl);
+    load_codes_half<kKB>(r.codes[kt], a.c.kq + sl * (16 * kKB) + 8 * kKB * h);
+    r.meta[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(a.c.kq_meta) +
+                                                 sl * kMetaWords + 2 * h);
+    r.pos[kt] = a.c.q_pos[sl];
   }
 }
 
@@ -639,49 +707,53 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, half2_t s2, half2_t m2) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// Elements 8 ks .. 8 ks + 7 of the lane's 64 (kKB-bit codes, element e at
+// bits kKB e of the words), dequantised with the group's {scale, min}.
 template <int kKB>
-__device__ __forceinline__ void dequant_group(uint4 out[4], const uint32_t w[kKB], uint32_t meta) {
+__device__ __forceinline__ uint4 dequant_slice(const uint32_t w[2 * kKB], int ks, uint32_t meta) {
   const half2_t sm = __builtin_bit_cast(half2_t, meta);
   const half2_t s2 = {sm[0], sm[0]}, m2 = {sm[1], sm[1]};
   if constexpr (kKB == 4) {
-    out[0] = dequant8(w[0], s2, m2);
-    out[1] = dequant8(w[1], s2, m2);
-    out[2] = dequant8(w[2], s2, m2);
-    out[3] = dequant8(w[3], s2, m2);
+    return dequant8(w[ks], s2, m2);
   } else {
-    // element e at bits kKB e of the group, in pairs under the exponent of 1024
     constexpr uint32_t kMask = (1u << kKB) - 1u;
     const half2_t k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
-    uint32_t o[16];
+    uint32_t o[4];
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int e = 2 * p;
+    for (int p = 0; p < 4; ++p) {
+      const int e = 8 * ks + 2 * p;
       const uint32_t c0 = (w[(kKB * e) >> 5] >> ((kKB * e) & 31)) & kMask;
       const uint32_t c1 = (w[(kKB * (e + 1)) >> 5] >> ((kKB * (e + 1)) & 31)) & kMask;
       const half2_t c = __builtin_bit_cast(half2_t, c0 | (c1 << 16) | 0x64006400u) - k1024;
       o[p] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(c, s2, m2));
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    return make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
-// fp16 operands of any 64 list entries, lane (n, j) holding dims
-// 32j .. 32j + 31 of entry k0 + 16x + n in kr[x] (zeros past the list) and its
-// position in pos[x] (kNoPos past the list).  Used for the few chunks that
-// are not all K4V4, so the loads are simply issued in order.
 template <int kKB>
-__device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelArgs& a,
-                                         const HybridList& h, int64_t u, int k0, int n, int j) {
+__device__ __forceinline__ void dequant_tile(uint4 kr[8], const uint32_t w[2 * kKB], uint2 meta) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int ki = k0 + 16 * x + n;
+  for (int ks = 0; ks < 8; ++ks) kr[ks] = dequant_slice<kKB>(w, ks, ks < 4 ? meta.x : meta.y);
+}
+
+// fp16 operands of any 64 list entries (zeros past the list) and their
+// positions (kNoPos past the list).  Used for the few chunks that are not
+// all K4V4, so the loads are simply issued in order.
+template <int kKB>
+__device__ __forceinline__ void load_any32(uint4 kr[2][8], int pos[2], const SelArgs& a,
+                                           const HybridList& h, int64_t u, int k0, int kl, int hh) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int ki = k0 + 32 * kt + kl;
     if (ki < h.nq) {
       const int64_t sl = k4_slot(a.c.k4_pages, a.cap_q, u, ki);
-      uint32_t w[kKB];
-      load_group_codes<kKB>(w, a.c.kq + sl * (16 * kKB) + 4 * kKB * j);
-      dequant_group<kKB>(kr[x], w, reinterpret_cast<const uint32_t*>(a.c.kq_meta)[sl * kMetaWords + j]);
-      pos[x] = a.c.q_pos[sl];
+      uint32_t w[2 * kKB];
+      load_codes_half<kKB>(w, a.c.kq + sl * (16 * kKB) + 8 * kKB * hh);
+      const uint2 meta = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint32_t*>(a.c.kq_meta) +
+                                                         sl * kMetaWords + 2 * hh);
+      dequant_tile<kKB>(kr[kt], w, meta);
+      pos[kt] = a.c.q_pos[sl];
     } else {
       int e = ki - h.nq;
       const uint16_t* row = nullptr;
@@ -696,87 +768,170 @@ __device__ __forceinline__ void load_any(uint4 kr[4][4], int pos[4], const SelAr
         p = a.t;
         row = a.c.kstg + u * a.cap_stg * kD;
       }
-      pos[x] = p;
+      pos[kt] = p;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kr[x][kk] = row ? ld16(row + 32 * j + 8 * kk) : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) kr[kt][ks] = row ? ld16(row + 64 * hh + 8 * ks) : make_uint4(0, 0, 0, 0);
     }
   }
 }
 
-// acc[4x + e] += sum over the row group's rows of exp2(c2 s - lse log2 e)
-// for list entry k0 + 16x + 4j + e; masked: a row counts only when the
-// entry's position kp (kNoPos past the list) is at most its own.
-template <bool kMasked>
-__device__ __forceinline__ void chunk_refresh(float acc[16], const uint4 kr[4][4], const QStage& sq,
-                                              const float* s_nl, const int* s_prow, const int kp[16],
-                                              float c2, int lane, int n) {
-  float4_t sc[4];
-  half8_t qb[4];
-  load_q(qb, sq, 0, lane);
-  mfma_scores(sc, kr, qb);
-  float nl_c = s_nl[n];
-  int pr_c = kMasked ? s_prow[n] : 0;
+// S of row tile rt for the first kNT key tiles: two chains of eight k-steps
+template <int kNT>
+__device__ __forceinline__ void scores32(f32x16_t s[2], const uint4 kr[2][8], const half8_t q[8]) {
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    float4_t sn[4];
-    float nl_n = 0.0f;
-    int pr_n = 0;
-    if (rb + 1 < kRB) {
-      load_q(qb, sq, rb + 1, lane);
-      nl_n = s_nl[(rb + 1) * 16 + n];
-      if (kMasked) pr_n = s_prow[(rb + 1) * 16 + n];
-      mfma_scores(sn, kr, qb);
-    }
+  for (int kt = 0; kt < kNT; ++kt)
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int i = 0; i < 16; ++i) s[kt][i] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sc[x][e], c2, nl_c));
-        if (kMasked) acc[4 * x + e] += (kp[4 * x + e] <= pr_c) ? p : 0.0f;
-        else acc[4 * x + e] += p;
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt) s[kt] = mfma32(as_half8(kr[kt][ks]), q[ks], s[kt]);
+}
+
+__device__ __forceinline__ void load_q32(half8_t q[8], const QTile32& t, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) q[ks] = as_half8(t[ks][lane]);
+}
+
+// acc[kt][r] += sum over the 256 rows of the slice of exp2(c2 s - lse log2 e)
+// for entry 32 kt + 8 (r / 4) + 4 h + r % 4 (this lane's share: its row
+// lane % 32 of every row tile).  A software pipeline in steps: step ks of
+// row tile rt issues the two MFMAs of k-step ks of tile rt + 1 (their query
+// operand read from LDS two steps earlier), the read for two steps later,
+// and the exponentials of four of tile rt's scores (key tile ks / 4, so the
+// first key tile's chain, which ends first, is consumed first).  Each step
+// is its own scheduling region, so the order holds.
+__device__ __forceinline__ void chunk_refresh32(float acc[2][16], const uint4 kr[2][8], const QTile32* sq,
+                                                const float* s_nl, float c2, int lane) {
+  constexpr int kNRT = kRG / 32;               // row tiles of the 256-row slice
+  const int rl = lane & 31;
+  half8_t q[3];                                // query operands of steps s, s + 1, s + 2 (slot s mod 3)
+  f32x16_t sc[2];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[kt][i] = 0.0f;
+  q[0] = as_half8(sq[0][0][lane]);
+  q[1] = as_half8(sq[0][1][lane]);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    q[(ks + 2) % 3] = as_half8(ks + 2 < 8 ? sq[0][ks + 2][lane] : sq[1][ks - 6][lane]);
+    sc[0] = mfma32(as_half8(kr[0][ks]), q[ks % 3], sc[0]);
+    sc[1] = mfma32(as_half8(kr[1][ks]), q[ks % 3], sc[1]);
+  }
+  float nl_c = s_nl[rl];
+#pragma unroll
+  for (int rt = 0; rt < kNRT; ++rt) {
+    f32x16_t sn[2];
+    const bool more = rt + 1 < kNRT;
+    const float nl_n = more ? s_nl[32 * (rt + 1) + rl] : 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sn[kt][i] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (more) {
+        const int gs = 8 * (rt + 1) + ks;      // step index of tile rt + 1's k-step ks
+        if (ks + 2 < 8) q[(gs + 2) % 3] = as_half8(sq[rt + 1][ks + 2][lane]);
+        else if (rt + 2 < kNRT) q[(gs + 2) % 3] = as_half8(sq[rt + 2][ks - 6][lane]);
+        sn[0] = mfma32(as_half8(kr[0][ks]), q[gs % 3], sn[0]);
+        sn[1] = mfma32(as_half8(kr[1][ks]), q[gs % 3], sn[1]);
       }
-    if (!kMasked && rb + 1 < kRB) {
-      // the next row block's 16 MFMAs interleaved with this block's 48 VALU
+      const int kt = ks >> 2, r0 = 4 * (ks & 3);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
+      for (int e = 0; e < 4; ++e) acc[kt][r0 + e] += __builtin_amdgcn_exp2f(fmaf(sc[kt][r0 + e], c2, nl_c));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (rb + 1 < kRB) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) sc[x] = sn[x];
-      nl_c = nl_n;
-      pr_c = pr_n;
-    }
+    for (int kt = 0; kt < 2; ++kt) sc[kt] = sn[kt];
+    nl_c = nl_n;
   }
 }
 
-// Workgroup (x, unit): list entries [x * wg_keys, ...), wave w taking
-// 64-entry chunks w, w + 8, ...; while a chunk is computed, the next one's
-// K4V4 codes are in flight (the other chunks, a few per unit, load in place).
-// Row groups (G * nb > 256) run one after another inside the workgroup, each
-// adding its mass to the score entries it owns.
-template <int kKB>
+// The masked form, for the few chunks holding entries that some rows must
+// not see (positions past a row's own, and entries past the list, kNoPos):
+// one row tile at a time, each entry's position read from the wave's LDS
+// list s_kpos.  Only the first kNT key tiles are computed (kNT = 1: the
+// list's tail, at most 32 entries).
+template <int kNT>
+__device__ __forceinline__ void chunk_refresh32_masked(float acc[2][16], const uint4 kr[2][8], const QTile32* sq,
+                                                       const float* s_nl, const int* s_prow, const int* kpos,
+                                                       float c2, int lane) {
+  constexpr int kNRT = kRG / 32;
+  const int rl = lane & 31, hh = lane >> 5;
+#pragma unroll 1
+  for (int rt = 0; rt < kNRT; ++rt) {
+    f32x16_t sc[2];
+    half8_t q[8];
+    load_q32(q, sq[rt], lane);
+    scores32<kNT>(sc, kr, q);
+    const float nl = s_nl[32 * rt + rl];
+    const int pr = s_prow[32 * rt + rl];
+#pragma unroll
+    for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], c2, nl));
+        acc[kt][r] += (kpos[32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3)] <= pr) ? p : 0.0f;
+      }
+  }
+}
+
+// Sum over the 32 row lanes of each half (lanes l, l ^ 16 by a row swap,
+// then the 16 lanes of a row by DPP): lane l ends with the total of value
+// v = l % 32 of the 32 acc[kt][r] (v = 16 kt + r).
+__device__ __forceinline__ float reduce_scatter32(const float acc[2][16], int lane) {
+  float t[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    // lanes with bit 4 clear keep kt = 0 and take the partner's kt = 0;
+    // lanes with bit 4 set keep kt = 1 (the swap pairs the rows so that the
+    // two results add to exactly that)
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0][q]), __float_as_uint(acc[1][q]),
+                                                    false, false);
+    t[q] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  }
+  return reduce_scatter16(t, lane & 15);
+}
+
+// Workgroup (x, unit) of the nwgr of a unit: its share of the unit's
+// 64-entry chunks, [x nch / nwgr, (x + 1) nch / nwgr), wave w taking chunks
+// w, w + 8, ... of it; while a chunk is computed, the next one's K4V4 codes
+// are in flight (the other chunks, a few per unit, load in place).  The
+// grid is one-dimensional: workgroup i runs on XCD i mod 8, so with
+// xcd_group set the workgroups of a unit are numbered to share one XCD
+// (its L2 then holds that unit's queries and codes only).  Row groups of
+// 32 kNRT rows (256, or 512 when G * nb > 256, so that a chunk's codes are
+// loaded and dequantised once per 512 rows) run one after another inside
+// the workgroup, each adding its mass to the score entries it owns.
+template <int kKB, int kNRT>
 __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
-  __shared__ QStage s_q;                                    // 64 KB
-  __shared__ float s_nl[kRG];                               // -lse * log2(e), -inf for padding
-  __shared__ int s_prow[kRG];                               // row position, -1 for padding
+  constexpr int kRows = 32 * kNRT;
+  __shared__ QStage32<kNRT> s_q;                            // 64 or 128 KB
+  __shared__ float s_nl[kRows];                             // -lse * log2(e), -inf for padding
+  __shared__ int s_prow[kRows];                             // row position, -1 for padding
   __shared__ int s_kpos[kSWaves][kChunk];                   // positions of the wave's chunk
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, j = lane >> 4;
-  const int64_t u = blockIdx.y;
+  const int kl = lane & 31, hh = lane >> 5;
+  int idx = blockIdx.x;
+  if (a.xcd_group) idx = (idx & 7) * (gridDim.x >> 3) + (idx >> 3);
+  const int64_t u = idx / a.nwgr;
+  const int xw = idx - static_cast<int>(u) * a.nwgr;
   const int64_t b = u / a.Hkv;
   const int h0 = static_cast<int>(u % a.Hkv) * a.G;
-  const int wg0 = blockIdx.x * a.wg_keys;
   const HybridList h = hybrid_list(a, u);
-  if (wg0 >= h.n) return;                                   // the whole workgroup leaves
+  const int nch = (h.n + kChunk - 1) / kChunk;
+  const int wg0 = static_cast<int>(static_cast<int64_t>(xw) * nch / a.nwgr) * kChunk;
+  const int wg1 = min(h.n, static_cast<int>(static_cast<int64_t>(xw + 1) * nch / a.nwgr) * kChunk);
+  if (wg0 >= wg1) return;                                   // the whole workgroup leaves
   // K4V4 and vertical-line positions precede t - W, so every row (position
   // t - nb + 1 or later) sees them when nb <= W + 1
   const int n_unmasked = (a.nb <= a.W + 1) ? h.nq + h.nvl : 0;
   float* sc_u = a.score + u * a.L;
-  const int own = 16 * (n >> 2) + 4 * j + (n & 3);
+  // the entry this lane owns after the reduction: v = lane % 32 of its half
+  const int own = 32 * ((lane >> 4) & 1) + 8 * ((lane & 15) >> 2) + 4 * hh + (lane & 3);
   for (int rg = 0; rg < a.nrg; ++rg) {
     if (rg > 0) {
       // this workgroup's score updates of the last row group are visible to
@@ -785,15 +940,15 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       __syncthreads();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    KRaw<kKB> raw;
+    KRaw32<kKB> raw;
     {
       const int k0 = wg0 + kChunk * wave;
-      if (k0 + kChunk <= h.nq) load_k4raw(raw, a, u, k0, n, j);
+      if (k0 < wg1 && k0 + kChunk <= h.nq) load_k4raw32(raw, a, u, k0, kl, hh);
     }
     uint4 qv[kStageIters];
-    stage_load(qv, a, b, h0, rg);                          // in flight with the LSE loads
-    for (int rr = tid; rr < kRG; rr += kSThreads) {
-      const int r = rg * kRG + rr;
+    stage32_load<kNRT>(qv, a, b, h0, rg, 0);               // in flight with the LSE loads
+    for (int rr = tid; rr < kRows; rr += kSThreads) {
+      const int r = rg * kRows + rr;
       float nl = -INFINITY;
       int pr = -1;
       if (r < a.R) {
@@ -804,46 +959,60 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
       s_nl[rr] = nl;
       s_prow[rr] = pr;
     }
-    stage_store(s_q, qv);
+    stage32_store<kNRT>(s_q, qv, 0);
+#pragma unroll
+    for (int part = 1; part < kRows / kRG; ++part) {
+      stage32_load<kNRT>(qv, a, b, h0, rg, part);
+      stage32_store<kNRT>(s_q, qv, part);
+    }
     __syncthreads();
-    for (int i = 0; i < a.C; ++i) {
-      const int k0 = wg0 + kChunk * (wave + kSWaves * i);
-      if (k0 >= h.n) break;
-      uint4 kr[4][4];
-      int kpos[4];
+    for (int k0 = wg0 + kChunk * wave; k0 < wg1; k0 += kChunk * kSWaves) {
+      uint4 kr[2][8];
+      int kpos[2];
       if (k0 + kChunk <= h.nq) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          dequant_group<kKB>(kr[x], raw.codes[x], raw.meta[x]);
-          kpos[x] = raw.pos[x];
+        for (int kt = 0; kt < 2; ++kt) {
+          dequant_tile<kKB>(kr[kt], raw.codes[kt], raw.meta[kt]);
+          kpos[kt] = raw.pos[kt];
         }
       } else {
-        load_any<kKB>(kr, kpos, a, h, u, k0, n, j);
+        load_any32<kKB>(kr, kpos, a, h, u, k0, kl, hh);
       }
-      // positions through LDS: lane (n, j) needs those of entries 16x + 4j + e
-#pragma unroll
-      for (int x = 0; x < 4; ++x) s_kpos[wave][16 * x + n] = kpos[x];
+      // positions through LDS (both halves of a key tile hold the same entries)
+      if (hh == 0) {
+        s_kpos[wave][kl] = kpos[0];
+        s_kpos[wave][32 + kl] = kpos[1];
+      }
       const int op = s_kpos[wave][own];
       const bool owned = op >= 0 && op < a.L;
       // the running score of the owned position, loaded before the prefetch
       const float prev = owned ? sc_u[op] : 0.0f;
       const int k1 = k0 + kChunk * kSWaves;
-      if (k1 + kChunk <= h.nq && i + 1 < a.C) load_k4raw(raw, a, u, k1, n, j);
+      if (k1 < wg1 && k1 + kChunk <= h.nq) load_k4raw32(raw, a, u, k1, kl, hh);
       __builtin_amdgcn_sched_barrier(0);                    // keep the prefetch ahead
-      float acc[16];
+      float acc[2][16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[kt][r] = 0.0f;
+      // the group's rows 256 at a time (one unrolled pass of 8 row tiles)
       if (k0 + kChunk <= n_unmasked) {
-        chunk_refresh<false>(acc, kr, s_q, s_nl, s_prow, nullptr, a.c2, lane, n);
+#pragma unroll 1
+        for (int hf = 0; hf < kNRT / 8; ++hf)
+          chunk_refresh32(acc, kr, &s_q[8 * hf], s_nl + kRG * hf, a.c2, lane);
+      } else if (h.n - k0 <= 32) {
+        // the list's tail: only the first key tile holds entries
+#pragma unroll 1
+        for (int hf = 0; hf < kNRT / 8; ++hf)
+          chunk_refresh32_masked<1>(acc, kr, &s_q[8 * hf], s_nl + kRG * hf, s_prow + kRG * hf, s_kpos[wave],
+                                    a.c2, lane);
       } else {
-        int kp[16];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) kp[4 * x + e] = s_kpos[wave][16 * x + 4 * j + e];
-        chunk_refresh<true>(acc, kr, s_q, s_nl, s_prow, kp, a.c2, lane, n);
+#pragma unroll 1
+        for (int hf = 0; hf < kNRT / 8; ++hf)
+          chunk_refresh32_masked<2>(acc, kr, &s_q[8 * hf], s_nl + kRG * hf, s_prow + kRG * hf, s_kpos[wave],
+                                    a.c2, lane);
       }
-      const float tot = reduce_scatter16(acc, n);
+      const float tot = reduce_scatter32(acc, lane);
       if (owned && k0 + own < h.n) sc_u[op] = prev + tot;
     }
   }
@@ -1429,18 +1598,31 @@ hipError_t launch_refresh(const hq_dims& d, const hq_cache& c, int32_t t, const 
   a.cap_stg = d.cap_stg;
   const size_t units = static_cast<size_t>(d.B) * d.Hkv;
   a.U = static_cast<int32_t>(units);
-  a.nrg = (a.R + kRG - 1) / kRG;
-  // a cache holding positions 0..t has t + 1 keys per unit
+  // 512 query rows a group when there are more than 256 (each chunk's codes
+  // loaded and dequantised once per 512 rows)
+  int rows = a.R > kRG ? 2 * kRG : kRG;
+  a.nrg = (a.R + rows - 1) / rows;
+  // a cache holding positions 0..t has t + 1 keys per unit: its chunks are
+  // split evenly over nwgr workgroups, as many as fill one workgroup per CU
+  // (the kernel's registers allow one), and at least eight chunks each
   const int64_t nk = static_cast<int64_t>(t) + 1;
-  const int64_t chunks = static_cast<int64_t>(units) * ((nk + kChunk - 1) / kChunk) * a.nrg;
-  a.C = static_cast<int32_t>(std::min<int64_t>(16, std::max<int64_t>(2, (chunks + 8191) / 8192)));
-  a.wg_keys = kChunk * kSWaves * a.C;
-  const unsigned nwg = static_cast<unsigned>((nk + a.wg_keys - 1) / a.wg_keys);
-  const unsigned U = static_cast<unsigned>(units);
+  const int64_t nch = (nk + kChunk - 1) / kChunk;
+  int64_t nwgr = std::max<int64_t>(1, std::min<int64_t>(kSelCUs / static_cast<int64_t>(units), nch / kSWaves));
+  a.nwgr = static_cast<int32_t>(nwgr);
+  const int64_t nwg_all = nwgr * static_cast<int64_t>(units);
+  a.xcd_group = nwg_all % 8 == 0 ? 1 : 0;
+  const unsigned nwg = static_cast<unsigned>(nwg_all);
   const int kb = kv_bits(d.k_bits);
-  if (kb == 2) hipLaunchKernelGGL(refresh_mass_kernel<2>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
-  else if (kb == 8) hipLaunchKernelGGL(refresh_mass_kernel<8>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
-  else hipLaunchKernelGGL(refresh_mass_kernel<4>, dim3(nwg, U), dim3(kSThreads), 0, s, a);
+  if (rows == kRG) {
+    if (kb == 2) hipLaunchKernelGGL((refresh_mass_kernel<2, kRB / 2>), dim3(nwg), dim3(kSThreads), 0, s, a);
+    else if (kb == 8) hipLaunchKernelGGL((refresh_mass_kernel<8, kRB / 2>), dim3(nwg), dim3(kSThreads), 0, s, a);
+    else hipLaunchKernelGGL((refresh_mass_kernel<4, kRB / 2>), dim3(nwg), dim3(kSThreads), 0, s, a);
+  } else {
+    if (kb == 2) hipLaunchKernelGGL((refresh_mass_kernel<2, kRB>), dim3(nwg), dim3(kSThreads), 0, s, a);
+    else if (kb == 8) hipLaunchKernelGGL((refresh_mass_kernel<8, kRB>), dim3(nwg), dim3(kSThreads), 0, s, a);
+    else hipLaunchKernelGGL((refresh_mass_kernel<4, kRB>), dim3(nwg), dim3(kSThreads), 0, s, a);
+  }
+  const unsigned U = static_cast<unsigned>(units);
   a.nrg = 1;                       // the scores are complete: nothing to fold
   if (cut) hipLaunchKernelGGL(topk_kernel<true>, dim3(U), dim3(kTopThreads), 0, s, a);
   else hipLaunchKernelGGL(topk_kernel<false>, dim3(U), dim3(kTopThreads), 0, s, a);
