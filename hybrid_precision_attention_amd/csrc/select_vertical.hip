@@ -851,15 +851,20 @@ __device__ __forceinline__ void chunk_refresh32(float acc[2][16], const uint4 kr
 
 // The masked form, for the few chunks holding entries that some rows must
 // not see (positions past a row's own, and entries past the list, kNoPos):
-// one row tile at a time, each entry's position read from the wave's LDS
-// list s_kpos.  Only the first kNT key tiles are computed (kNT = 1: the
-// list's tail, at most 32 entries).
+// one row tile at a time, with the lane's 32 entry positions read from the
+// wave's LDS list once.  Only the first kNT key tiles are computed (kNT = 1:
+// the list's tail, at most 32 entries).
 template <int kNT>
 __device__ __forceinline__ void chunk_refresh32_masked(float acc[2][16], const uint4 kr[2][8], const QTile32* sq,
                                                        const float* s_nl, const int* s_prow, const int* kpos,
                                                        float c2, int lane) {
   constexpr int kNRT = kRG / 32;
   const int rl = lane & 31, hh = lane >> 5;
+  int kp[2][16];
+#pragma unroll
+  for (int kt = 0; kt < kNT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) kp[kt][r] = kpos[32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3)];
 #pragma unroll 1
   for (int rt = 0; rt < kNRT; ++rt) {
     f32x16_t sc[2];
@@ -873,7 +878,7 @@ __device__ __forceinline__ void chunk_refresh32_masked(float acc[2][16], const u
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], c2, nl));
-        acc[kt][r] += (kpos[32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3)] <= pr) ? p : 0.0f;
+        acc[kt][r] += (kp[kt][r] <= pr) ? p : 0.0f;
       }
   }
 }
@@ -926,9 +931,10 @@ __global__ __launch_bounds__(kSThreads) void refresh_mass_kernel(SelArgs a) {
   const int wg0 = static_cast<int>(static_cast<int64_t>(xw) * nch / a.nwgr) * kChunk;
   const int wg1 = min(h.n, static_cast<int>(static_cast<int64_t>(xw + 1) * nch / a.nwgr) * kChunk);
   if (wg0 >= wg1) return;                                   // the whole workgroup leaves
-  // K4V4 and vertical-line positions precede t - W, so every row (position
-  // t - nb + 1 or later) sees them when nb <= W + 1
-  const int n_unmasked = (a.nb <= a.W + 1) ? h.nq + h.nvl : 0;
+  // Entries every row sees (position at most t - nb + 1, the first row's):
+  // when nb <= W + 1, the K4V4 slots and vertical lines (positions before
+  // t - W) and the window's first nwin - nb + 2 positions (t - nwin + e).
+  const int n_unmasked = (a.nb <= a.W + 1) ? h.nq + h.nvl + max(0, min(h.nwin, h.nwin - a.nb + 2)) : 0;
   float* sc_u = a.score + u * a.L;
   // the entry this lane owns after the reduction: v = lane % 32 of its half
   const int own = 32 * ((lane >> 4) & 1) + 8 * ((lane & 15) >> 2) + 4 * hh + (lane & 3);
