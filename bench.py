@@ -392,7 +392,7 @@ def main():
     if not (args.no_sweep and args.no_prefill and args.no_capacity):
         del caches, ws, K_rep, base, spare
         torch.cuda.empty_cache()
-    sweep, ceiling, widths, contexts, gqa16, streaming = None, None, None, None, None, None
+    sweep, ceiling, widths, contexts, gqa16, streaming, mfma = None, None, None, None, None, None, None
     if not args.no_sweep:
         sweep = decode_sweep(H, torch, workload)
         widths = width_sweep(H, torch, workload)
@@ -401,6 +401,7 @@ def main():
         streaming = streaming_run(H, torch, workload)
         ceiling = read_ceiling(torch, 4 << 30)
         ceiling["at_decode_footprint"] = read_ceiling_footprint(torch, dec_bytes)
+        mfma = mfma_rate(torch)
     prefill = None if args.no_prefill else prefill_timing(H, torch)
     capacity = None if args.no_capacity else capacity_run(H, torch)
     capacity_ragged = None if args.no_capacity else capacity_ragged_run(H, torch)
@@ -443,6 +444,7 @@ def main():
         "gqa16_grid": gqa16,
         "streaming_qwen3_32b": streaming,
         "read_ceiling": ceiling,
+        "mfma_rate": mfma,
         "prefill": prefill,
         "capacity": capacity,
         "capacity_ragged_paged": capacity_ragged,
@@ -1036,6 +1038,38 @@ def _probe_lib():
         f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int,
                       ctypes.c_void_p]
     return {"ordinary": lib.hq_probe_stream_read, "nt": lib.hq_probe_stream_read_nt}
+
+
+def mfma_rate(torch, iters=2048):
+    """The matrix-core rate probe (libhq_probe.so): fp16 MFMA chains of the
+    16x16x32 and 32x32x16 shapes, alone and with the column-mass exponential
+    work interleaved, at two and four waves per SIMD; TFLOP/s of each."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "hybrid_precision_attention_amd", "libhq_probe.so"))
+    lib.hq_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    names = {0: "16x16x32", 1: "32x32x16", 2: "16x16x32+exp_mix", 3: "32x32x16+exp_mix"}
+    res = {}
+    for which, name in names.items():
+        flop_per = (8 * 16384) if which in (0, 2) else (4 * 32768)
+        best = 0.0
+        for wps in (2, 4):                        # waves per SIMD: 256 CUs x wps workgroups of 4 waves
+            grid = 256 * wps
+            for _ in range(2):
+                if lib.hq_probe_mfma_rate(which, grid, iters, sink.data_ptr(), s):
+                    raise RuntimeError("mfma probe launch failed")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.hq_probe_mfma_rate(which, grid, iters, sink.data_ptr(), s)
+            e1.record()
+            torch.cuda.synchronize()
+            tflops = grid * 4 * iters * flop_per / (e0.elapsed_time(e1) * 1e-3) / 1e12
+            best = max(best, tflops)
+        res[name] = round(best, 1)
+    res["kernel"] = "mfma_rate_kernel (libhq_probe.so): independent fp16 MFMA chains, best of 2 and 4 waves per SIMD"
+    return res
 
 
 def read_ceiling(torch, nbytes=1 << 30):

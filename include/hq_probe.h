@@ -2,7 +2,8 @@
  * hq_probe.h -- measurement helper beside libhq.so (not part of the method).
  *
  * libhq_probe.so holds a plain streaming-read kernel, the achievable-HBM
- * reference that the benchmark reports next to the nominal 8 TB/s peak.
+ * reference that the benchmark reports next to the nominal 8 TB/s peak, and
+ * a matrix-core rate probe.
  */
 #ifndef HQ_PROBE_H
 #define HQ_PROBE_H
@@ -30,6 +31,18 @@ int hq_probe_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t
  * cache loads). */
 int hq_probe_stream_read_nt(const void* src, size_t bytes, uint32_t* sink, uint32_t never,
                             int grid, hipStream_t stream);
+
+/*
+ * Matrix-core rate: `grid` workgroups of 256 threads each run `iters` rounds
+ * of independent fp16 MFMA chains: which = 0: v_mfma_f32_16x16x32_f16, eight
+ * chains a wave; 1: v_mfma_f32_32x32x16_f16, four chains; 2 and 3: the same
+ * with the column-mass work of each MFMA's outputs (fma, exp2, add per output
+ * element and lane) interleaved.  FLOP per launch: grid * 4 waves * iters *
+ * chains * (16384 or 32768).  *sink (device, 256 floats) is written only for
+ * an impossible checksum.  Returns 0, -1 for bad arguments, -6 when the
+ * launch fails.
+ */
+int hq_probe_mfma_rate(int which, int grid, int iters, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

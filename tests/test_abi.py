@@ -29,6 +29,18 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(H.lib, n), n
 
 
+def test_probe_library_exports_its_header():
+    """libhq_probe.so (the benchmark's measurement helpers) exports every
+    function include/hq_probe.h declares."""
+    with open(os.path.join(ROOT, "include", "hq_probe.h")) as f:
+        src = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(hq_probe_[a-z0-9_]+)\s*\(", src)))
+    assert {"hq_probe_stream_read", "hq_probe_stream_read_nt", "hq_probe_mfma_rate"} <= set(names)
+    probe = ctypes.CDLL(os.path.join(ROOT, "hybrid_precision_attention_amd", "libhq_probe.so"))
+    for n in names:
+        assert hasattr(probe, n), n
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert H.hq_status_string(s) != "unknown status"
