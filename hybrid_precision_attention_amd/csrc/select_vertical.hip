@@ -334,14 +334,18 @@ __global__ __launch_bounds__(kSThreads) void row_stats_kernel(SelArgs a) {
   for (int i = 0; i < a.C; ++i) {
     const int k0 = wg0 + kChunk * (wave + kSWaves * i);
     if (k0 >= a.L) break;
+    // the next chunk's keys, only when this wave has one (a prefetch past
+    // the workgroup's range would read keys no wave of it uses)
+    const bool more = i + 1 < a.C && k0 + kChunk * kSWaves < a.L;
     uint4 kn[4][4];
-    load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
+    if (more) load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
     __builtin_amdgcn_sched_barrier(0);                      // keep the prefetch ahead
     // every key of the chunk precedes every buffered query: no causal mask
     if (k0 + kChunk <= a.L - a.nb)
       chunk_row_stats<false>(s_run[wave], kr, s_q, a, rg, k0, lane, n, j);
     else
       chunk_row_stats<true>(s_run[wave], kr, s_q, a, rg, k0, lane, n, j);
+    if (!more) break;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -559,8 +563,9 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
     // waiting for it does not wait for the next chunk's keys
     const int key = k0 + own;
     const float prev = (a.nrg == 1) ? sc[min(key, lim - 1)] : 0.0f;
+    const bool more = i + 1 < a.C && k0 + kChunk * kSWaves < lim;
     uint4 kn[4][4];
-    load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
+    if (more) load_keys(kn, kunit, k0 + kChunk * kSWaves, a.L, n, j);
     __builtin_amdgcn_sched_barrier(0);                      // keep the prefetch ahead
     float acc[16];
 #pragma unroll
@@ -575,6 +580,7 @@ __global__ __launch_bounds__(kSThreads) void col_mass_kernel(SelArgs a) {
       if (a.nrg == 1) sc[key] = prev + tot;
       else part[key] = tot;
     }
+    if (!more) break;
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
