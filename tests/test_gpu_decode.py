@@ -239,3 +239,48 @@ def test_streaming_full_size_qwen3_32b_sampled():
     for b, g in units:
         assert_unit_equal(unit_from_gpu(cache, b, g), refs[(b, g)], t, W, tag=f"b{b} g{g}")
 
+
+
+def test_step_large_batch_64bit_offsets():
+    """Byte offsets past 2^31 in the K4V4 arrays: the Qwen3-8B-shaped layer
+    at B=160, L=32768 (1280 units, so kq and vq each hold 2.67 GB), built by
+    hq_quant_pack, stepped once by hq_decode_step and then given one plain
+    merge.  Four seeded sequences are tiled on the device; the oracle packs
+    and merges sampled units on its own, the last unit at the highest
+    offsets.  The step's outputs lie within the decode tolerance and the
+    sampled units' caches are bit-exact at the end."""
+    wl = workload("qwen3_8b", B=160)
+    L, W, G = wl.L, wl.W, wl.G
+    print("case qwen3_8b B=160, 64-bit offsets", flush=True)
+    xs = batch(wl, steps=2, seqs=[0, 1, 2, 3])
+    _, _, f4 = O.select_vertical(xs["K"], xs["qbuf"], L, W, wl.rho)
+    rep = wl.B // 4
+    cache = H.HybridCache.allocate(wl.B, wl.Hq, wl.Hkv, W, wl.rho, L + 2)
+    kq = cache.t["kq"]
+    assert kq.numel() * kq.element_size() > 2 ** 31
+    K = dev(xs["K"]).repeat(rep, 1, 1, 1)
+    V = dev(xs["V"]).repeat(rep, 1, 1, 1)
+    F = dev(f4).repeat(rep, 1, 1)
+    H.hq_quant_pack(cache.dims, K, V, L, F, cache)
+    del K, V, F
+    tile = lambda a: np.ascontiguousarray(np.concatenate([a] * rep))
+    q = tile(xs["q_dec"][0])
+    ws = H.workspace(cache.dims, H.HQ_OP_DECODE, L + 1)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device="cuda")
+    lse = torch.empty((wl.B, wl.Hq), dtype=torch.float32, device="cuda")
+    H.hq_decode_step(cache.dims, cache, L, dev(tile(xs["k_dec"][0])), dev(tile(xs["v_dec"][0])), dev(q),
+                     out, ws, lse=lse)
+    H.hq_append_merge(cache.dims, cache, L + 1, dev(tile(xs["k_dec"][1])), dev(tile(xs["v_dec"][1])))
+    torch.cuda.synchronize()
+    units = [(0, 0), (81, 5), (130, 2), (159, 7)]
+    refs = {(b, g): O.quant_pack_unit(xs["K"][b % 4, g], xs["V"][b % 4, g], L, W, f4[b % 4, g])
+            for b, g in units}
+    for b, g in units:
+        O.append_merge_unit(refs[(b, g)], L, xs["k_dec"][0, b % 4, g], xs["v_dec"][0, b % 4, g])
+    ro, rl = zip(*(O.decode_fused(refs[(b, g)], q[b, g * G:(g + 1) * G], L) for b, g in units))
+    o, lg = out.cpu().numpy(), lse.cpu().numpy()
+    pick = lambda a: np.stack([a[b, g * G:(g + 1) * G] for b, g in units])
+    check_decode(pick(o), pick(lg), np.stack(ro), np.stack(rl), tag="B=160 sampled units")
+    for b, g in units:
+        O.append_merge_unit(refs[(b, g)], L + 1, xs["k_dec"][1, b % 4, g], xs["v_dec"][1, b % 4, g])
+        assert_unit_equal(unit_from_gpu(cache, b, g), refs[(b, g)], L + 1, W, tag=f"b{b} g{g}")
