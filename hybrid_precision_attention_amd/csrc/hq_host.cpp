@@ -19,10 +19,11 @@ namespace {
 
 constexpr int kMaxGroup = 16;      // query heads per KV head handled by one MFMA tile
 constexpr int kCUs = 256;          // MI355X compute units
-constexpr int kDecodeWaves = 4;    // waves per decode workgroup (two workgroups per CU)
+constexpr int kDecodeWaves = 4;    // waves per decode workgroup
 constexpr int kBlk = 32;           // tokens per decode block
 constexpr int kMaxWG = 8 * kCUs;   // decode workgroups per launch, at most (short prefixes)
-constexpr int kMaxPerCU = 2;       // decode workgroups per CU the byte plan aims at, at most
+constexpr int kMaxPerCU = 1;       // decode workgroups per CU the byte plan aims at, at most (G <= 4, 4/8-bit)
+constexpr int kMaxPerCUGen = 2;    // the same for the G > 4 scan and the 2-bit widths
 constexpr int kMaxSplit = 128;     // decode workgroups per unit, at most (LDS of the final merge)
 constexpr int kPartFloats = kPartFloatsPerRecord;
 constexpr double kWgBytes = 384.0 * 1024;  // bytes one decode workgroup streams at small batch
@@ -76,11 +77,14 @@ int32_t n_vertical(double rho, int32_t n_nw) {
 
 // Splits per unit for the decode: workgroups carry about equal bytes (160 per
 // K4V4 token, 16 (k_bits + v_bits) + 32 at other widths, 512 per FP16 token).
-// Small problems get one workgroup per CU; large ones two, so that the
-// launch is one round of long workgroups (two resident per CU at the scan's
-// register count): each workgroup's start-up loads and its merge then come
-// once per CU slot, not once per 384 KB (B = 32 at L = 32K: 268 us against
-// 283 us with up to eight workgroups per CU).
+// The launch is one round of long workgroups: each workgroup's start-up
+// loads and its merge then come once per CU slot, not once per 384 KB (B = 32
+// at L = 32K: 268 us against 283 us with up to eight workgroups per CU).  The
+// G <= 4 scan at 4- and 8-bit widths keeps one workgroup per CU at every
+// batch (side by side on one box: B = 16 133-134 against 137-138 us with two,
+// K8V8 at B = 32 438 against 450 us, K4V4 at B = 32 the same); the G > 4 scan
+// and the 2-bit widths go up to two (Qwen3-32B-shaped B = 32: 268 against
+// 275 us with one).
 static int64_t max_splits(int64_t units) {
   return std::min<int64_t>(kMaxSplit, cdiv(kMaxWG, units) + 3);
 }
@@ -99,7 +103,9 @@ DecodePlan plan_decode(const hq_dims& d, int32_t L) {
   const double q_tok = 16.0 * (kv_bits(d.k_bits) + kv_bits(d.v_bits)) + 32.0;
   const double per_unit = q_tok * static_cast<double>(n_q) + 512.0 * static_cast<double>(n_f);
   const double total = static_cast<double>(units) * per_unit;
-  const double per_cu = std::min<double>(kMaxPerCU, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
+  const bool one_per_cu = d.Hq / d.Hkv <= 4 && kv_bits(d.k_bits) != 2 && kv_bits(d.v_bits) != 2;
+  const int cap_cu = one_per_cu ? kMaxPerCU : kMaxPerCUGen;
+  const double per_cu = std::min<double>(cap_cu, std::max(1.0, std::floor(total / (kCUs * kWgBytes))));
   const double wg_bytes = std::max(total / (kCUs * per_cu), 1.0);
   const int64_t items = cdiv(n_q, kBlk) + cdiv(n_f, kBlk);
   int64_t ns = std::max<int64_t>(1, std::llround(per_unit / wg_bytes));
