@@ -1372,95 +1372,151 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   StepIn step_in{};
   if (merger) step_in = step_load(a, u, t_step, lane);
 
-  // The last workgroup merges the unit's nsplit * G records: thread (sub,
-  // head g, dims 4c..4c+3) folds the records of its output with split index
-  // sub, sub + S, ..., 16 at a time with all their loads in flight (device-
-  // scope buffer loads: 8 bytes of (max, sum) and 16 of the output per
-  // record).  The S partials of an output are then combined in LDS.  (Staging
-  // whole records through LDS first, with fewer and wider loads, measured
-  // slower: 17.5 against 16.8 us for the B = 1 launch.)
-  const int nrec = nsplit * G;
-  const int items = G * (kD / 4);
-  const int S = max(1, kThreads / items);
-  const int sub = tid / items;
-  const int n_items = (items + kThreads - 1) / kThreads;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      recs, static_cast<short>(0), nrec * kPart * 4, kRsrcWord3);
-  FinPart part[kFoldItems];
-#pragma unroll
-  for (int q = 0; q < kFoldItems; ++q) {
-    part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-    if (q >= n_items) break;
-    const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-    if (item >= items || sub >= S) continue;
+  // the normalised output of (head g, dims 4c..4c+3) from its folded state
+  auto finish = [&](int item, float mx, float lt, float4_t acc) {
     const int g = item >> 5, c = item & 31;
-    for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
-      float2 ml[16];
-      float4_t o4[16];
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    uint16_t* dst = a.out + (b * a.Hq + h0 + g) * kD + 4 * c;
+    uint2 pk;
+    pk.x = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[0] * inv)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[1] * inv)) << 16);
+    pk.y = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[2] * inv)) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[3] * inv)) << 16);
+    if (refused) pk = make_uint2(0x7E007E00u, 0x7E007E00u);          // fp16 quiet NaNs
+    *reinterpret_cast<uint2*>(dst) = pk;
+    if (c == 0 && a.lse)
+      a.lse[b * a.Hq + h0 + g] = refused ? __uint_as_float(0x7FC00000u)   // a quiet NaN
+                                 : lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  };
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      recs, static_cast<short>(0), nsplit * G * kPart * 4, kRsrcWord3);
+
+  // Both fold forms below run the same arithmetic on the same records in
+  // the same order (fold16 for each partial, then combine over the S
+  // partials), so a fused step's output equals the plain decode's bit for
+  // bit.
+  // fold16: partial pt takes 16 records (split indices s0, s0 + S, ...; past
+  // nsplit masked) into its running state
+  auto fold16 = [&](FinPart& pt, int s0, int S, const float2 (&ml)[16], const float4_t (&o4)[16]) {
+    float m16[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int sp = min(s0 + k * S, nsplit - 1);
-        const int at = (sp * G + g) * kPart * 4;
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, at, 0, kSc1);
-        ml[k] = make_float2(__uint_as_float(v2[0]), __uint_as_float(v2[1]));
-        o4[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at + 16 + 16 * c, 0, kSc1));
-      }
-      float m16[16];
+    for (int k = 0; k < 16; ++k) m16[k] = s0 + k * S < nsplit ? ml[k].x : -INFINITY;
+    float mx = pt.m;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) m16[k] = s0 + k * S < nsplit ? ml[k].x : -INFINITY;
-      float mx = part[q].m;
+    for (int k = 0; k < 16; ++k) mx = fmaxf(mx, m16[k]);
+    const float mu = mx == -INFINITY ? 0.0f : mx;
+    const float fa = __builtin_amdgcn_exp2f((pt.m - mu) * c2);
+    pt.l *= fa;
+    pt.o *= fa;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) mx = fmaxf(mx, m16[k]);
-      const float mu = mx == -INFINITY ? 0.0f : mx;
-      const float fa = __builtin_amdgcn_exp2f((part[q].m - mu) * c2);
-      part[q].l *= fa;
-      part[q].o *= fa;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float f = __builtin_amdgcn_exp2f((m16[k] - mu) * c2);
-        part[q].l = fmaf(f, ml[k].y, part[q].l);
-        part[q].o += f * o4[k];
-      }
-      part[q].m = mx;
+    for (int k = 0; k < 16; ++k) {
+      const float f = __builtin_amdgcn_exp2f((m16[k] - mu) * c2);
+      pt.l = fmaf(f, ml[k].y, pt.l);
+      pt.o += f * o4[k];
     }
-  }
+    pt.m = mx;
+  };
+  auto load16 = [&](int s0, int S, int g, int c, float2 (&ml)[16], float4_t (&o4)[16]) {
 #pragma unroll
-  for (int q = 0; q < kFoldItems; ++q) {
-    if (q >= n_items) break;                       // uniform: every thread has the same n_items
-    const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-    const bool active = item < items && sub < S;
-    __syncthreads();                               // the fold area / previous round's partials are free
-    s_lds.fin[tid] = part[q];
-    __syncthreads();
-    if (active && sub == 0) {
-      float mx = -INFINITY;
-      for (int w = 0; w < S; ++w) mx = fmaxf(mx, s_lds.fin[tid + w * items].m);
-      float lt = 0.0f;
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if (mx != -INFINITY) {
-        for (int w = 0; w < S; ++w) {
-          const FinPart& pw = s_lds.fin[tid + w * items];
-          const float f = __builtin_amdgcn_exp2f((pw.m - mx) * c2);
-          lt = fmaf(f, pw.l, lt);
-          acc += f * pw.o;
+    for (int k = 0; k < 16; ++k) {
+      const int sp = min(s0 + k * S, nsplit - 1);
+      const int at = (sp * G + g) * kPart * 4;
+      const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rs, at, 0, kSc1);
+      ml[k] = make_float2(__uint_as_float(v2[0]), __uint_as_float(v2[1]));
+      o4[k] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at + 16 + 16 * c, 0, kSc1));
+    }
+  };
+  // combine: partial w of the output (w < S), in order
+  auto combine_step = [&](float& mx, float& lt, float4_t& acc, float m, float l, float4_t o) {
+    const float f = __builtin_amdgcn_exp2f((m - mx) * c2);
+    lt = fmaf(f, l, lt);
+    acc += f * o;
+  };
+
+  // A fused step on the G <= 4 scan with two partials per output (G = 3, 4)
+  // and at most 32 splits: the threads of the outputs (waves 0 and 1) each
+  // load both partials' records in one round and fold and combine them in
+  // registers, while the last wave, which has no output, runs the step's
+  // merge beside them (after the fold it would add its quantisation and
+  // stores to the step's tail).
+  bool folded = false;
+  if constexpr (kG4) {
+    const int items = G * (kD / 4);
+    if (a.k_new && kThreads / items == 2 && nsplit <= 32) {
+      folded = true;
+      if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
+      if (tid < items) {
+        const int g = tid >> 5, c = tid & 31;
+        float2 ml0[16], ml1[16];
+        float4_t o40[16], o41[16];
+        load16(0, 2, g, c, ml0, o40);
+        load16(1, 2, g, c, ml1, o41);
+        FinPart p0{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+        FinPart p1 = p0;
+        fold16(p0, 0, 2, ml0, o40);
+        fold16(p1, 1, 2, ml1, o41);
+        float mx = fmaxf(fmaxf(-INFINITY, p0.m), p1.m);
+        float lt = 0.0f;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (mx != -INFINITY) {
+          combine_step(mx, lt, acc, p0.m, p0.l, p0.o);
+          combine_step(mx, lt, acc, p1.m, p1.l, p1.o);
         }
+        finish(tid, mx, lt, acc);
       }
-      const int g = item >> 5, c = item & 31;
-      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-      uint16_t* dst = a.out + (b * a.Hq + h0 + g) * kD + 4 * c;
-      uint2 pk;
-      pk.x = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[0] * inv)) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[1] * inv)) << 16);
-      pk.y = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[2] * inv)) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<_Float16>(acc[3] * inv)) << 16);
-      if (refused) pk = make_uint2(0x7E007E00u, 0x7E007E00u);          // fp16 quiet NaNs
-      *reinterpret_cast<uint2*>(dst) = pk;
-      if (c == 0 && a.lse)
-        a.lse[b * a.Hq + h0 + g] = refused ? __builtin_nanf("")
-                                   : lt > 0.0f ? (mx * c2 + log2f(lt)) * 0.69314718055994531f : -INFINITY;
     }
   }
-  if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
+  if (!folded) {
+    // Otherwise the last workgroup merges the unit's nsplit * G records: thread (sub,
+    // head g, dims 4c..4c+3) folds the records of its output with split index
+    // sub, sub + S, ..., 16 at a time with all their loads in flight (device-
+    // scope buffer loads: 8 bytes of (max, sum) and 16 of the output per
+    // record).  The S partials of an output are then combined in LDS.  (Staging
+    // whole records through LDS first, with fewer and wider loads, measured
+    // slower: 17.5 against 16.8 us for the B = 1 launch.)
+    const int items = G * (kD / 4);
+    const int S = max(1, kThreads / items);
+    const int sub = tid / items;
+    const int n_items = (items + kThreads - 1) / kThreads;
+    FinPart part[kFoldItems];
+#pragma unroll
+    for (int q = 0; q < kFoldItems; ++q) {
+      part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+      if (q >= n_items) break;
+      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+      if (item >= items || sub >= S) continue;
+      const int g = item >> 5, c = item & 31;
+      for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
+        float2 ml[16];
+        float4_t o4[16];
+        load16(s0, S, g, c, ml, o4);
+        fold16(part[q], s0, S, ml, o4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kFoldItems; ++q) {
+      if (q >= n_items) break;                       // uniform: every thread has the same n_items
+      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+      const bool active = item < items && sub < S;
+      __syncthreads();                               // the fold area / previous round's partials are free
+      s_lds.fin[tid] = part[q];
+      __syncthreads();
+      if (active && sub == 0) {
+        float mx = -INFINITY;
+        for (int w = 0; w < S; ++w) mx = fmaxf(mx, s_lds.fin[tid + w * items].m);
+        float lt = 0.0f;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (mx != -INFINITY) {
+          for (int w = 0; w < S; ++w) {
+            const FinPart& pw = s_lds.fin[tid + w * items];
+            combine_step(mx, lt, acc, pw.m, pw.l, pw.o);
+          }
+        }
+        finish(item, mx, lt, acc);
+      }
+    }
+    if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
+  }
   if (tid == 0) a.counters[u * kCounterStride] = 0;
 }
 
