@@ -1480,17 +1480,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int n_items = (items + kThreads - 1) / kThreads;
     FinPart part[kFoldItems];
 #pragma unroll
-    for (int q = 0; q < kFoldItems; ++q) {
-      part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-      if (q >= n_items) break;
-      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-      if (item >= items || sub >= S) continue;
-      const int g = item >> 5, c = item & 31;
-      for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
-        float2 ml[16];
-        float4_t o4[16];
-        load16(s0, S, g, c, ml, o4);
-        fold16(part[q], s0, S, ml, o4);
+    for (int q = 0; q < kFoldItems; ++q) part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+    if (n_items == 2 && nsplit <= 16) {
+      // G > 8 with one batch per output: both outputs' loads in one round
+      // (the same folds as the loop below, in the same order)
+      const int i1 = min(kThreads + tid, items - 1);
+      float2 ml0[16], ml1[16];
+      float4_t o40[16], o41[16];
+      load16(0, 1, tid >> 5, tid & 31, ml0, o40);
+      load16(0, 1, i1 >> 5, i1 & 31, ml1, o41);
+      fold16(part[0], 0, 1, ml0, o40);
+      fold16(part[1], 0, 1, ml1, o41);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kFoldItems; ++q) {
+        if (q >= n_items) break;
+        const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+        if (item >= items || sub >= S) continue;
+        const int g = item >> 5, c = item & 31;
+        for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
+          float2 ml[16];
+          float4_t o4[16];
+          load16(s0, S, g, c, ml, o4);
+          fold16(part[q], s0, S, ml, o4);
+        }
       }
     }
 #pragma unroll
