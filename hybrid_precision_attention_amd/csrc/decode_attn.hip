@@ -1481,51 +1481,80 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     FinPart part[kFoldItems];
 #pragma unroll
     for (int q = 0; q < kFoldItems; ++q) part[q] = FinPart{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
-    if (n_items == 2 && nsplit <= 16) {
-      // G > 8 with one batch per output: both outputs' loads in one round
-      // (the same folds as the loop below, in the same order)
-      const int i1 = min(kThreads + tid, items - 1);
-      float2 ml0[16], ml1[16];
-      float4_t o40[16], o41[16];
-      load16(0, 1, tid >> 5, tid & 31, ml0, o40);
-      load16(0, 1, i1 >> 5, i1 & 31, ml1, o41);
-      fold16(part[0], 0, 1, ml0, o40);
-      fold16(part[1], 0, 1, ml1, o41);
-    } else {
-#pragma unroll
-      for (int q = 0; q < kFoldItems; ++q) {
-        if (q >= n_items) break;
-        const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-        if (item >= items || sub >= S) continue;
-        const int g = item >> 5, c = item & 31;
-        for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
-          float2 ml[16];
-          float4_t o4[16];
-          load16(s0, S, g, c, ml, o4);
-          fold16(part[q], s0, S, ml, o4);
-        }
+    if (S == 2 && nsplit <= 32) {
+      // G = 3, 4 with one batch per partial: lane l of wave w folds partial
+      // l / 32 of output 32 w + l % 32, and the two partials of an output
+      // meet across the wave's halves (a lane exchange, no LDS round and no
+      // barrier), combined in the same order as below
+      const int wl = tid & 63, it = (tid >> 6) * 32 + (wl & 31), sb = wl >> 5;
+      const int ic = min(it, items - 1);
+      FinPart pt{-INFINITY, 0.0f, 0.0f, 0.0f, {0.f, 0.f, 0.f, 0.f}};
+      {
+        float2 ml[16];
+        float4_t o4[16];
+        load16(sb, 2, ic >> 5, ic & 31, ml, o4);
+        fold16(pt, sb, 2, ml, o4);
       }
-    }
-#pragma unroll
-    for (int q = 0; q < kFoldItems; ++q) {
-      if (q >= n_items) break;                       // uniform: every thread has the same n_items
-      const int item = n_items > 1 ? q * kThreads + tid : tid % items;
-      const bool active = item < items && sub < S;
-      __syncthreads();                               // the fold area / previous round's partials are free
-      s_lds.fin[tid] = part[q];
-      __syncthreads();
-      if (active && sub == 0) {
-        float mx = -INFINITY;
-        for (int w = 0; w < S; ++w) mx = fmaxf(mx, s_lds.fin[tid + w * items].m);
+      const float om = __shfl_xor(pt.m, 32), ol = __shfl_xor(pt.l, 32);
+      const float4_t oo = {__shfl_xor(pt.o[0], 32), __shfl_xor(pt.o[1], 32), __shfl_xor(pt.o[2], 32),
+                           __shfl_xor(pt.o[3], 32)};
+      if (sb == 0 && it < items) {
+        float mx = fmaxf(fmaxf(-INFINITY, pt.m), om);
         float lt = 0.0f;
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
         if (mx != -INFINITY) {
-          for (int w = 0; w < S; ++w) {
-            const FinPart& pw = s_lds.fin[tid + w * items];
-            combine_step(mx, lt, acc, pw.m, pw.l, pw.o);
+          combine_step(mx, lt, acc, pt.m, pt.l, pt.o);
+          combine_step(mx, lt, acc, om, ol, oo);
+        }
+        finish(it, mx, lt, acc);
+      }
+    } else {
+      if (n_items == 2 && nsplit <= 16) {
+        // G > 8 with one batch per output: both outputs' loads in one round
+        // (the same folds as the loop below, in the same order)
+        const int i1 = min(kThreads + tid, items - 1);
+        float2 ml0[16], ml1[16];
+        float4_t o40[16], o41[16];
+        load16(0, 1, tid >> 5, tid & 31, ml0, o40);
+        load16(0, 1, i1 >> 5, i1 & 31, ml1, o41);
+        fold16(part[0], 0, 1, ml0, o40);
+        fold16(part[1], 0, 1, ml1, o41);
+      } else {
+#pragma unroll
+        for (int q = 0; q < kFoldItems; ++q) {
+          if (q >= n_items) break;
+          const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+          if (item >= items || sub >= S) continue;
+          const int g = item >> 5, c = item & 31;
+          for (int s0 = sub; s0 < nsplit; s0 += 16 * S) {
+            float2 ml[16];
+            float4_t o4[16];
+            load16(s0, S, g, c, ml, o4);
+            fold16(part[q], s0, S, ml, o4);
           }
         }
-        finish(item, mx, lt, acc);
+      }
+#pragma unroll
+      for (int q = 0; q < kFoldItems; ++q) {
+        if (q >= n_items) break;                       // uniform: every thread has the same n_items
+        const int item = n_items > 1 ? q * kThreads + tid : tid % items;
+        const bool active = item < items && sub < S;
+        __syncthreads();                               // the fold area / previous round's partials are free
+        s_lds.fin[tid] = part[q];
+        __syncthreads();
+        if (active && sub == 0) {
+          float mx = -INFINITY;
+          for (int w = 0; w < S; ++w) mx = fmaxf(mx, s_lds.fin[tid + w * items].m);
+          float lt = 0.0f;
+          float4_t acc = {0.f, 0.f, 0.f, 0.f};
+          if (mx != -INFINITY) {
+            for (int w = 0; w < S; ++w) {
+              const FinPart& pw = s_lds.fin[tid + w * items];
+              combine_step(mx, lt, acc, pw.m, pw.l, pw.o);
+            }
+          }
+          finish(item, mx, lt, acc);
+        }
       }
     }
     if (merger) step_store<kKB, kVB>(a, u, t_step, lane, step_in);
