@@ -38,6 +38,11 @@ CASES = [
     ("tiny", {"W": 0, "rho": 0.0}),     # strict K4V4 (dequantise-then-attend)
     ("tiny", {"rho": 1.0}),             # full precision
     ("llama31_8b", {"L": 700, "W": 1000}),   # window covers the prefix
+    ("tiny", {"Hq": 2}),                # G = 1: eight partials per output in the fold
+    ("tiny", {"Hq": 4}),                # G = 2: four
+    ("tiny", {"Hq": 6}),                # G = 3: two, met by a lane exchange
+    ("tiny", {"Hq": 6, "L": 8192}),     # G = 3 with more than 32 splits: batches, LDS combine
+    ("llama31_8b", {"L": 4097, "Hq": 24}),   # G = 3 at 8 KV heads
 ]
 
 

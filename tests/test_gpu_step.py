@@ -105,7 +105,11 @@ def test_step_parity(name, over, kb, vb, mode):
 
 
 @pytest.mark.parametrize("name,over", [("tiny", {"L": 1500}), ("qwen3_32b", {"L": 900, "B": 2}),
-                                       ("tiny", {"L": 200, "W": 0})])
+                                       ("tiny", {"L": 200, "W": 0}),
+                                       # G = 1, 2, 3 (the step's own fold at G = 3 with at
+                                       # most 32 splits, the shared fold otherwise)
+                                       ("tiny", {"L": 1500, "Hq": 2}), ("tiny", {"L": 1500, "Hq": 4}),
+                                       ("tiny", {"L": 1500, "Hq": 6}), ("tiny", {"L": 8192, "Hq": 6})])
 def test_step_equals_merge_then_decode(name, over):
     wl = workload(name, **over)
     x = batch(wl, steps=T)
