@@ -1391,10 +1391,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       recs, static_cast<short>(0), nsplit * G * kPart * 4, kRsrcWord3);
 
-  // Both fold forms below run the same arithmetic on the same records in
-  // the same order (fold16 for each partial, then combine over the S
-  // partials), so a fused step's output equals the plain decode's bit for
-  // bit.
+  // Every fold form below runs the same arithmetic on the same records in
+  // the same order (fold16 for each partial, then combine_step over the S
+  // partials in index order), so the outputs do not depend on the form: a
+  // fused step's equal the plain decode's bit for bit.
   // fold16: partial pt takes 16 records (split indices s0, s0 + S, ...; past
   // nsplit masked) into its running state
   auto fold16 = [&](FinPart& pt, int s0, int S, const float2 (&ml)[16], const float4_t (&o4)[16]) {
