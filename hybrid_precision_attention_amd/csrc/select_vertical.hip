@@ -1431,6 +1431,9 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
           const uint32_t key = from_regs ? keys[k] : order_key(sc[min(i, n - 1)]);
           const bool t = i < n && key >= tcmp;
           if (kCut && t) tmin = min(tmin, key);
+          // the flag is known here (no tie is ranked): one byte a key, 64
+          // consecutive bytes a wave
+          if (i < a.L) flag[i] = t ? 1 : 0;
           const uint64_t b = __ballot(t);
           wa = write_lane<2 * k>(wa, static_cast<uint32_t>(b));
           wa = write_lane<2 * k + 1>(wa, static_cast<uint32_t>(b >> 32));
@@ -1483,22 +1486,26 @@ __global__ __launch_bounds__(kTopThreads) void topk_kernel(SelArgs a) {
       ++o;
     }
     base += tot_t;
-    eq32[tid] = take;                    // the taken bitmap, for the flags
-    __syncthreads();
-    if (flags4 && seg + kSeg <= a.L) {
-      // four positions a store: flag word q = positions seg + 4q .. + 3
+    // the flags, unless the comparisons above already wrote them
+    const bool flags_done = k_want > 0 && eq_all;
+    if (!flags_done) {
+      eq32[tid] = take;                    // the taken bitmap, for the flags
+      __syncthreads();
+      if (flags4 && seg + kSeg <= a.L) {
+        // four positions a store: flag word q = positions seg + 4q .. + 3
 #pragma unroll
-      for (int k = 0; k < kKeysPerThread / 4; ++k) {
-        const int q = tid + k * kTopThreads;
-        const uint32_t x = (eq32[q >> 3] >> (4 * (q & 7))) & 0xFu;
-        const uint32_t w = (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
-        reinterpret_cast<uint32_t*>(flag + seg)[q] = w;
-      }
-    } else {
+        for (int k = 0; k < kKeysPerThread / 4; ++k) {
+          const int q = tid + k * kTopThreads;
+          const uint32_t x = (eq32[q >> 3] >> (4 * (q & 7))) & 0xFu;
+          const uint32_t w = (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21);
+          reinterpret_cast<uint32_t*>(flag + seg)[q] = w;
+        }
+      } else {
 #pragma unroll 4
-      for (int k = 0; k < kKeysPerThread; ++k) {
-        const int pl = tid + k * kTopThreads;
-        if (seg + pl < a.L) flag[seg + pl] = static_cast<uint8_t>((eq32[pl >> 5] >> (pl & 31)) & 1u);
+        for (int k = 0; k < kKeysPerThread; ++k) {
+          const int pl = tid + k * kTopThreads;
+          if (seg + pl < a.L) flag[seg + pl] = static_cast<uint8_t>((eq32[pl >> 5] >> (pl & 31)) & 1u);
+        }
       }
     }
     __syncthreads();                     // before the next segment reuses the bitmaps
