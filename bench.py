@@ -52,7 +52,7 @@ PEAK_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0
 PEAK_I8_TOPS = 5000.0
 REFRESH = 64
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_traffic*.txt")
 
 
 def parse():
@@ -102,24 +102,26 @@ def graph_upload(g, torch):
 
 
 def load_traffic(wl_name, B):
-    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
-    or None when they were taken on another kernel source or workload."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    kv = {}
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            if "=" in line and not line.startswith("#"):
-                k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != src_hash():
-        return None
-    if kv.get("workload") != wl_name or int(kv.get("B", -1)) != B:
-        return None
-    try:
-        return float(kv["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs
+    (profiles/decode_traffic*.txt), or None when none was taken on this
+    kernel source and workload."""
+    import glob
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_sha256_16") != src_hash():
+            continue
+        if kv.get("workload") != wl_name or int(kv.get("B", -1)) != B:
+            continue
+        try:
+            return float(kv["traffic_bytes_per_launch"])
+        except (KeyError, ValueError):
+            return None
+    return None
 
 
 def main():
@@ -550,7 +552,15 @@ def decode_sweep(H, torch, workload, Bs=(1, 4, 16, 32)):
     L = 32768, W = 128, rho = 5 %): decode launches only, caches built on the
     device from bf16-rounded N(0,1) keys and values (timing inputs; parity is
     covered by the tests), each then holding one staged token as in a step."""
-    return [decode_point(H, torch, workload, B) for B in Bs]
+    pts = [decode_point(H, torch, workload, B) for B in Bs]
+    for p in pts:
+        # HBM bytes of the launch from the committed counter runs, where one
+        # was taken at this batch on the current decode source
+        t = load_traffic("qwen3_8b", p["B"])
+        if t is not None:
+            p["traffic"] = t
+            p["traffic_over_algorithmic"] = round(t / p["bytes"], 4)
+    return pts
 
 
 def width_sweep(H, torch, workload, points=((1, 8, 8), (1, 4, 2), (1, 2, 4), (32, 8, 8), (32, 4, 2), (32, 2, 4))):
