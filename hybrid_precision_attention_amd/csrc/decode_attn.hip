@@ -11,12 +11,14 @@
 // slots in 32-token blocks and its FP16 sequence (vertical lines, window
 // slots, staging) in 32-token blocks; of the unit's nsplit * 4 waves, each
 // takes a contiguous range of K4V4 blocks and every (nsplit * 4)-th FP16
-// block, sized so that every wave streams about the same bytes (wave_work).  Workgroups are four waves, so that two fit
-// on a CU at the register count of the scan and one's merge and ramp-up
-// overlap the other's streaming.  Each workgroup merges its four waves'
-// (max, sum, output) states through LDS into one partial record; the last
-// workgroup of the unit to arrive (an atomic counter in the workspace) merges
-// the unit's records by log-sum-exp and writes out/lse.
+// block, sized so that every wave streams about the same bytes (wave_work).
+// Workgroups are four waves, one per SIMD; the host's split plan puts one
+// workgroup on each CU for the G <= 4 scan at 4- and 8-bit widths and up to
+// two for the others (the scan's register count allows two).  Each workgroup
+// merges its four waves' (max, sum, output) states through LDS into one
+// partial record; the last workgroup of the unit to arrive (an atomic
+// counter in the workspace) merges the unit's records by log-sum-exp and
+// writes out/lse.
 //
 // Per 32-token block a wave runs, for the G query heads of the unit (padded
 // to 16):  S = K Q^T with two 16-token tiles x four k-steps of
