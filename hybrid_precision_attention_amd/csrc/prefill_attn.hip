@@ -214,6 +214,37 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, int
   }
 }
 
+// A far tile holds 64 keys that all exist (it ends before the workgroup's
+// first query), so its loads need no position test: each thread keeps its
+// byte offsets inside a tile for the whole loop, and only the tile's base
+// address, the same for every lane, moves from one tile to the next.
+struct FarOffsets {
+  uint32_t kc;   // INT8 codes: key tid / 4, bytes 32 (tid % 4) ..
+  uint32_t v;    // values: key 4 (tid / 16), dims 8 (tid % 16) .. (3 more keys at +256 B)
+};
+
+__device__ __forceinline__ FarOffsets far_offsets() {
+  const uint32_t tid = threadIdx.x;
+  return {(tid >> 2) * kD + 32 * (tid & 3), ((tid >> 4) * 4 * kD + 8 * (tid & 15)) * 2};
+}
+
+__device__ __forceinline__ void load_far(TileRegs& r, const PrefillArgs& a, int64_t u, int base,
+                                         const FarOffsets& o) {
+  const int64_t row0 = u * a.L + base;
+  const int tid = threadIdx.x;
+  if (tid < kTile) {
+    r.pos = base + tid;
+    r.sk = a.sk[row0 + tid];
+    r.vl = a.flag ? a.flag[row0 + tid] : 0;
+  }
+  const char* kc = reinterpret_cast<const char*>(a.k8 + row0 * kD) + o.kc;
+  r.kc[0] = ld16(kc);
+  r.kc[1] = ld16(kc + 16);
+  const char* v = reinterpret_cast<const char*>(a.v + row0 * kD) + o.v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r.v[e] = ld16(v + 2 * kD * e);
+}
+
 __device__ __forceinline__ void store_tile(TileBuf& sh, uint16_t (*kf)[kKP], const TileRegs& r, int kind) {
   const int tid = threadIdx.x;
   if (tid < kTile) {
@@ -459,14 +490,15 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
   // (buffer t % 2 is read while buffer (t + 1) % 2 is filled: it was last
   // read in the previous iteration, before that iteration's barrier)
   TileRegs tr;
+  const FarOffsets fo = far_offsets();
   if (n_far > 0) {
-    load_tile(tr, a, u, kFar, 0, kTile, nullptr);
+    load_far(tr, a, u, 0, fo);
     store_tile(sh.tb[0], sh.kf, tr, kFar);
   }
   __syncthreads();
   for (int t = 0; t < n_far; ++t) {
     const bool more = t + 1 < n_far;
-    if (more) load_tile(tr, a, u, kFar, (t + 1) * kTile, kTile, nullptr);
+    if (more) load_far(tr, a, u, (t + 1) * kTile, fo);
     far_tile(ws, sh.tb[t & 1], lane);
     if (more) store_tile(sh.tb[(t + 1) & 1], sh.kf, tr, kFar);
     __syncthreads();
