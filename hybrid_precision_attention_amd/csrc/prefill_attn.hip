@@ -142,18 +142,20 @@ struct PrefillArgs {
 
 constexpr int kCP = kD + 16;       // INT8 code tile row pitch in bytes
 
-struct TileBuf {
+// 16-byte aligned, so that 16-byte LDS accesses reach every field with the
+// instruction's own offset (a 4-byte read pair can only reach 1 KiB)
+struct alignas(16) TileBuf {
   uint16_t vt[kD][kVP];      // values, transposed: vt[dim][key]
   int8_t kc[kTile][kCP];     // INT8 key codes
-  float sk[kTile];           // key scales
-  float bias[kTile];         // -inf at a vertical line (its FP16 turn comes later), else 0
+  alignas(16) float sk[kTile];     // key scales
+  alignas(16) float bias[kTile];   // -inf at a vertical line (its FP16 turn comes later), else 0
   int32_t pos[kTile];        // key positions (-1: no key)
   uint8_t vl[kTile];         // vertical-line flags of the tile's keys
 };
 
 // Two tile buffers (the far tiles alternate between them, one barrier a
 // tile) and the FP16 keys of the near and line tiles.
-struct PrefillShared {
+struct alignas(16) PrefillShared {
   TileBuf tb[2];
   uint16_t kf[kTile][kKP];
 };
@@ -303,10 +305,10 @@ __device__ __forceinline__ float sum4(float x) {
 // operands for the two 32-key steps.
 __device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&y)[4][4], float scale,
                                               uint4 (&pb)[2]) {
-  float mx = -INFINITY;
+  // a chain of three-operand maxima (v_max3): two new values per instruction
+  float mx = fmaxf(y[0][0], y[0][1]);
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    mx = fmaxf(mx, fmaxf(fmaxf(y[kb][0], y[kb][1]), fmaxf(y[kb][2], y[kb][3])));
+  for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, y[e / 4][e % 4]), y[e / 4][e % 4 + 1]);
   mx = max4(mx) * scale;
   const float m_new = fmaxf(ws.m[cb], mx);
   const float mu = m_new == -INFINITY ? 0.0f : m_new;
@@ -402,13 +404,15 @@ __device__ __forceinline__ void far_tile(WaveState& ws, const TileBuf& sh, int l
   for (int cb = 0; cb < 2; ++cb) {
     float z[4][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      const float4_t s4 = *reinterpret_cast<const float4_t*>(&sh.sk[16 * kb + 4 * g]);
+      const float4_t b4 = *reinterpret_cast<const float4_t*>(&sh.bias[16 * kb + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * kb + 4 * g + r;
         const float acc = static_cast<float>(__builtin_bit_cast(int4_t, si[cb][kb])[r]);
-        z[kb][r] = fmaf(acc, sh.sk[j], sh.bias[j]);      // logit / qs2
+        z[kb][r] = fmaf(acc, s4[r], b4[r]);      // logit / qs2 of key 16 kb + 4 g + r
       }
+    }
     softmax_block(ws, cb, z, ws.qs2[cb], pb[cb]);
   }
   pv_tile(ws, sh, pb, lane);
