@@ -500,12 +500,18 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_attn_kernel(PrefillArgs 
     store_tile(sh.tb[0], sh.kf, tr, kFar);
   }
   __syncthreads();
-  for (int t = 0; t < n_far; ++t) {
+  // (two tiles an iteration, so that each buffer's LDS addresses are the
+  // instructions' constant offsets)
+  auto far_step = [&](int t, const TileBuf& cur, TileBuf& nxt) {
     const bool more = t + 1 < n_far;
     if (more) load_far(tr, a, u, (t + 1) * kTile, fo);
-    far_tile(ws, sh.tb[t & 1], lane);
-    if (more) store_tile(sh.tb[(t + 1) & 1], sh.kf, tr, kFar);
+    far_tile(ws, cur, lane);
+    if (more) store_tile(nxt, sh.kf, tr, kFar);
     __syncthreads();
+  };
+  for (int t = 0; t < n_far; t += 2) {
+    far_step(t, sh.tb[0], sh.tb[1]);
+    if (t + 1 < n_far) far_step(t + 1, sh.tb[1], sh.tb[0]);
   }
 
   // near-diagonal tiles and the vertical lines, with the FP16 queries
