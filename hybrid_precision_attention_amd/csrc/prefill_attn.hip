@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kTile = 64;          // keys per tile
 constexpr int kKP = kD + 8;        // K tile row pitch in halves (272-byte rows)
-constexpr int kVP = kTile + 4;     // V^T row pitch in halves (136-byte rows)
+constexpr int kVP = kTile + 8;     // V^T row pitch in halves (144-byte rows, 16-byte aligned)
 constexpr int kQW = 32;            // query positions per wave
 constexpr int kPThreads = 256;
 
@@ -142,10 +142,19 @@ struct PrefillArgs {
 
 constexpr int kCP = kD + 16;       // INT8 code tile row pitch in bytes
 
+// Column of key k of a tile in the V^T rows: within each 32-key half kk the
+// keys 4 g + r and 16 + 4 g + r (r = 0..3) sit side by side at 8 g + r and
+// 8 g + 4 + r, which is the key order of one lane's P^T operand, so the
+// matching V^T operand is a single 16-byte read.  Four consecutive keys 4 q
+// .. 4 q + 3 stay consecutive, at vslot(4 q).
+__host__ __device__ constexpr int vslot(int k) {
+  return ((k >> 5) << 5) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 // 16-byte aligned, so that 16-byte LDS accesses reach every field with the
 // instruction's own offset (a 4-byte read pair can only reach 1 KiB)
 struct alignas(16) TileBuf {
-  uint16_t vt[kD][kVP];      // values, transposed: vt[dim][key]
+  uint16_t vt[kD][kVP];      // values, transposed: vt[dim][vslot(key)]
   int8_t kc[kTile][kCP];     // INT8 key codes
   alignas(16) float sk[kTile];     // key scales
   alignas(16) float bias[kTile];   // -inf at a vertical line (its FP16 turn comes later), else 0
@@ -170,8 +179,9 @@ __device__ __forceinline__ float4_t mfma_i8(uint4 a, uint4 b, float4_t c_as_int)
 }
 
 // The global half of staging a tile, into registers: thread t takes key t / 4
-// (a quarter row: 32 dims of K, 32 codes) and, for V, keys 4 (t / 16) .. + 3
-// at dims 8 (t % 16) .. + 7.
+// (a quarter row: 32 dims of K, 32 codes) and, for V, keys 4 (t % 16) .. + 3
+// at dims 8 (t / 16) .. + 7 (so the 16 lanes of one LDS store cycle write one
+// V^T row's 16 four-key groups).
 struct TileRegs {
   uint4 kf[4];
   uint4 kc[2];
@@ -208,7 +218,7 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, int
     for (int i = 0; i < 2; ++i)
       r.kc[i] = p >= 0 ? *reinterpret_cast<const uint4*>(src + 16 * i) : make_uint4(0, 0, 0, 0);
   }
-  const int kq = tid >> 4, oct = tid & 15;
+  const int kq = tid & 15, oct = tid >> 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = slot_pos(kind, base, n, 4 * kq + e, list);
@@ -222,12 +232,12 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PrefillArgs& a, int
 // address, the same for every lane, moves from one tile to the next.
 struct FarOffsets {
   uint32_t kc;   // INT8 codes: key tid / 4, bytes 32 (tid % 4) ..
-  uint32_t v;    // values: key 4 (tid / 16), dims 8 (tid % 16) .. (3 more keys at +256 B)
+  uint32_t v;    // values: key 4 (tid % 16), dims 8 (tid / 16) .. (3 more keys at +256 B)
 };
 
 __device__ __forceinline__ FarOffsets far_offsets() {
   const uint32_t tid = threadIdx.x;
-  return {(tid >> 2) * kD + 32 * (tid & 3), ((tid >> 4) * 4 * kD + 8 * (tid & 15)) * 2};
+  return {(tid >> 2) * kD + 32 * (tid & 3), ((tid & 15) * 4 * kD + 8 * (tid >> 4)) * 2};
 }
 
 __device__ __forceinline__ void load_far(TileRegs& r, const PrefillArgs& a, int64_t u, int base,
@@ -264,7 +274,7 @@ __device__ __forceinline__ void store_tile(TileBuf& sh, uint16_t (*kf)[kKP], con
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&sh.kc[j][32 * qt + 16 * i]) = r.kc[i];
   }
-  const int kq = tid >> 4, oct = tid & 15;
+  const int kq = tid & 15, oct = tid >> 4, c0 = vslot(4 * kq);
   const uint32_t w[4][4] = {{r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w}, {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w},
                             {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w}, {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w}};
 #pragma unroll
@@ -273,8 +283,8 @@ __device__ __forceinline__ void store_tile(TileBuf& sh, uint16_t (*kf)[kKP], con
                                 __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u));
     const uint2 hi = make_uint2(__builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u),
                                 __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u));
-    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m][4 * kq]) = lo;
-    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m + 1][4 * kq]) = hi;
+    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m][c0]) = lo;
+    *reinterpret_cast<uint2*>(&sh.vt[8 * oct + 2 * m + 1][c0]) = hi;
   }
 }
 
@@ -341,7 +351,8 @@ __device__ __forceinline__ void softmax_block(WaveState& ws, int cb, float (&y)[
 }
 
 // O^T += V^T P^T; the V^T operand of dims 16 db + lane % 16 holds the same
-// key order as the P^T operand (keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g + r)
+// key order as the P^T operand (keys 32 kk + 4 g + r, then 32 kk + 16 + 4 g +
+// r), 16 bytes at vslot(32 kk + 4 g) = 32 kk + 8 g
 __device__ __forceinline__ void pv_tile(WaveState& ws, const TileBuf& sh, const uint4 (&pb)[2][2],
                                         int lane) {
   const int g = lane >> 4;
@@ -349,10 +360,7 @@ __device__ __forceinline__ void pv_tile(WaveState& ws, const TileBuf& sh, const 
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* row = sh.vt[16 * db + (lane & 15)] + 32 * kk + 4 * g;
-      const uint2 lo = *reinterpret_cast<const uint2*>(row);
-      const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
-      const half8_t va = as_h8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+      const half8_t va = as_h8(*reinterpret_cast<const uint4*>(sh.vt[16 * db + (lane & 15)] + 32 * kk + 8 * g));
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) ws.o[cb][db] = mfma16(va, as_h8(pb[cb][kk]), ws.o[cb][db]);
     }
